@@ -1,0 +1,143 @@
+"""Python front end of the fp64 CPU oracle (``gla_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may use this module; the GPU library and its binding never
+import it. It takes numpy arrays, widens bf16 bit patterns to fp32 exactly,
+and calls the plain token-by-token fp64 recurrence of the Laplace 3B /
+Trainium2 page, section "GLA mixer" (S_t = lambda_h S_{t-1} + k_t^T v_t,
+o_t = scale * q_t S_t, readout after the update).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gla_oracle.c with gcc into oracle/liboracle.so (plain C11, -O2,
+    generic x86-64 so the same file runs on any host of the image)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math",
+             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.oracle_gla_varlen.argtypes = [
+            ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            P, P, P, P, ctypes.c_double, P, P, P, ctypes.c_int]
+        lib.oracle_gla_varlen.restype = ctypes.c_int
+        lib.oracle_gla_decode.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            P, P, P, P, ctypes.c_double, P, P, ctypes.c_int]
+        lib.oracle_gla_decode.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    """Threads for the oracle: OMP_NUM_THREADS when set, else the visible
+    cores capped at 16 (a GPU machine's CPU share)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def widen(x) -> np.ndarray:
+    """Exact widening to fp32: a uint16 array is taken as bf16 bit patterns
+    (bits << 16); float arrays are cast to fp32 (they must hold fp32 values)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def gla_varlen(cu_seqlens, q, k, v, decay, scale=1.0, s0=None,
+               want_o=True, want_state=True, threads=None):
+    """Packed variable-length recurrence in fp64.
+
+    q, k: [total, H, dk]; v: [total, H, dv] (fp32 values or bf16 bits as
+    uint16); cu_seqlens: [N+1] ints; decay: [H] fp32; s0: [N, H, dk, dv]
+    (fp32, or fp64 for a state carried out of an earlier oracle call) or
+    None. Returns (o [total, H, dv] fp64 or None, s_final [N, H, dk, dv]
+    fp64 or None).
+    """
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    q, k, v = widen(q), widen(k), widen(v)
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    if k.shape != (total, H, dk) or v.shape[:2] != (total, H) or cu[-1] != total:
+        raise ValueError("shape mismatch")
+    lam = np.ascontiguousarray(np.asarray(decay, dtype=np.float32))
+    if lam.shape != (H,):
+        raise ValueError("decay must be [H]")
+    s0a = None
+    if s0 is not None:
+        s0 = np.asarray(s0)
+        s0a = s0 if s0.dtype == np.float64 else widen(s0).astype(np.float64)
+        s0a = np.ascontiguousarray(s0a.reshape(N, H, dk, dv))
+    o = np.zeros((total, H, dv), np.float64) if want_o else None
+    sf = np.zeros((N, H, dk, dv), np.float64) if want_state else None
+    rc = _load().oracle_gla_varlen(
+        N, _ptr(cu), H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+        float(scale), _ptr(s0a), _ptr(o), _ptr(sf),
+        int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_varlen failed: %d" % rc)
+    return o, sf
+
+
+def gla_fwd(q, k, v, decay, scale=1.0, s0=None, want_o=True, want_state=True,
+            threads=None):
+    """Fixed-length batch [B, T, H, d] through the same recurrence
+    (sequence b owns tokens b*T .. b*T+T-1 of the flattened batch)."""
+    q, k, v = widen(q), widen(k), widen(v)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    cu = np.arange(B + 1, dtype=np.int64) * T
+    o, sf = gla_varlen(cu, q.reshape(B * T, H, dk), k.reshape(B * T, H, dk),
+                       v.reshape(B * T, H, dv), decay, scale, s0,
+                       want_o, want_state, threads)
+    return (None if o is None else o.reshape(B, T, H, dv)), sf
+
+
+def gla_decode(q, k, v, decay, state, scale=1.0, threads=None):
+    """One decode step. q, k: [N, H, dk]; v: [N, H, dv]; state: [N, H, dk, dv]
+    fp64, updated IN PLACE. Returns o [N, H, dv] fp64."""
+    q, k, v = widen(q), widen(k), widen(v)
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if state.dtype != np.float64 or not state.flags.c_contiguous or \
+            state.shape != (N, H, dk, dv):
+        raise ValueError("state must be a C-contiguous fp64 [N,H,dk,dv] array")
+    lam = np.ascontiguousarray(np.asarray(decay, dtype=np.float32))
+    o = np.zeros((N, H, dv), np.float64)
+    rc = _load().oracle_gla_decode(
+        N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), float(scale),
+        _ptr(state), _ptr(o), int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_decode failed: %d" % rc)
+    return o
