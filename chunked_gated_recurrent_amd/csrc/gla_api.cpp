@@ -1,0 +1,353 @@
+// gla_api.cpp -- the C ABI declared in include/gla.h: host-side validation,
+// work planning and kernel dispatch. Validation and planning make no HIP
+// call, so every error path is testable on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "gla.h"
+#include "gla_internal.h"
+
+using namespace gla;
+
+namespace {
+
+constexpr long long kMaxTokens = 0x7fffffffLL;  // token indices are int32 on device
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+gla_status check_common(int dt, int H, int dk, int dv, int chunk) {
+  if (dt != GLA_F32 && dt != GLA_BF16) return GLA_ERR_DTYPE;
+  if (H < 1 || dk < 1 || dv < 1) return GLA_ERR_SHAPE;
+  if (H > GLA_MAX_HEADS) return GLA_ERR_UNSUPPORTED;
+  if (dk % 16 != 0 || dv % 16 != 0 || dk > 128 || dv > 256) return GLA_ERR_UNSUPPORTED;
+  if (chunk != 0 && chunk != 32 && chunk != 64 && chunk != 128) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
+gla_status check_decay(const float *d, int H) {
+  if (!d) return GLA_ERR_NULL;
+  for (int h = 0; h < H; ++h) {
+    const float x = d[h];
+    if (!isfinite(x) || !(x > 0.0f) || x > 1.0f) return GLA_ERR_DECAY;
+  }
+  return GLA_OK;
+}
+
+bool misaligned(const void *p) { return p && ((uintptr_t)p & 15u) != 0; }
+
+// [a, a+na) and [b, b+nb) share a byte (empty ranges never overlap)
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Workgroups the forward should have in flight before it pays for splitting
+// sequences into time segments (two per compute unit on a 256-CU part).
+int target_workgroups() {
+  const char *e = getenv("GLA_TARGET_WGS");
+  if (e && *e) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 1 && v <= (1L << 20)) return (int)v;
+  }
+  return 256;
+}
+
+struct HostPlan {
+  Plan p;
+  bool fast;
+  int chunk;      // tokens per chunk the kernels use
+  int ndt;        // dv tiles per (item, head)
+  bool segmented; // at least one sequence has more than one item
+  size_t off_index, off_items, off_slots, ws_bytes;
+};
+
+void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk) {
+  memset(&hp, 0, sizeof(hp));
+  hp.fast = fast_path_ok(dt, dk, dv, chunk);
+  hp.chunk = hp.fast ? 64 : generic_chunk(chunk);
+  hp.ndt = hp.fast ? dv / fast_dv_tile(dv) : dv / 16;
+}
+
+HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk) {
+  HostPlan hp;
+  base_plan(hp, dt, dk, dv, chunk);
+  const int C = hp.chunk;
+  const long long chains = (long long)B * H * hp.ndt;
+  const long long target = target_workgroups();
+  int G = 1;
+  if (T > 2 * C && chains < target) {
+    const long long want = (target + chains - 1) / chains;
+    const long long maxg = (T + 2 * C - 1) / (2 * C);  // segments of >= 2 chunks
+    G = (int)(want < maxg ? want : maxg);
+    if (G < 1) G = 1;
+  }
+  int seg = T > 0 ? (T + G - 1) / G : C;
+  seg = ((seg + C - 1) / C) * C;
+  G = T > 0 ? (T + seg - 1) / seg : 1;
+  Plan &p = hp.p;
+  p.mode = kPlanFixed;
+  p.n_seq = B;
+  p.T = T;
+  p.total_T = (int)((long long)B * T);
+  p.seg_len = seg;
+  p.G = G;
+  p.max_items = B * G;
+  hp.segmented = G > 1;
+  hp.off_slots = 0;
+  hp.ws_bytes = hp.segmented ? (size_t)B * G * H * dk * dv * sizeof(float) : 0;
+  return hp;
+}
+
+HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk) {
+  HostPlan hp;
+  base_plan(hp, dt, dk, dv, chunk);
+  const int C = hp.chunk;
+  const long long chains = (long long)N * H * hp.ndt;
+  const long long target = target_workgroups();
+  Plan &p = hp.p;
+  p.n_seq = N;
+  p.total_T = total_T;
+  const long long avg = N > 0 ? (long long)total_T / N : 0;
+  if (chains >= target || avg <= 2 * C) {
+    p.mode = kPlanVarlenDirect;
+    p.max_items = N;
+    p.seg_len = total_T > 0 ? total_T : C;
+    p.G = 1;
+    hp.segmented = false;
+    hp.ws_bytes = 0;
+    return hp;
+  }
+  const long long want = (target + chains - 1) / chains;  // segments per sequence
+  long long seg = (avg + want - 1) / want;
+  if (seg < 2 * C) seg = 2 * C;
+  seg = ((seg + C - 1) / C) * C;
+  p.mode = kPlanVarlenItems;
+  p.seg_len = (int)seg;
+  p.G = 0;
+  p.max_items = (int)(N + total_T / seg);
+  hp.segmented = true;
+  hp.off_index = 0;
+  hp.off_items = align256(sizeof(int32_t) * ((size_t)N + 2));
+  hp.off_slots = hp.off_items + align256(sizeof(int4) * (size_t)p.max_items);
+  hp.ws_bytes = hp.off_slots + (size_t)p.max_items * H * dk * dv * sizeof(float);
+  return hp;
+}
+
+Decay make_decay(const float *d, int H) {
+  Decay dec;
+  memset(&dec, 0, sizeof(dec));
+  for (int h = 0; h < H; ++h) dec.lam[h] = d[h];
+  return dec;
+}
+
+// Launch the planned forward: [planner] -> [local end states -> combine] ->
+// outputs -> [final gather].
+gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
+                       void *workspace, hipStream_t s) {
+  Plan p = hp.p;
+  (void)hipGetLastError();  // report only this call's launch errors
+  if (hp.segmented) {
+    char *ws = (char *)workspace;
+    a.slots = (float *)(ws + hp.off_slots);
+    if (p.mode == kPlanVarlenItems) {
+      p.index = (const int32_t *)(ws + hp.off_index);
+      p.items = (const int4 *)(ws + hp.off_items);
+      if (launch_planner(p, (int32_t *)(ws + hp.off_index), (int4 *)(ws + hp.off_items), s) != hipSuccess)
+        return GLA_ERR_HIP;
+    }
+    if (launch_fwd(dt, hp.fast, true, p, a, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
+    if (launch_combine(p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
+    // In place (s_final == s0): the first segment reads s0 while the last
+    // writes the final state, so the last writes its own slot and a gather
+    // copies it out afterwards.
+    a.final_in_slot = (a.s_final && a.s_final == a.s0) ? 1 : 0;
+  }
+  if (launch_fwd(dt, hp.fast, false, p, a, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
+  if (a.final_in_slot && launch_final_gather(p, a, s) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int gla_abi_version(void) { return GLA_ABI_VERSION; }
+
+const char *gla_status_str(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "ok";
+    case GLA_ERR_NULL: return "a required pointer is NULL";
+    case GLA_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case GLA_ERR_DTYPE: return "unknown dtype";
+    case GLA_ERR_DECAY: return "a decay is not finite or not in (0, 1]";
+    case GLA_ERR_ALIAS: return "an output overlaps an input it may not overlap";
+    case GLA_ERR_UNSUPPORTED: return "unsupported head count, head size or chunk";
+    case GLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GLA_ERR_HIP: return "a HIP kernel launch failed";
+    case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+size_t gla_chunk_fwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
+                                     int dv, int chunk) {
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || B < 1 || T < 0 ||
+      (long long)B * T > kMaxTokens)
+    return 0;
+  return plan_fixed(dt, B, T, H, dk, dv, chunk).ws_bytes;
+}
+
+gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                         int chunk, const void *q, const void *k,
+                         const void *v, const float *decay_host, float scale,
+                         const float *s0, void *o, float *s_final,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  if (B < 1 || T < 0 || (long long)B * T > kMaxTokens) return GLA_ERR_SHAPE;
+  if (!isfinite(scale)) return GLA_ERR_SHAPE;
+  st = check_decay(decay_host, H);
+  if (st != GLA_OK) return st;
+  const long long tok = (long long)B * T;
+  if (tok > 0 && (!q || !k || !v || !o)) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      misaligned(s0) || misaligned(s_final))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)tok * H * dk * es, nv = (size_t)tok * H * dv * es;
+  const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
+  if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
+      overlap(o, nv, s0, ns))
+    return GLA_ERR_ALIAS;
+  if (s_final) {
+    if (s_final != s0 && overlap(s_final, ns, s0, ns)) return GLA_ERR_ALIAS;
+    if (overlap(s_final, ns, q, nqk) || overlap(s_final, ns, k, nqk) ||
+        overlap(s_final, ns, v, nv) || overlap(s_final, ns, o, nv))
+      return GLA_ERR_ALIAS;
+  }
+  const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
+  if (hp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (overlap(workspace, hp.ws_bytes, q, nqk) || overlap(workspace, hp.ws_bytes, k, nqk) ||
+        overlap(workspace, hp.ws_bytes, v, nv) || overlap(workspace, hp.ws_bytes, o, nv) ||
+        overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns))
+      return GLA_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (tok == 0) {
+    if (s_final && s_final != s0) {
+      (void)hipGetLastError();
+      if (launch_state_fill(B, H, dk, dv, s0, s_final, s) != hipSuccess) return GLA_ERR_HIP;
+    }
+    return GLA_OK;
+  }
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
+  a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
+  return run_forward(dt, hp, a, make_decay(decay_host, H), workspace, s);
+}
+
+size_t gla_chunk_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,
+                                            int H, int dk, int dv, int chunk) {
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || N < 1 || total_T < 0)
+    return 0;
+  return plan_varlen(dt, N, total_T, H, dk, dv, chunk).ws_bytes;
+}
+
+gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
+                                int dk, int dv, int chunk,
+                                const int32_t *cu_seqlens, const void *q,
+                                const void *k, const void *v,
+                                const float *decay_host, float scale,
+                                const float *s0, void *o, float *s_final,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  if (N < 1 || total_T < 0 || N > (1 << 28)) return GLA_ERR_SHAPE;
+  if (!isfinite(scale)) return GLA_ERR_SHAPE;
+  st = check_decay(decay_host, H);
+  if (st != GLA_OK) return st;
+  if (!cu_seqlens) return GLA_ERR_NULL;
+  if (total_T > 0 && (!q || !k || !v || !o)) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      misaligned(s0) || misaligned(s_final) || ((uintptr_t)cu_seqlens & 3u))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)total_T * H * dk * es, nv = (size_t)total_T * H * dv * es;
+  const size_t ns = (size_t)N * H * dk * dv * sizeof(float);
+  const size_t ncu = sizeof(int32_t) * ((size_t)N + 1);
+  if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
+      overlap(o, nv, s0, ns) || overlap(o, nv, cu_seqlens, ncu))
+    return GLA_ERR_ALIAS;
+  if (s_final) {
+    if (s_final != s0 && overlap(s_final, ns, s0, ns)) return GLA_ERR_ALIAS;
+    if (overlap(s_final, ns, q, nqk) || overlap(s_final, ns, k, nqk) ||
+        overlap(s_final, ns, v, nv) || overlap(s_final, ns, o, nv) ||
+        overlap(s_final, ns, cu_seqlens, ncu))
+      return GLA_ERR_ALIAS;
+  }
+  const HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk);
+  if (hp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (overlap(workspace, hp.ws_bytes, q, nqk) || overlap(workspace, hp.ws_bytes, k, nqk) ||
+        overlap(workspace, hp.ws_bytes, v, nv) || overlap(workspace, hp.ws_bytes, o, nv) ||
+        overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns) ||
+        overlap(workspace, hp.ws_bytes, cu_seqlens, ncu))
+      return GLA_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (total_T == 0) {
+    if (s_final && s_final != s0) {
+      (void)hipGetLastError();
+      if (launch_state_fill(N, H, dk, dv, s0, s_final, s) != hipSuccess) return GLA_ERR_HIP;
+    }
+    return GLA_OK;
+  }
+  Plan p = hp.p;
+  p.cu = cu_seqlens;
+  HostPlan hq = hp;
+  hq.p = p;
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
+  a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
+  return run_forward(dt, hq, a, make_decay(decay_host, H), workspace, s);
+}
+
+gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
+                           const void *q, const void *k, const void *v,
+                           const float *decay_host, float scale, float *state,
+                           void *o, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, 0);
+  if (st != GLA_OK) return st;
+  if (N < 0 || (long long)N * H > kMaxTokens) return GLA_ERR_SHAPE;
+  if (!isfinite(scale)) return GLA_ERR_SHAPE;
+  st = check_decay(decay_host, H);
+  if (st != GLA_OK) return st;
+  if (N == 0) return GLA_OK;
+  if (!q || !k || !v || !o || !state) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(state))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)N * H * dk * es, nv = (size_t)N * H * dv * es;
+  const size_t ns = (size_t)N * H * dk * dv * sizeof(float);
+  if (overlap(state, ns, q, nqk) || overlap(state, ns, k, nqk) ||
+      overlap(state, ns, v, nv) || overlap(state, ns, o, nv) ||
+      overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv))
+    return GLA_ERR_ALIAS;
+  (void)hipGetLastError();
+  if (launch_decode(dt, N, H, dk, dv, q, k, v, make_decay(decay_host, H), scale,
+                    state, o, (hipStream_t)stream) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+}  // extern "C"

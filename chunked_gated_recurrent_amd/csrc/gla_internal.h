@@ -1,0 +1,73 @@
+// gla_internal.h -- types shared by the host dispatch (gla_api.cpp) and the
+// HIP kernels (gla_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+constexpr int kMaxHeads = 64;
+
+// Per-head decays, passed to kernels by value (256 bytes of kernel args).
+struct Decay {
+  float lam[kMaxHeads];
+};
+
+// How the token stream is cut into work items. An item is a contiguous token
+// range [t0, t1) of one sequence (a whole sequence, or one time segment of a
+// long one). Items of one sequence are consecutive; item i > first reads its
+// incoming state from slot i-1 of the workspace.
+enum PlanMode : int {
+  kPlanFixed = 0,         // B sequences of T tokens, G segments each (arithmetic)
+  kPlanVarlenDirect = 1,  // one item per packed sequence, bounds from cu_seqlens
+  kPlanVarlenItems = 2,   // items written to the workspace by the planner kernel
+};
+
+struct Plan {
+  int mode;
+  int n_seq;      // B or N
+  int T;          // fixed mode: tokens per sequence
+  int total_T;    // tokens in the packed arrays (bounds clamp)
+  int seg_len;    // tokens per segment (a multiple of the chunk)
+  int G;          // fixed mode: segments per sequence
+  int max_items;  // item slots covered by the launch grids
+  const int32_t *cu;     // varlen: [n_seq + 1] device
+  const int4 *items;     // kPlanVarlenItems: [max_items] {n, t0, t1, flags}
+  const int32_t *index;  // kPlanVarlenItems: [0] = item count, [1 + n] = first item of n
+};
+
+// Item flags
+constexpr int kFirstSeg = 1;
+constexpr int kLastSeg = 2;
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  const float *s0;
+  float *s_final;
+  float *slots;  // [max_items][H][dk][dv] fp32 or nullptr
+  float scale;
+  int H, dk, dv;
+  int final_in_slot;  // last segment writes its final state to its own slot
+};
+
+// ---- launchers (gla_kernels.hip) -------------------------------------------
+// All return the hipGetLastError() of their launches.
+bool fast_path_ok(int dt, int dk, int dv, int chunk);
+int fast_dv_tile(int dv);
+int generic_chunk(int chunk);
+hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items, hipStream_t s);
+hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
+                      const FwdArgs &a, const Decay &dec, int chunk,
+                      hipStream_t s);
+hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,
+                          hipStream_t s);
+hipError_t launch_final_gather(const Plan &p, const FwdArgs &a, hipStream_t s);
+hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
+                             const float *s0, float *s_final, hipStream_t s);
+hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
+                         const void *k, const void *v, const Decay &dec,
+                         float scale, float *state, void *o, hipStream_t s);
+
+}  // namespace gla

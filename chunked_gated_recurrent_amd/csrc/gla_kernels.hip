@@ -1,0 +1,967 @@
+// gla_kernels.hip -- HIP kernels of Simple GLA for gfx950 (MI355X).
+//
+// The recurrence (Laplace 3B / Trainium2 page, section "GLA mixer"):
+//     S_t = lambda_h S_{t-1} + k_t^T v_t,      o_t = scale * q_t S_t
+// computed chunkwise (same page, section "Challenge 1"). For a chunk of L
+// tokens starting from the carried state S_prev, with in-chunk positions
+// i, j = 0..L-1:
+//     P_ij  = (q_i . k_j) * lambda^(i-j)   if j <= i, else 0
+//     o_i   = scale * ( sum_j P_ij v_j  +  lambda^(i+1) q_i S_prev )
+//     S_new = lambda^L S_prev + sum_j lambda^(L-1-j) k_j^T v_j
+// which is the token recurrence regrouped exactly. Only the state carry is
+// sequential across chunks; for long sequences it is further split into time
+// segments whose local end states compose as affine maps
+//     S_in(g+1) = lambda^(len g) S_in(g) + U_g
+// (a scan over segments; U_g is the segment's end state from a zero start).
+//
+// Kernels:
+//   fwd_mfma   bf16, dk = 96: one workgroup (4 waves) per (item, head, dv
+//              tile); chunk tiles staged in LDS; all four contractions on
+//              v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the state
+//              tile lives in registers as MFMA accumulators across chunks.
+//   fwd_valu   any supported shape, fp32 or bf16 inputs, fp32 arithmetic
+//              on the vector ALUs (the fp32 path and the fallback).
+//   planner    varlen: cuts packed sequences into items on the device.
+//   combine    scan of segment end states.
+//   decode     one token per sequence: streams the fp32 state from HBM once
+//              (read-modify-write), float4 per lane, readout reduced in LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gla_internal.h"
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+// lambda^n by binary exponentiation in fp64, rounded once to fp32.
+__device__ __forceinline__ float pow_f64(float lam, long long n) {
+  double r = 1.0, x = (double)lam;
+  while (n > 0) {
+    if (n & 1) r *= x;
+    x *= x;
+    n >>= 1;
+  }
+  return (float)r;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+struct Item {
+  int n, t0, t1, flags;
+};
+
+// Item `idx` of the plan; false when idx is past the last item.
+__device__ __forceinline__ bool load_item(const Plan &p, int idx, Item &it) {
+  if (p.mode == kPlanFixed) {
+    if (idx >= p.max_items) return false;
+    const int n = idx / p.G;
+    const int g = idx - n * p.G;
+    const int base = n * p.T;
+    it.n = n;
+    it.t0 = base + g * p.seg_len;
+    it.t1 = min(it.t0 + p.seg_len, base + p.T);
+    it.flags = (g == 0 ? kFirstSeg : 0) | (g == p.G - 1 ? kLastSeg : 0);
+    return true;
+  }
+  if (p.mode == kPlanVarlenDirect) {
+    if (idx >= p.n_seq) return false;
+    const int a = clampi(p.cu[idx], 0, p.total_T);
+    const int b = clampi(p.cu[idx + 1], a, p.total_T);
+    it.n = idx;
+    it.t0 = a;
+    it.t1 = b;
+    it.flags = kFirstSeg | kLastSeg;
+    return true;
+  }
+  const int cnt = min(p.index[0], p.max_items);
+  if (idx >= cnt) return false;
+  const int4 x = p.items[idx];
+  it.n = x.x;
+  it.t0 = x.y;
+  it.t1 = x.z;
+  it.flags = x.w;
+  return true;
+}
+
+// Sequence n's item range [first, last) in the plan.
+__device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
+                                          int &last) {
+  if (p.mode == kPlanFixed) {
+    first = n * p.G;
+    last = first + p.G;
+  } else if (p.mode == kPlanVarlenDirect) {
+    first = n;
+    last = n + 1;
+  } else {
+    const int cap = p.max_items;
+    first = clampi(p.index[1 + n], 0, cap);
+    last = clampi(p.index[2 + n], first, cap);
+  }
+}
+
+// Workgroup -> (unit, dv tile) with the dv tiles of one unit on the same XCD
+// (workgroups are dealt to the 8 XCDs round-robin by id), so that the
+// q/k re-reads of the sibling tiles hit that XCD's L2.
+__device__ __forceinline__ void xcd_unit(int ndt, int &unit, int &dtile) {
+  const int P = blockIdx.x;
+  const int xcd = P & 7;
+  const int r = P >> 3;
+  unit = (r / ndt) * 8 + xcd;
+  dtile = r - (r / ndt) * ndt;
+}
+
+static inline unsigned xcd_grid(long long units, int ndt) {
+  const long long rounds = (units + 7) / 8;
+  return (unsigned)(rounds * 8 * ndt);
+}
+
+// ===========================================================================
+// Chunked forward, bf16 inputs, MFMA
+// ===========================================================================
+//
+// Shapes: DK = dk (96), DVT = dv tile (96 or 64), C = chunk (64), 4 waves.
+// LDS (bf16 unless noted):
+//   sQ  [C][DK+8]    row-major q tile      (B operand of K Q^T and S^T Q^T)
+//   sK  [C][DK+8]    row-major k tile      (A operand of K Q^T)
+//   sKt [DK][C+8]    decay-scaled k, transposed: lambda^(L-1-j) k_j  (A of dS)
+//   sVt [DVT][C+8]   v tile transposed                          (A of O, B of dS)
+//   sSt [DVT][DK+8]  bf16 copy of the carried state, transposed (A of O_inter)
+//   sPow[C+1] fp32   lambda^n
+// The +8 element pads make the 16-byte fragment reads bank-conflict free.
+//
+// Orientation: every product is arranged so that each operand's contraction
+// index is contiguous in LDS, and the fp32 result layout of one MFMA feeds
+// the next without a trip through LDS:
+//   P^T[j][i]    = K Q^T                     (M = j, N = i, K = d)
+//   O^T[c][i]    = lambda^(i+1) S^T Q^T + V^T P^T
+//                  (P^T stays in registers as the B operand: the D layout of
+//                   one 16x16 tile pair is exactly the B layout for a 32-deep
+//                   k step with k-set {4g..4g+3, 16+4g..16+4g+3})
+//   S[d][c]     <- lambda^L S + Kt V         (M = d, N = c, K = j)
+// MFMA v_mfma_f32_16x16x32_bf16 lane layout (lane l, l16 = l % 16, g = l / 16):
+//   A: row l16, 8 k-values of group g; B: column l16, the same 8 k-values;
+//   D: rows 4g..4g+3, column l16.
+template <int C, int DK, int DVT>
+struct MfmaCfg {
+  static constexpr int NT = 256;
+  static constexpr int QS = DK + 8;     // row stride of sQ, sK, sSt (elements)
+  static constexpr int TS = C + 8;      // row stride of sKt, sVt
+  static constexpr int NDT = DK / 16;   // 16-row tiles over dk
+  static constexpr int NCT = DVT / 16;  // 16-col tiles over the dv tile
+  static constexpr int NKS = DK / 32;   // 32-deep k steps over dk
+  static constexpr int NJS = C / 32;    // 32-deep k steps over the chunk
+  static constexpr int NIB = C / 16;    // 16-row blocks of the chunk
+  static constexpr int NJB = C / 4;     // 4-row load blocks
+  static constexpr int NQV = DK / 8;    // 16-byte vectors per q row
+  static constexpr int QV = (C * NQV + NT - 1) / NT;
+  static constexpr int KB = (NJB * (DK / 8) + NT - 1) / NT;
+  static constexpr int VB = (NJB * (DVT / 8) + NT - 1) / NT;
+  // state tiles per wave: a (NDT/2) x (NCT/2) block
+  static constexpr int SDT = NDT / 2;
+  static constexpr int SCT = NCT / 2;
+  static constexpr int LDS_BF16 = 2 * C * QS + DVT * QS + DK * TS + DVT * TS;
+  static_assert(C == 64, "the MFMA kernel is written for 64-token chunks");
+  static_assert(DK % 32 == 0 && DVT % 32 == 0, "tile shapes");
+  static_assert(NDT % 2 == 0 && NCT % 2 == 0, "state tile split");
+};
+
+template <typename V8>
+__device__ __forceinline__ V8 lds8(const bf16 *p) {
+  return *reinterpret_cast<const V8 *>(p);
+}
+
+// 4x8 load block b of a C x W tile -> (row block jb, 8-col group cb).
+// Lane order inside a wave alternates row and column blocks so that both the
+// row-major and the transposed LDS writes of a wave spread over the banks.
+template <int NJB>
+__device__ __forceinline__ void block_rc(int b, int &jb, int &cb) {
+  const int jlo = b & 3, clo = (b >> 2) & 3, rest = b >> 4;
+  constexpr int JH = NJB / 4;
+  jb = jlo + 4 * (rest % JH);
+  cb = clo + 4 * (rest / JH);
+}
+
+template <int C, int DK, int DVT, bool STATE_ONLY>
+__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, bf16 *__restrict__ o,
+    const float *__restrict__ s0, float *__restrict__ s_final,
+    float *__restrict__ slots, Plan plan, Decay dec, float scale, int H,
+    int dv, int final_in_slot) {
+  using Cfg = MfmaCfg<C, DK, DVT>;
+  constexpr int QS = Cfg::QS, TS = Cfg::TS;
+  __shared__ __attribute__((aligned(16))) bf16 smem[Cfg::LDS_BF16];
+  __shared__ float sPow[C + 4];
+  bf16 *sQ = smem;
+  bf16 *sK = sQ + C * QS;
+  bf16 *sSt = sK + C * QS;
+  bf16 *sKt = sSt + DVT * QS;
+  bf16 *sVt = sKt + DK * TS;
+
+  const int ndt = dv / DVT;
+  int unit, dtile;
+  xcd_unit(ndt, unit, dtile);
+  if (unit >= plan.max_items * H) return;
+  const int idx = unit / H;
+  const int h = unit - idx * H;
+  Item it;
+  if (!load_item(plan, idx, it)) return;
+  if (STATE_ONLY && (it.flags & kLastSeg)) return;  // no successor needs it
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int c0 = dtile * DVT;
+  const long long rowK = (long long)H * DK;  // elements between tokens (q, k)
+  const long long rowV = (long long)H * dv;  // elements between tokens (v, o)
+  const float lam = dec.lam[h];
+  const int len = it.t1 - it.t0;
+  const int nch = (len + C - 1) / C;
+
+  // lambda^n table
+  if (tid <= C) sPow[tid] = pow_f64(lam, tid);
+
+  // ---- state accumulators: wave w owns d tiles [SDT*(w/2), +SDT) and
+  // c tiles [SCT*(w%2), +SCT) of the DK x DVT state
+  const int dt0 = Cfg::SDT * (w >> 1);
+  const int ct0 = Cfg::SCT * (w & 1);
+  f32x4 accS[Cfg::SDT][Cfg::SCT];
+  {
+    // incoming state: s0 (or zeros) for a sequence's first item, else the
+    // combined state left in slot idx-1; a local end state starts from zero
+    const float *src = nullptr;
+    if (!STATE_ONLY) {
+      if (it.flags & kFirstSeg)
+        src = s0 ? s0 + ((long long)it.n * H + h) * DK * dv : nullptr;
+      else
+        src = slots + ((long long)(idx - 1) * H + h) * DK * dv;
+    }
+#pragma unroll
+    for (int a = 0; a < Cfg::SDT; ++a)
+#pragma unroll
+      for (int b = 0; b < Cfg::SCT; ++b) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (src) {
+          const int d = 16 * (dt0 + a) + 4 * g;
+          const int c = c0 + 16 * (ct0 + b) + l16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = src[(long long)(d + r) * dv + c];
+        }
+        accS[a][b] = x;
+      }
+  }
+
+  // ---- global -> register staging of one chunk
+  uint4 rq[Cfg::QV];
+  uint4 rk[Cfg::KB][4];
+  uint4 rv[Cfg::VB][4];
+  const uint4 zero4 = {0u, 0u, 0u, 0u};
+
+  auto load_chunk = [&](int ch) {
+    const int tb = it.t0 + ch * C;
+    const int L = min(C, it.t1 - tb);
+    if (!STATE_ONLY) {
+#pragma unroll
+      for (int m = 0; m < Cfg::QV; ++m) {
+        const int vi = tid + m * Cfg::NT;
+        const int row = vi / Cfg::NQV, col = vi - row * Cfg::NQV;
+        rq[m] = zero4;
+        if (vi < C * Cfg::NQV && row < L)
+          rq[m] = *reinterpret_cast<const uint4 *>(
+              q + (long long)(tb + row) * rowK + (long long)h * DK + 8 * col);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < Cfg::KB; ++m) {
+      const int b = tid + m * Cfg::NT;
+      int jb, cb;
+      block_rc<Cfg::NJB>(b, jb, cb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rk[m][r] = zero4;
+        if (b < Cfg::NJB * (DK / 8) && 4 * jb + r < L)
+          rk[m][r] = *reinterpret_cast<const uint4 *>(
+              k + (long long)(tb + 4 * jb + r) * rowK + (long long)h * DK + 8 * cb);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < Cfg::VB; ++m) {
+      const int b = tid + m * Cfg::NT;
+      int jb, cb;
+      block_rc<Cfg::NJB>(b, jb, cb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rv[m][r] = zero4;
+        if (b < Cfg::NJB * (DVT / 8) && 4 * jb + r < L)
+          rv[m][r] = *reinterpret_cast<const uint4 *>(
+              v + (long long)(tb + 4 * jb + r) * rowV + (long long)h * dv + c0 + 8 * cb);
+      }
+    }
+  };
+
+  auto store_chunk = [&](int L) {
+    if (!STATE_ONLY) {
+#pragma unroll
+      for (int m = 0; m < Cfg::QV; ++m) {
+        const int vi = tid + m * Cfg::NT;
+        const int row = vi / Cfg::NQV, col = vi - row * Cfg::NQV;
+        if (vi < C * Cfg::NQV)
+          *reinterpret_cast<uint4 *>(sQ + row * QS + 8 * col) = rq[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < Cfg::KB; ++m) {
+      const int b = tid + m * Cfg::NT;
+      if (b < Cfg::NJB * (DK / 8)) {
+        int jb, cb;
+        block_rc<Cfg::NJB>(b, jb, cb);
+        float wgt[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 4 * jb + r;
+          wgt[r] = (j < L) ? sPow[L - 1 - j] : 0.f;
+          if (!STATE_ONLY)
+            *reinterpret_cast<uint4 *>(sK + j * QS + 8 * cb) = rk[m][r];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 t;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bf16x8 kv = __builtin_bit_cast(bf16x8, rk[m][r]);
+            t[r] = (bf16)((float)kv[e] * wgt[r]);
+          }
+          *reinterpret_cast<bf16x4 *>(sKt + (8 * cb + e) * TS + 4 * jb) = t;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < Cfg::VB; ++m) {
+      const int b = tid + m * Cfg::NT;
+      if (b < Cfg::NJB * (DVT / 8)) {
+        int jb, cb;
+        block_rc<Cfg::NJB>(b, jb, cb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16x4 t;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, rv[m][r]);
+            t[r] = vv[e];
+          }
+          *reinterpret_cast<bf16x4 *>(sVt + (8 * cb + e) * TS + 4 * jb) = t;
+        }
+      }
+    }
+  };
+
+  auto store_state_lds = [&]() {
+#pragma unroll
+    for (int a = 0; a < Cfg::SDT; ++a)
+#pragma unroll
+      for (int b = 0; b < Cfg::SCT; ++b) {
+        bf16x4 t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = (bf16)accS[a][b][r];
+        const int c = 16 * (ct0 + b) + l16;
+        const int d = 16 * (dt0 + a) + 4 * g;
+        *reinterpret_cast<bf16x4 *>(sSt + c * QS + d) = t;
+      }
+  };
+
+  if (nch > 0) load_chunk(0);
+  __syncthreads();  // sPow ready
+  if (nch > 0) {
+    store_chunk(min(C, len));
+    if (!STATE_ONLY) store_state_lds();
+  }
+  __syncthreads();
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int tb = it.t0 + ch * C;
+    const int L = min(C, it.t1 - tb);
+    if (ch + 1 < nch) load_chunk(ch + 1);
+
+    if (!STATE_ONLY) {
+      // ---------------- outputs of rows i in block I = w ----------------
+      const int I = w;
+      const int i = 16 * I + l16;
+      bf16x8 qf[Cfg::NKS];
+#pragma unroll
+      for (int s = 0; s < Cfg::NKS; ++s) qf[s] = lds8<bf16x8>(sQ + i * QS + 32 * s + 8 * g);
+
+      // P^T tiles (J <= I), masked and decay-weighted in fp32
+      f32x4 p[Cfg::NIB];
+#pragma unroll
+      for (int J = 0; J < Cfg::NIB; ++J) {
+        p[J] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (J <= I) {
+#pragma unroll
+          for (int s = 0; s < Cfg::NKS; ++s) {
+            const bf16x8 kf = lds8<bf16x8>(sK + (16 * J + l16) * QS + 32 * s + 8 * g);
+            p[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], p[J], 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int diff = i - (16 * J + 4 * g + r);
+            p[J][r] = diff >= 0 ? p[J][r] * sPow[diff] : 0.f;
+          }
+        }
+      }
+      bf16x8 pb[Cfg::NJS];
+#pragma unroll
+      for (int s = 0; s < Cfg::NJS; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pb[s][r] = (bf16)p[2 * s][r];
+          pb[s][4 + r] = (bf16)p[2 * s + 1][r];
+        }
+      }
+
+      const float lam_i1 = sPow[i + 1];
+      const bool row_ok = i < L;
+      bf16 *orow = o + (long long)(tb + i) * rowV + (long long)h * dv + c0;
+#pragma unroll
+      for (int ct = 0; ct < Cfg::NCT; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < Cfg::NKS; ++s) {
+          const bf16x8 sf = lds8<bf16x8>(sSt + (16 * ct + l16) * QS + 32 * s + 8 * g);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf, qf[s], acc, 0, 0, 0);
+        }
+        acc *= lam_i1;
+#pragma unroll
+        for (int s = 0; s < Cfg::NJS; ++s) {
+          if (2 * s <= I) {
+            const bf16 *vp = sVt + (16 * ct + l16) * TS + 32 * s + 4 * g;
+            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 16);
+            const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[s], acc, 0, 0, 0);
+          }
+        }
+        if (row_ok) {
+          bf16x4 t;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[r] = (bf16)(scale * acc[r]);
+          *reinterpret_cast<bf16x4 *>(orow + 16 * ct + 4 * g) = t;
+        }
+      }
+    }
+
+    // ---------------- state: S <- lambda^L S + Kt V ----------------
+    {
+      const float lamL = sPow[L];
+#pragma unroll
+      for (int a = 0; a < Cfg::SDT; ++a)
+#pragma unroll
+        for (int b = 0; b < Cfg::SCT; ++b) accS[a][b] *= lamL;
+#pragma unroll
+      for (int s = 0; s < Cfg::NJS; ++s) {
+        bf16x8 af[Cfg::SDT], bfr[Cfg::SCT];
+#pragma unroll
+        for (int a = 0; a < Cfg::SDT; ++a)
+          af[a] = lds8<bf16x8>(sKt + (16 * (dt0 + a) + l16) * TS + 32 * s + 8 * g);
+#pragma unroll
+        for (int b = 0; b < Cfg::SCT; ++b)
+          bfr[b] = lds8<bf16x8>(sVt + (16 * (ct0 + b) + l16) * TS + 32 * s + 8 * g);
+#pragma unroll
+        for (int a = 0; a < Cfg::SDT; ++a)
+#pragma unroll
+          for (int b = 0; b < Cfg::SCT; ++b)
+            accS[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], accS[a][b], 0, 0, 0);
+      }
+    }
+
+    __syncthreads();  // every wave is done reading this chunk's tiles
+    if (ch + 1 < nch) {
+      store_chunk(min(C, it.t1 - (tb + C)));
+      if (!STATE_ONLY) store_state_lds();
+    }
+    __syncthreads();
+  }
+
+  // ---- final state: local end state to its slot, or the sequence's final
+  float *dst = nullptr;
+  if (STATE_ONLY || ((it.flags & kLastSeg) && final_in_slot))
+    dst = slots + ((long long)idx * H + h) * DK * dv;
+  else if ((it.flags & kLastSeg) && s_final)
+    dst = s_final + ((long long)it.n * H + h) * DK * dv;
+  if (dst) {
+#pragma unroll
+    for (int a = 0; a < Cfg::SDT; ++a)
+#pragma unroll
+      for (int b = 0; b < Cfg::SCT; ++b) {
+        const int d = 16 * (dt0 + a) + 4 * g;
+        const int c = c0 + 16 * (ct0 + b) + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(long long)(d + r) * dv + c] = accS[a][b][r];
+      }
+  }
+}
+
+// ===========================================================================
+// Chunked forward on the vector ALUs (fp32 arithmetic, any supported shape)
+// ===========================================================================
+// One workgroup per (item, head, 16-column dv tile). Everything in LDS as
+// fp32: the q/k/v chunk tiles, the masked score tile and the state tile.
+constexpr int kValuDvt = 16;
+
+template <typename Tin>
+__device__ __forceinline__ float ld_in(const Tin *p) {
+  return (float)(*p);
+}
+
+template <typename Tin>
+__device__ __forceinline__ void st_out(Tin *p, float x) {
+  *p = (Tin)x;
+}
+
+template <typename Tin, bool STATE_ONLY>
+__global__ __launch_bounds__(256) void fwd_valu_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k,
+    const Tin *__restrict__ v, Tin *__restrict__ o,
+    const float *__restrict__ s0, float *__restrict__ s_final,
+    float *__restrict__ slots, Plan plan, Decay dec, float scale, int H,
+    int dk, int dv, int C, int final_in_slot) {
+  extern __shared__ float vsm[];
+  float *sQ = vsm;                      // [C][dk]
+  float *sK = sQ + C * dk;              // [C][dk]
+  float *sV = sK + C * dk;              // [C][16]
+  float *sP = sV + C * kValuDvt;        // [C][C]
+  float *sS = sP + C * C;               // [dk][16]
+  float *sPow = sS + dk * kValuDvt;     // [C+1]
+
+  const int ndt = dv / kValuDvt;
+  int unit, dtile;
+  xcd_unit(ndt, unit, dtile);
+  if (unit >= plan.max_items * H) return;
+  const int idx = unit / H;
+  const int h = unit - idx * H;
+  Item it;
+  if (!load_item(plan, idx, it)) return;
+  if (STATE_ONLY && (it.flags & kLastSeg)) return;
+
+  const int tid = threadIdx.x;
+  const int c0 = dtile * kValuDvt;
+  const long long rowK = (long long)H * dk, rowV = (long long)H * dv;
+  const float lam = dec.lam[h];
+  const int len = it.t1 - it.t0;
+  const int nch = (len + C - 1) / C;
+
+  for (int n = tid; n <= C; n += blockDim.x) sPow[n] = pow_f64(lam, n);
+  {
+    const float *src = nullptr;
+    if (!STATE_ONLY) {
+      if (it.flags & kFirstSeg)
+        src = s0 ? s0 + ((long long)it.n * H + h) * dk * dv : nullptr;
+      else
+        src = slots + ((long long)(idx - 1) * H + h) * dk * dv;
+    }
+    for (int e = tid; e < dk * kValuDvt; e += blockDim.x) {
+      const int d = e / kValuDvt, c = e - d * kValuDvt;
+      sS[e] = src ? src[(long long)d * dv + c0 + c] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int tb = it.t0 + ch * C;
+    const int L = min(C, it.t1 - tb);
+    for (int e = tid; e < C * dk; e += blockDim.x) {
+      const int r = e / dk, d = e - r * dk;
+      const bool ok = r < L;
+      const long long off = (long long)(tb + r) * rowK + (long long)h * dk + d;
+      if (!STATE_ONLY) sQ[e] = ok ? ld_in(q + off) : 0.f;
+      sK[e] = ok ? ld_in(k + off) : 0.f;
+    }
+    for (int e = tid; e < C * kValuDvt; e += blockDim.x) {
+      const int r = e / kValuDvt, c = e - r * kValuDvt;
+      sV[e] = r < L ? ld_in(v + (long long)(tb + r) * rowV + (long long)h * dv + c0 + c) : 0.f;
+    }
+    __syncthreads();
+    if (!STATE_ONLY) {
+      for (int e = tid; e < C * C; e += blockDim.x) {
+        const int i = e / C, j = e - i * C;
+        float acc = 0.f;
+        if (j <= i) {
+          for (int d = 0; d < dk; ++d) acc = fmaf(sQ[i * dk + d], sK[j * dk + d], acc);
+          acc *= sPow[i - j];
+        }
+        sP[e] = acc;
+      }
+      __syncthreads();
+      for (int e = tid; e < C * kValuDvt; e += blockDim.x) {
+        const int i = e / kValuDvt, c = e - i * kValuDvt;
+        if (i < L) {
+          float inter = 0.f;
+          for (int d = 0; d < dk; ++d) inter = fmaf(sQ[i * dk + d], sS[d * kValuDvt + c], inter);
+          float intra = 0.f;
+          for (int j = 0; j <= i; ++j) intra = fmaf(sP[i * C + j], sV[j * kValuDvt + c], intra);
+          st_out(o + (long long)(tb + i) * rowV + (long long)h * dv + c0 + c,
+                 scale * fmaf(sPow[i + 1], inter, intra));
+        }
+      }
+      __syncthreads();
+    }
+    const float lamL = sPow[L];
+    for (int e = tid; e < dk * kValuDvt; e += blockDim.x) {
+      const int d = e / kValuDvt, c = e - d * kValuDvt;
+      float acc = 0.f;
+      for (int j = 0; j < L; ++j) acc = fmaf(sPow[L - 1 - j] * sK[j * dk + d], sV[j * kValuDvt + c], acc);
+      sS[e] = fmaf(lamL, sS[e], acc);
+    }
+    __syncthreads();
+  }
+
+  float *dst = nullptr;
+  if (STATE_ONLY || ((it.flags & kLastSeg) && final_in_slot))
+    dst = slots + ((long long)idx * H + h) * dk * dv;
+  else if ((it.flags & kLastSeg) && s_final)
+    dst = s_final + ((long long)it.n * H + h) * dk * dv;
+  if (dst)
+    for (int e = tid; e < dk * kValuDvt; e += blockDim.x) {
+      const int d = e / kValuDvt, c = e - d * kValuDvt;
+      dst[(long long)d * dv + c0 + c] = sS[e];
+    }
+}
+
+// ===========================================================================
+// Varlen planner: cut each packed sequence into items of seg_len tokens
+// ===========================================================================
+// One workgroup of 1024 threads. Thread t takes a contiguous range of
+// sequences, counts their segments, a block scan turns counts into offsets,
+// then each thread writes its items. index[0] = item count, index[1+n] =
+// first item of sequence n (index[1+N] = count). Items past max_items are
+// dropped (only reachable with an invalid cu_seqlens).
+__global__ __launch_bounds__(1024) void planner_kernel(Plan p, int32_t *index,
+                                                       int4 *items) {
+  __shared__ int scan[1024];
+  const int tid = threadIdx.x;
+  const int N = p.n_seq;
+  const int per = (N + 1023) / 1024;
+  const int nb = min(N, tid * per), ne = min(N, nb + per);
+  auto bounds = [&](int n, int &a, int &b) {
+    a = clampi(p.cu[n], 0, p.total_T);
+    b = clampi(p.cu[n + 1], a, p.total_T);
+  };
+  int cnt = 0;
+  for (int n = nb; n < ne; ++n) {
+    int a, b;
+    bounds(n, a, b);
+    const int L = b - a;
+    cnt += L > 0 ? (L + p.seg_len - 1) / p.seg_len : 1;
+  }
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += x;
+    __syncthreads();
+  }
+  int pos = scan[tid] - cnt;  // exclusive prefix
+  for (int n = nb; n < ne; ++n) {
+    int a, b;
+    bounds(n, a, b);
+    const int L = b - a;
+    const int ns = L > 0 ? (L + p.seg_len - 1) / p.seg_len : 1;
+    index[1 + n] = min(pos, p.max_items);
+    for (int gi = 0; gi < ns; ++gi, ++pos) {
+      if (pos >= p.max_items) continue;
+      const int t0 = a + gi * p.seg_len;
+      const int t1 = min(t0 + p.seg_len, b);
+      const int fl = (gi == 0 ? kFirstSeg : 0) | (gi == ns - 1 ? kLastSeg : 0);
+      items[pos] = make_int4(n, t0, t1, fl);
+    }
+  }
+  if (tid == 1023) {
+    index[0] = min(scan[1023], p.max_items);
+    index[1 + N] = min(scan[1023], p.max_items);
+  }
+}
+
+// ===========================================================================
+// Segment combine: S_in(i+1) = lambda^(len i) S_in(i) + U_i, in place
+// ===========================================================================
+// Slot i holds U_i (local end state of item i) on entry and S_in(i+1) on
+// exit. One thread per 4 consecutive state elements of one (sequence, head).
+__global__ __launch_bounds__(256) void combine_kernel(
+    Plan p, const float *__restrict__ s0, float *__restrict__ slots, Decay dec,
+    int H, int dk, int dv) {
+  const int per_state = dk * dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const int unit = blockIdx.x / blocks_per;
+  const int part = blockIdx.x - unit * blocks_per;
+  const int n = unit / H, h = unit - (unit / H) * H;
+  if (n >= p.n_seq) return;
+  const int e = (part * 256 + threadIdx.x) * 4;
+  if (e >= per_state) return;
+  int first, last;
+  seq_items(p, n, first, last);
+  if (last - first < 2) return;
+  const float lam = dec.lam[h];
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (s0) S = *reinterpret_cast<const float4 *>(s0 + ((long long)n * H + h) * per_state + e);
+  for (int i = first; i < last - 1; ++i) {
+    Item it;
+    if (!load_item(p, i, it)) break;
+    const float a = pow_f64(lam, it.t1 - it.t0);
+    float4 *slot = reinterpret_cast<float4 *>(slots + ((long long)i * H + h) * per_state + e);
+    const float4 U = *slot;
+    S.x = fmaf(a, S.x, U.x);
+    S.y = fmaf(a, S.y, U.y);
+    S.z = fmaf(a, S.z, U.z);
+    S.w = fmaf(a, S.w, U.w);
+    *slot = S;
+  }
+}
+
+// s_final[n] <- slot of sequence n's last item (in-place final state with
+// segments: the last segment cannot write s_final while the first segment of
+// the same sequence may still be reading it as s0).
+__global__ __launch_bounds__(256) void final_gather_kernel(
+    Plan p, const float *__restrict__ slots, float *__restrict__ s_final, int H,
+    int dk, int dv) {
+  const int per_state = dk * dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const int unit = blockIdx.x / blocks_per;
+  const int part = blockIdx.x - unit * blocks_per;
+  const int n = unit / H, h = unit - (unit / H) * H;
+  if (n >= p.n_seq) return;
+  const int e = (part * 256 + threadIdx.x) * 4;
+  if (e >= per_state) return;
+  int first, last;
+  seq_items(p, n, first, last);
+  if (last <= first) return;
+  const float4 x = *reinterpret_cast<const float4 *>(
+      slots + ((long long)(last - 1) * H + h) * per_state + e);
+  *reinterpret_cast<float4 *>(s_final + ((long long)n * H + h) * per_state + e) = x;
+}
+
+// s_final <- s0 (or zeros) for sequences with no tokens in a fixed batch.
+__global__ __launch_bounds__(256) void state_fill_kernel(long long n4,
+                                                         const float *__restrict__ s0,
+                                                         float *__restrict__ s_final) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (s0) x = reinterpret_cast<const float4 *>(s0)[i];
+  reinterpret_cast<float4 *>(s_final)[i] = x;
+}
+
+// ===========================================================================
+// Decode: one token per sequence, state updated in place
+// ===========================================================================
+// One workgroup per (sequence, head). Thread t owns 4 consecutive columns
+// (cq = t % quads) of RPT consecutive rows (row group t / quads). All RPT
+// float4 loads of the state are issued before any arithmetic so that each
+// thread keeps RPT x 16 bytes in flight; every state byte is read once and
+// written once.
+template <typename Tin, int RPT>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k,
+    const Tin *__restrict__ v, Decay dec, float scale, float *__restrict__ state,
+    Tin *__restrict__ o, int H, int dk, int dv, int rpt_rt) {
+  extern __shared__ float dsm[];
+  const int quads = dv / 4;
+  const int rg_n = dk / (RPT > 0 ? RPT : rpt_rt);
+  float *sq = dsm;             // [dk]
+  float *sk = sq + dk;         // [dk]
+  float *sv = sk + dk;         // [dv]
+  float *part = sv + dv;       // [rg_n][dv]
+  const long long unit = blockIdx.x;
+  const int h = (int)(unit % H);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < dk; e += blockDim.x) {
+    sq[e] = (float)q[unit * dk + e];
+    sk[e] = (float)k[unit * dk + e];
+  }
+  for (int e = tid; e < dv; e += blockDim.x) sv[e] = (float)v[unit * dv + e];
+  __syncthreads();
+  const float lam = dec.lam[h];
+  const int cq = tid % quads, rg = tid / quads;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (rg < rg_n) {
+    const float4 vq = *reinterpret_cast<const float4 *>(sv + 4 * cq);
+    float *base = state + unit * (long long)dk * dv + 4 * cq;
+    if constexpr (RPT > 0) {
+      const int r0 = rg * RPT;
+      float4 s[RPT];
+#pragma unroll
+      for (int m = 0; m < RPT; ++m)
+        s[m] = *reinterpret_cast<const float4 *>(base + (long long)(r0 + m) * dv);
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        const float kr = sk[r0 + m], qr = sq[r0 + m];
+        float4 x = s[m];
+        x.x = fmaf(lam, x.x, kr * vq.x);
+        x.y = fmaf(lam, x.y, kr * vq.y);
+        x.z = fmaf(lam, x.z, kr * vq.z);
+        x.w = fmaf(lam, x.w, kr * vq.w);
+        *reinterpret_cast<float4 *>(base + (long long)(r0 + m) * dv) = x;
+        acc.x = fmaf(qr, x.x, acc.x);
+        acc.y = fmaf(qr, x.y, acc.y);
+        acc.z = fmaf(qr, x.z, acc.z);
+        acc.w = fmaf(qr, x.w, acc.w);
+      }
+    } else {
+      const int r0 = rg * rpt_rt;
+      for (int m = 0; m < rpt_rt; ++m) {
+        float4 x = *reinterpret_cast<const float4 *>(base + (long long)(r0 + m) * dv);
+        const float kr = sk[r0 + m], qr = sq[r0 + m];
+        x.x = fmaf(lam, x.x, kr * vq.x);
+        x.y = fmaf(lam, x.y, kr * vq.y);
+        x.z = fmaf(lam, x.z, kr * vq.z);
+        x.w = fmaf(lam, x.w, kr * vq.w);
+        *reinterpret_cast<float4 *>(base + (long long)(r0 + m) * dv) = x;
+        acc.x = fmaf(qr, x.x, acc.x);
+        acc.y = fmaf(qr, x.y, acc.y);
+        acc.z = fmaf(qr, x.z, acc.z);
+        acc.w = fmaf(qr, x.w, acc.w);
+      }
+    }
+    *reinterpret_cast<float4 *>(part + rg * dv + 4 * cq) = acc;
+  }
+  __syncthreads();
+  for (int c = tid; c < dv; c += blockDim.x) {
+    float sum = 0.f;
+    for (int r = 0; r < rg_n; ++r) sum += part[r * dv + c];
+    o[unit * dv + c] = (Tin)(scale * sum);
+  }
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+bool fast_path_ok(int dt, int dk, int dv, int chunk) {
+  return dt == 1 && dk == 96 && (dv % 64 == 0) && (chunk == 0 || chunk == 64);
+}
+
+int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }
+
+int generic_chunk(int chunk) { return chunk == 32 ? 32 : 64; }
+
+hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(planner_kernel, dim3(1), dim3(1024), 0, s, p, index, items);
+  return hipGetLastError();
+}
+
+template <int DVT, bool SO>
+static void launch_mfma(const Plan &p, const FwdArgs &a, const Decay &dec,
+                        hipStream_t s) {
+  const int ndt = a.dv / DVT;
+  const unsigned grid = xcd_grid((long long)p.max_items * a.H, ndt);
+  hipLaunchKernelGGL((fwd_mfma_kernel<64, 96, DVT, SO>), dim3(grid), dim3(256),
+                     0, s, (const bf16 *)a.q, (const bf16 *)a.k,
+                     (const bf16 *)a.v, (bf16 *)a.o, a.s0, a.s_final, a.slots,
+                     p, dec, a.scale, a.H, a.dv, a.final_in_slot);
+}
+
+template <typename Tin, bool SO>
+static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
+                        int C, hipStream_t s) {
+  const int ndt = a.dv / kValuDvt;
+  const unsigned grid = xcd_grid((long long)p.max_items * a.H, ndt);
+  const size_t lds = sizeof(float) * ((size_t)2 * C * a.dk + C * kValuDvt +
+                                      (size_t)C * C + a.dk * kValuDvt + C + 4);
+  if (lds > 65536)  // beyond the default dynamic-LDS limit (gfx950 has 160 KB)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_valu_kernel<Tin, SO>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((fwd_valu_kernel<Tin, SO>), dim3(grid), dim3(256), lds, s,
+                     (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v,
+                     (Tin *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
+                     a.H, a.dk, a.dv, C, a.final_in_slot);
+}
+
+hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
+                      const FwdArgs &a, const Decay &dec, int chunk,
+                      hipStream_t s) {
+  if (fast) {
+    const int dvt = fast_dv_tile(a.dv);
+    if (dvt == 96) {
+      if (state_only) launch_mfma<96, true>(p, a, dec, s);
+      else launch_mfma<96, false>(p, a, dec, s);
+    } else {
+      if (state_only) launch_mfma<64, true>(p, a, dec, s);
+      else launch_mfma<64, false>(p, a, dec, s);
+    }
+  } else {
+    const int C = generic_chunk(chunk);
+    if (dt == 1) {
+      if (state_only) launch_valu<bf16, true>(p, a, dec, C, s);
+      else launch_valu<bf16, false>(p, a, dec, C, s);
+    } else {
+      if (state_only) launch_valu<float, true>(p, a, dec, C, s);
+      else launch_valu<float, false>(p, a, dec, C, s);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,
+                          hipStream_t s) {
+  const int per_state = a.dk * a.dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const unsigned grid = (unsigned)((long long)p.n_seq * a.H * blocks_per);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, s, p, a.s0,
+                     a.slots, dec, a.H, a.dk, a.dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_final_gather(const Plan &p, const FwdArgs &a, hipStream_t s) {
+  const int per_state = a.dk * a.dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const unsigned grid = (unsigned)((long long)p.n_seq * a.H * blocks_per);
+  hipLaunchKernelGGL(final_gather_kernel, dim3(grid), dim3(256), 0, s, p,
+                     a.slots, a.s_final, a.H, a.dk, a.dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
+                             const float *s0, float *s_final, hipStream_t s) {
+  const long long n4 = (long long)n_states * H * dk * dv / 4;
+  const unsigned grid = (unsigned)((n4 + 255) / 256);
+  hipLaunchKernelGGL(state_fill_kernel, dim3(grid), dim3(256), 0, s, n4, s0, s_final);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
+                         const void *k, const void *v, const Decay &dec,
+                         float scale, float *state, void *o, hipStream_t s) {
+  const int quads = dv / 4;
+  // row groups: the largest divisor of dk with quads * groups <= 256
+  int rg = 1;
+  for (int c = 1; c <= dk; ++c)
+    if (dk % c == 0 && quads * c <= 256) rg = c;
+  const int rpt = dk / rg;
+  const unsigned threads = (unsigned)(quads * rg);
+  const size_t lds = sizeof(float) * (size_t)(2 * dk + dv + rg * dv);
+  const unsigned grid = (unsigned)((long long)N * H);
+#define GLA_DECODE(T, R)                                                       \
+  hipLaunchKernelGGL((decode_kernel<T, R>), dim3(grid), dim3(threads), lds, s, \
+                     (const T *)q, (const T *)k, (const T *)v, dec, scale,     \
+                     state, (T *)o, H, dk, dv, rpt)
+  if (dt == 1) {
+    if (rpt == 24) GLA_DECODE(bf16, 24);
+    else GLA_DECODE(bf16, 0);
+  } else {
+    if (rpt == 24) GLA_DECODE(float, 24);
+    else GLA_DECODE(float, 0);
+  }
+#undef GLA_DECODE
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -1,0 +1,216 @@
+"""Thin Python binding of libgla.so (the C ABI in include/gla.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and workspace are allocated with torch, and the raw
+device pointers plus torch's current HIP stream go to the library. Every step
+of the computation runs in the library's HIP kernels; there is no fallback
+of any kind. If libgla.so has not been built the first call raises.
+
+Functions mirror the C entry points:
+    gla_chunk_fwd(q, k, v, decay, ...)          -> (o, s_final)
+    gla_chunk_fwd_varlen(q, k, v, cu, decay, ...) -> (o, s_final)
+    gla_decode_step(q, k, v, decay, state, ...)  -> o   (state updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgla.so")
+
+GLA_F32, GLA_BF16 = 0, 1
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "gla_abi_version": ([], _I),
+    "gla_status_str": ([_I], ctypes.c_char_p),
+    "gla_chunk_fwd_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
+    "gla_chunk_fwd": ([_I] * 7 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                  _P, ctypes.c_size_t, _P], _I),
+    "gla_chunk_fwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
+    "gla_chunk_fwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                         _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
+}
+EXPORTS = tuple(_SIGS)
+
+
+class GlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s (status %d)" % (where, status_str(code), code))
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libgla.so is not built (%s); run "
+                "`python -m chunked_gated_recurrent_amd.build`" % LIB_PATH)
+        import torch  # noqa: F401  -- bind to the HIP runtime torch loaded
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().gla_abi_version()
+
+
+def status_str(code: int) -> str:
+    return lib().gla_status_str(code).decode()
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GLA_BF16
+    if t.dtype == torch.float32:
+        return GLA_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _decay_array(decay, H):
+    d = np.ascontiguousarray(np.asarray(decay, dtype=np.float32).reshape(-1))
+    if d.shape[0] != H:
+        raise ValueError("decay must have H = %d entries" % H)
+    return d, d.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(t, name, dev, dtype=None, shape=None):
+    if not t.is_cuda or t.device != dev:
+        raise ValueError("%s must be on %s" % (name, dev))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _stream(dev):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def gla_chunk_fwd(q, k, v, decay, scale: float = 1.0, initial_state=None,
+                  output_final_state: bool = True, chunk: int = 0, out=None,
+                  final_state=None, workspace=None):
+    """Chunked forward of a fixed-length batch.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype);
+    decay: H floats on the host; initial_state: [B, H, dk, dv] fp32 or None.
+    Returns (o [B, T, H, dv], s_final [B, H, dk, dv] fp32 or None).
+    `final_state` may be `initial_state` itself (updated in place).
+    """
+    import torch
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (B, T, H, dk))
+    _check(v, "v", dev, q.dtype, (B, T, H, dv))
+    dt = _dt(q)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, (B, H, dk, dv))
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (B, T, H, dv))
+    sf = final_state
+    if sf is None and output_final_state:
+        sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if sf is not None:
+        _check(sf, "final_state", dev, torch.float32, (B, H, dk, dv))
+    L = lib()
+    need = L.gla_chunk_fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _d, dptr = _decay_array(decay, H)
+    rc = L.gla_chunk_fwd(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v),
+                         dptr, float(scale), _ptr(initial_state), _ptr(o),
+                         _ptr(sf), _ptr(ws), wsb, _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_chunk_fwd")
+    return o, sf
+
+
+def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,
+                         initial_state=None, output_final_state: bool = True,
+                         chunk: int = 0, out=None, final_state=None,
+                         workspace=None):
+    """Chunked forward of N packed sequences.
+
+    q, k: [total_T, H, dk]; v: [total_T, H, dv]; cu_seqlens: [N+1] int32 on
+    the device. Returns (o [total_T, H, dv], s_final [N, H, dk, dv] or None).
+    """
+    import torch
+    dev = q.device
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (total, H, dk))
+    _check(v, "v", dev, q.dtype, (total, H, dv))
+    _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    dt = _dt(q)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, (N, H, dk, dv))
+    o = torch.empty((total, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (total, H, dv))
+    sf = final_state
+    if sf is None and output_final_state:
+        sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if sf is not None:
+        _check(sf, "final_state", dev, torch.float32, (N, H, dk, dv))
+    L = lib()
+    need = L.gla_chunk_fwd_varlen_workspace_bytes(dt, N, total, H, dk, dv, chunk)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _d, dptr = _decay_array(decay, H)
+    rc = L.gla_chunk_fwd_varlen(dt, N, total, H, dk, dv, chunk, _ptr(cu_seqlens),
+                                _ptr(q), _ptr(k), _ptr(v), dptr, float(scale),
+                                _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(ws),
+                                wsb, _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_chunk_fwd_varlen")
+    return o, sf
+
+
+def gla_decode_step(q, k, v, decay, state, scale: float = 1.0, out=None):
+    """One decode step: state [N, H, dk, dv] fp32 is updated in place;
+    returns o [N, H, dv]."""
+    import torch
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (N, H, dk))
+    _check(v, "v", dev, q.dtype, (N, H, dv))
+    _check(state, "state", dev, torch.float32, (N, H, dk, dv))
+    dt = _dt(q)
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (N, H, dv))
+    _d, dptr = _decay_array(decay, H)
+    rc = lib().gla_decode_step(dt, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), dptr,
+                               float(scale), _ptr(state), _ptr(o), _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_decode_step")
+    return o

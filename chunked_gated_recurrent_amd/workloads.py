@@ -32,11 +32,13 @@ def bf16_bits(x) -> np.ndarray:
     """Round fp32 values to bf16 (round-to-nearest-even); returns the uint16
     bit patterns. NaN stays NaN (quiet)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    one = np.uint32(1)
+    # finite values cannot overflow 32 bits here (largest: 0xFF7FFFFF + 0x8000)
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & one))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        r[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return r
 
 

@@ -1,0 +1,144 @@
+/*
+ * gla.h -- C ABI of the Simple GLA library for AMD MI355X (gfx950).
+ *
+ * Simple GLA is the gated-linear-attention token mixer of the Laplace 3B
+ * model (page "Beyond the KV cache: training and serving i14's Laplace 3B
+ * linear attention model on AWS Trainium2", section "GLA mixer"). For every
+ * head h a dk x dv fp32 matrix state S is decayed by a fixed per-head factor
+ * lambda_h (section "Decay scheme": fixed at initialisation, not learned) and
+ * receives the key/value outer product of each token; the token's output
+ * reads the updated state with its query:
+ *
+ *     S_t = lambda_h * S_{t-1} + k_t^T v_t        o_t = scale * q_t S_t
+ *
+ * (k_t, q_t are 1 x dk rows, v_t and o_t are 1 x dv rows; the readout uses
+ * the state after the update.)
+ *
+ * Prefill computes this chunkwise (same page, section "Challenge 1": inside a
+ * chunk a masked, decay-weighted linear attention; across chunks a carried
+ * state advanced by the decay accumulated over the chunk). Decode updates one
+ * fixed-size state per sequence in place (section "Inference optimisation on
+ * Trainium2": one fixed state page per sequence, read and written back at
+ * every token).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers to caller-owned memory, dense and
+ *     row-major in the documented layout, 16-byte aligned. The library never
+ *     allocates, frees or keeps a pointer after it returns.
+ *   - `decay_host` is a HOST array of H floats, read during the call only.
+ *     Every lambda must be finite with 0 < lambda <= 1.
+ *   - `dt` is the dtype of q, k, v and o (GLA_F32 or GLA_BF16). States and
+ *     initial states are always fp32.
+ *   - Shapes: 1 <= H <= 64; dk and dv multiples of 16 with dk <= 128 and
+ *     dv <= 256. `chunk` is 0 (library default) or 32, 64 or 128; results do
+ *     not depend on it beyond rounding.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is
+ *     enqueued on it; no call synchronises.
+ *   - Arguments are validated on the host before any HIP call. On an error
+ *     nothing is launched and no output is touched. A launch failure returns
+ *     GLA_ERR_HIP; faults inside kernels surface at the caller's next
+ *     synchronisation, as for any HIP work.
+ *   - Calls are stateless and re-entrant. Results are bitwise reproducible
+ *     run to run (no atomics feed any output).
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_ABI_VERSION 1
+#define GLA_MAX_HEADS 64
+
+typedef enum gla_status {
+  GLA_OK = 0,
+  GLA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  GLA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent */
+  GLA_ERR_DTYPE = 3,       /* dt is not GLA_F32 / GLA_BF16                     */
+  GLA_ERR_DECAY = 4,       /* a lambda is not finite or not in (0, 1]          */
+  GLA_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap   */
+  GLA_ERR_UNSUPPORTED = 6, /* valid but unsupported (dk, dv, H or chunk)       */
+  GLA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required       */
+  GLA_ERR_HIP = 8,         /* a HIP launch failed                              */
+  GLA_ERR_ALIGN = 9        /* a tensor pointer is not 16-byte aligned          */
+} gla_status;
+
+typedef enum gla_dtype { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+/* ABI version of the loaded library (GLA_ABI_VERSION at build time). */
+int gla_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char *gla_status_str(gla_status s);
+
+/*
+ * Chunked forward (prefill / training forward) of a fixed-length batch.
+ *   q, k    : [B, T, H, dk]  dt
+ *   v       : [B, T, H, dv]  dt
+ *   s0      : [B, H, dk, dv] fp32, or NULL for zero initial states
+ *   o       : [B, T, H, dv]  dt, written (not read)
+ *   s_final : [B, H, dk, dv] fp32, or NULL to skip; may equal s0 (in place),
+ *             otherwise must not overlap any other argument
+ *   workspace: device scratch of at least gla_chunk_fwd_workspace_bytes()
+ *             bytes (NULL allowed when that is 0); its contents on entry
+ *             are ignored, and it must not be used by other work on other
+ *             streams while the call's kernels run.
+ * T = 0 is valid: o is untouched and s_final receives s0 (or zeros).
+ * B * T must stay below 2^31 tokens.
+ */
+size_t gla_chunk_fwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
+                                     int dv, int chunk);
+gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                         int chunk, const void *q, const void *k,
+                         const void *v, const float *decay_host, float scale,
+                         const float *s0, void *o, float *s_final,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Chunked forward of N packed variable-length sequences. Sequence n owns
+ * tokens [cu_seqlens[n], cu_seqlens[n+1]) of the packed arrays; chunks never
+ * cross a sequence boundary and each sequence starts from its own state.
+ *   cu_seqlens: [N + 1] int32 DEVICE array, cu[0] = 0, non-decreasing,
+ *               cu[N] = total_T. (It lives on the device, so it is not
+ *               validated; values outside [0, total_T] are clamped into that
+ *               range so that no access leaves the arrays, but the results
+ *               are then meaningless.)
+ *   q, k    : [total_T, H, dk]  dt        v, o : [total_T, H, dv]  dt
+ *   s0      : [N, H, dk, dv] fp32 or NULL; s_final : [N, H, dk, dv] or NULL
+ * A zero-length sequence is valid: its s_final is s0[n] (or zeros).
+ */
+size_t gla_chunk_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,
+                                            int H, int dk, int dv, int chunk);
+gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
+                                int dk, int dv, int chunk,
+                                const int32_t *cu_seqlens, const void *q,
+                                const void *k, const void *v,
+                                const float *decay_host, float scale,
+                                const float *s0, void *o, float *s_final,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * One decode step for N independent sequences (one token each):
+ *   state[n,h] <- lambda_h * state[n,h] + k[n,h]^T v[n,h]    (in place)
+ *   o[n,h]     <- scale * q[n,h] state[n,h]                  (after update)
+ *   q, k  : [N, H, dk] dt      v : [N, H, dv] dt      o : [N, H, dv] dt
+ *   state : [N, H, dk, dv] fp32, read and written in place; must not
+ *           overlap q, k, v or o.
+ * N = 0 is valid and does nothing.
+ */
+gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
+                           const void *q, const void *k, const void *v,
+                           const float *decay_host, float scale, float *state,
+                           void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H */

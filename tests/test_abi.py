@@ -1,0 +1,160 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/gla.h declares, and rejects every invalid argument with its documented
+status before any HIP call. CPU only: every call here fails validation, so
+no kernel is ever launched (the pointers passed are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from chunked_gated_recurrent_amd import gla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gla.h")
+
+OK, NULL, SHAPE, DTYPE, DECAY, ALIAS, UNSUP, WS, HIP, ALIGN = range(10)
+BF16, F32 = gla.GLA_BF16, gla.GLA_F32
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gla.LIB_PATH):
+        from chunked_gated_recurrent_amd import build
+        build.build(verbose=False)
+    return gla.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(gla.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", gla.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gla_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert L.gla_abi_version() == 1
+    seen = set()
+    for code in range(10):
+        s = gla.status_str(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert gla.status_str(99) == "unknown status"
+
+
+# fake, 256-byte aligned, far-apart device addresses: never dereferenced
+A = [ctypes.c_void_p(0x7f0000000000 + i * (1 << 36)) for i in range(8)]
+GOOD = np.array([0.5, 0.9, 0.99, 1.0], np.float32)
+
+
+def dptr(arr):
+    return arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(L, dt=BF16, B=2, T=128, H=4, dk=96, dv=192, chunk=0, q=A[0], k=A[1],
+        v=A[2], decay=None, scale=1.0, s0=None, o=A[3], sf=None, ws=None,
+        wsb=0):
+    dec = GOOD if decay is None else decay
+    return L.gla_chunk_fwd(dt, B, T, H, dk, dv, chunk, q, k, v,
+                           None if decay is False else dptr(dec), scale, s0, o,
+                           sf, ws, wsb, None)
+
+
+def test_fwd_argument_errors(L):
+    assert fwd(L, dt=7) == DTYPE
+    assert fwd(L, H=0) == SHAPE
+    assert fwd(L, B=0) == SHAPE
+    assert fwd(L, T=-1) == SHAPE
+    assert fwd(L, B=1 << 16, T=1 << 16) == SHAPE  # 2^32 tokens
+    assert fwd(L, H=65, decay=np.full(65, 0.9, np.float32)) == UNSUP
+    assert fwd(L, dk=17) == UNSUP
+    assert fwd(L, dv=512) == UNSUP
+    assert fwd(L, dk=144) == UNSUP
+    assert fwd(L, chunk=48) == UNSUP
+    assert fwd(L, decay=False) == NULL
+    assert fwd(L, q=None) == NULL
+    assert fwd(L, o=None) == NULL
+    assert fwd(L, scale=float("nan")) == SHAPE
+    for bad in (0.0, -0.5, 1.0000001, float("nan"), float("inf")):
+        d = GOOD.copy()
+        d[2] = bad
+        assert fwd(L, decay=d) == DECAY, bad
+    assert fwd(L, q=ctypes.c_void_p(0x7f0000000008)) == ALIGN
+    assert fwd(L, sf=ctypes.c_void_p(0x7f0000000004)) == ALIGN
+    # o overlapping q / s_final partially overlapping s0 / s_final on o
+    assert fwd(L, o=ctypes.c_void_p(A[0].value + 4096)) == ALIAS
+    assert fwd(L, s0=A[4], sf=ctypes.c_void_p(A[4].value + 256)) == ALIAS
+    assert fwd(L, sf=A[3]) == ALIAS
+
+
+def test_fwd_workspace_contract(L):
+    # one long sequence must be split into segments and needs scratch
+    need = L.gla_chunk_fwd_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 0)
+    assert need > 0 and need % (16 * 96 * 192 * 4) == 0
+    dec = np.full(16, 0.9, np.float32)
+    assert fwd(L, B=1, T=65536, H=16, decay=dec) == WS
+    assert fwd(L, B=1, T=65536, H=16, decay=dec, ws=A[5], wsb=need - 1) == WS
+    # scratch overlapping an input is rejected
+    assert fwd(L, B=1, T=65536, H=16, decay=dec, ws=A[0], wsb=need) == ALIAS
+    # Laplace-shaped batch: enough chains, no scratch
+    assert L.gla_chunk_fwd_workspace_bytes(BF16, 8, 2048, 16, 96, 192, 0) == 0
+    assert L.gla_chunk_fwd_workspace_bytes(BF16, 0, 2048, 16, 96, 192, 0) == 0
+    assert L.gla_chunk_fwd_workspace_bytes(9, 1, 2048, 16, 96, 192, 0) == 0
+
+
+def varlen(L, dt=BF16, N=3, total=300, H=4, dk=96, dv=192, chunk=0, cu=A[6],
+           q=A[0], k=A[1], v=A[2], decay=None, s0=None, o=A[3], sf=None,
+           ws=None, wsb=0):
+    dec = GOOD if decay is None else decay
+    return L.gla_chunk_fwd_varlen(dt, N, total, H, dk, dv, chunk, cu, q, k, v,
+                                  dptr(dec), 1.0, s0, o, sf, ws, wsb, None)
+
+
+def test_varlen_argument_errors(L):
+    assert varlen(L, N=0) == SHAPE
+    assert varlen(L, total=-1) == SHAPE
+    assert varlen(L, cu=None) == NULL
+    assert varlen(L, k=None) == NULL
+    assert varlen(L, cu=ctypes.c_void_p(A[6].value + 2)) == ALIGN
+    assert varlen(L, o=A[6]) == ALIAS          # o on top of cu_seqlens
+    assert varlen(L, sf=ctypes.c_void_p(A[6].value)) == ALIAS
+    assert varlen(L, dk=8) == UNSUP
+    d = GOOD.copy()
+    d[0] = 0.0
+    assert varlen(L, decay=d) == DECAY
+    need = L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 0)
+    assert need > 0
+    dec = np.full(16, 0.9, np.float32)
+    assert varlen(L, N=1, total=65536, H=16, decay=dec) == WS
+    # 32 sequences x 16 heads: enough chains, no scratch
+    assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 32, 131072, 16, 96, 192, 0) == 0
+
+
+def test_decode_argument_errors(L):
+    def dec(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], st=A[3],
+            o=A[4], decay=GOOD):
+        return L.gla_decode_step(dt, N, H, dk, dv, q, k, v, dptr(decay), 1.0, st, o, None)
+    assert dec(dt=3) == DTYPE
+    assert dec(N=-1) == SHAPE
+    assert dec(N=0) == OK                      # nothing to do, nothing launched
+    assert dec(st=None) == NULL
+    assert dec(o=None) == NULL
+    assert dec(dv=40) == UNSUP
+    assert dec(st=ctypes.c_void_p(A[3].value + 8)) == ALIGN
+    assert dec(o=ctypes.c_void_p(A[3].value + 1024)) == ALIAS   # o inside state
+    assert dec(st=ctypes.c_void_p(A[2].value + 512)) == ALIAS   # state on v
+    d = GOOD.copy()
+    d[1] = 2.0
+    assert dec(decay=d) == DECAY

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs. Bar: max|gpu - oracle| <= 1e-2 * max|oracle| for bf16
+inputs and <= 1e-4 for fp32 inputs, for outputs and final states.
+
+Full-size workloads are run in full on the GPU; where the oracle would take
+too long, it checks a sample of heads or sequences (each (sequence, head)
+chain is independent, so a sampled chain is checked exactly as in the full
+run)."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_recurrent_amd import gla
+from chunked_gated_recurrent_amd import workloads as W
+from oracle import oracle as O
+from gla_testutil import TOL, dev, env, host, oracle_fixed, oracle_varlen, per_head, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gla.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_fixed(x, chunk=0, s_in_place=False):
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    if s_in_place:
+        o, sf = gla.gla_chunk_fwd(q, k, v, x["decay"], initial_state=s0,
+                                  final_state=s0, chunk=chunk)
+    else:
+        o, sf = gla.gla_chunk_fwd(q, k, v, x["decay"], initial_state=s0, chunk=chunk)
+    torch.cuda.synchronize()
+    return host(o), host(sf)
+
+
+def check(name, got_o, ref_o, got_s, ref_s, tol, head_axis_o=2, head_axis_s=1):
+    eo, es = rel_err(got_o, ref_o), rel_err(got_s, ref_s)
+    print("%s: o err %.3e  S err %.3e  (tol %.0e)" % (name, eo, es, tol))
+    if ref_o.size and ref_o.ndim > head_axis_o:
+        print("  per-head o:", " ".join("%.1e" % e for e in per_head(got_o, ref_o, head_axis_o)))
+    assert np.isfinite(got_o).all() and np.isfinite(got_s).all()
+    assert eo <= tol, (name, "o", eo)
+    assert es <= tol, (name, "S", es)
+
+
+# ---------------------------------------------------------------------------
+# the named workloads
+# ---------------------------------------------------------------------------
+def test_tiny_fp32_workload():
+    x = W.spec_inputs("tiny_fp32")
+    o, s = run_fixed(x, chunk=32)
+    ro, rs = oracle_fixed(x)
+    check("tiny_fp32", o, ro, s, rs, TOL["f32"])
+
+
+def test_laplace_prefill_full():
+    x = W.spec_inputs("laplace_prefill")
+    o, s = run_fixed(x)
+    ro, rs = oracle_fixed(x)
+    check("laplace_prefill B8 T2048", o, ro, s, rs, TOL["bf16"])
+
+
+def test_long_context_sampled_heads():
+    """B1 T65536: all heads on the GPU (segmented carry), the oracle on the
+    fastest, a middle and the slowest head over the whole sequence."""
+    x = W.spec_inputs("long_context")
+    o, s = run_fixed(x, chunk=64)
+    heads = [0, 7, 15]
+    ro, rs = oracle_fixed(x, heads=heads)
+    check("long_context T65536 heads 0,7,15", o[:, :, heads], ro, s[:, heads], rs, TOL["bf16"])
+
+
+def test_varlen_workload_sampled_heads():
+    x = W.spec_inputs("varlen")
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    cu = dev(x["cu_seqlens"])
+    o, sf = gla.gla_chunk_fwd_varlen(q, k, v, cu, x["decay"], initial_state=s0)
+    torch.cuda.synchronize()
+    heads = [0, 9, 15]
+    ro, rs = oracle_varlen(x, heads=heads)
+    check("varlen N32 heads 0,9,15", host(o)[:, heads], ro, host(sf)[:, heads], rs,
+          TOL["bf16"], head_axis_o=1)
+
+
+def test_batched_decode_100_steps_sampled():
+    spec = W.WORKLOADS["batched_decode"]
+    N, H, dk, dv, steps = spec["N"], spec["H"], spec["dk"], spec["dv"], spec["steps"]
+    seed = spec["seed"]
+    lam = W.decays_for(spec)
+    S = W.decode_state(seed, N, H, dk, dv, spec["state_sigma"])
+    sample = np.unique(np.linspace(0, N - 1, 24).astype(int))
+    ref_state = S[sample].astype(np.float64)
+    state = dev(S)
+    del S
+    worst = 0.0
+    for t in range(steps):
+        q, k, v = W.decode_tokens(seed, t, N, H, dk, dv)
+        o = gla.gla_decode_step(dev(q), dev(k), dev(v), lam, state)
+        ro = O.gla_decode(q[sample], k[sample], v[sample], lam, ref_state)
+        e = rel_err(host(o)[sample], ro)
+        worst = max(worst, e)
+        assert e <= TOL["bf16"], (t, e)
+    es = rel_err(host(state)[sample], ref_state)
+    print("decode N1280 x100: worst o err %.3e, S err %.3e" % (worst, es))
+    assert es <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# edge shapes on the MFMA path (dk 96) and the vector-ALU path
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 200])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_ragged_lengths_mfma(T, with_s0):
+    x = W.prefill_inputs(100 + T, 2, T, 3, 96, 192, "bf16", 0.1 if with_s0 else None,
+                         W.geometric_decays(3))
+    o, s = run_fixed(x)
+    ro, rs = oracle_fixed(x)
+    check("mfma T%d s0=%s" % (T, with_s0), o, ro, s, rs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T,chunk", [
+    ("bf16", 16, 32, 100, 32), ("f32", 32, 64, 130, 64), ("f32", 128, 256, 70, 0),
+    ("bf16", 64, 128, 129, 0), ("f32", 96, 192, 257, 128), ("bf16", 96, 128, 150, 0),
+    ("bf16", 96, 64, 150, 0)])
+def test_shapes(dtype, dk, dv, T, chunk):
+    x = W.prefill_inputs(7 + dk + T, 2, T, 2, dk, dv, dtype, 0.1, np.array([0.9, 0.995], np.float32))
+    o, s = run_fixed(x, chunk=chunk)
+    ro, rs = oracle_fixed(x)
+    check("%s dk%d dv%d T%d C%d" % (dtype, dk, dv, T, chunk), o, ro, s, rs, TOL[dtype])
+
+
+def test_max_heads_and_lambda_one():
+    lam = np.concatenate([[1.0], W.geometric_decays(63)]).astype(np.float32)
+    x = W.prefill_inputs(55, 1, 96, 64, 96, 192, "bf16", 0.1, lam)
+    o, s = run_fixed(x)
+    ro, rs = oracle_fixed(x)
+    check("H64 with lambda=1", o, ro, s, rs, TOL["bf16"])
+
+
+def test_empty_sequence_passes_state_through():
+    x = W.prefill_inputs(3, 2, 0, 4, 96, 192, "bf16", 0.1, W.geometric_decays(4))
+    s0 = dev(x["s0"])
+    o, sf = gla.gla_chunk_fwd(dev(x["q"]), dev(x["k"]), dev(x["v"]), x["decay"], initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert torch.equal(sf, s0)
+
+
+# ---------------------------------------------------------------------------
+# invariants of the recurrence, checked on the GPU path
+# ---------------------------------------------------------------------------
+def test_segmented_carry_matches_oracle_and_in_place_state():
+    """Force time segmentation on a batch (and write the final state over the
+    initial one) and compare with the oracle."""
+    x = W.prefill_inputs(21, 2, 1000, 4, 96, 192, "bf16", 0.1, W.geometric_decays(4))
+    ro, rs = oracle_fixed(x)
+    with env(GLA_TARGET_WGS=100000):
+        need = gla.lib().gla_chunk_fwd_workspace_bytes(1, 2, 1000, 4, 96, 192, 0)
+        assert need > 0
+        o, s = run_fixed(x)
+        check("segmented", o, ro, s, rs, TOL["bf16"])
+        o2, s2 = run_fixed(x, s_in_place=True)
+        check("segmented in place", o2, ro, s2, rs, TOL["bf16"])
+    o3, s3 = run_fixed(x, s_in_place=True)
+    check("unsegmented in place", o3, ro, s3, rs, TOL["bf16"])
+
+
+def test_chunk_sizes_agree():
+    x = W.prefill_inputs(31, 1, 300, 2, 96, 192, "bf16", 0.1, np.array([0.97, 0.999], np.float32))
+    ro, rs = oracle_fixed(x)
+    for c in (0, 32, 64, 128):
+        o, s = run_fixed(x, chunk=c)
+        check("chunk %d" % c, o, ro, s, rs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T1", [1, 63, 64, 65, 255])
+def test_split_invariance(T1):
+    x = W.prefill_inputs(41, 2, 256, 3, 96, 192, "bf16", 0.1, W.geometric_decays(3))
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    o, s = gla.gla_chunk_fwd(q, k, v, x["decay"], initial_state=s0)
+    oa, sa = gla.gla_chunk_fwd(q[:, :T1].contiguous(), k[:, :T1].contiguous(),
+                               v[:, :T1].contiguous(), x["decay"], initial_state=s0)
+    ob, sb = gla.gla_chunk_fwd(q[:, T1:].contiguous(), k[:, T1:].contiguous(),
+                               v[:, T1:].contiguous(), x["decay"], initial_state=sa)
+    torch.cuda.synchronize()
+    ro, rs = oracle_fixed(x)
+    check("split at %d" % T1, np.concatenate([host(oa), host(ob)], axis=1), ro,
+          host(sb), rs, TOL["bf16"])
+    check("unsplit", host(o), ro, host(s), rs, TOL["bf16"])
+
+
+def test_decode_steps_equal_chunked_and_handoff():
+    """T decode steps from S0 equal one chunked call; a prefill followed by
+    decode steps equals one longer prefill."""
+    T, Tp = 40, 25
+    x = W.prefill_inputs(51, 3, T, 4, 96, 192, "bf16", 0.1, W.geometric_decays(4))
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    ro, rs = oracle_fixed(x)
+    state = s0.clone()
+    outs = []
+    for t in range(T):
+        outs.append(host(gla.gla_decode_step(q[:, t].contiguous(), k[:, t].contiguous(),
+                                             v[:, t].contiguous(), x["decay"], state)))
+    check("decode x%d" % T, np.stack(outs, axis=1), ro, host(state), rs, TOL["bf16"])
+    op, sp = gla.gla_chunk_fwd(q[:, :Tp].contiguous(), k[:, :Tp].contiguous(),
+                               v[:, :Tp].contiguous(), x["decay"], initial_state=s0)
+    outs = [host(op)]
+    for t in range(Tp, T):
+        outs.append(host(gla.gla_decode_step(q[:, t].contiguous(), k[:, t].contiguous(),
+                                             v[:, t].contiguous(), x["decay"], sp))[:, None])
+    check("prefill %d + decode" % Tp, np.concatenate(outs, axis=1), ro, host(sp), rs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("segmented", [False, True])
+def test_varlen_ragged_and_empty_sequences(segmented):
+    lens = [0, 1, 63, 64, 65, 300, 0, 1000]
+    x = W.varlen_inputs(61, 0, 0, 4, 96, 192, "bf16", 0.1, W.geometric_decays(4), lengths=lens)
+    ro, rs = oracle_varlen(x)
+    knob = dict(GLA_TARGET_WGS=100000) if segmented else {}
+    with env(**knob):
+        q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+        o, sf = gla.gla_chunk_fwd_varlen(q, k, v, dev(x["cu_seqlens"]), x["decay"], initial_state=s0)
+        torch.cuda.synchronize()
+        check("varlen ragged seg=%s" % segmented, host(o), ro, host(sf), rs, TOL["bf16"], head_axis_o=1)
+        # sequences are independent: each equals its own fixed-length call
+        cu = x["cu_seqlens"]
+        for n, L in enumerate(lens):
+            if L == 0:
+                assert torch.equal(sf[n], s0[n])
+                continue
+            a, b = int(cu[n]), int(cu[n + 1])
+            on, sn = gla.gla_chunk_fwd(q[None, a:b], k[None, a:b], v[None, a:b], x["decay"],
+                                       initial_state=s0[n:n + 1].contiguous())
+            torch.cuda.synchronize()
+            assert rel_err(host(on)[0], host(o)[a:b]) <= TOL["bf16"]
+            assert rel_err(host(sn)[0], host(sf)[n]) <= TOL["bf16"]
+
+
+def test_varlen_fp32_path():
+    x = W.varlen_inputs(62, 0, 0, 2, 32, 64, "f32", 0.1, np.array([0.9, 0.99], np.float32),
+                        lengths=[5, 0, 130, 64])
+    o, sf = gla.gla_chunk_fwd_varlen(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["cu_seqlens"]),
+                                     x["decay"], initial_state=dev(x["s0"]))
+    torch.cuda.synchronize()
+    ro, rs = oracle_varlen(x)
+    check("varlen fp32", host(o), ro, host(sf), rs, TOL["f32"], head_axis_o=1)
+
+
+def test_causality_future_tokens_do_not_leak():
+    """Changing tokens after t0 leaves outputs up to t0 unchanged; NaN placed
+    in the next chunk never reaches earlier outputs. (A NaN inside the same
+    chunk would reach them through 0 * NaN in the masked product.)"""
+    T, t0 = 192, 100
+    x = W.prefill_inputs(71, 1, T, 2, 96, 192, "bf16", None, W.geometric_decays(2))
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    o, _ = gla.gla_chunk_fwd(q, k, v, x["decay"])
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in (q2, k2, v2):
+        t[:, t0 + 1:] = 7.0
+    o2, _ = gla.gla_chunk_fwd(q2, k2, v2, x["decay"])
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :t0 + 1], o2[:, :t0 + 1])
+    for t in (q2, k2, v2):
+        t[:, 128:] = float("nan")
+    o3, _ = gla.gla_chunk_fwd(q2, k2, v2, x["decay"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o3[:, :128]).all()
+    assert torch.equal(o[:, :t0 + 1], o3[:, :t0 + 1])
+
+
+def test_run_to_run_bitwise_determinism():
+    x = W.prefill_inputs(81, 1, 3000, 16, 96, 192, "bf16", 0.1)
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    o1, s1 = gla.gla_chunk_fwd(q, k, v, x["decay"], initial_state=s0)
+    o2, s2 = gla.gla_chunk_fwd(q, k, v, x["decay"], initial_state=s0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
