@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the Simple GLA hot path on one MI355X.
+
+A step is one call of the chunked forward on the Laplace-shaped prefill
+workload (B=8, T=2048, H=16, dk=96, dv=192, bf16, C=64, geometric decays):
+16,384 tokens through all 16 heads of one layer, inputs resident in HBM.
+The headline `value` is tokens per second over exactly `--steps` timed
+steps. Four input/output buffer sets are rotated so that no step finds its
+inputs in the 256 MB last-level cache.
+
+The same JSON line also carries:
+  roofline      the dominant kernel (the MFMA chunk kernel; HBM-bound):
+                algorithmic bytes per launch / mean launch duration from HIP
+                events recorded on the launch stream around every timed step;
+  cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
+                sample of the same workload;
+  secondary     long_context (B1 T65536), batched_decode (1,280 sequences,
+                100 consecutive steps) and varlen (32 packed sequences),
+                each with its own throughput and HBM roofline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       [--no-secondary] [--only {prefill,long,decode,varlen}]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GLA fwd tokens/s (H16,dk96,dv192) + decode seq-steps/s; % MFMA / HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+H, DK, DV = 16, 96, 192
+# algorithmic bytes per token (all heads): q, k, v read once, o written once, bf16
+PREFILL_BYTES_PER_TOKEN = H * (DK + DK + DV + DV) * 2
+STATE_BYTES = H * DK * DV * 4  # one sequence's fp32 state, all heads
+# chunked-form flops per token at C = 64 (causal triangle counted once)
+PREFILL_FLOPS_PER_TOKEN = H * (65 * (DK + DV) + 4 * DK * DV)
+# decode bytes per seq-step: state read + write, bf16 q, k, v in and o out
+DECODE_BYTES_PER_SEQSTEP = 2 * STATE_BYTES + H * (DK + DK + DV) * 2 + H * DV * 2
+DECODE_FLOPS_PER_SEQSTEP = H * DK * DV * 5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed(fn, steps, warmup, stream_events=True):
+    """Run fn(i) for warmup + steps iterations; time exactly `steps` between
+    two device synchronisations and record HIP events around every timed
+    call on the current stream. Returns (wall_s, mean_event_ms)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)] if stream_events else []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if stream_events:
+            ev[i][0].record()
+        fn(warmup + i)
+        if stream_events:
+            ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_ms = (sum(a.elapsed_time(b) for a, b in ev) / steps) if stream_events else None
+    return wall, mean_ms
+
+
+def roofline(bytes_per_launch, launch_ms, bound="hbm"):
+    ach = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+    return {"bound": bound, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(steps, warmup):
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    spec = W.WORKLOADS["laplace_prefill"]
+    B, T = spec["B"], spec["T"]
+    lam = W.decays_for(spec)
+    x = W.spec_inputs("laplace_prefill")
+    dev = torch.device("cuda")
+    sets = []
+    for r in range(4):  # rotate buffer sets past the last-level cache
+        q, k, v = (W.as_torch(x[n], dev) for n in ("q", "k", "v"))
+        if r:
+            q, k, v = q.clone(), k.clone(), v.clone()
+        o = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
+        sf = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+        sets.append((q, k, v, o, sf))
+    ws = gla.lib().gla_chunk_fwd_workspace_bytes(1, B, T, H, DK, DV, 64)
+    assert ws == 0, "the headline shape runs as one kernel without scratch"
+
+    def step(i):
+        q, k, v, o, sf = sets[i % 4]
+        gla.gla_chunk_fwd(q, k, v, lam, chunk=64, out=o, final_state=sf)
+
+    wall, ev_ms = timed(step, steps, warmup)
+    tokens = B * T
+    bytes_call = tokens * PREFILL_BYTES_PER_TOKEN + B * STATE_BYTES
+    flops_call = tokens * PREFILL_FLOPS_PER_TOKEN
+    res = dict(value=tokens * steps / wall, ms_per_step=wall / steps * 1e3,
+               event_ms=ev_ms, bytes=bytes_call, flops=flops_call, x=x, lam=lam)
+    res["roofline"] = roofline(bytes_call, ev_ms)
+    res["mfma_frac"] = flops_call / (ev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    return res
+
+
+def bench_long(steps, warmup):
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    spec = W.WORKLOADS["long_context"]
+    B, T = spec["B"], spec["T"]
+    lam = W.decays_for(spec)
+    dev = torch.device("cuda")
+    sets = []
+    for r in range(2):
+        q, k, v, s0 = W.device_normal_inputs(spec["seed"] + 100 * r, (B, T), H, DK, DV, dev,
+                                             (B, H, DK, DV), spec["s0_sigma"])
+        o = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
+        sf = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+        sets.append((q, k, v, s0, o, sf))
+    need = gla.lib().gla_chunk_fwd_workspace_bytes(1, B, T, H, DK, DV, 64)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, s0, o, sf = sets[i % 2]
+        gla.gla_chunk_fwd(q, k, v, lam, initial_state=s0, chunk=64, out=o,
+                          final_state=sf, workspace=ws)
+
+    wall, ev_ms = timed(step, steps, warmup)
+    tokens = B * T
+    bytes_call = tokens * PREFILL_BYTES_PER_TOKEN + 2 * B * STATE_BYTES
+    return {"workload": "long_context", "config": {"B": B, "T": T, "chunk": 64},
+            "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_call": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(bytes_call, ev_ms),
+                             kernel="whole call (state pass + combine + outputs)"),
+            "mfma_frac": round(tokens * PREFILL_FLOPS_PER_TOKEN / (ev_ms * 1e-3) / 1e12
+                               / BF16_PEAK_TFLOPS, 4),
+            "workspace_bytes": need}
+
+
+def bench_decode(warmup_runs=1):
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    spec = W.WORKLOADS["batched_decode"]
+    N, steps = spec["N"], spec["steps"]
+    lam = W.decays_for(spec)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(spec["seed"])
+    state = torch.randn(N, H, DK, DV, generator=g, device=dev).mul_(spec["state_sigma"])
+    q, k, v, _ = W.device_normal_inputs(spec["seed"] + 1, (steps, N), H, DK, DV, dev)
+    o = torch.empty(N, H, DV, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        t = i % steps
+        gla.gla_decode_step(q[t], k[t], v[t], lam, state, out=o)
+
+    wall, ev_ms = timed(step, steps, warmup_runs * steps)
+    return {"workload": "batched_decode", "config": {"N": N, "steps": steps},
+            "value": round(N * steps / wall, 1), "unit": "seq-steps/s",
+            "ms_per_step": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(N * DECODE_BYTES_PER_SEQSTEP, ev_ms),
+                             kernel="decode_kernel"),
+            "tokens_per_s_all_heads": round(N * steps / wall, 1)}
+
+
+def bench_varlen(steps, warmup):
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    spec = W.WORKLOADS["varlen"]
+    lam = W.decays_for(spec)
+    lens = W.varlen_lengths(spec["seed"], spec["N"], spec["max_len"])
+    import numpy as np
+    cu_np = np.zeros(len(lens) + 1, np.int32)
+    cu_np[1:] = np.cumsum(lens)
+    total = int(cu_np[-1])
+    N = len(lens)
+    dev = torch.device("cuda")
+    q, k, v, s0 = W.device_normal_inputs(spec["seed"], (total,), H, DK, DV, dev,
+                                         (N, H, DK, DV), spec["s0_sigma"])
+    cu = torch.from_numpy(cu_np).to(dev)
+    o = torch.empty(total, H, DV, dtype=torch.bfloat16, device=dev)
+    sf = torch.empty(N, H, DK, DV, dtype=torch.float32, device=dev)
+    need = gla.lib().gla_chunk_fwd_varlen_workspace_bytes(1, N, total, H, DK, DV, 64)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        gla.gla_chunk_fwd_varlen(q, k, v, cu, lam, initial_state=s0, chunk=64, out=o,
+                                 final_state=sf, workspace=ws)
+
+    wall, ev_ms = timed(step, steps, warmup)
+    bytes_call = total * PREFILL_BYTES_PER_TOKEN + 2 * N * STATE_BYTES
+    return {"workload": "varlen", "config": {"N": N, "total_tokens": total,
+                                             "max_len": int(lens.max()), "chunk": 64},
+            "value": round(total * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_call": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel="whole call"),
+            "workspace_bytes": need}
+
+
+def cpu_baseline(x, lam, budget_s=10.0):
+    """The fp64 oracle on this host, on whole sequences of the headline
+    workload, repeated until about `budget_s` seconds have passed."""
+    from oracle import oracle as O
+    threads = O.default_threads()
+    B = x["q"].shape[0]
+    T = x["q"].shape[1]
+    t0 = time.perf_counter()
+    seqs = 0
+    b = 0
+    while True:
+        O.gla_fwd(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], lam,
+                  threads=threads)
+        seqs += 1
+        b = (b + 1) % B
+        el = time.perf_counter() - t0
+        if el >= budget_s or seqs >= 4 * B:
+            break
+    return {"value": round(seqs * T / el, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d whole sequences (T=%d, all 16 heads) of the laplace_prefill "
+                      "workload, fp64 token-by-token recurrence, %.1f s wall" % (seqs, T, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "long", "decode", "varlen"])
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from chunked_gated_recurrent_amd import gla
+    gla.lib()
+
+    if args.only:
+        fn = {"prefill": lambda: bench_prefill(args.steps, args.warmup),
+              "long": lambda: bench_long(args.steps, args.warmup),
+              "decode": lambda: bench_decode(),
+              "varlen": lambda: bench_varlen(args.steps, args.warmup)}[args.only]
+        r = fn()
+        r.pop("x", None)
+        r.pop("lam", None)
+        print(json.dumps(r, default=float))
+        return
+
+    log("prefill: laplace_prefill B8 T2048 ...")
+    pre = bench_prefill(args.steps, args.warmup)
+    secondary = {}
+    if not args.no_secondary:
+        log("long_context ...")
+        secondary["long_context"] = bench_long(max(10, args.steps // 10), 3)
+        log("batched_decode ...")
+        secondary["batched_decode"] = bench_decode()
+        log("varlen ...")
+        secondary["varlen"] = bench_varlen(max(10, args.steps // 10), 3)
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(pre["x"], pre["lam"])
+    line = {
+        "metric": METRIC,
+        "value": round(pre["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "laplace_prefill", "B": 8, "T": 2048, "H": H, "dk": DK,
+                   "dv": DV, "chunk": 64, "decays": "geometric, memory 32..4096 tokens",
+                   "initial_state": "zero", "buffer_sets": 4},
+        "roofline": dict(pre["roofline"], kernel="fwd_mfma_kernel<64,96,96>",
+                         bytes_per_launch=pre["bytes"], launch_ms=round(pre["event_ms"], 5)),
+        "mfma_frac": round(pre["mfma_frac"], 4),
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -27,102 +27,12 @@
 //              (read-modify-write), float4 per lane, readout reduced in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
+#include "gla_device.h"
 #include "gla_internal.h"
 
 namespace gla {
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// small helpers
-// ---------------------------------------------------------------------------
-// lambda^n by binary exponentiation in fp64, rounded once to fp32.
-__device__ __forceinline__ float pow_f64(float lam, long long n) {
-  double r = 1.0, x = (double)lam;
-  while (n > 0) {
-    if (n & 1) r *= x;
-    x *= x;
-    n >>= 1;
-  }
-  return (float)r;
-}
-
-__device__ __forceinline__ int clampi(int x, int lo, int hi) {
-  return x < lo ? lo : (x > hi ? hi : x);
-}
-
-struct Item {
-  int n, t0, t1, flags;
-};
-
-// Item `idx` of the plan; false when idx is past the last item.
-__device__ __forceinline__ bool load_item(const Plan &p, int idx, Item &it) {
-  if (p.mode == kPlanFixed) {
-    if (idx >= p.max_items) return false;
-    const int n = idx / p.G;
-    const int g = idx - n * p.G;
-    const int base = n * p.T;
-    it.n = n;
-    it.t0 = base + g * p.seg_len;
-    it.t1 = min(it.t0 + p.seg_len, base + p.T);
-    it.flags = (g == 0 ? kFirstSeg : 0) | (g == p.G - 1 ? kLastSeg : 0);
-    return true;
-  }
-  if (p.mode == kPlanVarlenDirect) {
-    if (idx >= p.n_seq) return false;
-    const int a = clampi(p.cu[idx], 0, p.total_T);
-    const int b = clampi(p.cu[idx + 1], a, p.total_T);
-    it.n = idx;
-    it.t0 = a;
-    it.t1 = b;
-    it.flags = kFirstSeg | kLastSeg;
-    return true;
-  }
-  const int cnt = min(p.index[0], p.max_items);
-  if (idx >= cnt) return false;
-  const int4 x = p.items[idx];
-  it.n = x.x;
-  it.t0 = x.y;
-  it.t1 = x.z;
-  it.flags = x.w;
-  return true;
-}
-
-// Sequence n's item range [first, last) in the plan.
-__device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
-                                          int &last) {
-  if (p.mode == kPlanFixed) {
-    first = n * p.G;
-    last = first + p.G;
-  } else if (p.mode == kPlanVarlenDirect) {
-    first = n;
-    last = n + 1;
-  } else {
-    const int cap = p.max_items;
-    first = clampi(p.index[1 + n], 0, cap);
-    last = clampi(p.index[2 + n], first, cap);
-  }
-}
-
-// Workgroup -> (unit, dv tile) with the dv tiles of one unit on the same XCD
-// (workgroups are dealt to the 8 XCDs round-robin by id), so that the
-// q/k re-reads of the sibling tiles hit that XCD's L2.
-__device__ __forceinline__ void xcd_unit(int ndt, int &unit, int &dtile) {
-  const int P = blockIdx.x;
-  const int xcd = P & 7;
-  const int r = P >> 3;
-  unit = (r / ndt) * 8 + xcd;
-  dtile = r - (r / ndt) * ndt;
-}
-
-static inline unsigned xcd_grid(long long units, int ndt) {
-  const long long rounds = (units + 7) / 8;
-  return (unsigned)(rounds * 8 * ndt);
-}
 
 // ===========================================================================
 // Chunked forward, bf16 inputs, MFMA
@@ -888,7 +798,9 @@ static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s) {
-  if (fast) {
+  if (fast && !getenv("GLA_FWD_V1")) {
+    launch_fwd_mfma2(state_only, fast_dv_tile(a.dv), p, a, dec, s);
+  } else if (fast) {
     const int dvt = fast_dv_tile(a.dv);
     if (dvt == 96) {
       if (state_only) launch_mfma<96, true>(p, a, dec, s);

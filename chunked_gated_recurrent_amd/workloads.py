@@ -203,3 +203,30 @@ def to_numpy_bits(t) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def device_normal_inputs(seed: int, lead, H: int, dk: int, dv: int, device,
+                         s0_shape=None, s0_sigma=None):
+    """The same recipe drawn on the device with torch's seeded generator
+    (for timing runs of large workloads, where host generation would dominate
+    the wall clock): bf16 q, k, v ~ N(0,1) with q, k scaled by dk**-0.5 in
+    fp32 before rounding; optional fp32 initial state N(0, sigma^2)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    sc = 1.0 / float(np.sqrt(dk))
+    lead = tuple(lead)
+
+    def draw(shape, s):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if s != 1.0:
+            x.mul_(s)
+        return x
+
+    q = draw(lead + (H, dk), sc).to(torch.bfloat16)
+    k = draw(lead + (H, dk), sc).to(torch.bfloat16)
+    v = draw(lead + (H, dv), 1.0).to(torch.bfloat16)
+    s0 = None
+    if s0_shape is not None:
+        s0 = draw(tuple(s0_shape), float(s0_sigma))
+    return q, k, v, s0
