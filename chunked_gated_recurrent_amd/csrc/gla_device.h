@@ -86,20 +86,25 @@ __device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
   }
 }
 
-// Workgroup -> (unit, dv tile) with the dv tiles of one unit on the same XCD
-// (workgroups are dealt to the 8 XCDs round-robin by id), so that the
-// q/k re-reads of the sibling tiles hit that XCD's L2.
-__device__ __forceinline__ void xcd_unit(int ndt, int &unit, int &dtile) {
+// Workgroup -> (unit, dv tile). Workgroups are dealt to the 8 XCDs
+// round-robin by id, so id P runs on XCD P % 8. Units are given to XCDs in
+// contiguous blocks (consecutive heads of one item, and all dv tiles of a
+// unit, share an XCD): rows of q, k, v and o that two neighbouring heads or
+// two dv tiles split at a 128-byte line then meet in the same L2.
+__device__ __forceinline__ void xcd_unit(int ndt, int units, int &unit,
+                                         int &dtile) {
   const int P = blockIdx.x;
   const int xcd = P & 7;
   const int r = P >> 3;
-  unit = (r / ndt) * 8 + xcd;
-  dtile = r - (r / ndt) * ndt;
+  const int per = (units + 7) / 8;
+  const int ur = r / ndt;
+  unit = xcd * per + ur;
+  dtile = r - ur * ndt;
 }
 
 inline unsigned xcd_grid(long long units, int ndt) {
-  const long long rounds = (units + 7) / 8;
-  return (unsigned)(rounds * 8 * ndt);
+  const long long per = (units + 7) / 8;
+  return (unsigned)(per * 8 * ndt);
 }
 
 }  // namespace gla

@@ -61,8 +61,8 @@ hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items, hipStream_
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s);
-void launch_fwd_mfma2(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
-                      const Decay &dec, hipStream_t s);
+void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
+                     const Decay &dec, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,
                           hipStream_t s);
 hipError_t launch_final_gather(const Plan &p, const FwdArgs &a, hipStream_t s);

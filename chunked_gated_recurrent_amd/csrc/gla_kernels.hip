@@ -15,10 +15,7 @@
 // (a scan over segments; U_g is the segment's end state from a zero start).
 //
 // Kernels:
-//   fwd_mfma   bf16, dk = 96: one workgroup (4 waves) per (item, head, dv
-//              tile); chunk tiles staged in LDS; all four contractions on
-//              v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the state
-//              tile lives in registers as MFMA accumulators across chunks.
+//   (the bf16 dk = 96 matrix-core forward lives in gla_fwd_mfma.hip)
 //   fwd_valu   any supported shape, fp32 or bf16 inputs, fp32 arithmetic
 //              on the vector ALUs (the fp32 path and the fallback).
 //   planner    varlen: cuts packed sequences into items on the device.
@@ -27,398 +24,11 @@
 //              (read-modify-write), float4 per lane, readout reduced in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "gla_device.h"
 #include "gla_internal.h"
 
 namespace gla {
-
-// ===========================================================================
-// Chunked forward, bf16 inputs, MFMA
-// ===========================================================================
-//
-// Shapes: DK = dk (96), DVT = dv tile (96 or 64), C = chunk (64), 4 waves.
-// LDS (bf16 unless noted):
-//   sQ  [C][DK+8]    row-major q tile      (B operand of K Q^T and S^T Q^T)
-//   sK  [C][DK+8]    row-major k tile      (A operand of K Q^T)
-//   sKt [DK][C+8]    decay-scaled k, transposed: lambda^(L-1-j) k_j  (A of dS)
-//   sVt [DVT][C+8]   v tile transposed                          (A of O, B of dS)
-//   sSt [DVT][DK+8]  bf16 copy of the carried state, transposed (A of O_inter)
-//   sPow[C+1] fp32   lambda^n
-// The +8 element pads make the 16-byte fragment reads bank-conflict free.
-//
-// Orientation: every product is arranged so that each operand's contraction
-// index is contiguous in LDS, and the fp32 result layout of one MFMA feeds
-// the next without a trip through LDS:
-//   P^T[j][i]    = K Q^T                     (M = j, N = i, K = d)
-//   O^T[c][i]    = lambda^(i+1) S^T Q^T + V^T P^T
-//                  (P^T stays in registers as the B operand: the D layout of
-//                   one 16x16 tile pair is exactly the B layout for a 32-deep
-//                   k step with k-set {4g..4g+3, 16+4g..16+4g+3})
-//   S[d][c]     <- lambda^L S + Kt V         (M = d, N = c, K = j)
-// MFMA v_mfma_f32_16x16x32_bf16 lane layout (lane l, l16 = l % 16, g = l / 16):
-//   A: row l16, 8 k-values of group g; B: column l16, the same 8 k-values;
-//   D: rows 4g..4g+3, column l16.
-template <int C, int DK, int DVT>
-struct MfmaCfg {
-  static constexpr int NT = 256;
-  static constexpr int QS = DK + 8;     // row stride of sQ, sK, sSt (elements)
-  static constexpr int TS = C + 8;      // row stride of sKt, sVt
-  static constexpr int NDT = DK / 16;   // 16-row tiles over dk
-  static constexpr int NCT = DVT / 16;  // 16-col tiles over the dv tile
-  static constexpr int NKS = DK / 32;   // 32-deep k steps over dk
-  static constexpr int NJS = C / 32;    // 32-deep k steps over the chunk
-  static constexpr int NIB = C / 16;    // 16-row blocks of the chunk
-  static constexpr int NJB = C / 4;     // 4-row load blocks
-  static constexpr int NQV = DK / 8;    // 16-byte vectors per q row
-  static constexpr int QV = (C * NQV + NT - 1) / NT;
-  static constexpr int KB = (NJB * (DK / 8) + NT - 1) / NT;
-  static constexpr int VB = (NJB * (DVT / 8) + NT - 1) / NT;
-  // state tiles per wave: a (NDT/2) x (NCT/2) block
-  static constexpr int SDT = NDT / 2;
-  static constexpr int SCT = NCT / 2;
-  static constexpr int LDS_BF16 = 2 * C * QS + DVT * QS + DK * TS + DVT * TS;
-  static_assert(C == 64, "the MFMA kernel is written for 64-token chunks");
-  static_assert(DK % 32 == 0 && DVT % 32 == 0, "tile shapes");
-  static_assert(NDT % 2 == 0 && NCT % 2 == 0, "state tile split");
-};
-
-template <typename V8>
-__device__ __forceinline__ V8 lds8(const bf16 *p) {
-  return *reinterpret_cast<const V8 *>(p);
-}
-
-// 4x8 load block b of a C x W tile -> (row block jb, 8-col group cb).
-// Lane order inside a wave alternates row and column blocks so that both the
-// row-major and the transposed LDS writes of a wave spread over the banks.
-template <int NJB>
-__device__ __forceinline__ void block_rc(int b, int &jb, int &cb) {
-  const int jlo = b & 3, clo = (b >> 2) & 3, rest = b >> 4;
-  constexpr int JH = NJB / 4;
-  jb = jlo + 4 * (rest % JH);
-  cb = clo + 4 * (rest / JH);
-}
-
-template <int C, int DK, int DVT, bool STATE_ONLY>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-    const bf16 *__restrict__ v, bf16 *__restrict__ o,
-    const float *__restrict__ s0, float *__restrict__ s_final,
-    float *__restrict__ slots, Plan plan, Decay dec, float scale, int H,
-    int dv, int final_in_slot) {
-  using Cfg = MfmaCfg<C, DK, DVT>;
-  constexpr int QS = Cfg::QS, TS = Cfg::TS;
-  __shared__ __attribute__((aligned(16))) bf16 smem[Cfg::LDS_BF16];
-  __shared__ float sPow[C + 4];
-  bf16 *sQ = smem;
-  bf16 *sK = sQ + C * QS;
-  bf16 *sSt = sK + C * QS;
-  bf16 *sKt = sSt + DVT * QS;
-  bf16 *sVt = sKt + DK * TS;
-
-  const int ndt = dv / DVT;
-  int unit, dtile;
-  xcd_unit(ndt, unit, dtile);
-  if (unit >= plan.max_items * H) return;
-  const int idx = unit / H;
-  const int h = unit - idx * H;
-  Item it;
-  if (!load_item(plan, idx, it)) return;
-  if (STATE_ONLY && (it.flags & kLastSeg)) return;  // no successor needs it
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
-  const int c0 = dtile * DVT;
-  const long long rowK = (long long)H * DK;  // elements between tokens (q, k)
-  const long long rowV = (long long)H * dv;  // elements between tokens (v, o)
-  const float lam = dec.lam[h];
-  const int len = it.t1 - it.t0;
-  const int nch = (len + C - 1) / C;
-
-  // lambda^n table
-  if (tid <= C) sPow[tid] = pow_f64(lam, tid);
-
-  // ---- state accumulators: wave w owns d tiles [SDT*(w/2), +SDT) and
-  // c tiles [SCT*(w%2), +SCT) of the DK x DVT state
-  const int dt0 = Cfg::SDT * (w >> 1);
-  const int ct0 = Cfg::SCT * (w & 1);
-  f32x4 accS[Cfg::SDT][Cfg::SCT];
-  {
-    // incoming state: s0 (or zeros) for a sequence's first item, else the
-    // combined state left in slot idx-1; a local end state starts from zero
-    const float *src = nullptr;
-    if (!STATE_ONLY) {
-      if (it.flags & kFirstSeg)
-        src = s0 ? s0 + ((long long)it.n * H + h) * DK * dv : nullptr;
-      else
-        src = slots + ((long long)(idx - 1) * H + h) * DK * dv;
-    }
-#pragma unroll
-    for (int a = 0; a < Cfg::SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < Cfg::SCT; ++b) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (src) {
-          const int d = 16 * (dt0 + a) + 4 * g;
-          const int c = c0 + 16 * (ct0 + b) + l16;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = src[(long long)(d + r) * dv + c];
-        }
-        accS[a][b] = x;
-      }
-  }
-
-  // ---- global -> register staging of one chunk
-  uint4 rq[Cfg::QV];
-  uint4 rk[Cfg::KB][4];
-  uint4 rv[Cfg::VB][4];
-  const uint4 zero4 = {0u, 0u, 0u, 0u};
-
-  auto load_chunk = [&](int ch) {
-    const int tb = it.t0 + ch * C;
-    const int L = min(C, it.t1 - tb);
-    if (!STATE_ONLY) {
-#pragma unroll
-      for (int m = 0; m < Cfg::QV; ++m) {
-        const int vi = tid + m * Cfg::NT;
-        const int row = vi / Cfg::NQV, col = vi - row * Cfg::NQV;
-        rq[m] = zero4;
-        if (vi < C * Cfg::NQV && row < L)
-          rq[m] = *reinterpret_cast<const uint4 *>(
-              q + (long long)(tb + row) * rowK + (long long)h * DK + 8 * col);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg::KB; ++m) {
-      const int b = tid + m * Cfg::NT;
-      int jb, cb;
-      block_rc<Cfg::NJB>(b, jb, cb);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rk[m][r] = zero4;
-        if (b < Cfg::NJB * (DK / 8) && 4 * jb + r < L)
-          rk[m][r] = *reinterpret_cast<const uint4 *>(
-              k + (long long)(tb + 4 * jb + r) * rowK + (long long)h * DK + 8 * cb);
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg::VB; ++m) {
-      const int b = tid + m * Cfg::NT;
-      int jb, cb;
-      block_rc<Cfg::NJB>(b, jb, cb);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rv[m][r] = zero4;
-        if (b < Cfg::NJB * (DVT / 8) && 4 * jb + r < L)
-          rv[m][r] = *reinterpret_cast<const uint4 *>(
-              v + (long long)(tb + 4 * jb + r) * rowV + (long long)h * dv + c0 + 8 * cb);
-      }
-    }
-  };
-
-  auto store_chunk = [&](int L) {
-    if (!STATE_ONLY) {
-#pragma unroll
-      for (int m = 0; m < Cfg::QV; ++m) {
-        const int vi = tid + m * Cfg::NT;
-        const int row = vi / Cfg::NQV, col = vi - row * Cfg::NQV;
-        if (vi < C * Cfg::NQV)
-          *reinterpret_cast<uint4 *>(sQ + row * QS + 8 * col) = rq[m];
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg::KB; ++m) {
-      const int b = tid + m * Cfg::NT;
-      if (b < Cfg::NJB * (DK / 8)) {
-        int jb, cb;
-        block_rc<Cfg::NJB>(b, jb, cb);
-        float wgt[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 4 * jb + r;
-          wgt[r] = (j < L) ? sPow[L - 1 - j] : 0.f;
-          if (!STATE_ONLY)
-            *reinterpret_cast<uint4 *>(sK + j * QS + 8 * cb) = rk[m][r];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16x4 t;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bf16x8 kv = __builtin_bit_cast(bf16x8, rk[m][r]);
-            t[r] = (bf16)((float)kv[e] * wgt[r]);
-          }
-          *reinterpret_cast<bf16x4 *>(sKt + (8 * cb + e) * TS + 4 * jb) = t;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < Cfg::VB; ++m) {
-      const int b = tid + m * Cfg::NT;
-      if (b < Cfg::NJB * (DVT / 8)) {
-        int jb, cb;
-        block_rc<Cfg::NJB>(b, jb, cb);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16x4 t;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bf16x8 vv = __builtin_bit_cast(bf16x8, rv[m][r]);
-            t[r] = vv[e];
-          }
-          *reinterpret_cast<bf16x4 *>(sVt + (8 * cb + e) * TS + 4 * jb) = t;
-        }
-      }
-    }
-  };
-
-  auto store_state_lds = [&]() {
-#pragma unroll
-    for (int a = 0; a < Cfg::SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < Cfg::SCT; ++b) {
-        bf16x4 t;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] = (bf16)accS[a][b][r];
-        const int c = 16 * (ct0 + b) + l16;
-        const int d = 16 * (dt0 + a) + 4 * g;
-        *reinterpret_cast<bf16x4 *>(sSt + c * QS + d) = t;
-      }
-  };
-
-  if (nch > 0) load_chunk(0);
-  __syncthreads();  // sPow ready
-  if (nch > 0) {
-    store_chunk(min(C, len));
-    if (!STATE_ONLY) store_state_lds();
-  }
-  __syncthreads();
-
-  for (int ch = 0; ch < nch; ++ch) {
-    const int tb = it.t0 + ch * C;
-    const int L = min(C, it.t1 - tb);
-    if (ch + 1 < nch) load_chunk(ch + 1);
-
-    if (!STATE_ONLY) {
-      // ---------------- outputs of rows i in block I = w ----------------
-      const int I = w;
-      const int i = 16 * I + l16;
-      bf16x8 qf[Cfg::NKS];
-#pragma unroll
-      for (int s = 0; s < Cfg::NKS; ++s) qf[s] = lds8<bf16x8>(sQ + i * QS + 32 * s + 8 * g);
-
-      // P^T tiles (J <= I), masked and decay-weighted in fp32
-      f32x4 p[Cfg::NIB];
-#pragma unroll
-      for (int J = 0; J < Cfg::NIB; ++J) {
-        p[J] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        if (J <= I) {
-#pragma unroll
-          for (int s = 0; s < Cfg::NKS; ++s) {
-            const bf16x8 kf = lds8<bf16x8>(sK + (16 * J + l16) * QS + 32 * s + 8 * g);
-            p[J] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], p[J], 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int diff = i - (16 * J + 4 * g + r);
-            p[J][r] = diff >= 0 ? p[J][r] * sPow[diff] : 0.f;
-          }
-        }
-      }
-      bf16x8 pb[Cfg::NJS];
-#pragma unroll
-      for (int s = 0; s < Cfg::NJS; ++s) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb[s][r] = (bf16)p[2 * s][r];
-          pb[s][4 + r] = (bf16)p[2 * s + 1][r];
-        }
-      }
-
-      const float lam_i1 = sPow[i + 1];
-      const bool row_ok = i < L;
-      bf16 *orow = o + (long long)(tb + i) * rowV + (long long)h * dv + c0;
-#pragma unroll
-      for (int ct = 0; ct < Cfg::NCT; ++ct) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < Cfg::NKS; ++s) {
-          const bf16x8 sf = lds8<bf16x8>(sSt + (16 * ct + l16) * QS + 32 * s + 8 * g);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sf, qf[s], acc, 0, 0, 0);
-        }
-        acc *= lam_i1;
-#pragma unroll
-        for (int s = 0; s < Cfg::NJS; ++s) {
-          if (2 * s <= I) {
-            const bf16 *vp = sVt + (16 * ct + l16) * TS + 32 * s + 4 * g;
-            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 16);
-            const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[s], acc, 0, 0, 0);
-          }
-        }
-        if (row_ok) {
-          bf16x4 t;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) t[r] = (bf16)(scale * acc[r]);
-          *reinterpret_cast<bf16x4 *>(orow + 16 * ct + 4 * g) = t;
-        }
-      }
-    }
-
-    // ---------------- state: S <- lambda^L S + Kt V ----------------
-    {
-      const float lamL = sPow[L];
-#pragma unroll
-      for (int a = 0; a < Cfg::SDT; ++a)
-#pragma unroll
-        for (int b = 0; b < Cfg::SCT; ++b) accS[a][b] *= lamL;
-#pragma unroll
-      for (int s = 0; s < Cfg::NJS; ++s) {
-        bf16x8 af[Cfg::SDT], bfr[Cfg::SCT];
-#pragma unroll
-        for (int a = 0; a < Cfg::SDT; ++a)
-          af[a] = lds8<bf16x8>(sKt + (16 * (dt0 + a) + l16) * TS + 32 * s + 8 * g);
-#pragma unroll
-        for (int b = 0; b < Cfg::SCT; ++b)
-          bfr[b] = lds8<bf16x8>(sVt + (16 * (ct0 + b) + l16) * TS + 32 * s + 8 * g);
-#pragma unroll
-        for (int a = 0; a < Cfg::SDT; ++a)
-#pragma unroll
-          for (int b = 0; b < Cfg::SCT; ++b)
-            accS[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], accS[a][b], 0, 0, 0);
-      }
-    }
-
-    __syncthreads();  // every wave is done reading this chunk's tiles
-    if (ch + 1 < nch) {
-      store_chunk(min(C, it.t1 - (tb + C)));
-      if (!STATE_ONLY) store_state_lds();
-    }
-    __syncthreads();
-  }
-
-  // ---- final state: local end state to its slot, or the sequence's final
-  float *dst = nullptr;
-  if (STATE_ONLY || ((it.flags & kLastSeg) && final_in_slot))
-    dst = slots + ((long long)idx * H + h) * DK * dv;
-  else if ((it.flags & kLastSeg) && s_final)
-    dst = s_final + ((long long)it.n * H + h) * DK * dv;
-  if (dst) {
-#pragma unroll
-    for (int a = 0; a < Cfg::SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < Cfg::SCT; ++b) {
-        const int d = 16 * (dt0 + a) + 4 * g;
-        const int c = c0 + 16 * (ct0 + b) + l16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(long long)(d + r) * dv + c] = accS[a][b][r];
-      }
-  }
-}
 
 // ===========================================================================
 // Chunked forward on the vector ALUs (fp32 arithmetic, any supported shape)
@@ -454,7 +64,7 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
 
   const int ndt = dv / kValuDvt;
   int unit, dtile;
-  xcd_unit(ndt, unit, dtile);
+  xcd_unit(ndt, plan.max_items * H, unit, dtile);
   if (unit >= plan.max_items * H) return;
   const int idx = unit / H;
   const int h = unit - idx * H;
@@ -768,17 +378,6 @@ hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items,
   return hipGetLastError();
 }
 
-template <int DVT, bool SO>
-static void launch_mfma(const Plan &p, const FwdArgs &a, const Decay &dec,
-                        hipStream_t s) {
-  const int ndt = a.dv / DVT;
-  const unsigned grid = xcd_grid((long long)p.max_items * a.H, ndt);
-  hipLaunchKernelGGL((fwd_mfma_kernel<64, 96, DVT, SO>), dim3(grid), dim3(256),
-                     0, s, (const bf16 *)a.q, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (bf16 *)a.o, a.s0, a.s_final, a.slots,
-                     p, dec, a.scale, a.H, a.dv, a.final_in_slot);
-}
-
 template <typename Tin, bool SO>
 static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
                         int C, hipStream_t s) {
@@ -798,17 +397,8 @@ static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s) {
-  if (fast && !getenv("GLA_FWD_V1")) {
-    launch_fwd_mfma2(state_only, fast_dv_tile(a.dv), p, a, dec, s);
-  } else if (fast) {
-    const int dvt = fast_dv_tile(a.dv);
-    if (dvt == 96) {
-      if (state_only) launch_mfma<96, true>(p, a, dec, s);
-      else launch_mfma<96, false>(p, a, dec, s);
-    } else {
-      if (state_only) launch_mfma<64, true>(p, a, dec, s);
-      else launch_mfma<64, false>(p, a, dec, s);
-    }
+  if (fast) {
+    launch_fwd_mfma(state_only, fast_dv_tile(a.dv), p, a, dec, s);
   } else {
     const int C = generic_chunk(chunk);
     if (dt == 1) {
