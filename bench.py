@@ -174,7 +174,8 @@ def bench_decode(warmup_runs=1):
             "value": round(N * steps / wall, 1), "unit": "seq-steps/s",
             "ms_per_step": round(wall / steps * 1e3, 4),
             "roofline": dict(roofline(N * DECODE_BYTES_PER_SEQSTEP, ev_ms),
-                             kernel="decode_kernel"),
+                             kernel="decode_kernel<bf16,16>",
+                             traffic=measured_traffic("decode_kernel<bf16,16>@batched_decode")),
             "tokens_per_s_all_heads": round(N * steps / wall, 1)}
 
 
@@ -214,27 +215,58 @@ def bench_varlen(steps, warmup):
 
 
 def cpu_baseline(x, lam, budget_s=10.0):
-    """The fp64 oracle on this host, on whole sequences of the headline
-    workload, repeated until about `budget_s` seconds have passed."""
+    """The fp64 oracle on this host, on the whole headline workload (8
+    sequences x 2,048 tokens x 16 heads), repeated until about `budget_s`
+    seconds have passed."""
     from oracle import oracle as O
     threads = O.default_threads()
-    B = x["q"].shape[0]
-    T = x["q"].shape[1]
+    B, T = x["q"].shape[0], x["q"].shape[1]
     t0 = time.perf_counter()
-    seqs = 0
-    b = 0
+    calls = 0
     while True:
-        O.gla_fwd(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], lam,
-                  threads=threads)
-        seqs += 1
-        b = (b + 1) % B
+        O.gla_fwd(x["q"], x["k"], x["v"], lam, threads=threads)
+        calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or seqs >= 4 * B:
+        if el >= budget_s:
             break
-    return {"value": round(seqs * T / el, 1), "unit": "tokens/s", "cores": threads,
+    return {"value": round(calls * B * T / el, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d whole sequences (T=%d, all 16 heads) of the laplace_prefill "
-                      "workload, fp64 token-by-token recurrence, %.1f s wall" % (seqs, T, el)}
+            "sample": "%d passes over the laplace_prefill workload (B=%d, T=%d, 16 heads), "
+                      "fp64 token-by-token recurrence, %.1f s wall" % (calls, B, T, el)}
+
+
+def copy_bandwidth(gib=1.0):
+    """Achievable HBM bandwidth of a plain device copy (read + write), for
+    context beside the datasheet peak."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(2 * n * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken with the current kernel source (else None)."""
+    f = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        from chunked_gated_recurrent_amd.profiling import source_sha256
+        with open(f) as fh:
+            rec = json.load(fh).get(key)
+        if rec and rec.get("source_sha256") == source_sha256():
+            return int(rec["traffic_bytes"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def main():
@@ -277,6 +309,7 @@ def main():
         secondary["batched_decode"] = bench_decode()
         log("varlen ...")
         secondary["varlen"] = bench_varlen(max(10, args.steps // 10), 3)
+    copy_bw = copy_bandwidth()
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
@@ -297,8 +330,10 @@ def main():
         "config": {"workload": "laplace_prefill", "B": 8, "T": 2048, "H": H, "dk": DK,
                    "dv": DV, "chunk": 64, "decays": "geometric, memory 32..4096 tokens",
                    "initial_state": "zero", "buffer_sets": 4},
-        "roofline": dict(pre["roofline"], kernel="fwd_mfma_kernel<64,96,96>",
+        "roofline": dict(pre["roofline"], kernel="fwd_out_kernel<96>",
+                         traffic=measured_traffic("fwd_out_kernel<96>@laplace_prefill"),
                          bytes_per_launch=pre["bytes"], launch_ms=round(pre["event_ms"], 5)),
+        "hbm_copy_GBps": copy_bw,
         "mfma_frac": round(pre["mfma_frac"], 4),
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -285,21 +285,25 @@ __global__ __launch_bounds__(256) void state_fill_kernel(long long n4,
 // ===========================================================================
 // One workgroup per (sequence, head). Thread t owns 4 consecutive columns
 // (cq = t % quads) of RPT consecutive rows (row group t / quads). All RPT
-// float4 loads of the state are issued before any arithmetic so that each
+// 16-byte loads of the state are issued before any arithmetic, so each
 // thread keeps RPT x 16 bytes in flight; every state byte is read once and
-// written once.
+// written once, both with non-temporal hints (the 1.5 GB state of a large
+// batch has no reuse within a step).
+typedef float f32x4n __attribute__((ext_vector_type(4)));
+
 template <typename Tin, int RPT>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(512) void decode_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k,
     const Tin *__restrict__ v, Decay dec, float scale, float *__restrict__ state,
     Tin *__restrict__ o, int H, int dk, int dv, int rpt_rt) {
   extern __shared__ float dsm[];
   const int quads = dv / 4;
-  const int rg_n = dk / (RPT > 0 ? RPT : rpt_rt);
-  float *sq = dsm;             // [dk]
-  float *sk = sq + dk;         // [dk]
-  float *sv = sk + dk;         // [dv]
-  float *part = sv + dv;       // [rg_n][dv]
+  const int rpt = RPT > 0 ? RPT : rpt_rt;
+  const int rg_n = dk / rpt;
+  float *sq = dsm;        // [dk]
+  float *sk = sq + dk;    // [dk]
+  float *sv = sk + dk;    // [dv]
+  float *part = sv + dv;  // [rg_n][dv]
   const long long unit = blockIdx.x;
   const int h = (int)(unit % H);
   const int tid = threadIdx.x;
@@ -311,47 +315,36 @@ __global__ __launch_bounds__(256) void decode_kernel(
   __syncthreads();
   const float lam = dec.lam[h];
   const int cq = tid % quads, rg = tid / quads;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  f32x4n acc = {0.f, 0.f, 0.f, 0.f};
   if (rg < rg_n) {
-    const float4 vq = *reinterpret_cast<const float4 *>(sv + 4 * cq);
+    const f32x4n vq = *reinterpret_cast<const f32x4n *>(sv + 4 * cq);
     float *base = state + unit * (long long)dk * dv + 4 * cq;
+    const int r0 = rg * rpt;
+    auto step = [&](f32x4n x, int r) {
+      const float kr = sk[r], qr = sq[r];
+      x.x = fmaf(lam, x.x, kr * vq.x);
+      x.y = fmaf(lam, x.y, kr * vq.y);
+      x.z = fmaf(lam, x.z, kr * vq.z);
+      x.w = fmaf(lam, x.w, kr * vq.w);
+      __builtin_nontemporal_store(x, reinterpret_cast<f32x4n *>(base + (long long)r * dv));
+      acc.x = fmaf(qr, x.x, acc.x);
+      acc.y = fmaf(qr, x.y, acc.y);
+      acc.z = fmaf(qr, x.z, acc.z);
+      acc.w = fmaf(qr, x.w, acc.w);
+    };
     if constexpr (RPT > 0) {
-      const int r0 = rg * RPT;
-      float4 s[RPT];
+      f32x4n s[RPT];
 #pragma unroll
       for (int m = 0; m < RPT; ++m)
-        s[m] = *reinterpret_cast<const float4 *>(base + (long long)(r0 + m) * dv);
+        s[m] = __builtin_nontemporal_load(reinterpret_cast<f32x4n *>(base + (long long)(r0 + m) * dv));
 #pragma unroll
-      for (int m = 0; m < RPT; ++m) {
-        const float kr = sk[r0 + m], qr = sq[r0 + m];
-        float4 x = s[m];
-        x.x = fmaf(lam, x.x, kr * vq.x);
-        x.y = fmaf(lam, x.y, kr * vq.y);
-        x.z = fmaf(lam, x.z, kr * vq.z);
-        x.w = fmaf(lam, x.w, kr * vq.w);
-        *reinterpret_cast<float4 *>(base + (long long)(r0 + m) * dv) = x;
-        acc.x = fmaf(qr, x.x, acc.x);
-        acc.y = fmaf(qr, x.y, acc.y);
-        acc.z = fmaf(qr, x.z, acc.z);
-        acc.w = fmaf(qr, x.w, acc.w);
-      }
+      for (int m = 0; m < RPT; ++m) step(s[m], r0 + m);
     } else {
-      const int r0 = rg * rpt_rt;
-      for (int m = 0; m < rpt_rt; ++m) {
-        float4 x = *reinterpret_cast<const float4 *>(base + (long long)(r0 + m) * dv);
-        const float kr = sk[r0 + m], qr = sq[r0 + m];
-        x.x = fmaf(lam, x.x, kr * vq.x);
-        x.y = fmaf(lam, x.y, kr * vq.y);
-        x.z = fmaf(lam, x.z, kr * vq.z);
-        x.w = fmaf(lam, x.w, kr * vq.w);
-        *reinterpret_cast<float4 *>(base + (long long)(r0 + m) * dv) = x;
-        acc.x = fmaf(qr, x.x, acc.x);
-        acc.y = fmaf(qr, x.y, acc.y);
-        acc.z = fmaf(qr, x.z, acc.z);
-        acc.w = fmaf(qr, x.w, acc.w);
-      }
+      for (int m = 0; m < rpt; ++m)
+        step(__builtin_nontemporal_load(reinterpret_cast<f32x4n *>(base + (long long)(r0 + m) * dv)),
+             r0 + m);
     }
-    *reinterpret_cast<float4 *>(part + rg * dv + 4 * cq) = acc;
+    *reinterpret_cast<f32x4n *>(part + rg * dv + 4 * cq) = acc;
   }
   __syncthreads();
   for (int c = tid; c < dv; c += blockDim.x) {
@@ -443,10 +436,11 @@ hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
                          const void *k, const void *v, const Decay &dec,
                          float scale, float *state, void *o, hipStream_t s) {
   const int quads = dv / 4;
-  // row groups: the largest divisor of dk with quads * groups <= 256
+  // row groups: the largest divisor of dk with quads * groups <= 320 threads
+  // (for dk 96, dv 192: 6 groups of 16 rows, 288 threads)
   int rg = 1;
   for (int c = 1; c <= dk; ++c)
-    if (dk % c == 0 && quads * c <= 256) rg = c;
+    if (dk % c == 0 && quads * c <= 320) rg = c;
   const int rpt = dk / rg;
   const unsigned threads = (unsigned)(quads * rg);
   const size_t lds = sizeof(float) * (size_t)(2 * dk + dv + rg * dv);
@@ -456,10 +450,10 @@ hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
                      (const T *)q, (const T *)k, (const T *)v, dec, scale,     \
                      state, (T *)o, H, dk, dv, rpt)
   if (dt == 1) {
-    if (rpt == 24) GLA_DECODE(bf16, 24);
+    if (rpt == 16) GLA_DECODE(bf16, 16);
     else GLA_DECODE(bf16, 0);
   } else {
-    if (rpt == 24) GLA_DECODE(float, 24);
+    if (rpt == 16) GLA_DECODE(float, 16);
     else GLA_DECODE(float, 0);
   }
 #undef GLA_DECODE

@@ -1,0 +1,137 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+    python -m chunked_gated_recurrent_amd.profiling stats DIR [--kernel SUBSTR]
+        kernel-trace statistics (calls, mean / min / max duration) from the
+        *_kernel_stats.csv files rocprofv3 writes with --stats -f csv
+    python -m chunked_gated_recurrent_amd.profiling counters DIR --kernel SUBSTR
+        mean per-dispatch value of every counter in *_counter_collection.csv
+    python -m chunked_gated_recurrent_amd.profiling copy [GIB]
+        a plain device copy of GIB GiB (three times), the reference kernel whose
+        FETCH_SIZE / WRITE_SIZE readings calibrate the HBM byte counters
+    python -m chunked_gated_recurrent_amd.profiling traffic FETCH_DIR WRITE_DIR
+            CAL_FETCH_DIR CAL_WRITE_DIR --kernel SUBSTR [--gib 1]
+        HBM bytes per dispatch of a kernel: each counter divided by the ratio
+        counter / true bytes that the same counter shows for the copy kernel
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _find(d, suffix):
+    return sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+
+
+def kernel_stats(d, kernel=None):
+    rows = []
+    for f in _find(d, "kernel_stats.csv"):
+        for r in csv.DictReader(open(f)):
+            if kernel and kernel not in r["Name"]:
+                continue
+            rows.append(dict(name=r["Name"], calls=int(r["Calls"]),
+                             total_ns=float(r["TotalDurationNs"]),
+                             avg_ns=float(r["AverageNs"]), min_ns=float(r["MinNs"]),
+                             max_ns=float(r["MaxNs"]), pct=float(r["Percentage"])))
+    return rows
+
+
+def counters(d, kernel):
+    """{counter: mean per dispatch} over dispatches whose name contains
+    `kernel` (per-dispatch values summed over their instances first)."""
+    per = defaultdict(lambda: defaultdict(float))
+    for f in _find(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            per[r["Counter_Name"]][(f, r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {c: sum(v.values()) / len(v) for c, v in per.items() if v}, \
+        {c: len(v) for c, v in per.items()}
+
+
+def copy_kernel(gib=1.0):
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied %d bytes three times" % (n * 4))
+
+
+def source_sha256():
+    """sha256 over every source file of the HIP library (names and bytes), so
+    that any change to the kernels invalidates recorded counter readings."""
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel, gib=1.0):
+    true_bytes = int(gib * (1 << 30)) // 4 * 4
+    f_kb, fn = counters(fetch_dir, kernel)
+    w_kb, wn = counters(write_dir, kernel)
+    cf, _ = counters(cal_fetch_dir, "copyBuffer")
+    cw, _ = counters(cal_write_dir, "copyBuffer")
+    f_ratio = cf["FETCH_SIZE"] * 1024 / true_bytes
+    w_ratio = cw["WRITE_SIZE"] * 1024 / true_bytes
+    fetch = f_kb["FETCH_SIZE"] * 1024 / f_ratio
+    write = w_kb["WRITE_SIZE"] * 1024 / w_ratio
+    return dict(kernel=kernel, dispatches=fn.get("FETCH_SIZE", 0),
+                fetch_counter_kb=f_kb["FETCH_SIZE"], write_counter_kb=w_kb["WRITE_SIZE"],
+                copy_fetch_ratio=f_ratio, copy_write_ratio=w_ratio,
+                fetch_bytes=fetch, write_bytes=write, traffic_bytes=fetch + write)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--kernel")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", required=True)
+    cp = sub.add_parser("copy")
+    cp.add_argument("gib", nargs="?", type=float, default=1.0)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("cal_fetch_dir")
+    t.add_argument("cal_write_dir")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--gib", type=float, default=1.0)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        rows = kernel_stats(a.dir, a.kernel)
+        print("%-60s %7s %12s %12s %12s %6s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct"))
+        for r in sorted(rows, key=lambda r: -r["total_ns"]):
+            print("%-60s %7d %12.3f %12.3f %12.3f %6.2f" % (
+                r["name"][:60], r["calls"], r["avg_ns"] / 1e3, r["min_ns"] / 1e3,
+                r["max_ns"] / 1e3, r["pct"]))
+    elif a.cmd == "counters":
+        vals, n = counters(a.dir, a.kernel)
+        for k in sorted(vals):
+            print("%-36s dispatches %4d  mean %.6g" % (k, n[k], vals[k]))
+    elif a.cmd == "copy":
+        copy_kernel(a.gib)
+    elif a.cmd == "traffic":
+        r = traffic(a.fetch_dir, a.write_dir, a.cal_fetch_dir, a.cal_write_dir, a.kernel, a.gib)
+        r["source_sha256"] = source_sha256()
+        print(json.dumps(r, indent=1))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
