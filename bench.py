@@ -18,6 +18,10 @@ The same JSON line also carries:
                 100 consecutive steps) and varlen (32 packed sequences),
                 each with its own throughput and HBM roofline.
 
+The GPU reaches its steady clocks only after some tens of milliseconds of
+work, so the default warm-up (400 steps, about 30 ms) runs before the timed
+region.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--no-secondary] [--only {prefill,long,decode,varlen}]
 """
@@ -272,8 +276,8 @@ def measured_traffic(key):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "long", "decode", "varlen"])
@@ -304,11 +308,11 @@ def main():
     secondary = {}
     if not args.no_secondary:
         log("long_context ...")
-        secondary["long_context"] = bench_long(max(10, args.steps // 10), 3)
+        secondary["long_context"] = bench_long(max(10, args.steps // 10), max(3, args.warmup // 10))
         log("batched_decode ...")
         secondary["batched_decode"] = bench_decode()
         log("varlen ...")
-        secondary["varlen"] = bench_varlen(max(10, args.steps // 10), 3)
+        secondary["varlen"] = bench_varlen(max(10, args.steps // 10), max(3, args.warmup // 10))
     copy_bw = copy_bandwidth()
     cpu = None
     if not args.no_cpu:

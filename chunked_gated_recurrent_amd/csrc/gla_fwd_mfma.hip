@@ -34,8 +34,8 @@
 //     element i % 4 of the 8-byte loads of lanes 4e + i / 4 (e = 0..3); when
 //     lane s of the group loads row kb + s / 4, columns nb + 4 (s % 4) .. +3,
 //     lane i receives rows kb .. kb+3 of column nb + i;
-//   * outputs are staged through a per-wave LDS tile and written as 16-byte
-//     row segments.
+//   * outputs are staged through LDS (in the wave's own, already consumed
+//     rows of the q tile) and written as 16-byte row segments.
 //
 // MFMA lane layout (lane l, l16 = l % 16, g = l / 16): A row l16 and B column
 // l16 with the same 8 k-values for lane group g; D rows 4g..4g+3, column l16.
@@ -74,8 +74,12 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 template <int DVT>
 struct MfCfg {
   static constexpr int C = 64, DK = 96;
-  static constexpr int QS = DK + 8;      // LDS row stride of q, k, ks, S^T (elements)
-  static constexpr int VS = DVT + 8;     // LDS row stride of v and the output tile
+  // LDS row strides (elements). A stride of 8 mod 16 dwords (112 bf16 for 96
+  // columns, 80 for 64) keeps both the 16-byte fragment reads (16 rows, one
+  // column block) and the transpose reads (rows 4g + l16/4) free of bank
+  // conflicts on gfx950 (measured with the LDS conflict counters).
+  static constexpr int QS = DK + 16;     // q, k, ks and S^T
+  static constexpr int VS = DVT + 16;    // v and the staged output tile
   static constexpr int NCT = DVT / 16;   // 16-column tiles of the dv tile
   static constexpr int NDT = DK / 16;    // 16-row tiles of dk
   static constexpr int NKS = DK / 32;    // 32-deep steps over dk
@@ -107,6 +111,7 @@ __device__ __forceinline__ void state_role(
     float *__restrict__ slots, const Item &it, int idx, int h, int H, int dv,
     int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
     bf16 *sSt0, bf16 *sSt1, const float *sPow) {
+  // sK, sKs and sV hold two chunk buffers each (FUSED) or one (state pass)
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
@@ -168,22 +173,24 @@ __device__ __forceinline__ void state_role(
     for (int m = 0; m < VV; ++m)
       rv[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, rowV[m] * rowVb + colV[m] * 16, 0, 0);
   };
-  auto store_kv = [&](int L, const u32x4(&rk)[QV], const u32x4(&rv)[VV]) {
+  constexpr int KBUF = C * QS, VBUF = C * VS;  // elements per chunk buffer
+  auto store_kv = [&](int L, int buf, const u32x4(&rk)[QV], const u32x4(&rv)[VV]) {
+    bf16 *dK = sK + buf * KBUF, *dKs = sKs + buf * KBUF, *dV = sV + buf * VBUF;
 #pragma unroll
     for (int m = 0; m < QV; ++m) {
       const int r = rowK[m];
-      if (FUSED) *reinterpret_cast<u32x4 *>(sK + r * QS + 8 * colK[m]) = rk[m];
+      if (FUSED) *reinterpret_cast<u32x4 *>(dK + r * QS + 8 * colK[m]) = rk[m];
       // decay-scaled copy lambda^(L-1-r) k_r; rows past the end are zero
       const float wgt = r < L ? sPow[max(L - 1 - r, 0)] : 0.f;
       const bf16x8 kv = __builtin_bit_cast(bf16x8, rk[m]);
       bf16x8 ks;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ks[e] = (bf16)((float)kv[e] * wgt);
-      *reinterpret_cast<bf16x8 *>(sKs + r * QS + 8 * colK[m]) = ks;
+      *reinterpret_cast<bf16x8 *>(dKs + r * QS + 8 * colK[m]) = ks;
     }
 #pragma unroll
     for (int m = 0; m < VV; ++m)
-      *reinterpret_cast<u32x4 *>(sV + rowV[m] * VS + 8 * colV[m]) = rv[m];
+      *reinterpret_cast<u32x4 *>(dV + rowV[m] * VS + 8 * colV[m]) = rv[m];
   };
   auto publish = [&](bf16 *dst) {
 #pragma unroll
@@ -198,18 +205,25 @@ __device__ __forceinline__ void state_role(
       }
   };
 
+  // Chunk ch lives in LDS buffer ch & 1 (FUSED; the state pass has one
+  // buffer and a second barrier instead). Per chunk: one barrier, then the
+  // loads of chunk ch+2 are issued, the registers holding chunk ch+1 are
+  // written to the other buffer, and chunk ch is processed.
   u32x4 ka[QV], kb[QV], va[VV], vb[VV];
   load_kv(0, ka, va);
   load_kv(1, kb, vb);
   __syncthreads();  // sPow ready
-  store_kv(chunk_rows(it, 0), ka, va);
+  store_kv(chunk_rows(it, 0), 0, ka, va);
   if (FUSED) publish(sSt1);  // S_{-1}: the incoming state
-  __syncthreads();
 
   auto body = [&](int ch, u32x4(&rkn)[QV], u32x4(&rvn)[VV], const u32x4(&rkx)[QV],
                   const u32x4(&rvx)[VV], bf16 *st_pub) {
     const int L = chunk_rows(it, ch);
+    const int cur = FUSED ? (ch & 1) : 0;
+    __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
     load_kv(ch + 2, rkn, rvn);
+    if (FUSED) store_kv(chunk_rows(it, ch + 1), cur ^ 1, rkx, rvx);
+    const bf16 *cKs = sKs + cur * KBUF, *cV = sV + cur * VBUF;
     const float lamL = sPow[L];
 #pragma unroll
     for (int a = 0; a < SDT; ++a)
@@ -218,26 +232,28 @@ __device__ __forceinline__ void state_role(
 #pragma unroll
     for (int s = 0; s < M::NJS; ++s) {
       bf16x8 af[SDT], bfr[SCT];
-      const int row = 32 * s + 8 * g + tr_row;
+      const int row = 32 * s + 4 * g + tr_row;
 #pragma unroll
       for (int a = 0; a < SDT; ++a) {
-        const bf16 *base = sKs + row * QS + 16 * (dt0 + a) + tr_col;
-        af[a] = cat8(tr4(base), tr4(base + 4 * QS));
+        const bf16 *base = cKs + row * QS + 16 * (dt0 + a) + tr_col;
+        af[a] = cat8(tr4(base), tr4(base + 16 * QS));
       }
 #pragma unroll
       for (int b = 0; b < SCT; ++b) {
-        const bf16 *base = sV + row * VS + 16 * (ct0 + b) + tr_col;
-        bfr[b] = cat8(tr4(base), tr4(base + 4 * VS));
+        const bf16 *base = cV + row * VS + 16 * (ct0 + b) + tr_col;
+        bfr[b] = cat8(tr4(base), tr4(base + 16 * VS));
       }
 #pragma unroll
       for (int a = 0; a < SDT; ++a)
 #pragma unroll
         for (int b = 0; b < SCT; ++b) accS[a][b] = mfma(af[a], bfr[b], accS[a][b]);
     }
-    if (FUSED) publish(st_pub);  // S_ch for the next chunk's readout
-    __syncthreads();              // every wave is done with chunk ch
-    store_kv(chunk_rows(it, ch + 1), rkx, rvx);
-    __syncthreads();
+    if (FUSED) {
+      publish(st_pub);  // S_ch for the next chunk's readout
+    } else {
+      __syncthreads();  // single buffer: all waves are done with chunk ch
+      store_kv(chunk_rows(it, ch + 1), 0, rkx, rvx);
+    }
   };
   for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
     body(ch, ka, va, kb, vb, sSt0);
@@ -270,7 +286,7 @@ __device__ __forceinline__ void output_role(
     const bf16 *__restrict__ q, bf16 *__restrict__ o, const Item &it, int h,
     int H, int dv, int c0, float scale, int rt, int w, bf16 *sQ,
     const bf16 *sK, const bf16 *sV, const bf16 *sSt0, const bf16 *sSt1,
-    bf16 *sO, const float *sPow) {
+    const float *sPow) {
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NCT = M::NCT, NKS = M::NKS, NJS = M::NJS, QV = M::QV;
@@ -294,10 +310,11 @@ __device__ __forceinline__ void output_role(
     for (int m = 0; m < QV; ++m)
       r[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, rowQ[m] * rowKb + colQ[m] * 16, 0, 0);
   };
-  auto store_q = [&](const u32x4(&r)[QV]) {
+  constexpr int KBUF = C * QS, VBUF = C * VS;  // elements per chunk buffer
+  auto store_q = [&](int buf, const u32x4(&r)[QV]) {
 #pragma unroll
     for (int m = 0; m < QV; ++m)
-      *reinterpret_cast<u32x4 *>(sQ + rowQ[m] * QS + 8 * colQ[m]) = r[m];
+      *reinterpret_cast<u32x4 *>(sQ + buf * KBUF + rowQ[m] * QS + 8 * colQ[m]) = r[m];
   };
 
   u32x4 ra[QV], rb[QV];
@@ -314,18 +331,20 @@ __device__ __forceinline__ void output_role(
       const int diff = i_row - (16 * J + 4 * g + r);
       maskw[J][r] = diff >= 0 ? sPow[max(diff, 0)] : 0.f;
     }
-  store_q(ra);
-  __syncthreads();
+  store_q(0, ra);
 
-  bf16 *so = sO + w * 16 * VS;
   auto body = [&](int ch, u32x4(&rnew)[QV], const u32x4(&rnext)[QV], const bf16 *st) {
     const long long tb = (long long)it.t0 + (long long)ch * C;
     const int L = chunk_rows(it, ch);
+    const int cur = ch & 1;
+    __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
     load_q(ch + 2, rnew);
+    store_q(cur ^ 1, rnext);
+    const bf16 *cQ = sQ + cur * KBUF, *cK = sK + cur * KBUF, *cV = sV + cur * VBUF;
     bf16x8 qf[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8 *>(sQ + i_row * QS + 32 * s + 8 * g);
+      qf[s] = *reinterpret_cast<const bf16x8 *>(cQ + i_row * QS + 32 * s + 8 * g);
     // P^T tiles for j blocks 0..3 (tiles above the diagonal mask to zero)
     f32x4 p[4];
 #pragma unroll
@@ -334,7 +353,7 @@ __device__ __forceinline__ void output_role(
     for (int s = 0; s < NKS; ++s)
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sK + (16 * J + l16) * QS + 32 * s + 8 * g);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(cK + (16 * J + l16) * QS + 32 * s + 8 * g);
         p[J] = mfma(kf, qf[s], p[J]);
       }
     bf16x8 pb[NJS];
@@ -362,17 +381,20 @@ __device__ __forceinline__ void output_role(
     for (int s = 0; s < NJS; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const bf16 *base = sV + (32 * s + 4 * g + tr_row) * VS + 16 * ct + tr_col;
+        const bf16 *base = cV + (32 * s + 4 * g + tr_row) * VS + 16 * ct + tr_col;
         const bf16x8 vf = cat8(tr4(base), tr4(base + 16 * VS));
         oacc[ct] = mfma(vf, pb[s], oacc[ct]);
       }
-    // stage the 16 x DVT output tile of this wave, then 16-byte row stores
+    // stage the 16 x DVT output tile of this wave in its own rows of the
+    // current q buffer (only this wave reads them, and qf is already loaded),
+    // then write 16-byte row segments
+    bf16 *so = sQ + cur * KBUF + 16 * w * QS;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       bf16x4 t;
 #pragma unroll
       for (int r = 0; r < 4; ++r) t[r] = (bf16)(scale * oacc[ct][r]);
-      *reinterpret_cast<bf16x4 *>(so + l16 * VS + 16 * ct + 4 * g) = t;
+      *reinterpret_cast<bf16x4 *>(so + l16 * QS + 16 * ct + 4 * g) = t;
     }
     const __amdgpu_buffer_rsrc_t bo =
         buf_rsrc(o + tb * H * dv + (long long)h * dv + c0, (unsigned)L * rowVb);
@@ -380,12 +402,9 @@ __device__ __forceinline__ void output_role(
     for (int m = 0; m < M::OV; ++m) {
       const int vi = lane + 64 * m;
       const int row = vi / M::NVV, col = vi - (vi / M::NVV) * M::NVV;
-      const u32x4 val = *reinterpret_cast<const u32x4 *>(so + row * VS + 8 * col);
+      const u32x4 val = *reinterpret_cast<const u32x4 *>(so + row * QS + 8 * col);
       __builtin_amdgcn_raw_buffer_store_b128(val, bo, (16 * w + row) * rowVb + col * 16, 0, 0);
     }
-    __syncthreads();  // every wave is done with chunk ch
-    store_q(rnext);
-    __syncthreads();
   };
   for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
     body(ch, ra, rb, sSt1);               // reads S_{ch-1}
@@ -404,13 +423,12 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H, int dv,
     int final_in_slot) {
   using M = MfCfg<DVT>;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[M::C * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sK[M::C * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sKs[M::C * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[M::C * M::VS];
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
   __shared__ __attribute__((aligned(16))) bf16 sSt0[DVT * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sSt1[DVT * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sO[4 * 16 * M::VS];
   __shared__ float sPow[M::C + 4];
 
   const int ndt = dv / DVT;
@@ -427,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
   const int c0 = dtile * DVT;
   if (role_wave < 4)
     output_role<DVT>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ, sK,
-                     sV, sSt0, sSt1, sO, sPow);
+                     sV, sSt0, sSt1, sPow);
   else
     state_role<DVT, true>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
                           final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
