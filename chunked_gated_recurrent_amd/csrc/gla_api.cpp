@@ -61,7 +61,8 @@ struct HostPlan {
   int chunk;      // tokens per chunk the kernels use
   int ndt;        // dv tiles per (item, head)
   bool segmented; // at least one sequence has more than one item
-  size_t off_index, off_items, off_slots, ws_bytes;
+  bool ordered;   // items are dispatched longest first (order in workspace)
+  size_t off_index, off_items, off_order, off_slots, ws_bytes;
 };
 
 void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk) {
@@ -117,7 +118,9 @@ HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chun
     p.seg_len = total_T > 0 ? total_T : C;
     p.G = 1;
     hp.segmented = false;
-    hp.ws_bytes = 0;
+    hp.ordered = N > 1 && N <= kOrderMaxItems;
+    hp.off_order = 0;
+    hp.ws_bytes = hp.ordered ? align256(sizeof(int32_t) * (size_t)N) : 0;
     return hp;
   }
   const long long want = (target + chains - 1) / chains;  // segments per sequence
@@ -129,9 +132,12 @@ HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chun
   p.G = 0;
   p.max_items = (int)(N + total_T / seg);
   hp.segmented = true;
+  hp.ordered = p.max_items <= kOrderMaxItems;
   hp.off_index = 0;
   hp.off_items = align256(sizeof(int32_t) * ((size_t)N + 2));
-  hp.off_slots = hp.off_items + align256(sizeof(int4) * (size_t)p.max_items);
+  hp.off_order = hp.off_items + align256(sizeof(int4) * (size_t)p.max_items);
+  hp.off_slots = hp.off_order +
+                 (hp.ordered ? align256(sizeof(int32_t) * (size_t)p.max_items) : 0);
   hp.ws_bytes = hp.off_slots + (size_t)p.max_items * H * dk * dv * sizeof(float);
   return hp;
 }
@@ -148,17 +154,27 @@ Decay make_decay(const float *d, int H) {
 gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
                        void *workspace, hipStream_t s) {
   Plan p = hp.p;
+  char *ws = (char *)workspace;
   (void)hipGetLastError();  // report only this call's launch errors
+  if (p.mode == kPlanVarlenItems) {
+    p.index = (const int32_t *)(ws + hp.off_index);
+    p.items = (const int4 *)(ws + hp.off_items);
+    if (launch_planner(p, (int32_t *)(ws + hp.off_index), (int4 *)(ws + hp.off_items), s) != hipSuccess)
+      return GLA_ERR_HIP;
+  }
+  if (hp.ordered) {
+    if (launch_order(p, hp.chunk, (int32_t *)(ws + hp.off_order), s) != hipSuccess)
+      return GLA_ERR_HIP;
+    p.order = (const int32_t *)(ws + hp.off_order);
+  }
+  // Units of a packed batch differ in length: deal them in pairs over the
+  // XCDs. A fixed batch's output pass has equal units: blocked.
+  p.deal = p.mode == kPlanFixed ? 0 : 1;
   if (hp.segmented) {
-    char *ws = (char *)workspace;
     a.slots = (float *)(ws + hp.off_slots);
-    if (p.mode == kPlanVarlenItems) {
-      p.index = (const int32_t *)(ws + hp.off_index);
-      p.items = (const int4 *)(ws + hp.off_items);
-      if (launch_planner(p, (int32_t *)(ws + hp.off_index), (int4 *)(ws + hp.off_items), s) != hipSuccess)
-        return GLA_ERR_HIP;
-    }
-    if (launch_fwd(dt, hp.fast, true, p, a, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
+    Plan ps = p;
+    ps.deal = 1;  // the state pass skips every last segment
+    if (launch_fwd(dt, hp.fast, true, ps, a, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
     if (launch_combine(p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
     // In place (s_final == s0): the first segment reads s0 while the last
     // writes the final state, so the last writes its own slot and a gather

@@ -86,25 +86,53 @@ __device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
   }
 }
 
+// Dispatch slot -> (item index, item). Slots are taken longest item first
+// when the plan carries an order; false past the last item.
+__device__ __forceinline__ bool slot_item(const Plan &p, int slot, int &idx,
+                                          Item &it) {
+  int cnt = p.max_items;
+  if (p.mode == kPlanVarlenDirect) cnt = p.n_seq;
+  else if (p.mode == kPlanVarlenItems) cnt = min(p.index[0], p.max_items);
+  if (slot >= cnt) return false;
+  idx = p.order ? clampi(p.order[slot], 0, cnt - 1) : slot;
+  return load_item(p, idx, it);
+}
+
 // Workgroup -> (unit, dv tile). Workgroups are dealt to the 8 XCDs
-// round-robin by id, so id P runs on XCD P % 8. Units are given to XCDs in
-// contiguous blocks (consecutive heads of one item, and all dv tiles of a
-// unit, share an XCD): rows of q, k, v and o that two neighbouring heads or
-// two dv tiles split at a 128-byte line then meet in the same L2.
-__device__ __forceinline__ void xcd_unit(int ndt, int units, int &unit,
-                                         int &dtile) {
+// round-robin by id (id P runs on XCD P % 8); a unit's dv tiles stay on one
+// XCD, so the q and k rows they share are fetched into one L2.
+//  - blocked (p.deal == 0): XCD x takes the x-th contiguous eighth of the
+//    units, so each XCD streams its own contiguous part of the arrays. Used
+//    when every unit carries the same work.
+//  - pairs (p.deal == 1): units are taken in pairs (two neighbouring heads of
+//    one item, whose q and k rows share a 128-byte line) and the pairs are
+//    dealt round-robin over the XCDs, so every XCD gets an equal share of
+//    every item. Used when units differ in length (packed sequences, a state
+//    pass that skips last segments).
+__device__ __forceinline__ void xcd_unit(const Plan &p, int ndt, int units,
+                                         int &unit, int &dtile) {
   const int P = blockIdx.x;
   const int xcd = P & 7;
   const int r = P >> 3;
-  const int per = (units + 7) / 8;
-  const int ur = r / ndt;
-  unit = xcd * per + ur;
-  dtile = r - ur * ndt;
+  if (p.deal == 0) {
+    const int per = (units + 7) / 8;
+    const int ur = r / ndt;
+    unit = xcd * per + ur;
+    dtile = r - ur * ndt;
+  } else {
+    const int per_pair = 2 * ndt;
+    const int pr = r / per_pair;
+    const int rem = r - pr * per_pair;
+    unit = (pr * 8 + xcd) * 2 + rem / ndt;
+    dtile = rem - (rem / ndt) * ndt;
+  }
 }
 
-inline unsigned xcd_grid(long long units, int ndt) {
-  const long long per = (units + 7) / 8;
-  return (unsigned)(per * 8 * ndt);
+// Workgroups xcd_unit needs to cover `units` units of `ndt` dv tiles.
+inline unsigned xcd_grid(int deal, long long units, int ndt) {
+  if (deal == 0) return (unsigned)((units + 7) / 8 * 8 * ndt);
+  const long long pairs = (units + 1) / 2;
+  return (unsigned)((pairs + 7) / 8 * 8 * 2 * ndt);
 }
 
 }  // namespace gla

@@ -433,12 +433,13 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
 
   const int ndt = dv / DVT;
   int unit, dtile;
-  xcd_unit(ndt, plan.max_items * H, unit, dtile);
+  xcd_unit(plan, ndt, plan.max_items * H, unit, dtile);
   if (unit >= plan.max_items * H) return;
-  const int idx = unit / H;
-  const int h = unit - idx * H;
+  const int slot = unit / H;
+  const int h = unit - slot * H;
+  int idx;
   Item it;
-  if (!load_item(plan, idx, it)) return;
+  if (!slot_item(plan, slot, idx, it)) return;
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -463,12 +464,13 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
 
   const int ndt = dv / DVT;
   int unit, dtile;
-  xcd_unit(ndt, plan.max_items * H, unit, dtile);
+  xcd_unit(plan, ndt, plan.max_items * H, unit, dtile);
   if (unit >= plan.max_items * H) return;
-  const int idx = unit / H;
-  const int h = unit - idx * H;
+  const int slot = unit / H;
+  const int h = unit - slot * H;
+  int idx;
   Item it;
-  if (!load_item(plan, idx, it)) return;
+  if (!slot_item(plan, slot, idx, it)) return;
   if (it.flags & kLastSeg) return;  // no later segment reads it
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
 template <int DVT>
 static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
                        const Decay &dec, hipStream_t s) {
-  const unsigned grid = xcd_grid((long long)p.max_items * a.H, a.dv / DVT);
+  const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
   if (state_only)
     hipLaunchKernelGGL((fwd_state_kernel<DVT>), dim3(grid), dim3(256), 0, s,
                        (const bf16 *)a.k, (const bf16 *)a.v, a.slots, p, dec, a.H, a.dv);

@@ -35,6 +35,8 @@ struct Plan {
   const int32_t *cu;     // varlen: [n_seq + 1] device
   const int4 *items;     // kPlanVarlenItems: [max_items] {n, t0, t1, flags}
   const int32_t *index;  // kPlanVarlenItems: [0] = item count, [1 + n] = first item of n
+  const int32_t *order;  // optional: dispatch slot -> item, longest item first
+  int deal;              // workgroup -> XCD mapping: 0 blocked, 1 pairs round-robin
 };
 
 // Item flags
@@ -58,6 +60,10 @@ bool fast_path_ok(int dt, int dk, int dv, int chunk);
 int fast_dv_tile(int dv);
 int generic_chunk(int chunk);
 hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items, hipStream_t s);
+hipError_t launch_order(const Plan &p, int chunk, int32_t *order, hipStream_t s);
+
+// Plans with more items than this run in index order (no dispatch order).
+constexpr int kOrderMaxItems = 16384;
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s);

@@ -64,12 +64,13 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
 
   const int ndt = dv / kValuDvt;
   int unit, dtile;
-  xcd_unit(ndt, plan.max_items * H, unit, dtile);
+  xcd_unit(plan, ndt, plan.max_items * H, unit, dtile);
   if (unit >= plan.max_items * H) return;
-  const int idx = unit / H;
-  const int h = unit - idx * H;
+  const int slot = unit / H;
+  const int h = unit - slot * H;
+  int idx;
   Item it;
-  if (!load_item(plan, idx, it)) return;
+  if (!slot_item(plan, slot, idx, it)) return;
   if (STATE_ONLY && (it.flags & kLastSeg)) return;
 
   const int tid = threadIdx.x;
@@ -209,6 +210,57 @@ __global__ __launch_bounds__(1024) void planner_kernel(Plan p, int32_t *index,
     index[0] = min(scan[1023], p.max_items);
     index[1 + N] = min(scan[1023], p.max_items);
   }
+}
+
+// ===========================================================================
+// Dispatch order: the plan's items, longest first
+// ===========================================================================
+// One workgroup. A counting sort of the items by chunk count (descending,
+// counts above kOrderBins - 1 share the last bin): an LDS histogram, an
+// exclusive scan of the bins, then each item takes the next position of its
+// bin. Items of equal chunk count land in no particular order, which changes
+// no result (each item's arithmetic is independent of when it runs); giving
+// the long items the first workgroups keeps them off the tail of the launch.
+constexpr int kOrderBins = 4096;
+
+__global__ __launch_bounds__(1024) void order_kernel(Plan p, int chunk,
+                                                     int32_t *order) {
+  __shared__ int bins[kOrderBins];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int cnt = p.mode == kPlanVarlenItems ? min(p.index[0], p.max_items)
+                                             : min(p.n_seq, p.max_items);
+  auto bin_of = [&](int i) {
+    Item it;
+    if (!load_item(p, i, it)) return kOrderBins - 1;
+    const int c = (it.t1 - it.t0 + chunk - 1) / chunk;
+    return kOrderBins - 1 - min(c, kOrderBins - 1);
+  };
+  for (int b = tid; b < kOrderBins; b += 1024) bins[b] = 0;
+  __syncthreads();
+  for (int i = tid; i < cnt; i += 1024) atomicAdd(&bins[bin_of(i)], 1);
+  __syncthreads();
+  constexpr int kPer = kOrderBins / 1024;
+  int own[kPer], sum = 0;
+  for (int j = 0; j < kPer; ++j) {
+    own[j] = bins[tid * kPer + j];
+    sum += own[j];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  int pos = part[tid] - sum;
+  for (int j = 0; j < kPer; ++j) {
+    bins[tid * kPer + j] = pos;
+    pos += own[j];
+  }
+  __syncthreads();
+  for (int i = tid; i < cnt; i += 1024) order[atomicAdd(&bins[bin_of(i)], 1)] = i;
 }
 
 // ===========================================================================
@@ -371,11 +423,16 @@ hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items,
   return hipGetLastError();
 }
 
+hipError_t launch_order(const Plan &p, int chunk, int32_t *order, hipStream_t s) {
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, p, chunk, order);
+  return hipGetLastError();
+}
+
 template <typename Tin, bool SO>
 static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
                         int C, hipStream_t s) {
   const int ndt = a.dv / kValuDvt;
-  const unsigned grid = xcd_grid((long long)p.max_items * a.H, ndt);
+  const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, ndt);
   const size_t lds = sizeof(float) * ((size_t)2 * C * a.dk + C * kValuDvt +
                                       (size_t)C * C + a.dk * kValuDvt + C + 4);
   if (lds > 65536)  // beyond the default dynamic-LDS limit (gfx950 has 160 KB)

@@ -110,6 +110,12 @@ gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
  *               are then meaningless.)
  *   q, k    : [total_T, H, dk]  dt        v, o : [total_T, H, dv]  dt
  *   s0      : [N, H, dk, dv] fp32 or NULL; s_final : [N, H, dk, dv] or NULL
+ *   workspace: as for gla_chunk_fwd, at least
+ *             gla_chunk_fwd_varlen_workspace_bytes() bytes. With more than
+ *             one sequence it is never 0: it holds at least the dispatch
+ *             order (the sequences sorted longest first, computed on the
+ *             device), and, when there are too few sequences to fill the
+ *             GPU, the time segments and their states.
  * A zero-length sequence is valid: its s_final is s0[n] (or zeros).
  */
 size_t gla_chunk_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,

@@ -138,8 +138,12 @@ def test_varlen_argument_errors(L):
     assert need > 0
     dec = np.full(16, 0.9, np.float32)
     assert varlen(L, N=1, total=65536, H=16, decay=dec) == WS
-    # 32 sequences x 16 heads: enough chains, no scratch
-    assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 32, 131072, 16, 96, 192, 0) == 0
+    # 32 sequences x 16 heads: enough chains, no time segments; the scratch
+    # is the dispatch order alone (32 int32, rounded up to 256 bytes)
+    assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 32, 131072, 16, 96, 192, 0) == 256
+    assert varlen(L, N=32, total=131072, H=16, decay=dec) == WS
+    # one short sequence needs no scratch at all
+    assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 1, 100, 16, 96, 192, 0) == 0
 
 
 def test_decode_argument_errors(L):
