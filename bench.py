@@ -53,28 +53,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def timed(fn, steps, warmup, stream_events=True):
+def timed(fn, steps, warmup):
     """Run fn(i) for warmup + steps iterations; time exactly `steps` between
-    two device synchronisations and record HIP events around every timed
-    call on the current stream. Returns (wall_s, mean_event_ms)."""
+    two device synchronisations, with one HIP event pair on the current
+    stream (the stream the library launches on) around the same region.
+    Returns (wall_s, event_ms_per_step). Events around every call would put
+    two marker packets between consecutive kernels and slow the stream down,
+    so the per-launch duration is the event span over the steps (it includes
+    the few-microsecond gaps between back-to-back launches)."""
     import torch
     for i in range(warmup):
         fn(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)] if stream_events else []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        if stream_events:
-            ev[i][0].record()
         fn(warmup + i)
-        if stream_events:
-            ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    mean_ms = (sum(a.elapsed_time(b) for a, b in ev) / steps) if stream_events else None
-    return wall, mean_ms
+    return wall, e0.elapsed_time(e1) / steps
 
 
 def roofline(bytes_per_launch, launch_ms, bound="hbm"):
@@ -149,7 +149,8 @@ def bench_long(steps, warmup):
             "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
             "roofline": dict(roofline(bytes_call, ev_ms),
-                             kernel="whole call (state pass + combine + outputs)"),
+                             kernel="whole call (state pass + combine + outputs)",
+                             traffic=measured_traffic("whole call@long_context")),
             "mfma_frac": round(tokens * PREFILL_FLOPS_PER_TOKEN / (ev_ms * 1e-3) / 1e12
                                / BF16_PEAK_TFLOPS, 4),
             "workspace_bytes": need}
@@ -214,7 +215,8 @@ def bench_varlen(steps, warmup):
                                              "max_len": int(lens.max()), "chunk": 64},
             "value": round(total * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
-            "roofline": dict(roofline(bytes_call, ev_ms), kernel="whole call"),
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel="whole call (order + outputs)",
+                             traffic=measured_traffic("whole call@varlen")),
             "workspace_bytes": need}
 
 

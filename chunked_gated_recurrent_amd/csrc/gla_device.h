@@ -98,6 +98,18 @@ __device__ __forceinline__ bool slot_item(const Plan &p, int slot, int &idx,
   return load_item(p, idx, it);
 }
 
+// The item is the same for every lane of the workgroup; saying so (values
+// read back through readfirstlane) lets the compiler keep everything derived
+// from it in scalar registers: buffer descriptors built from a value it must
+// treat as per-lane cost a loop around every buffer access.
+__device__ __forceinline__ void make_uniform(int &idx, Item &it) {
+  idx = __builtin_amdgcn_readfirstlane(idx);
+  it.n = __builtin_amdgcn_readfirstlane(it.n);
+  it.t0 = __builtin_amdgcn_readfirstlane(it.t0);
+  it.t1 = __builtin_amdgcn_readfirstlane(it.t1);
+  it.flags = __builtin_amdgcn_readfirstlane(it.flags);
+}
+
 // Workgroup -> (unit, dv tile). Workgroups are dealt to the 8 XCDs
 // round-robin by id (id P runs on XCD P % 8); a unit's dv tiles stay on one
 // XCD, so the q and k rows they share are fetched into one L2.

@@ -51,10 +51,18 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Raw buffer resource (gfx9 family descriptor word 3) over `bytes` bytes.
+// Callers pass workgroup-uniform values; reading them back through
+// readfirstlane puts the descriptor in scalar registers (a descriptor the
+// compiler must treat as per-lane costs a loop around every access).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base,
                                                            unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
-                                           (int)bytes, 0x00020000);
+  const unsigned long long a = (unsigned long long)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  void *p = (void *)(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 
 // Four bf16 of one column from four consecutive rows (see the header).
@@ -440,6 +448,7 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
   int idx;
   Item it;
   if (!slot_item(plan, slot, idx, it)) return;
+  make_uniform(idx, it);
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -471,6 +480,7 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
   int idx;
   Item it;
   if (!slot_item(plan, slot, idx, it)) return;
+  make_uniform(idx, it);
   if (it.flags & kLastSeg) return;  // no later segment reads it
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);

@@ -93,18 +93,23 @@ def _decay_array(decay, H):
 
 
 def _check(t, name, dev, dtype=None, shape=None):
-    if not t.is_cuda or t.device != dev:
-        raise ValueError("%s must be on %s" % (name, dev))
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+    if t.device != dev or dev.type != "cuda":
+        raise ValueError("%s must be on the GPU of q (%s), got %s" % (name, dev, t.device))
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
 def _stream(dev):
+    """torch's current stream on `dev` (a device with an index), as the
+    hipStream_t the library launches on."""
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return ctypes.c_void_p(raw(dev.index))
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 

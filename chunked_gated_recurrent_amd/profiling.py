@@ -3,15 +3,21 @@
     python -m chunked_gated_recurrent_amd.profiling stats DIR [--kernel SUBSTR]
         kernel-trace statistics (calls, mean / min / max duration) from the
         *_kernel_stats.csv files rocprofv3 writes with --stats -f csv
+    python -m chunked_gated_recurrent_amd.profiling trace DIR --kernel SUBSTR --last N
+        duration of the last N dispatches of a kernel (the timed steps of a
+        run that warms up first) from *_kernel_trace.csv: mean, median, min,
+        max, and the mean gap between consecutive dispatches
     python -m chunked_gated_recurrent_amd.profiling counters DIR --kernel SUBSTR
         mean per-dispatch value of every counter in *_counter_collection.csv
     python -m chunked_gated_recurrent_amd.profiling copy [GIB]
         a plain device copy of GIB GiB (three times), the reference kernel whose
         FETCH_SIZE / WRITE_SIZE readings calibrate the HBM byte counters
     python -m chunked_gated_recurrent_amd.profiling traffic FETCH_DIR WRITE_DIR
-            CAL_FETCH_DIR CAL_WRITE_DIR --kernel SUBSTR [--gib 1]
+            CAL_FETCH_DIR CAL_WRITE_DIR --kernel SUBSTR [--kernel SUBSTR ...] [--gib 1]
         HBM bytes per dispatch of a kernel: each counter divided by the ratio
-        counter / true bytes that the same counter shows for the copy kernel
+        counter / true bytes that the same counter shows for the copy kernel.
+        With several --kernel names, the per-dispatch figures are summed: the
+        bytes of one call that launches each of those kernels once.
 """
 from __future__ import annotations
 
@@ -42,6 +48,23 @@ def kernel_stats(d, kernel=None):
                              avg_ns=float(r["AverageNs"]), min_ns=float(r["MinNs"]),
                              max_ns=float(r["MaxNs"]), pct=float(r["Percentage"])))
     return rows
+
+
+def trace(d, kernel, last):
+    """Durations (ns) of the last `last` dispatches whose name contains
+    `kernel`, in dispatch order, and the gaps between them."""
+    rows = []
+    for f in _find(d, "kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            if kernel in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    rows = rows[-last:]
+    dur = sorted(e - b for b, e in rows)
+    gaps = [rows[i + 1][0] - rows[i][1] for i in range(len(rows) - 1)]
+    n = len(dur)
+    return dict(n=n, mean_ns=sum(dur) / n, median_ns=dur[n // 2], min_ns=dur[0],
+                max_ns=dur[-1], mean_gap_ns=(sum(gaps) / len(gaps)) if gaps else 0.0)
 
 
 def counters(d, kernel):
@@ -79,18 +102,26 @@ def source_sha256():
     return h.hexdigest()
 
 
-def traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel, gib=1.0):
+def traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernels, gib=1.0):
+    if isinstance(kernels, str):
+        kernels = [kernels]
     true_bytes = int(gib * (1 << 30)) // 4 * 4
-    f_kb, fn = counters(fetch_dir, kernel)
-    w_kb, wn = counters(write_dir, kernel)
     cf, _ = counters(cal_fetch_dir, "copyBuffer")
     cw, _ = counters(cal_write_dir, "copyBuffer")
     f_ratio = cf["FETCH_SIZE"] * 1024 / true_bytes
     w_ratio = cw["WRITE_SIZE"] * 1024 / true_bytes
-    fetch = f_kb["FETCH_SIZE"] * 1024 / f_ratio
-    write = w_kb["WRITE_SIZE"] * 1024 / w_ratio
-    return dict(kernel=kernel, dispatches=fn.get("FETCH_SIZE", 0),
-                fetch_counter_kb=f_kb["FETCH_SIZE"], write_counter_kb=w_kb["WRITE_SIZE"],
+    f_kb = w_kb = 0.0
+    disp = {}
+    for kname in kernels:
+        f, fn = counters(fetch_dir, kname)
+        w, _ = counters(write_dir, kname)
+        f_kb += f["FETCH_SIZE"]
+        w_kb += w["WRITE_SIZE"]
+        disp[kname] = fn.get("FETCH_SIZE", 0)
+    fetch = f_kb * 1024 / f_ratio
+    write = w_kb * 1024 / w_ratio
+    return dict(kernel=" + ".join(kernels), dispatches=disp,
+                fetch_counter_kb=f_kb, write_counter_kb=w_kb,
                 copy_fetch_ratio=f_ratio, copy_write_ratio=w_ratio,
                 fetch_bytes=fetch, write_bytes=write, traffic_bytes=fetch + write)
 
@@ -101,6 +132,10 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--kernel")
+    tr = sub.add_parser("trace")
+    tr.add_argument("dir")
+    tr.add_argument("--kernel", required=True)
+    tr.add_argument("--last", type=int, required=True)
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--kernel", required=True)
@@ -111,7 +146,7 @@ def main(argv=None):
     t.add_argument("write_dir")
     t.add_argument("cal_fetch_dir")
     t.add_argument("cal_write_dir")
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, action="append")
     t.add_argument("--gib", type=float, default=1.0)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
@@ -121,6 +156,11 @@ def main(argv=None):
             print("%-60s %7d %12.3f %12.3f %12.3f %6.2f" % (
                 r["name"][:60], r["calls"], r["avg_ns"] / 1e3, r["min_ns"] / 1e3,
                 r["max_ns"] / 1e3, r["pct"]))
+    elif a.cmd == "trace":
+        r = trace(a.dir, a.kernel, a.last)
+        print("%s: last %d dispatches  mean %.3f us  median %.3f us  min %.3f us  max %.3f us"
+              "  mean gap %.3f us" % (a.kernel, r["n"], r["mean_ns"] / 1e3, r["median_ns"] / 1e3,
+                                      r["min_ns"] / 1e3, r["max_ns"] / 1e3, r["mean_gap_ns"] / 1e3))
     elif a.cmd == "counters":
         vals, n = counters(a.dir, a.kernel)
         for k in sorted(vals):
