@@ -260,6 +260,28 @@ def copy_bandwidth(gib=1.0):
     return round(2 * n * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
+def mfma_achievable(n=8192):
+    """Achievable dense bf16 matrix-core rate of a plain library GEMM
+    (n x n x n, fp32 accumulate), TFLOP/s, for context beside the datasheet
+    peak."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    del c
+    return round(2.0 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+
+
 def measured_traffic(key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken with the current kernel source (else None)."""
@@ -316,6 +338,7 @@ def main():
         log("varlen ...")
         secondary["varlen"] = bench_varlen(max(10, args.steps // 10), max(3, args.warmup // 10))
     copy_bw = copy_bandwidth()
+    mfma_tf = mfma_achievable()
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
@@ -341,6 +364,8 @@ def main():
                          bytes_per_launch=pre["bytes"], launch_ms=round(pre["event_ms"], 5)),
         "hbm_copy_GBps": copy_bw,
         "mfma_frac": round(pre["mfma_frac"], 4),
+        "mfma_bf16_gemm_TFLOPs": mfma_tf,
+        "mfma_frac_of_gemm": round(pre["mfma_frac"] * BF16_PEAK_TFLOPS / mfma_tf, 4),
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

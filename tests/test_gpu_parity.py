@@ -279,3 +279,76 @@ def test_run_to_run_bitwise_determinism():
     o2, s2 = gla.gla_chunk_fwd(q, k, v, x["decay"], initial_state=s0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------
+# closed forms at the long-context size (any-size properties, no oracle run)
+# ---------------------------------------------------------------------------
+def _long_inputs(seed, s0_sigma=None):
+    T, H = 65536, 16
+    x = W.prefill_inputs(seed, 1, T, H, 96, 192, "bf16", s0_sigma, W.geometric_decays(H))
+    return x, T, H
+
+
+def test_constant_tokens_geometric_series_long():
+    """k_t = k and v_t = v for every token, zero initial state: the state is
+    a geometric series, S_t = (1 - lam^(t+1)) / (1 - lam) k^T v, so
+    o_t = (q_t . k) (1 - lam^(t+1)) / (1 - lam) v. Checked for every token
+    of T = 65,536 (segmented carry over 1,024 chunks), all 16 heads."""
+    x, T, H = _long_inputs(300)
+    k0 = x["k"][:, :1].copy()
+    v0 = x["v"][:, :1].copy()
+    x["k"][:] = k0
+    x["v"][:] = v0
+    o, s = run_fixed(x, chunk=64)
+    lam = x["decay"].astype(np.float64)
+    qf = W.bf16_to_f32(x["q"][0]).astype(np.float64)          # [T, H, dk]
+    kf = W.bf16_to_f32(k0[0, 0]).astype(np.float64)            # [H, dk]
+    vf = W.bf16_to_f32(v0[0, 0]).astype(np.float64)            # [H, dv]
+    t = np.arange(T, dtype=np.float64)
+    worst_o = worst_s = 0.0
+    den_o = den_s = 0.0
+    errs = []
+    for h in range(H):
+        g = (1.0 - lam[h] ** (t + 1.0)) / (1.0 - lam[h])
+        ref = ((qf[:, h] @ kf[h]) * g)[:, None] * vf[h][None, :]
+        got = o[0, :, h]
+        err = np.max(np.abs(got - ref))
+        den = np.max(np.abs(ref))
+        errs.append(err / den)
+        worst_o, den_o = max(worst_o, err), max(den_o, den)
+        sref = np.outer(kf[h], vf[h]) * (1.0 - lam[h] ** T) / (1.0 - lam[h])
+        worst_s = max(worst_s, np.max(np.abs(s[0, h] - sref)))
+        den_s = max(den_s, np.max(np.abs(sref)))
+    print("constant tokens T65536: o err %.3e  S err %.3e" % (worst_o / den_o, worst_s / den_s))
+    print("  per-head o:", " ".join("%.1e" % e for e in errs))
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert worst_o / den_o <= TOL["bf16"]
+    assert worst_s / den_s <= TOL["bf16"]
+
+
+def test_decay_only_long():
+    """v = 0: nothing is added to the state, so S_T = lam^T S0 and
+    o_t = lam^(t+1) q_t S0 for every token of T = 65,536 (the carried state
+    crosses 1,024 chunks and every time segment)."""
+    x, T, H = _long_inputs(301, s0_sigma=0.1)
+    x["v"][:] = 0
+    o, s = run_fixed(x, chunk=64)
+    lam = x["decay"].astype(np.float64)
+    qf = W.bf16_to_f32(x["q"][0]).astype(np.float64)
+    s0 = x["s0"][0].astype(np.float64)
+    t = np.arange(T, dtype=np.float64)
+    worst_o = den_o = 0.0
+    worst_s = den_s = 0.0
+    for h in range(H):
+        ref = (lam[h] ** (t + 1.0))[:, None] * (qf[:, h] @ s0[h])
+        worst_o = max(worst_o, np.max(np.abs(o[0, :, h] - ref)))
+        den_o = max(den_o, np.max(np.abs(ref)))
+        sref = lam[h] ** T * s0[h]
+        worst_s = max(worst_s, np.max(np.abs(s[0, h] - sref)))
+        den_s = max(den_s, np.max(np.abs(sref)))
+    print("decay only T65536: o err %.3e  S err %.3e (max|S_ref| %.2e)"
+          % (worst_o / den_o, worst_s / den_s, den_s))
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert worst_o / den_o <= TOL["bf16"]
+    assert worst_s / den_s <= TOL["bf16"]
