@@ -184,6 +184,39 @@ def bench_decode(warmup_runs=1):
             "tokens_per_s_all_heads": round(N * steps / wall, 1)}
 
 
+def bench_decode_pool(warmup_runs=1, pool_pages=2048):
+    """Decode against a pool of per-sequence state pages: the 1,280
+    sequences of the decode workload live in a scattered subset of 2,048
+    pages (a seeded permutation), 100 steps."""
+    import numpy as np
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    spec = W.WORKLOADS["batched_decode"]
+    N, steps = spec["N"], spec["steps"]
+    lam = W.decays_for(spec)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(spec["seed"])
+    pool = torch.randn(pool_pages, H, DK, DV, generator=g, device=dev).mul_(spec["state_sigma"])
+    slots = torch.from_numpy(np.random.default_rng(spec["seed"]).permutation(pool_pages)[:N]
+                             .astype(np.int32)).to(dev)
+    q, k, v, _ = W.device_normal_inputs(spec["seed"] + 1, (steps, N), H, DK, DV, dev)
+    o = torch.empty(N, H, DV, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        t = i % steps
+        gla.gla_decode_step_pool(q[t], k[t], v[t], lam, pool, slots, out=o)
+
+    wall, ev_ms = timed(step, steps, warmup_runs * steps)
+    return {"workload": "batched_decode_pool", "config": {"N": N, "pool_pages": pool_pages,
+                                                          "steps": steps},
+            "value": round(N * steps / wall, 1), "unit": "seq-steps/s",
+            "ms_per_step": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(N * DECODE_BYTES_PER_SEQSTEP, ev_ms),
+                             kernel="decode_kernel<bf16,16> (slot table)")}
+
+
 def bench_varlen(steps, warmup):
     import torch
     from chunked_gated_recurrent_amd import gla
@@ -304,7 +337,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "long", "decode", "varlen"])
+    ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -320,6 +353,7 @@ def main():
         fn = {"prefill": lambda: bench_prefill(args.steps, args.warmup),
               "long": lambda: bench_long(args.steps, args.warmup),
               "decode": lambda: bench_decode(),
+              "decode_pool": lambda: bench_decode_pool(),
               "varlen": lambda: bench_varlen(args.steps, args.warmup)}[args.only]
         r = fn()
         r.pop("x", None)
@@ -335,6 +369,8 @@ def main():
         secondary["long_context"] = bench_long(max(10, args.steps // 10), max(3, args.warmup // 10))
         log("batched_decode ...")
         secondary["batched_decode"] = bench_decode()
+        log("batched_decode_pool ...")
+        secondary["batched_decode_pool"] = bench_decode_pool()
         log("varlen ...")
         secondary["varlen"] = bench_varlen(max(10, args.steps // 10), max(3, args.warmup // 10))
     copy_bw = copy_bandwidth()

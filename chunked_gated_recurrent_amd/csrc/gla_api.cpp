@@ -366,4 +366,37 @@ gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
   return GLA_OK;
 }
 
+gla_status gla_decode_step_pool(gla_dtype dt, int N, int H, int dk, int dv,
+                                const void *q, const void *k, const void *v,
+                                const float *decay_host, float scale,
+                                const int32_t *slots, int pool_size,
+                                float *state_pool, void *o, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, 0);
+  if (st != GLA_OK) return st;
+  if (N < 0 || (long long)N * H > kMaxTokens) return GLA_ERR_SHAPE;
+  if (pool_size < 1 || (long long)pool_size * H > kMaxTokens) return GLA_ERR_SHAPE;
+  if (!isfinite(scale)) return GLA_ERR_SHAPE;
+  st = check_decay(decay_host, H);
+  if (st != GLA_OK) return st;
+  if (N == 0) return GLA_OK;
+  if (!q || !k || !v || !o || !state_pool || !slots) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      misaligned(state_pool) || ((uintptr_t)slots & 3u))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)N * H * dk * es, nv = (size_t)N * H * dv * es;
+  const size_t ns = (size_t)pool_size * H * dk * dv * sizeof(float);
+  const size_t nsl = sizeof(int32_t) * (size_t)N;
+  if (overlap(state_pool, ns, q, nqk) || overlap(state_pool, ns, k, nqk) ||
+      overlap(state_pool, ns, v, nv) || overlap(state_pool, ns, o, nv) ||
+      overlap(state_pool, ns, slots, nsl) || overlap(o, nv, q, nqk) ||
+      overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) || overlap(o, nv, slots, nsl))
+    return GLA_ERR_ALIAS;
+  (void)hipGetLastError();
+  if (launch_decode(dt, N, H, dk, dv, q, k, v, make_decay(decay_host, H), scale,
+                    state_pool, o, (hipStream_t)stream, slots, pool_size) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 }  // extern "C"

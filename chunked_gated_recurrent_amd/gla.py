@@ -10,6 +10,7 @@ Functions mirror the C entry points:
     gla_chunk_fwd(q, k, v, decay, ...)          -> (o, s_final)
     gla_chunk_fwd_varlen(q, k, v, cu, decay, ...) -> (o, s_final)
     gla_decode_step(q, k, v, decay, state, ...)  -> o   (state updated in place)
+    gla_decode_step_pool(q, k, v, decay, state_pool, slots, ...) -> o
 """
 from __future__ import annotations
 
@@ -36,6 +37,7 @@ _SIGS = {
     "gla_chunk_fwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P], _I),
     "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
+    "gla_decode_step_pool": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _I, _P, _P, _P], _I),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -218,4 +220,31 @@ def gla_decode_step(q, k, v, decay, state, scale: float = 1.0, out=None):
                                float(scale), _ptr(state), _ptr(o), _stream(dev))
     if rc != 0:
         raise GlaError(rc, "gla_decode_step")
+    return o
+
+
+def gla_decode_step_pool(q, k, v, decay, state_pool, slots, scale: float = 1.0, out=None):
+    """One decode step against a state pool: row n of q [N, H, dk], k, v
+    [N, H, dv] updates state_pool[slots[n]] ([P, H, dk, dv] fp32, in place);
+    slots is an int32 tensor [N] on the device, and a slot outside [0, P)
+    marks a padding row (o row zero, no state touched). Returns o [N, H, dv]."""
+    import torch
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    P = state_pool.shape[0]
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (N, H, dk))
+    _check(v, "v", dev, q.dtype, (N, H, dv))
+    _check(state_pool, "state_pool", dev, torch.float32, (P, H, dk, dv))
+    _check(slots, "slots", dev, torch.int32, (N,))
+    dt = _dt(q)
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (N, H, dv))
+    _d, dptr = _decay_array(decay, H)
+    rc = lib().gla_decode_step_pool(dt, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), dptr,
+                                    float(scale), _ptr(slots), P, _ptr(state_pool),
+                                    _ptr(o), _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_decode_step_pool")
     return o

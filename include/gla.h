@@ -143,6 +143,32 @@ gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
                            const float *decay_host, float scale, float *state,
                            void *o, void *stream);
 
+/*
+ * One decode step for N sequences whose states live in a pool of fixed,
+ * per-sequence pages (a state page per sequence that stays in place across
+ * steps, and batches padded to fixed widths: the inference section of the
+ * Laplace 3B / Trainium2 page). Row n of q, k, v and o belongs to the
+ * sequence whose state is pool entry slots[n]:
+ *   state_pool[s,h] <- lambda_h * state_pool[s,h] + k[n,h]^T v[n,h]
+ *   o[n,h]          <- scale * q[n,h] state_pool[s,h]     with s = slots[n]
+ *   slots      : [N] int32 DEVICE array. A value outside [0, pool_size)
+ *                marks a padding row: its o row is written as zeros and no
+ *                state is read or written. The valid slots of one call must
+ *                be distinct (two rows updating one entry race); this lives
+ *                on the device and is not checked.
+ *   state_pool : [pool_size, H, dk, dv] fp32, updated in place; entries no
+ *                row names are not touched.
+ *   q, k, v, o : as for gla_decode_step. Checks as for gla_decode_step, plus
+ *                pool_size >= 1, slots non-NULL and 4-byte aligned, and no
+ *                overlap of state_pool or o with any other argument.
+ * N = 0 is valid and does nothing.
+ */
+gla_status gla_decode_step_pool(gla_dtype dt, int N, int H, int dk, int dv,
+                                const void *q, const void *k, const void *v,
+                                const float *decay_host, float scale,
+                                const int32_t *slots, int pool_size,
+                                float *state_pool, void *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

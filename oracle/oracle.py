@@ -141,3 +141,29 @@ def gla_decode(q, k, v, decay, state, scale=1.0, threads=None):
     if rc != 0:
         raise RuntimeError("oracle_gla_decode failed: %d" % rc)
     return o
+
+
+def gla_decode_pool(q, k, v, decay, pool, slots, scale=1.0, threads=None):
+    """One decode step against a pool of per-sequence state pages (Laplace
+    3B / Trainium2 page, inference section: each sequence keeps a fixed
+    state page, batches are padded to fixed widths). Row n updates pool
+    entry slots[n]; a slot outside [0, P) is a padding row whose output is
+    zero and which touches no state. The valid slots must be distinct.
+    pool: [P, H, dk, dv] fp64, updated IN PLACE. Returns o [N, H, dv] fp64.
+
+    Written as the plain definition: gather the named pages, run the direct
+    decode step on them, scatter them back."""
+    slots = np.asarray(slots, dtype=np.int64).reshape(-1)
+    P = pool.shape[0]
+    valid = np.nonzero((slots >= 0) & (slots < P))[0]
+    if np.unique(slots[valid]).size != valid.size:
+        raise ValueError("valid slots must be distinct")
+    q, k, v = widen(q), widen(k), widen(v)
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((N, H, dv), np.float64)
+    if valid.size:
+        pages = np.ascontiguousarray(pool[slots[valid]])
+        o[valid] = gla_decode(q[valid], k[valid], v[valid], decay, pages, scale, threads)
+        pool[slots[valid]] = pages
+    return o

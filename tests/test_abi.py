@@ -162,3 +162,25 @@ def test_decode_argument_errors(L):
     d = GOOD.copy()
     d[1] = 2.0
     assert dec(decay=d) == DECAY
+
+
+def test_decode_pool_argument_errors(L):
+    def pool(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], sl=A[5],
+             P=8, st=A[3], o=A[4], decay=GOOD):
+        return L.gla_decode_step_pool(dt, N, H, dk, dv, q, k, v, dptr(decay), 1.0,
+                                      sl, P, st, o, None)
+    assert pool(dt=3) == DTYPE
+    assert pool(N=-1) == SHAPE
+    assert pool(P=0) == SHAPE
+    assert pool(N=0) == OK                     # nothing to do, nothing launched
+    assert pool(sl=None) == NULL
+    assert pool(st=None) == NULL
+    assert pool(dk=8) == UNSUP
+    assert pool(sl=ctypes.c_void_p(A[5].value + 2)) == ALIGN
+    assert pool(st=ctypes.c_void_p(A[3].value + 8)) == ALIGN
+    assert pool(sl=ctypes.c_void_p(A[3].value + 4096)) == ALIAS  # slots inside the pool
+    assert pool(o=ctypes.c_void_p(A[5].value)) == ALIAS          # o on the slots
+    assert pool(st=ctypes.c_void_p(A[0].value + 512)) == ALIAS   # pool on q
+    d = GOOD.copy()
+    d[2] = -0.5
+    assert pool(decay=d) == DECAY

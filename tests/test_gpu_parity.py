@@ -352,3 +352,85 @@ def test_decay_only_long():
     assert np.isfinite(o).all() and np.isfinite(s).all()
     assert worst_o / den_o <= TOL["bf16"]
     assert worst_s / den_s <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# decode against a state pool (per-sequence pages, padded batches)
+# ---------------------------------------------------------------------------
+def _pool_slots(rng, N, P, n_pad):
+    """Distinct valid slots for N - n_pad rows, padding rows get -1 or a
+    value >= P."""
+    slots = rng.permutation(P)[:N].astype(np.int32)
+    pad = rng.permutation(N)[:n_pad]
+    slots[pad] = np.where(rng.random(n_pad) < 0.5, -1, P + rng.integers(0, 5, n_pad))
+    return slots
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_pool_matches_oracle_over_steps(dtype):
+    rng = np.random.default_rng(40)
+    N, H, dk, dv, P, steps = 48, 4, 96, 192, 100, 6
+    lam = W.geometric_decays(H)
+    pool0 = (rng.standard_normal((P, H, dk, dv)) * 0.3).astype(np.float32)
+    ref = pool0.astype(np.float64)
+    pool = dev(pool0)
+    touched = np.zeros(P, bool)
+    tol = TOL[dtype]
+    for t in range(steps):
+        x = W.prefill_inputs(500 + t, 1, N, H, dk, dv, dtype, None, lam)
+        q, k, v = x["q"][0], x["k"][0], x["v"][0]
+        slots = _pool_slots(rng, N, P, 7)
+        o = gla.gla_decode_step_pool(dev(q), dev(k), dev(v), lam, pool, dev(slots))
+        ro = O.gla_decode_pool(q, k, v, lam, ref, slots)
+        got = host(o)
+        valid = (slots >= 0) & (slots < P)
+        touched[slots[valid]] = True
+        assert not got[~valid].any(), "padding rows must read zero"
+        e = rel_err(got[valid], ro[valid])
+        print("pool step %d: o err %.3e" % (t, e))
+        assert e <= tol, (t, e)
+    fin = host(pool)
+    assert rel_err(fin[touched], ref[touched]) <= tol
+    np.testing.assert_array_equal(fin[~touched], pool0[~touched].astype(np.float64))
+
+
+def test_decode_pool_is_bitwise_the_direct_step():
+    """The pool step on a permuted pool equals the direct step on the same
+    states gathered into batch order, bit for bit (same kernel arithmetic)."""
+    rng = np.random.default_rng(41)
+    N, H, dk, dv, P = 64, 16, 96, 192, 96
+    lam = W.geometric_decays(H)
+    x = W.prefill_inputs(600, 1, N, H, dk, dv, "bf16", None, lam)
+    q, k, v = dev(x["q"][0]), dev(x["k"][0]), dev(x["v"][0])
+    slots = rng.permutation(P)[:N].astype(np.int32)
+    pool = torch.randn(P, H, dk, dv, device="cuda") * 0.3
+    direct = pool[torch.from_numpy(slots).long().cuda()].contiguous()
+    o_pool = gla.gla_decode_step_pool(q, k, v, lam, pool, dev(slots))
+    o_dir = gla.gla_decode_step(q, k, v, lam, direct)
+    torch.cuda.synchronize()
+    assert torch.equal(o_pool, o_dir)
+    assert torch.equal(pool[torch.from_numpy(slots).long().cuda()], direct)
+
+
+def test_decode_pool_full_size_sampled():
+    """1,280 rows (128 of them padding) against a pool of 2,048 pages at the
+    Laplace head shape; sampled rows against the oracle."""
+    rng = np.random.default_rng(42)
+    spec = W.WORKLOADS["batched_decode"]
+    N, H, dk, dv = spec["N"], spec["H"], spec["dk"], spec["dv"]
+    P = 2048
+    lam = W.decays_for(spec)
+    pool = torch.randn(P, H, dk, dv, device="cuda").mul_(spec["state_sigma"])
+    slots = _pool_slots(rng, N, P, 128)
+    valid = np.nonzero((slots >= 0) & (slots < P))[0]
+    sample = valid[np.linspace(0, valid.size - 1, 24).astype(int)]
+    ref = host(pool[torch.from_numpy(slots[sample]).long().cuda()])
+    q, k, v = W.decode_tokens(spec["seed"], 0, N, H, dk, dv)
+    o = host(gla.gla_decode_step_pool(dev(q), dev(k), dev(v), lam, pool, dev(slots)))
+    ro = O.gla_decode(q[sample], k[sample], v[sample], lam, ref)
+    e = rel_err(o[sample], ro)
+    es = rel_err(host(pool[torch.from_numpy(slots[sample]).long().cuda()]), ref)
+    print("pool decode N1280 P2048: o err %.3e  S err %.3e" % (e, es))
+    pad = np.setdiff1d(np.arange(N), valid)
+    assert not o[pad].any()
+    assert e <= TOL["bf16"] and es <= TOL["bf16"]

@@ -218,6 +218,51 @@ def test_decode_steps_equal_forward():
     np.testing.assert_array_equal(state, sf)
 
 
+def test_decode_pool_equals_forward_per_sequence_and_leaves_the_rest():
+    """A state pool with per-sequence pages and padded batches: three
+    sequences live in pages 4, 1 and 3 of a 6-page pool and get tokens in a
+    batch of 4 rows whose row order changes each step; unused rows are padding
+    (slot -1 or >= P). Each page must end as the chunked forward over the
+    tokens its sequence received (and each output must equal that forward's
+    output at the same position); pages 0, 2 and 5 stay bit-identical and
+    padding rows read zero."""
+    rng = np.random.default_rng(21)
+    H, dk, dv, P, steps = 2, 5, 4, 6, 5
+    lam = np.array([0.7, 0.97], np.float32)
+    page = {0: 4, 1: 1, 2: 3}
+    pool0 = _rand(rng, (P, H, dk, dv)).astype(np.float64)
+    pool = pool0.copy()
+    hist = {n: [] for n in page}  # per sequence: (q, k, v, o) per step it ran
+    for t in range(steps):
+        seqs = [n for n in page if rng.random() < 0.8]
+        rows = list(rng.permutation(4))
+        slots = np.full(4, -1, np.int64)
+        slots[rows[3]] = P + 2                     # out of range: padding too
+        for n, r in zip(seqs, rows):
+            slots[r] = page[n]
+        q, k, v = _rand(rng, (4, H, dk)), _rand(rng, (4, H, dk)), _rand(rng, (4, H, dv))
+        o = O.gla_decode_pool(q, k, v, lam, pool, slots, 0.5)
+        for r in range(4):
+            if not (0 <= slots[r] < P):
+                assert not o[r].any()
+        for n, r in zip(seqs, rows):
+            hist[n].append((q[r], k[r], v[r], o[r]))
+    for n, pg in page.items():
+        if not hist[n]:
+            np.testing.assert_array_equal(pool[pg], pool0[pg])
+            continue
+        qs = np.stack([h[0] for h in hist[n]])[None]
+        ks = np.stack([h[1] for h in hist[n]])[None]
+        vs = np.stack([h[2] for h in hist[n]])[None]
+        of, sf = O.gla_fwd(qs, ks, vs, lam, 0.5, pool0[pg][None].astype(np.float32))
+        np.testing.assert_allclose(np.stack([h[3] for h in hist[n]]), of[0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(pool[pg], sf[0], rtol=1e-12, atol=1e-12)
+    for pg in (0, 2, 5):
+        np.testing.assert_array_equal(pool[pg], pool0[pg])
+    with pytest.raises(ValueError):
+        O.gla_decode_pool(q, k, v, lam, pool, np.array([1, 1, -1, -1]))
+
+
 def test_varlen_equals_separate_calls_and_empty_sequences():
     rng = np.random.default_rng(9)
     lens = [5, 0, 17, 1, 0]
