@@ -251,3 +251,154 @@ int oracle_gla_decode(int N, int H, int dk, int dv, const float *q,
   pthread_mutex_destroy(&J.mu);
   return J.failed ? -2 : 0;
 }
+
+
+/*
+ * Backward of the same recurrence (gradients by the chain rule, token by
+ * token). The page trains the model, and its "Challenge 3" section
+ * differentiates through every sequential state update of the chain; here
+ * that is written out directly. With upstream gradients dO_t = dL/do_t and
+ * dS_fin = dL/dS_final (zero when not given):
+ *
+ *   forward sweep (recomputes S_t):   dq_t = scale * dO_t S_t^T
+ *   backward sweep, R = dS_fin, then for t = T-1 .. 0:
+ *       G_t  = R + scale * q_t^T dO_t      (dL/dS_t, all later uses included)
+ *       dk_t = v_t G_t^T                   (dk_t[i] = sum_j G_t[i][j] v_t[j])
+ *       dv_t = k_t G_t                     (dv_t[j] = sum_i k_t[i] G_t[i][j])
+ *       R    = lambda * G_t
+ *   dS0 = R after token 0.
+ * Sums run over the contracted index in ascending order, in double.
+ */
+typedef struct {
+  int N, H, dk, dv;
+  const int64_t *cu;
+  const float *q, *k, *v, *decay, *dout;
+  const double *s0, *ds_fin;
+  double scale;
+  double *dq, *dkk, *dvv, *ds0;
+  int64_t next;
+  pthread_mutex_t mu;
+  int failed;
+} bjob_t;
+
+static void *bworker(void *arg) {
+  bjob_t *J = (bjob_t *)arg;
+  const int dk = J->dk, dv = J->dv, H = J->H;
+  const int64_t sz = (int64_t)dk * dv;
+  double *S = (double *)malloc(sizeof(double) * (size_t)(2 * sz));
+  if (!S) {
+    pthread_mutex_lock(&J->mu);
+    J->failed = 1;
+    pthread_mutex_unlock(&J->mu);
+    return NULL;
+  }
+  double *G = S + sz;
+  const int64_t total = (int64_t)J->N * H;
+  const int64_t row_k = (int64_t)H * dk, row_v = (int64_t)H * dv;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    const int64_t w = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (w >= total) break;
+    const int n = (int)(w / H), h = (int)(w % H);
+    const int64_t t0 = J->cu[n], t1 = J->cu[n + 1];
+    const double lam = (double)J->decay[h];
+    /* forward sweep: S_t, then dq_t = scale * dO_t S_t^T */
+    if (J->s0)
+      memcpy(S, J->s0 + ((int64_t)n * H + h) * sz, sizeof(double) * (size_t)sz);
+    else
+      memset(S, 0, sizeof(double) * (size_t)sz);
+    for (int64_t t = t0; t < t1; ++t) {
+      const float *kt = J->k + t * row_k + (int64_t)h * dk;
+      const float *vt = J->v + t * row_v + (int64_t)h * dv;
+      const float *dot = J->dout + t * row_v + (int64_t)h * dv;
+      double *dqt = J->dq + t * row_k + (int64_t)h * dk;
+      for (int i = 0; i < dk; ++i) {
+        double *Si = S + (int64_t)i * dv;
+        const double ki = (double)kt[i];
+        for (int j = 0; j < dv; ++j) Si[j] = lam * Si[j] + ki * (double)vt[j];
+        double a = 0.0;
+        for (int j = 0; j < dv; ++j) a += (double)dot[j] * Si[j];
+        dqt[i] = J->scale * a;
+      }
+    }
+    /* backward sweep: R carries dL/dS from the later tokens */
+    if (J->ds_fin)
+      memcpy(G, J->ds_fin + ((int64_t)n * H + h) * sz, sizeof(double) * (size_t)sz);
+    else
+      memset(G, 0, sizeof(double) * (size_t)sz);
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+      const float *qt = J->q + t * row_k + (int64_t)h * dk;
+      const float *kt = J->k + t * row_k + (int64_t)h * dk;
+      const float *vt = J->v + t * row_v + (int64_t)h * dv;
+      const float *dot = J->dout + t * row_v + (int64_t)h * dv;
+      double *dkt = J->dkk + t * row_k + (int64_t)h * dk;
+      double *dvt = J->dvv + t * row_v + (int64_t)h * dv;
+      /* G_t = R + scale * q_t^T dO_t (R is in G on entry) */
+      for (int i = 0; i < dk; ++i) {
+        double *Gi = G + (int64_t)i * dv;
+        const double sq = J->scale * (double)qt[i];
+        for (int j = 0; j < dv; ++j) Gi[j] += sq * (double)dot[j];
+      }
+      for (int i = 0; i < dk; ++i) {
+        const double *Gi = G + (int64_t)i * dv;
+        double a = 0.0;
+        for (int j = 0; j < dv; ++j) a += Gi[j] * (double)vt[j];
+        dkt[i] = a;
+      }
+      for (int j = 0; j < dv; ++j) {
+        double a = 0.0;
+        for (int i = 0; i < dk; ++i) a += (double)kt[i] * G[(int64_t)i * dv + j];
+        dvt[j] = a;
+      }
+      /* R = lambda * G_t for the token before */
+      for (int64_t e = 0; e < sz; ++e) G[e] *= lam;
+    }
+    if (J->ds0)
+      memcpy(J->ds0 + ((int64_t)n * H + h) * sz, G, sizeof(double) * (size_t)sz);
+  }
+  free(S);
+  return NULL;
+}
+
+/*
+ * Packed variable-length backward: the inputs of oracle_gla_varlen plus
+ *   dout   : [total, H, dv] fp32 (dL/do)
+ *   ds_fin : [N, H, dk, dv] fp64 or NULL (dL/dS_final; NULL means zero)
+ * and outputs dq, dk : [total, H, dk] fp64, dv : [total, H, dv] fp64,
+ * ds0 : [N, H, dk, dv] fp64 or NULL.
+ * Returns 0, -1 on bad arguments, -2 when memory runs out.
+ */
+int oracle_gla_bwd_varlen(int N, const int64_t *cu, int H, int dk, int dv,
+                          const float *q, const float *k, const float *v,
+                          const float *decay, double scale, const double *s0,
+                          const float *dout, const double *ds_fin, double *dq,
+                          double *dkk, double *dvv, double *ds0, int nthreads) {
+  if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || !cu || !decay) return -1;
+  for (int n = 0; n < N; ++n)
+    if (cu[n + 1] < cu[n]) return -1;
+  if (cu[N] > cu[0] && (!q || !k || !v || !dout || !dq || !dkk || !dvv)) return -1;
+  bjob_t J;
+  memset(&J, 0, sizeof(J));
+  J.N = N; J.H = H; J.dk = dk; J.dv = dv; J.cu = cu;
+  J.q = q; J.k = k; J.v = v; J.decay = decay; J.dout = dout;
+  J.s0 = s0; J.ds_fin = ds_fin; J.scale = scale;
+  J.dq = dq; J.dkk = dkk; J.dvv = dvv; J.ds0 = ds0;
+  if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+  if (nthreads <= 0) nthreads = 1;
+  const int64_t total = (int64_t)N * H;
+  if (nthreads > total) nthreads = (int)(total > 0 ? total : 1);
+  pthread_mutex_init(&J.mu, NULL);
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!th) return -2;
+  int started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    if (pthread_create(&th[i], NULL, bworker, &J) != 0) break;
+    ++started;
+  }
+  if (started == 0) bworker(&J);
+  for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.mu);
+  return J.failed ? -2 : 0;
+}

@@ -48,6 +48,10 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             P, P, P, P, ctypes.c_double, P, P, ctypes.c_int]
         lib.oracle_gla_decode.restype = ctypes.c_int
+        lib.oracle_gla_bwd_varlen.argtypes = [
+            ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            P, P, P, P, ctypes.c_double, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.oracle_gla_bwd_varlen.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -122,6 +126,62 @@ def gla_fwd(q, k, v, decay, scale=1.0, s0=None, want_o=True, want_state=True,
                        v.reshape(B * T, H, dv), decay, scale, s0,
                        want_o, want_state, threads)
     return (None if o is None else o.reshape(B, T, H, dv)), sf
+
+
+def gla_bwd_varlen(cu_seqlens, q, k, v, decay, dout, scale=1.0, s0=None,
+                   ds_final=None, threads=None):
+    """Backward of the packed recurrence in fp64 (chain rule written out
+    token by token: a forward sweep for dq, a reverse sweep carrying
+    dL/dS for dk, dv and dS0; the training backward of the Laplace 3B /
+    Trainium2 page, section "Challenge 3").
+
+    dout: [total, H, dv] (fp32 or bf16 bits); ds_final: [N, H, dk, dv] or
+    None (zero). Returns (dq, dk [total, H, dk], dv [total, H, dv],
+    ds0 [N, H, dk, dv]), all fp64."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    q, k, v, dout = widen(q), widen(k), widen(v), widen(dout)
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    if k.shape != (total, H, dk) or v.shape != (total, H, dv) or \
+            dout.shape != (total, H, dv) or cu[-1] != total:
+        raise ValueError("shape mismatch")
+    lam = np.ascontiguousarray(np.asarray(decay, dtype=np.float32))
+    if lam.shape != (H,):
+        raise ValueError("decay must be [H]")
+
+    def state(x):
+        if x is None:
+            return None
+        x = np.asarray(x)
+        x = x if x.dtype == np.float64 else widen(x).astype(np.float64)
+        return np.ascontiguousarray(x.reshape(N, H, dk, dv))
+    s0a, dsf = state(s0), state(ds_final)
+    dq = np.zeros((total, H, dk), np.float64)
+    dk_ = np.zeros((total, H, dk), np.float64)
+    dv_ = np.zeros((total, H, dv), np.float64)
+    ds0 = np.zeros((N, H, dk, dv), np.float64)
+    rc = _load().oracle_gla_bwd_varlen(
+        N, _ptr(cu), H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+        float(scale), _ptr(s0a), _ptr(dout), _ptr(dsf), _ptr(dq), _ptr(dk_),
+        _ptr(dv_), _ptr(ds0), int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle_gla_bwd_varlen failed: %d" % rc)
+    return dq, dk_, dv_, ds0
+
+
+def gla_bwd(q, k, v, decay, dout, scale=1.0, s0=None, ds_final=None, threads=None):
+    """Backward of a fixed-length batch [B, T, H, d]; returns (dq, dk, dv
+    [B, T, H, d], ds0 [B, H, dk, dv]) in fp64."""
+    q, k, v, dout = widen(q), widen(k), widen(v), widen(dout)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    cu = np.arange(B + 1, dtype=np.int64) * T
+    dq, dk_, dv_, ds0 = gla_bwd_varlen(
+        cu, q.reshape(B * T, H, dk), k.reshape(B * T, H, dk), v.reshape(B * T, H, dv),
+        decay, dout.reshape(B * T, H, dv), scale, s0, ds_final, threads)
+    return (dq.reshape(B, T, H, dk), dk_.reshape(B, T, H, dk),
+            dv_.reshape(B, T, H, dv), ds0)
 
 
 def gla_decode(q, k, v, decay, state, scale=1.0, threads=None):
