@@ -188,6 +188,39 @@ gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
 
 size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
 
+// Backward plan: one work item per sequence (no time segments), the matrix-
+// core path only. The workspace holds the fp32 dv-tile partials of dq and dk.
+struct BwdPlan {
+  Plan p;
+  int ndt, dvt, nchp;
+  size_t part_bytes, ws_bytes;
+};
+
+bool bwd_supported(int dt, int dk, int dv, int chunk) {
+  return fast_path_ok(dt, dk, dv, chunk);
+}
+
+BwdPlan plan_bwd(int B, int T, int H, int dk, int dv) {
+  BwdPlan bp;
+  memset(&bp, 0, sizeof(bp));
+  bp.dvt = fast_dv_tile(dv);
+  bp.ndt = dv / bp.dvt;
+  const int nch = (T + 63) / 64;
+  bp.nchp = nch + (nch & 1);
+  Plan &p = bp.p;
+  p.mode = kPlanFixed;
+  p.n_seq = B;
+  p.T = T;
+  p.total_T = (int)((long long)B * T);
+  p.seg_len = T > 0 ? T : 64;
+  p.G = 1;
+  p.max_items = B;
+  p.deal = 0;
+  bp.part_bytes = align256((size_t)bp.ndt * B * H * bp.nchp * 64 * dk * sizeof(float));
+  bp.ws_bytes = T > 0 ? 2 * bp.part_bytes : 0;
+  return bp;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +369,75 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
   a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
   a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
   return run_forward(dt, hq, a, make_decay(decay_host, H), workspace, s);
+}
+
+size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
+                                     int dv, int chunk) {
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || !bwd_supported(dt, dk, dv, chunk) ||
+      B < 1 || T < 0 || (long long)B * T > kMaxTokens)
+    return 0;
+  return plan_bwd(B, T, H, dk, dv).ws_bytes;
+}
+
+gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                         int chunk, const void *q, const void *k, const void *v,
+                         const float *decay_host, float scale, const float *s0,
+                         const void *dout, const float *ds_final, void *dq,
+                         void *dk_out, void *dv_out, float *ds0, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  if (!bwd_supported(dt, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
+  if (B < 1 || T < 0 || (long long)B * T > kMaxTokens) return GLA_ERR_SHAPE;
+  if (!isfinite(scale)) return GLA_ERR_SHAPE;
+  st = check_decay(decay_host, H);
+  if (st != GLA_OK) return st;
+  const long long tok = (long long)B * T;
+  if (tok > 0 && (!q || !k || !v || !dout || !dq || !dk_out || !dv_out)) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) ||
+      misaligned(dq) || misaligned(dk_out) || misaligned(dv_out) || misaligned(s0) ||
+      misaligned(ds_final) || misaligned(ds0))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)tok * H * dk * es, nv = (size_t)tok * H * dv * es;
+  const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
+  // outputs overlap no input and no other output
+  const void *in[6] = {q, k, v, dout, s0, ds_final};
+  const size_t in_n[6] = {nqk, nqk, nv, nv, ns, ns};
+  const void *out[4] = {dq, dk_out, dv_out, ds0};
+  const size_t out_n[4] = {nqk, nqk, nv, ns};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlap(out[a], out_n[a], in[b], in_n[b])) return GLA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
+  }
+  const BwdPlan bp = plan_bwd(B, T, H, dk, dv);
+  if (bp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
+    for (int b = 0; b < 6; ++b)
+      if (overlap(workspace, bp.ws_bytes, in[b], in_n[b])) return GLA_ERR_ALIAS;
+    for (int a = 0; a < 4; ++a)
+      if (overlap(workspace, bp.ws_bytes, out[a], out_n[a])) return GLA_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (tok == 0) {  // no tokens: the gradient passes straight through
+    if (ds0 && launch_state_fill(B, H, dk, dv, ds_final, ds0, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    return GLA_OK;
+  }
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.s0 = s0; a.ds_final = ds_final;
+  a.dq = dq; a.dk = dk_out; a.dv_out = dv_out; a.ds0 = ds0;
+  a.slots = nullptr;
+  a.part_dq = (float *)workspace;
+  a.part_dk = (float *)((char *)workspace + bp.part_bytes);
+  a.scale = scale; a.H = H; a.dv = dv; a.nchp = bp.nchp;
+  if (launch_bwd_mfma(bp.dvt, bp.p, a, make_decay(decay_host, H), s) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
 }
 
 gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,

@@ -42,249 +42,9 @@
 // The D layout of two P^T tiles (j blocks 2s, 2s+1) is exactly a B operand
 // over the k-set {32s + 4g + r, 32s + 16 + 4g + r}, so P^T never leaves
 // registers; the matching A operand (V^T) is read with the same k-set.
-#include "gla_device.h"
+#include "gla_mfma.h"
 
 namespace gla {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Raw buffer resource (gfx9 family descriptor word 3) over `bytes` bytes.
-// Callers pass workgroup-uniform values; reading them back through
-// readfirstlane puts the descriptor in scalar registers (a descriptor the
-// compiler must treat as per-lane costs a loop around every access).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base,
-                                                           unsigned bytes) {
-  const unsigned long long a = (unsigned long long)base;
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  void *p = (void *)(((unsigned long long)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, 0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           0x00020000);
-}
-
-// Four bf16 of one column from four consecutive rows (see the header).
-__device__ __forceinline__ bf16x4 tr4(const bf16 *p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
-  return __builtin_bit_cast(bf16x4, r);
-}
-
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-  return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-template <int DVT>
-struct MfCfg {
-  static constexpr int C = 64, DK = 96;
-  // LDS row strides (elements). A stride of 8 mod 16 dwords (112 bf16 for 96
-  // columns, 80 for 64) keeps both the 16-byte fragment reads (16 rows, one
-  // column block) and the transpose reads (rows 4g + l16/4) free of bank
-  // conflicts on gfx950 (measured with the LDS conflict counters).
-  static constexpr int QS = DK + 16;     // q, k, ks and S^T
-  static constexpr int VS = DVT + 16;    // v and the staged output tile
-  static constexpr int NCT = DVT / 16;   // 16-column tiles of the dv tile
-  static constexpr int NDT = DK / 16;    // 16-row tiles of dk
-  static constexpr int NKS = DK / 32;    // 32-deep steps over dk
-  static constexpr int NJS = C / 32;     // 32-deep steps over the chunk
-  static constexpr int SDT = NDT / 2, SCT = NCT / 2;  // state tiles per state wave
-  static constexpr int NQV = DK / 8, NVV = DVT / 8;   // 16-byte vectors per row
-  static constexpr int QV = C * NQV / 256;  // q (or k) vectors per role thread
-  static constexpr int VV = C * NVV / 256;  // v vectors per state thread
-  static constexpr int OV = 16 * NVV / 64;  // output vectors per output lane
-  static_assert(C * NQV % 256 == 0 && C * NVV % 256 == 0 && 16 * NVV % 64 == 0, "split");
-  static_assert(NCT % 2 == 0 && NDT % 2 == 0, "state split");
-};
-
-// Valid rows of chunk ch of an item (0 for chunks past its end).
-__device__ __forceinline__ int chunk_rows(const Item &it, int ch) {
-  return max(0, min(64, it.t1 - (it.t0 + ch * 64)));
-}
-
-// ---------------------------------------------------------------------------
-// State role: 4 waves (role thread rt = 0..255, role wave w = 0..3).
-//   FUSED: runs beside the output role (also stores raw k for it and
-//          publishes the bf16 state each chunk); otherwise the state-only
-//          pass that computes a segment's local end state.
-// ---------------------------------------------------------------------------
-template <int DVT, bool FUSED>
-__device__ __forceinline__ void state_role(
-    const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const float *__restrict__ s0, float *__restrict__ s_final,
-    float *__restrict__ slots, const Item &it, int idx, int h, int H, int dv,
-    int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
-    bf16 *sSt0, bf16 *sSt1, const float *sPow) {
-  // sK, sKs and sV hold two chunk buffers each (FUSED) or one (state pass)
-  using M = MfCfg<DVT>;
-  constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
-  constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
-  const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
-  const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
-  const unsigned rowKb = (unsigned)(H * DK * 2), rowVb = (unsigned)(H * dv * 2);
-  const int nch = (it.t1 - it.t0 + C - 1) / C;
-  const int dt0 = SDT * (w >> 1), ct0 = SCT * (w & 1);
-
-  f32x4 accS[SDT][SCT];
-  {
-    // incoming state: s0 (or zeros) for a sequence's first item, else the
-    // combined state in slot idx-1; a local end state starts from zero
-    const float *src = nullptr;
-    if (FUSED) {
-      if (it.flags & kFirstSeg)
-        src = s0 ? s0 + ((long long)it.n * H + h) * DK * dv : nullptr;
-      else
-        src = slots + ((long long)(idx - 1) * H + h) * DK * dv;
-    }
-#pragma unroll
-    for (int a = 0; a < SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < SCT; ++b) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (src) {
-          const int d = 16 * (dt0 + a) + 4 * g;
-          const int c = c0 + 16 * (ct0 + b) + l16;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = src[(long long)(d + r) * dv + c];
-        }
-        accS[a][b] = x;
-      }
-  }
-
-  int rowK[QV], colK[QV], rowV[VV], colV[VV];
-#pragma unroll
-  for (int m = 0; m < QV; ++m) {
-    const int vi = rt + 256 * m;
-    rowK[m] = vi / M::NQV;
-    colK[m] = vi - rowK[m] * M::NQV;
-  }
-#pragma unroll
-  for (int m = 0; m < VV; ++m) {
-    const int vi = rt + 256 * m;
-    rowV[m] = vi / M::NVV;
-    colV[m] = vi - rowV[m] * M::NVV;
-  }
-  auto load_kv = [&](int ch, u32x4(&rk)[QV], u32x4(&rv)[VV]) {
-    const long long tb = (long long)it.t0 + (long long)ch * C;
-    const unsigned L = (unsigned)chunk_rows(it, ch);
-    const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, L * rowKb);
-    const __amdgpu_buffer_rsrc_t bv =
-        buf_rsrc(v + tb * H * dv + (long long)h * dv + c0, L * rowVb);
-#pragma unroll
-    for (int m = 0; m < QV; ++m)
-      rk[m] = __builtin_amdgcn_raw_buffer_load_b128(bk, rowK[m] * rowKb + colK[m] * 16, 0, 0);
-#pragma unroll
-    for (int m = 0; m < VV; ++m)
-      rv[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, rowV[m] * rowVb + colV[m] * 16, 0, 0);
-  };
-  constexpr int KBUF = C * QS, VBUF = C * VS;  // elements per chunk buffer
-  auto store_kv = [&](int L, int buf, const u32x4(&rk)[QV], const u32x4(&rv)[VV]) {
-    bf16 *dK = sK + buf * KBUF, *dKs = sKs + buf * KBUF, *dV = sV + buf * VBUF;
-#pragma unroll
-    for (int m = 0; m < QV; ++m) {
-      const int r = rowK[m];
-      if (FUSED) *reinterpret_cast<u32x4 *>(dK + r * QS + 8 * colK[m]) = rk[m];
-      // decay-scaled copy lambda^(L-1-r) k_r; rows past the end are zero
-      const float wgt = r < L ? sPow[max(L - 1 - r, 0)] : 0.f;
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, rk[m]);
-      bf16x8 ks;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ks[e] = (bf16)((float)kv[e] * wgt);
-      *reinterpret_cast<bf16x8 *>(dKs + r * QS + 8 * colK[m]) = ks;
-    }
-#pragma unroll
-    for (int m = 0; m < VV; ++m)
-      *reinterpret_cast<u32x4 *>(dV + rowV[m] * VS + 8 * colV[m]) = rv[m];
-  };
-  auto publish = [&](bf16 *dst) {
-#pragma unroll
-    for (int a = 0; a < SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < SCT; ++b) {
-        bf16x4 t;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] = (bf16)accS[a][b][r];
-        const int c = 16 * (ct0 + b) + l16;
-        *reinterpret_cast<bf16x4 *>(dst + c * QS + 16 * (dt0 + a) + 4 * g) = t;
-      }
-  };
-
-  // Chunk ch lives in LDS buffer ch & 1 (FUSED; the state pass has one
-  // buffer and a second barrier instead). Per chunk: one barrier, then the
-  // loads of chunk ch+2 are issued, the registers holding chunk ch+1 are
-  // written to the other buffer, and chunk ch is processed.
-  u32x4 ka[QV], kb[QV], va[VV], vb[VV];
-  load_kv(0, ka, va);
-  load_kv(1, kb, vb);
-  __syncthreads();  // sPow ready
-  store_kv(chunk_rows(it, 0), 0, ka, va);
-  if (FUSED) publish(sSt1);  // S_{-1}: the incoming state
-
-  auto body = [&](int ch, u32x4(&rkn)[QV], u32x4(&rvn)[VV], const u32x4(&rkx)[QV],
-                  const u32x4(&rvx)[VV], bf16 *st_pub) {
-    const int L = chunk_rows(it, ch);
-    const int cur = FUSED ? (ch & 1) : 0;
-    __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
-    load_kv(ch + 2, rkn, rvn);
-    if (FUSED) store_kv(chunk_rows(it, ch + 1), cur ^ 1, rkx, rvx);
-    const bf16 *cKs = sKs + cur * KBUF, *cV = sV + cur * VBUF;
-    const float lamL = sPow[L];
-#pragma unroll
-    for (int a = 0; a < SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < SCT; ++b) accS[a][b] *= lamL;
-#pragma unroll
-    for (int s = 0; s < M::NJS; ++s) {
-      bf16x8 af[SDT], bfr[SCT];
-      const int row = 32 * s + 4 * g + tr_row;
-#pragma unroll
-      for (int a = 0; a < SDT; ++a) {
-        const bf16 *base = cKs + row * QS + 16 * (dt0 + a) + tr_col;
-        af[a] = cat8(tr4(base), tr4(base + 16 * QS));
-      }
-#pragma unroll
-      for (int b = 0; b < SCT; ++b) {
-        const bf16 *base = cV + row * VS + 16 * (ct0 + b) + tr_col;
-        bfr[b] = cat8(tr4(base), tr4(base + 16 * VS));
-      }
-#pragma unroll
-      for (int a = 0; a < SDT; ++a)
-#pragma unroll
-        for (int b = 0; b < SCT; ++b) accS[a][b] = mfma(af[a], bfr[b], accS[a][b]);
-    }
-    if (FUSED) {
-      publish(st_pub);  // S_ch for the next chunk's readout
-    } else {
-      __syncthreads();  // single buffer: all waves are done with chunk ch
-      store_kv(chunk_rows(it, ch + 1), 0, rkx, rvx);
-    }
-  };
-  for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
-    body(ch, ka, va, kb, vb, sSt0);
-    body(ch + 1, kb, vb, ka, va, sSt1);
-  }
-
-  float *dst = nullptr;
-  if (!FUSED || ((it.flags & kLastSeg) && final_in_slot))
-    dst = slots + ((long long)idx * H + h) * DK * dv;
-  else if ((it.flags & kLastSeg) && s_final)
-    dst = s_final + ((long long)it.n * H + h) * DK * dv;
-  if (dst) {
-#pragma unroll
-    for (int a = 0; a < SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < SCT; ++b) {
-        const int d = 16 * (dt0 + a) + 4 * g;
-        const int c = c0 + 16 * (ct0 + b) + l16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(long long)(d + r) * dv + c] = accS[a][b][r];
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Output role: 4 waves (role wave w owns rows 16 w .. 16 w + 15 of a chunk).

@@ -54,6 +54,18 @@ struct FwdArgs {
   int final_in_slot;  // last segment writes its final state to its own slot
 };
 
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  const float *s0, *ds_final;
+  void *dq, *dk, *dv_out;
+  float *ds0;
+  float *slots;              // incoming states of time segments (none yet)
+  float *part_dq, *part_dk;  // [dv tiles][sequences][H][nchp][64 * 96] fp32
+  float scale;
+  int H, dv;
+  int nchp;  // chunks per sequence in the partial layout (rounded up to even)
+};
+
 // ---- launchers (gla_kernels.hip) -------------------------------------------
 // All return the hipGetLastError() of their launches.
 bool fast_path_ok(int dt, int dk, int dv, int chunk);
@@ -67,6 +79,8 @@ constexpr int kOrderMaxItems = 16384;
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s);
+hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
+                           const Decay &dec, hipStream_t s);
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,

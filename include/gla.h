@@ -130,6 +130,36 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
                                 void *stream);
 
 /*
+ * Backward of gla_chunk_fwd (training): given dL/do and optionally
+ * dL/dS_final, the gradients with respect to q, k, v and the initial state.
+ * The chain rule through the recurrence (Laplace 3B / Trainium2 page,
+ * sections "GLA mixer" and "Challenge 3": training differentiates through
+ * every sequential state update), with G_t = dL/dS_t:
+ *   G_t = lambda G_{t+1} + scale q_t^T dO_t   (dL/dS_final enters at t = T-1)
+ *   dq_t = scale dO_t S_t^T   dk_t = v_t G_t^T   dv_t = k_t G_t   dS0 = lambda G_0
+ * The decays are fixed, so there is no decay gradient.
+ *   q, k, v, s0, scale, decay_host : exactly as given to the forward
+ *   dout     : [B, T, H, dv] dt (dL/do)
+ *   ds_final : [B, H, dk, dv] fp32 or NULL (zero)
+ *   dq, dk_grad : [B, T, H, dk] dt, written    dv_grad : [B, T, H, dv] dt, written
+ *   ds0      : [B, H, dk, dv] fp32 or NULL to skip
+ *   workspace: at least gla_chunk_bwd_workspace_bytes() bytes (fp32 partial
+ *              sums of dq and dk over dv tiles); NULL allowed when that is 0.
+ * Supported: bf16 with dk = 96, dv a multiple of 64 and chunk 0 or 64
+ * (GLA_ERR_UNSUPPORTED otherwise). Checks as for gla_chunk_fwd; no output may
+ * overlap an input or another output. T = 0 is valid: ds0 receives ds_final
+ * (or zeros).
+ */
+size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
+                                     int dv, int chunk);
+gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                         int chunk, const void *q, const void *k, const void *v,
+                         const float *decay_host, float scale, const float *s0,
+                         const void *dout, const float *ds_final, void *dq,
+                         void *dk_grad, void *dv_grad, float *ds0, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for N independent sequences (one token each):
  *   state[n,h] <- lambda_h * state[n,h] + k[n,h]^T v[n,h]    (in place)
  *   o[n,h]     <- scale * q[n,h] state[n,h]                  (after update)

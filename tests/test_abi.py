@@ -164,6 +164,37 @@ def test_decode_argument_errors(L):
     assert dec(decay=d) == DECAY
 
 
+def test_backward_argument_errors(L):
+    def bwd(dt=BF16, B=2, T=100, H=4, dk=96, dv=192, chunk=0, q=A[0], k=A[1], v=A[2],
+            s0=None, do=A[3], dsf=None, dq=A[4], dk_=A[5], dv_=A[6], ds0=None,
+            ws=A[7], wsb=1 << 40, decay=GOOD):
+        return L.gla_chunk_bwd(dt, B, T, H, dk, dv, chunk, q, k, v, dptr(decay), 1.0, s0,
+                               do, dsf, dq, dk_, dv_, ds0, ws, wsb, None)
+    assert bwd(dt=7) == DTYPE
+    assert bwd(dt=F32) == UNSUP              # the backward runs on the bf16 matrix-core path
+    assert bwd(dk=64) == UNSUP
+    assert bwd(chunk=32) == UNSUP
+    assert bwd(B=0) == SHAPE
+    assert bwd(T=-1) == SHAPE
+    assert bwd(do=None) == NULL
+    assert bwd(dq=None) == NULL
+    assert bwd(dq=ctypes.c_void_p(A[4].value + 4)) == ALIGN
+    assert bwd(dk_=A[4]) == ALIAS                            # dk on top of dq
+    assert bwd(dv_=ctypes.c_void_p(A[3].value + 4096)) == ALIAS  # dv inside dout
+    assert bwd(ds0=ctypes.c_void_p(A[1].value)) == ALIAS    # ds0 on k
+    assert bwd(ws=None) == WS
+    assert bwd(wsb=16) == WS
+    assert bwd(ws=A[0]) == ALIAS                             # workspace on q
+    d = GOOD.copy()
+    d[3] = float("inf")
+    assert bwd(decay=d) == DECAY
+    need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 192, 0)
+    # dq and dk partials: 2 dv tiles x 8 x 16 heads x 32 chunks x 64 x 96 fp32, twice
+    assert need == 2 * 2 * 8 * 16 * 32 * 64 * 96 * 4
+    assert L.gla_chunk_bwd_workspace_bytes(F32, 8, 2048, 16, 96, 192, 0) == 0
+    assert L.gla_chunk_bwd_workspace_bytes(BF16, 8, 0, 16, 96, 192, 0) == 0
+
+
 def test_decode_pool_argument_errors(L):
     def pool(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], sl=A[5],
              P=8, st=A[3], o=A[4], decay=GOOD):

@@ -1,0 +1,106 @@
+"""GPU parity of the backward (gla_chunk_bwd) against the fp64 oracle's
+backward on the same seeded inputs and upstream gradients. Bar, per output
+(dq, dk, dv, dS0): max|gpu - oracle| <= 1e-2 * max|oracle| (bf16 inputs)."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_recurrent_amd import gla
+from chunked_gated_recurrent_amd import workloads as W
+from oracle import oracle as O
+from gla_testutil import TOL, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gla.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(seed, B, T, H, dv, with_s0=True, with_dsf=True):
+    x = W.prefill_inputs(seed, B, T, H, 96, dv, "bf16", 0.1 if with_s0 else None,
+                         W.geometric_decays(H))
+    rng = np.random.default_rng(seed + 1000)
+    do = W.bf16_bits(rng.standard_normal((B, T, H, dv), dtype=np.float32))
+    dsf = (rng.standard_normal((B, H, 96, dv), dtype=np.float32) * np.float32(0.5)
+           if with_dsf else None)
+    return x, do, dsf
+
+
+def _run(x, do, dsf, scale=1.0, heads=None):
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    dq, dk, dv, ds0 = gla.gla_chunk_bwd(q, k, v, x["decay"], dev(do), scale, s0, dev(dsf))
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv), host(ds0)
+
+
+def _oracle(x, do, dsf, scale=1.0, heads=None):
+    q, k, v, s0, d, lam = x["q"], x["k"], x["v"], x["s0"], do, x["decay"]
+    f = dsf
+    if heads is not None:
+        q, k, v, d = q[:, :, heads], k[:, :, heads], v[:, :, heads], d[:, :, heads]
+        s0 = None if s0 is None else s0[:, heads]
+        f = None if f is None else f[:, heads]
+        lam = lam[heads]
+    return O.gla_bwd(q, k, v, lam, d, scale, s0, f)
+
+
+def _check(name, got, ref):
+    names = ("dq", "dk", "dv", "dS0")
+    errs = [rel_err(g, r) for g, r in zip(got, ref)]
+    print("%s: " % name + "  ".join("%s %.2e" % (n, e) for n, e in zip(names, errs)))
+    for n, g, e in zip(names, got, errs):
+        assert np.isfinite(g).all(), n
+        assert e <= TOL["bf16"], (name, n, e)
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 130, 200])
+@pytest.mark.parametrize("dv", [192, 128])
+def test_backward_ragged_lengths(T, dv):
+    x, do, dsf = _inputs(700 + T, 2, T, 3, dv)
+    _check("bwd T%d dv%d" % (T, dv), _run(x, do, dsf), _oracle(x, do, dsf))
+
+
+def test_backward_without_initial_state_or_final_gradient():
+    x, do, dsf = _inputs(710, 2, 150, 4, 192, with_s0=False, with_dsf=False)
+    _check("bwd no s0 / dS_final", _run(x, do, dsf), _oracle(x, do, dsf))
+
+
+def test_backward_scale():
+    x, do, dsf = _inputs(711, 1, 130, 2, 192)
+    _check("bwd scale 0.37", _run(x, do, dsf, 0.37), _oracle(x, do, dsf, 0.37))
+
+
+def test_backward_laplace_prefill_sampled_heads():
+    """The Laplace-shaped batch (B8 T2048 H16 96/192), all heads on the GPU,
+    the oracle on the fastest, a middle and the slowest head."""
+    spec = W.WORKLOADS["laplace_prefill"]
+    x = W.spec_inputs("laplace_prefill")
+    rng = np.random.default_rng(712)
+    B, T, H, dv = spec["B"], spec["T"], spec["H"], spec["dv"]
+    do = W.bf16_bits(rng.standard_normal((B, T, H, dv), dtype=np.float32))
+    got = _run(x, do, None)
+    heads = [0, 7, 15]
+    ref = _oracle(x, do, None, heads=heads)
+    sel = (got[0][:, :, heads], got[1][:, :, heads], got[2][:, :, heads], got[3][:, heads])
+    _check("bwd laplace B8 T2048 heads 0,7,15", sel, ref)
+
+
+def test_backward_empty_sequence_passes_gradient_through():
+    x, do, dsf = _inputs(713, 2, 0, 2, 192)
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    _, _, _, ds0 = gla.gla_chunk_bwd(q, k, v, x["decay"], dev(do), 1.0, s0, dev(dsf))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ds0), dsf.astype(np.float64))
+
+
+def test_backward_is_bitwise_deterministic():
+    x, do, dsf = _inputs(714, 2, 300, 4, 192)
+    a = _run(x, do, dsf)
+    b = _run(x, do, dsf)
+    for u, w in zip(a, b):
+        np.testing.assert_array_equal(u, w)
