@@ -217,6 +217,49 @@ def bench_decode_pool(warmup_runs=1, pool_pages=2048):
                              kernel="decode_kernel<bf16,16> (slot table)")}
 
 
+BACKWARD_BYTES_PER_TOKEN = 16 * (96 + 96 + 192 + 192) * 2 + 16 * (96 + 96 + 192) * 2
+
+
+def bench_backward(steps, warmup):
+    """Backward of the Laplace-shaped prefill (B8 T2048 H16 96/192): dq, dk,
+    dv and dS0 from dO and dS_final, zero initial state."""
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    spec = W.WORKLOADS["laplace_prefill"]
+    B, T = spec["B"], spec["T"]
+    lam = W.decays_for(spec)
+    dev = torch.device("cuda")
+    sets = []
+    for r in range(2):
+        q, k, v, _ = W.device_normal_inputs(spec["seed"] + 50 + r, (B, T), H, DK, DV, dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(spec["seed"] + 60 + r)
+        do = torch.randn(B, T, H, DV, generator=g, device=dev).to(torch.bfloat16)
+        dsf = torch.randn(B, H, DK, DV, generator=g, device=dev)
+        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev))
+        sets.append((q, k, v, do, dsf, outs))
+    need = gla.lib().gla_chunk_bwd_workspace_bytes(1, B, T, H, DK, DV, 64)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        q, k, v, do, dsf, (dq, dk, dv, ds0) = sets[i % 2]
+        gla.gla_chunk_bwd(q, k, v, lam, do, 1.0, None, dsf, chunk=64, dq=dq, dk=dk,
+                          dv=dv, ds0=ds0, workspace=ws)
+
+    wall, ev_ms = timed(step, steps, warmup)
+    tokens = B * T
+    bytes_call = tokens * BACKWARD_BYTES_PER_TOKEN + 2 * B * STATE_BYTES
+    return {"workload": "laplace_backward", "config": {"B": B, "T": T, "chunk": 64},
+            "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_call": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(bytes_call, ev_ms),
+                             kernel="whole call (dq pass + dk/dv pass + partial sums)",
+                             traffic=measured_traffic("whole call@laplace_backward")),
+            "workspace_bytes": need}
+
+
 def bench_varlen(steps, warmup):
     import torch
     from chunked_gated_recurrent_amd import gla
@@ -337,7 +380,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen"])
+    ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen",
+                                       "backward"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -354,6 +398,7 @@ def main():
               "long": lambda: bench_long(args.steps, args.warmup),
               "decode": lambda: bench_decode(),
               "decode_pool": lambda: bench_decode_pool(),
+              "backward": lambda: bench_backward(args.steps, args.warmup),
               "varlen": lambda: bench_varlen(args.steps, args.warmup)}[args.only]
         r = fn()
         r.pop("x", None)
@@ -371,6 +416,9 @@ def main():
         secondary["batched_decode"] = bench_decode()
         log("batched_decode_pool ...")
         secondary["batched_decode_pool"] = bench_decode_pool()
+        log("laplace_backward ...")
+        secondary["laplace_backward"] = bench_backward(max(10, args.steps // 10),
+                                                       max(3, args.warmup // 10))
         log("varlen ...")
         secondary["varlen"] = bench_varlen(max(10, args.steps // 10), max(3, args.warmup // 10))
     copy_bw = copy_bandwidth()

@@ -543,11 +543,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // dq, dk <- sum of the dv-tile partials, as bf16 in [tokens, H, 96]
 // ---------------------------------------------------------------------------
+// One workgroup per (sequence, head, chunk). Each thread loads its 6 float4
+// of every partial tile (non-temporal: each partial is read once), sums them,
+// and writes the bf16 tile row-major into LDS; the rows then go out as
+// 16-byte segments.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(
     const float *__restrict__ part_dq, const float *__restrict__ part_dk,
     bf16 *__restrict__ dq, bf16 *__restrict__ dk, Plan plan, int H, int ndt,
     int nchp) {
-  constexpr int NDT = 6;
+  constexpr int NDT = 6, PER = kPartTile / 4 / 256, RS = 96 + 8;
+  typedef float f32x4n __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) bf16 sq[64 * RS];
+  __shared__ __attribute__((aligned(16))) bf16 sk[64 * RS];
   const long long tile = blockIdx.x;  // (n, h, ch)
   const int ch = (int)(tile % nchp);
   const long long nh = tile / nchp;
@@ -557,29 +564,42 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(
   Item it;
   if (!load_item(plan, n, it)) return;
   const long long tok0 = (long long)it.t0 + (long long)ch * 64;
-  for (int j = threadIdx.x; j < kPartTile / 4; j += blockDim.x) {
-    const int w = j / (NDT * 64);
-    const int dt = (j / 64) % NDT;
-    const int lane = j & 63;
-    const int i = 16 * w + (lane & 15);
-    const long long t = tok0 + i;
-    if (t >= it.t1) continue;
-    f32x4 sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
-    for (int d = 0; d < ndt; ++d) {
-      const long long off = part_offset(d, n, h, ch, plan.n_seq, H, nchp) + 4LL * j;
-      sq += *reinterpret_cast<const f32x4 *>(part_dq + off);
-      sk += *reinterpret_cast<const f32x4 *>(part_dk + off);
+  if (tok0 >= it.t1) return;  // a padding chunk of the partial layout
+  const int tid = threadIdx.x;
+  f32x4n aq[PER], ak[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) aq[m] = ak[m] = (f32x4n){0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < ndt; ++d) {
+    const long long off = part_offset(d, n, h, ch, plan.n_seq, H, nchp);
+    const f32x4n *pq = reinterpret_cast<const f32x4n *>(part_dq + off);
+    const f32x4n *pk = reinterpret_cast<const f32x4n *>(part_dk + off);
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      aq[m] += __builtin_nontemporal_load(pq + tid + 256 * m);
+      ak[m] += __builtin_nontemporal_load(pk + tid + 256 * m);
     }
-    const int col = 16 * dt + 4 * (lane >> 4);
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int j = tid + 256 * m;
+    const int w = j / (NDT * 64), dt = (j / 64) % NDT, lane = j & 63;
+    const int i = 16 * w + (lane & 15), col = 16 * dt + 4 * (lane >> 4);
     bf16x4 oq, ok;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      oq[r] = (bf16)sq[r];
-      ok[r] = (bf16)sk[r];
+      oq[r] = (bf16)aq[m][r];
+      ok[r] = (bf16)ak[m][r];
     }
-    const long long o = (t * H + h) * 96 + col;
-    *reinterpret_cast<bf16x4 *>(dq + o) = oq;
-    *reinterpret_cast<bf16x4 *>(dk + o) = ok;
+    *reinterpret_cast<bf16x4 *>(sq + i * RS + col) = oq;
+    *reinterpret_cast<bf16x4 *>(sk + i * RS + col) = ok;
+  }
+  __syncthreads();
+  const int rows = (int)min((long long)64, it.t1 - tok0);
+  for (int e = tid; e < rows * 12; e += 256) {
+    const int i = e / 12, c = e - i * 12;
+    const long long o = ((tok0 + i) * H + h) * 96 + 8 * c;
+    *reinterpret_cast<u32x4 *>(dq + o) = *reinterpret_cast<const u32x4 *>(sq + i * RS + 8 * c);
+    *reinterpret_cast<u32x4 *>(dk + o) = *reinterpret_cast<const u32x4 *>(sk + i * RS + 8 * c);
   }
 }
 
