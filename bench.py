@@ -220,13 +220,13 @@ def bench_decode_pool(warmup_runs=1, pool_pages=2048):
 BACKWARD_BYTES_PER_TOKEN = 16 * (96 + 96 + 192 + 192) * 2 + 16 * (96 + 96 + 192) * 2
 
 
-def bench_backward(steps, warmup):
-    """Backward of the Laplace-shaped prefill (B8 T2048 H16 96/192): dq, dk,
-    dv and dS0 from dO and dS_final, zero initial state."""
+def bench_backward(steps, warmup, workload="laplace_prefill"):
+    """Backward of a prefill workload (default the Laplace-shaped B8 T2048
+    H16 96/192): dq, dk, dv and dS0 from dO and dS_final, zero initial state."""
     import torch
     from chunked_gated_recurrent_amd import gla
     from chunked_gated_recurrent_amd import workloads as W
-    spec = W.WORKLOADS["laplace_prefill"]
+    spec = W.WORKLOADS[workload]
     B, T = spec["B"], spec["T"]
     lam = W.decays_for(spec)
     dev = torch.device("cuda")
@@ -251,12 +251,13 @@ def bench_backward(steps, warmup):
     wall, ev_ms = timed(step, steps, warmup)
     tokens = B * T
     bytes_call = tokens * BACKWARD_BYTES_PER_TOKEN + 2 * B * STATE_BYTES
-    return {"workload": "laplace_backward", "config": {"B": B, "T": T, "chunk": 64},
+    name = "laplace_backward" if workload == "laplace_prefill" else workload + "_backward"
+    return {"workload": name, "config": {"B": B, "T": T, "chunk": 64},
             "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
             "roofline": dict(roofline(bytes_call, ev_ms),
                              kernel="whole call (dq pass + dk/dv pass + partial sums)",
-                             traffic=measured_traffic("whole call@laplace_backward")),
+                             traffic=measured_traffic("whole call@" + name)),
             "workspace_bytes": need}
 
 
@@ -381,7 +382,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen",
-                                       "backward"])
+                                       "backward", "long_backward"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -399,6 +400,7 @@ def main():
               "decode": lambda: bench_decode(),
               "decode_pool": lambda: bench_decode_pool(),
               "backward": lambda: bench_backward(args.steps, args.warmup),
+              "long_backward": lambda: bench_backward(args.steps, args.warmup, "long_context"),
               "varlen": lambda: bench_varlen(args.steps, args.warmup)}[args.only]
         r = fn()
         r.pop("x", None)

@@ -188,36 +188,36 @@ gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
 
 size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
 
-// Backward plan: one work item per sequence (no time segments), the matrix-
-// core path only. The workspace holds the fp32 dv-tile partials of dq and dk.
+// Backward plan: the forward's work items (time segments when the batch
+// alone cannot fill the GPU), the matrix-core path only. The workspace holds
+// the fp32 dv-tile partials of dq and dk and, with time segments, the
+// segments' incoming states (forward combine) and carried gradients
+// (reverse combine).
 struct BwdPlan {
   Plan p;
+  bool segmented;
   int ndt, dvt, nchp;
-  size_t part_bytes, ws_bytes;
+  size_t part_bytes, slot_bytes, ws_bytes;
 };
 
 bool bwd_supported(int dt, int dk, int dv, int chunk) {
   return fast_path_ok(dt, dk, dv, chunk);
 }
 
-BwdPlan plan_bwd(int B, int T, int H, int dk, int dv) {
+BwdPlan plan_bwd(int dt, int B, int T, int H, int dk, int dv, int chunk) {
   BwdPlan bp;
   memset(&bp, 0, sizeof(bp));
+  const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
+  bp.p = hp.p;
+  bp.p.deal = 0;
+  bp.segmented = hp.segmented;
   bp.dvt = fast_dv_tile(dv);
   bp.ndt = dv / bp.dvt;
   const int nch = (T + 63) / 64;
   bp.nchp = nch + (nch & 1);
-  Plan &p = bp.p;
-  p.mode = kPlanFixed;
-  p.n_seq = B;
-  p.T = T;
-  p.total_T = (int)((long long)B * T);
-  p.seg_len = T > 0 ? T : 64;
-  p.G = 1;
-  p.max_items = B;
-  p.deal = 0;
   bp.part_bytes = align256((size_t)bp.ndt * B * H * bp.nchp * 64 * dk * sizeof(float));
-  bp.ws_bytes = T > 0 ? 2 * bp.part_bytes : 0;
+  bp.slot_bytes = bp.segmented ? align256((size_t)bp.p.max_items * H * dk * dv * sizeof(float)) : 0;
+  bp.ws_bytes = T > 0 ? 2 * bp.part_bytes + 2 * bp.slot_bytes : 0;
   return bp;
 }
 
@@ -376,7 +376,7 @@ size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
   if (check_common(dt, H, dk, dv, chunk) != GLA_OK || !bwd_supported(dt, dk, dv, chunk) ||
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
-  return plan_bwd(B, T, H, dk, dv).ws_bytes;
+  return plan_bwd(dt, B, T, H, dk, dv, chunk).ws_bytes;
 }
 
 gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
@@ -412,7 +412,7 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
     for (int b = a + 1; b < 4; ++b)
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
-  const BwdPlan bp = plan_bwd(B, T, H, dk, dv);
+  const BwdPlan bp = plan_bwd(dt, B, T, H, dk, dv, chunk);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
     for (int b = 0; b < 6; ++b)
@@ -431,12 +431,26 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.s0 = s0; a.ds_final = ds_final;
   a.dq = dq; a.dk = dk_out; a.dv_out = dv_out; a.ds0 = ds0;
-  a.slots = nullptr;
-  a.part_dq = (float *)workspace;
-  a.part_dk = (float *)((char *)workspace + bp.part_bytes);
+  char *ws = (char *)workspace;
+  a.part_dq = (float *)ws;
+  a.part_dk = (float *)(ws + bp.part_bytes);
   a.scale = scale; a.H = H; a.dv = dv; a.nchp = bp.nchp;
-  if (launch_bwd_mfma(bp.dvt, bp.p, a, make_decay(decay_host, H), s) != hipSuccess)
-    return GLA_ERR_HIP;
+  const Decay dec = make_decay(decay_host, H);
+  if (bp.segmented) {
+    // incoming forward states of the segments: the forward's state pass
+    // and combine, exactly as in gla_chunk_fwd
+    a.slots = (float *)(ws + 2 * bp.part_bytes);
+    a.cslots = (float *)(ws + 2 * bp.part_bytes + bp.slot_bytes);
+    FwdArgs f;
+    memset(&f, 0, sizeof(f));
+    f.q = q; f.k = k; f.v = v; f.s0 = s0; f.slots = a.slots;
+    f.scale = scale; f.H = H; f.dk = dk; f.dv = dv;
+    Plan ps = bp.p;
+    ps.deal = 1;  // the state pass skips every last segment
+    if (launch_fwd(dt, true, true, ps, f, dec, 64, s) != hipSuccess) return GLA_ERR_HIP;
+    if (launch_combine(bp.p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
+  }
+  if (launch_bwd_mfma(bp.dvt, bp.p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
 

@@ -150,11 +150,14 @@ __device__ __forceinline__ void dq_role(
         const bf16 *base = cK + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
         acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), pb[s], acc[dt]);
       }
-    // partial dq of this dv tile, in the MFMA output layout
-    float *dst = part + (long long)ch * kPartTile + (w * NDT * 64 + lane) * 4;
+    // partial dq of this dv tile, in the MFMA output layout (the padding
+    // chunk past the item's end writes nothing: it may be the next item's)
+    if (ch < nch) {
+      float *dst = part + (long long)ch * kPartTile + (w * NDT * 64 + lane) * 4;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<f32x4 *>(dst + dt * 64 * 4) = acc[dt] * scale;
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(dst + dt * 64 * 4) = acc[dt] * scale;
+    }
   };
   for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
     body(ch, ra, rb, sSt1);               // reads S_{ch-1}
@@ -191,8 +194,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = dtile * DVT;
+  // chunk index of the item's first chunk within its sequence
+  const int ch0 = (it.t0 - it.n * plan.T) / M::C;
   if (role_wave < 4)
-    dq_role<DVT>(dout, part_dq + part_offset(dtile, it.n, h, 0, plan.n_seq, H, nchp),
+    dq_role<DVT>(dout, part_dq + part_offset(dtile, it.n, h, ch0, plan.n_seq, H, nchp),
                  it, h, H, dv, c0, scale, tid & 255, role_wave, sD, sK, sV, sSt0,
                  sSt1, sPow);
   else
@@ -208,9 +213,10 @@ template <int DVT>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
-    const float *__restrict__ ds_final, bf16 *__restrict__ dv_out,
-    float *__restrict__ ds0, float *__restrict__ part_dk, Plan plan, Decay dec,
-    float scale, int H, int dv, int nchp) {
+    const float *__restrict__ ds_final, const float *__restrict__ cslots,
+    bf16 *__restrict__ dv_out, float *__restrict__ ds0,
+    float *__restrict__ part_dk, Plan plan, Decay dec, float scale, int H,
+    int dv, int nchp) {
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NDT = M::NDT, NCT = M::NCT, NJS = M::NJS, NKS = M::NKS;
@@ -247,6 +253,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int nch = (it.t1 - it.t0 + C - 1) / C;
   const int i_row = 16 * w + l16;
   const long long state_off = ((long long)it.n * H + h) * DK * dv;
+  const int ch0 = (it.t0 - it.n * plan.T) / C;  // first chunk within the sequence
 
   // Chunk rows; chunks before the first (ch < 0) are empty.
   auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
@@ -305,19 +312,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     }
   };
 
-  // carried gradient Ch (dv waves): SDT x SCT tiles of 16 x 16, fp32
+  // carried gradient Ch (dv waves): SDT x SCT tiles of 16 x 16, fp32. It
+  // starts as dL/dS_final for a sequence's last item, else as the combined
+  // carry flowing out of the next item (its slot)
   const int dt0 = SDT * (w >> 1), ct0 = SCT * (w & 1);
+  const float *cin = (it.flags & kLastSeg)
+                         ? (ds_final ? ds_final + state_off : nullptr)
+                         : cslots + ((long long)(idx + 1) * H + h) * DK * dv;
   f32x4 accC[SDT][SCT];
 #pragma unroll
   for (int a = 0; a < SDT; ++a)
 #pragma unroll
     for (int b = 0; b < SCT; ++b) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (dv_role && ds_final) {
+      if (dv_role && cin) {
         const int d = 16 * (dt0 + a) + 4 * g;
         const int c = c0 + 16 * (ct0 + b) + l16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = ds_final[state_off + (long long)(d + r) * dv + c];
+        for (int r = 0; r < 4; ++r) x[r] = cin[(long long)(d + r) * dv + c];
       }
       accC[a][b] = x;
     }
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), bm[s], acc[dt]);
         }
       if (ch >= 0) {
-        float *dst = part_dk + part_offset(dtile, it.n, h, ch, plan.n_seq, H, nchp) +
+        float *dst = part_dk + part_offset(dtile, it.n, h, ch0 + ch, plan.n_seq, H, nchp) +
                      (w * NDT * 64 + lane) * 4;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + dt * 64 * 4) = acc[dt];
@@ -527,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   }
   // after the first chunk Ch is dL/dS0 (an extra empty step leaves it as is:
   // lambda^0 = 1 and no rows)
-  if (dv_role && ds0) {
+  if (dv_role && ds0 && (it.flags & kFirstSeg)) {
 #pragma unroll
     for (int a = 0; a < SDT; ++a)
 #pragma unroll
@@ -538,6 +550,152 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         for (int r = 0; r < 4; ++r) ds0[state_off + (long long)(d + r) * dv + c] = accC[a][b][r];
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Local carries of time segments: for every item but a sequence's first,
+// U_g = scale sum_{t in item} lambda^(t - t0 + 1) q_t^T dO_t (the carried
+// gradient the item passes back when nothing flows into it), by the same
+// reverse chunk walk as the dv waves of bwd_dkdv_kernel, into slot g.
+// ---------------------------------------------------------------------------
+template <int DVT>
+__global__ __launch_bounds__(256, 2) void bwd_carry_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ dout,
+    float *__restrict__ cslots, Plan plan, Decay dec, float scale, int H, int dv) {
+  using M = MfCfg<DVT>;
+  constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
+  constexpr int NJS = M::NJS, SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
+  constexpr int NVV = M::NVV;
+  constexpr int KBUF = C * QS, VBUF = C * VS;
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2 * C * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sD[2 * C * VS];
+  __shared__ float sPow[C + 4];
+
+  const int ndt = dv / DVT;
+  int unit, dtile;
+  xcd_unit(plan, ndt, plan.max_items * H, unit, dtile);
+  if (unit >= plan.max_items * H) return;
+  const int slot = unit / H;
+  const int h = unit - slot * H;
+  int idx;
+  Item it;
+  if (!slot_item(plan, slot, idx, it)) return;
+  make_uniform(idx, it);
+  if (it.flags & kFirstSeg) return;  // no earlier item reads it
+  const int tid = threadIdx.x;
+  if (tid <= C) sPow[tid] = pow_f64(dec.lam[h], tid);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
+  const int c0 = dtile * DVT;
+  const unsigned rowKb = (unsigned)(H * DK * 2), rowVb = (unsigned)(H * dv * 2);
+  const int nch = (it.t1 - it.t0 + C - 1) / C;
+  const int dt0 = SDT * (w >> 1), ct0 = SCT * (w & 1);
+  auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
+
+  int rowA[QV], colA[QV], rowB[VV], colB[VV];
+#pragma unroll
+  for (int m = 0; m < QV; ++m) {
+    const int vi = tid + 256 * m;
+    rowA[m] = vi / M::NQV;
+    colA[m] = vi - rowA[m] * M::NQV;
+  }
+#pragma unroll
+  for (int m = 0; m < VV; ++m) {
+    const int vi = tid + 256 * m;
+    rowB[m] = vi / NVV;
+    colB[m] = vi - rowB[m] * NVV;
+  }
+  auto load = [&](int ch, u32x4(&rq)[QV], u32x4(&rd)[VV]) {
+    const unsigned L = (unsigned)rows_of(ch);
+    const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
+    const __amdgpu_buffer_rsrc_t bq = buf_rsrc(q + (tb * H + h) * DK, L * rowKb);
+    const __amdgpu_buffer_rsrc_t bd =
+        buf_rsrc(dout + tb * H * dv + (long long)h * dv + c0, L * rowVb);
+#pragma unroll
+    for (int m = 0; m < QV; ++m)
+      rq[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, rowA[m] * rowKb + colA[m] * 16, 0, 0);
+#pragma unroll
+    for (int m = 0; m < VV; ++m)
+      rd[m] = __builtin_amdgcn_raw_buffer_load_b128(bd, rowB[m] * rowVb + colB[m] * 16, 0, 0);
+  };
+  auto store = [&](int buf, const u32x4(&rq)[QV], const u32x4(&rd)[VV]) {
+#pragma unroll
+    for (int m = 0; m < QV; ++m)
+      *reinterpret_cast<u32x4 *>(sQ + buf * KBUF + rowA[m] * QS + 8 * colA[m]) = rq[m];
+#pragma unroll
+    for (int m = 0; m < VV; ++m)
+      *reinterpret_cast<u32x4 *>(sD + buf * VBUF + rowB[m] * VS + 8 * colB[m]) = rd[m];
+  };
+
+  f32x4 accC[SDT][SCT];
+#pragma unroll
+  for (int a = 0; a < SDT; ++a)
+#pragma unroll
+    for (int b = 0; b < SCT; ++b) accC[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  u32x4 qa_[QV], da_[VV], qb_[QV], db_[VV];
+  load(nch - 1, qa_, da_);
+  load(nch - 2, qb_, db_);
+  __syncthreads();  // sPow ready
+  float fq[NJS][8];
+#pragma unroll
+  for (int s = 0; s < NJS; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      fq[s][e] = scale * sPow[32 * s + 4 * g + e + 1];
+      fq[s][4 + e] = scale * sPow[32 * s + 16 + 4 * g + e + 1];
+    }
+  store((nch - 1) & 1, qa_, da_);
+
+  auto body = [&](int ch, u32x4(&nq)[QV], u32x4(&nd)[VV], const u32x4(&xq)[QV],
+                  const u32x4(&xd)[VV]) {
+    const int L = rows_of(ch);
+    const int cur = ch & 1;
+    __syncthreads();  // chunk ch is in LDS; the chunk after is done
+    load(ch - 2, nq, nd);
+    store(cur ^ 1, xq, xd);
+    const bf16 *cQ = sQ + cur * KBUF, *cD = sD + cur * VBUF;
+    const float lamL = sPow[L];
+#pragma unroll
+    for (int a = 0; a < SDT; ++a)
+#pragma unroll
+      for (int b = 0; b < SCT; ++b) accC[a][b] *= lamL;
+#pragma unroll
+    for (int s = 0; s < NJS; ++s) {
+      bf16x8 qs[SDT], dfr[SCT];
+      const int row = 32 * s + 4 * g + tr_row;
+#pragma unroll
+      for (int a = 0; a < SDT; ++a) {
+        const bf16 *base = cQ + row * QS + 16 * (dt0 + a) + tr_col;
+        const bf16x8 raw = cat8(tr4(base), tr4(base + 16 * QS));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[a][e] = (bf16)((float)raw[e] * fq[s][e]);
+      }
+#pragma unroll
+      for (int b = 0; b < SCT; ++b) {
+        const bf16 *base = cD + row * VS + 16 * (ct0 + b) + tr_col;
+        dfr[b] = cat8(tr4(base), tr4(base + 16 * VS));
+      }
+#pragma unroll
+      for (int a = 0; a < SDT; ++a)
+#pragma unroll
+        for (int b = 0; b < SCT; ++b) accC[a][b] = mfma(qs[a], dfr[b], accC[a][b]);
+    }
+  };
+  for (int p = 0; p < nch; p += 2) {
+    body(nch - 1 - p, qa_, da_, qb_, db_);
+    body(nch - 2 - p, qb_, db_, qa_, da_);
+  }
+  float *dst = cslots + ((long long)idx * H + h) * DK * dv;
+#pragma unroll
+  for (int a = 0; a < SDT; ++a)
+#pragma unroll
+    for (int b = 0; b < SCT; ++b) {
+      const int d = 16 * (dt0 + a) + 4 * g;
+      const int c = c0 + 16 * (ct0 + b) + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(long long)(d + r) * dv + c] = accC[a][b][r];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -561,10 +719,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(
   const int h = (int)(nh % H);
   const int n = (int)(nh / H);
   if (n >= plan.n_seq) return;
-  Item it;
-  if (!load_item(plan, n, it)) return;
-  const long long tok0 = (long long)it.t0 + (long long)ch * 64;
-  if (tok0 >= it.t1) return;  // a padding chunk of the partial layout
+  // the sequence's token range: from its first item to its last
+  int first, last;
+  seq_items(plan, n, first, last);
+  Item a, b;
+  if (last <= first || !load_item(plan, first, a) || !load_item(plan, last - 1, b)) return;
+  const long long seq_t1 = b.t1;
+  const long long tok0 = (long long)a.t0 + (long long)ch * 64;
+  if (tok0 >= seq_t1) return;  // a padding chunk of the partial layout
   const int tid = threadIdx.x;
   f32x4n aq[PER], ak[PER];
 #pragma unroll
@@ -594,7 +756,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(
     *reinterpret_cast<bf16x4 *>(sk + i * RS + col) = ok;
   }
   __syncthreads();
-  const int rows = (int)min((long long)64, it.t1 - tok0);
+  const int rows = (int)min((long long)64, seq_t1 - tok0);
   for (int e = tid; e < rows * 12; e += 256) {
     const int i = e / 12, c = e - i * 12;
     const long long o = ((tok0 + i) * H + h) * 96 + 8 * c;
@@ -607,13 +769,22 @@ template <int DVT>
 static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
+  if (a.cslots) {  // time segments: local carries, combined in reverse
+    Plan pc = p;
+    pc.deal = 1;  // the carry pass skips every first segment
+    const unsigned gc = xcd_grid(1, (long long)p.max_items * a.H, a.dv / DVT);
+    hipLaunchKernelGGL((bwd_carry_kernel<DVT>), dim3(gc), dim3(256), 0, s,
+                       (const bf16 *)a.q, (const bf16 *)a.dout, a.cslots, pc, dec,
+                       a.scale, a.H, a.dv);
+    (void)launch_rcombine(p, a.ds_final, a.cslots, dec, a.H, 96, a.dv, s);  // errors surface below
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<DVT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
                      a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv, a.nchp);
   hipLaunchKernelGGL((bwd_dkdv_kernel<DVT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-                     (const bf16 *)a.dout, a.ds_final, (bf16 *)a.dv_out, a.ds0,
-                     a.part_dk, p, dec, a.scale, a.H, a.dv, a.nchp);
+                     (const bf16 *)a.dout, a.ds_final, a.cslots, (bf16 *)a.dv_out,
+                     a.ds0, a.part_dk, p, dec, a.scale, a.H, a.dv, a.nchp);
 }
 
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,

@@ -59,7 +59,8 @@ struct BwdArgs {
   const float *s0, *ds_final;
   void *dq, *dk, *dv_out;
   float *ds0;
-  float *slots;              // incoming states of time segments (none yet)
+  float *slots;              // time segments: incoming states (forward combine)
+  float *cslots;             // time segments: carried gradients (reverse combine)
   float *part_dq, *part_dk;  // [dv tiles][sequences][H][nchp][64 * 96] fp32
   float scale;
   int H, dv;
@@ -79,6 +80,8 @@ constexpr int kOrderMaxItems = 16384;
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s);
+hipError_t launch_rcombine(const Plan &p, const float *ds_final, float *cslots,
+                           const Decay &dec, int H, int dk, int dv, hipStream_t s);
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
                            const Decay &dec, hipStream_t s);
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,

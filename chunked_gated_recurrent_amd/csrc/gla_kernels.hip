@@ -299,6 +299,43 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+// Reverse combine of carried gradients over a sequence's items: slot i
+// holds the local carry U_i on entry and, on exit, the carry flowing out of
+// item i into item i-1: C_out(i) = lambda^(len i) C_in(i) + U_i, with
+// C_in(last) = dL/dS_final (or 0) and C_in(i) = C_out(i+1). One thread per 4
+// consecutive state elements of one (sequence, head).
+__global__ __launch_bounds__(256) void rcombine_kernel(
+    Plan p, const float *__restrict__ ds_final, float *__restrict__ slots, Decay dec,
+    int H, int dk, int dv) {
+  const int per_state = dk * dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const int unit = blockIdx.x / blocks_per;
+  const int part = blockIdx.x - unit * blocks_per;
+  const int n = unit / H, h = unit - (unit / H) * H;
+  if (n >= p.n_seq) return;
+  const int e = (part * 256 + threadIdx.x) * 4;
+  if (e >= per_state) return;
+  int first, last;
+  seq_items(p, n, first, last);
+  if (last - first < 2) return;
+  const float lam = dec.lam[h];
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (ds_final)
+    S = *reinterpret_cast<const float4 *>(ds_final + ((long long)n * H + h) * per_state + e);
+  for (int i = last - 1; i > first; --i) {
+    Item it;
+    if (!load_item(p, i, it)) break;
+    const float a = pow_f64(lam, it.t1 - it.t0);
+    float4 *slot = reinterpret_cast<float4 *>(slots + ((long long)i * H + h) * per_state + e);
+    const float4 U = *slot;
+    S.x = fmaf(a, S.x, U.x);
+    S.y = fmaf(a, S.y, U.y);
+    S.z = fmaf(a, S.z, U.z);
+    S.w = fmaf(a, S.w, U.w);
+    *slot = S;
+  }
+}
+
 // s_final[n] <- slot of sequence n's last item (in-place final state with
 // segments: the last segment cannot write s_final while the first segment of
 // the same sequence may still be reading it as s0).
@@ -488,6 +525,16 @@ hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,
   const unsigned grid = (unsigned)((long long)p.n_seq * a.H * blocks_per);
   hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, s, p, a.s0,
                      a.slots, dec, a.H, a.dk, a.dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_rcombine(const Plan &p, const float *ds_final, float *cslots,
+                           const Decay &dec, int H, int dk, int dv, hipStream_t s) {
+  const int per_state = dk * dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const unsigned grid = (unsigned)((long long)p.n_seq * H * blocks_per);
+  hipLaunchKernelGGL(rcombine_kernel, dim3(grid), dim3(256), 0, s, p, ds_final,
+                     cslots, dec, H, dk, dv);
   return hipGetLastError();
 }
 

@@ -144,7 +144,9 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
  *   dq, dk_grad : [B, T, H, dk] dt, written    dv_grad : [B, T, H, dv] dt, written
  *   ds0      : [B, H, dk, dv] fp32 or NULL to skip
  *   workspace: at least gla_chunk_bwd_workspace_bytes() bytes (fp32 partial
- *              sums of dq and dk over dv tiles); NULL allowed when that is 0.
+ *              sums of dq and dk over dv tiles and, when sequences are split
+ *              into time segments, the segments' incoming states and carried
+ *              gradients); NULL allowed when that is 0.
  * Supported: bf16 with dk = 96, dv a multiple of 64 and chunk 0 or 64
  * (GLA_ERR_UNSUPPORTED otherwise). Checks as for gla_chunk_fwd; no output may
  * overlap an input or another output. T = 0 is valid: ds0 receives ds_final

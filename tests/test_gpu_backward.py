@@ -104,3 +104,31 @@ def test_backward_is_bitwise_deterministic():
     b = _run(x, do, dsf)
     for u, w in zip(a, b):
         np.testing.assert_array_equal(u, w)
+
+
+@pytest.mark.parametrize("T", [700, 1000])
+def test_backward_time_segments(T):
+    """Few chains and a high workgroup target force time segments: the
+    forward state pass and combine give each segment its incoming state,
+    the carry pass and reverse combine its incoming gradient."""
+    from gla_testutil import env
+    x, do, dsf = _inputs(720 + T, 2, T, 3, 192)
+    with env(GLA_TARGET_WGS=4096):
+        got = _run(x, do, dsf)
+    _check("bwd segmented T%d" % T, got, _oracle(x, do, dsf))
+
+
+def test_backward_long_context_sampled_heads():
+    """B1 T65536 (time segments by default): all heads on the GPU, the
+    oracle on the fastest and the slowest head over the whole sequence."""
+    spec = W.WORKLOADS["long_context"]
+    x = W.spec_inputs("long_context")
+    rng = np.random.default_rng(721)
+    B, T, H, dv = spec["B"], spec["T"], spec["H"], spec["dv"]
+    do = W.bf16_bits(rng.standard_normal((B, T, H, dv), dtype=np.float32))
+    dsf = rng.standard_normal((B, H, 96, dv), dtype=np.float32) * np.float32(0.5)
+    got = _run(x, do, dsf)
+    heads = [0, 15]
+    ref = _oracle(x, do, dsf, heads=heads)
+    sel = (got[0][:, :, heads], got[1][:, :, heads], got[2][:, :, heads], got[3][:, heads])
+    _check("bwd long_context T65536 heads 0,15", sel, ref)
