@@ -188,37 +188,76 @@ gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
 
 size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
 
-// Backward plan: the forward's work items (time segments when the batch
-// alone cannot fill the GPU), the matrix-core path only. The workspace holds
-// the fp32 dv-tile partials of dq and dk and, with time segments, the
-// segments' incoming states (forward combine) and carried gradients
-// (reverse combine).
+// Backward layout: the forward's plan (work items, dispatch order, time
+// segments and their incoming-state slots, in the forward's workspace
+// layout), then, with time segments, the carried-gradient slots, then the
+// fp32 dv-tile partials of dq and dk ([dv tile][H][token][96] each). The
+// matrix-core path only.
 struct BwdPlan {
-  Plan p;
-  bool segmented;
-  int ndt, dvt, nchp;
-  size_t part_bytes, slot_bytes, ws_bytes;
+  HostPlan hp;
+  int ndt, dvt;
+  size_t off_cslots, off_part, part_bytes, ws_bytes;
 };
 
 bool bwd_supported(int dt, int dk, int dv, int chunk) {
   return fast_path_ok(dt, dk, dv, chunk);
 }
 
-BwdPlan plan_bwd(int dt, int B, int T, int H, int dk, int dv, int chunk) {
+BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv) {
   BwdPlan bp;
   memset(&bp, 0, sizeof(bp));
-  const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
-  bp.p = hp.p;
-  bp.p.deal = 0;
-  bp.segmented = hp.segmented;
+  bp.hp = hp;
   bp.dvt = fast_dv_tile(dv);
   bp.ndt = dv / bp.dvt;
-  const int nch = (T + 63) / 64;
-  bp.nchp = nch + (nch & 1);
-  bp.part_bytes = align256((size_t)bp.ndt * B * H * bp.nchp * 64 * dk * sizeof(float));
-  bp.slot_bytes = bp.segmented ? align256((size_t)bp.p.max_items * H * dk * dv * sizeof(float)) : 0;
-  bp.ws_bytes = T > 0 ? 2 * bp.part_bytes + 2 * bp.slot_bytes : 0;
+  const size_t base = align256(hp.ws_bytes);
+  const size_t slot_bytes =
+      hp.segmented ? align256((size_t)hp.p.max_items * H * dk * dv * sizeof(float)) : 0;
+  bp.off_cslots = base;
+  bp.off_part = base + slot_bytes;
+  bp.part_bytes = align256((size_t)bp.ndt * H * total_T * dk * sizeof(float));
+  bp.ws_bytes = total_T > 0 ? bp.off_part + 2 * bp.part_bytes : 0;
   return bp;
+}
+
+// Launch the planned backward: [planner] [order] [forward state pass ->
+// combine] -> [carry pass -> reverse combine] -> dq pass -> dk/dv pass ->
+// partial sums.
+gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
+                        void *workspace, hipStream_t s) {
+  const HostPlan &hp = bp.hp;
+  Plan p = hp.p;
+  char *ws = (char *)workspace;
+  (void)hipGetLastError();  // report only this call's launch errors
+  if (p.mode == kPlanVarlenItems) {
+    p.index = (const int32_t *)(ws + hp.off_index);
+    p.items = (const int4 *)(ws + hp.off_items);
+    if (launch_planner(p, (int32_t *)(ws + hp.off_index), (int4 *)(ws + hp.off_items), s) != hipSuccess)
+      return GLA_ERR_HIP;
+  }
+  if (hp.ordered) {
+    if (launch_order(p, hp.chunk, (int32_t *)(ws + hp.off_order), s) != hipSuccess)
+      return GLA_ERR_HIP;
+    p.order = (const int32_t *)(ws + hp.off_order);
+  }
+  p.deal = p.mode == kPlanFixed ? 0 : 1;
+  a.part_dq = (float *)(ws + bp.off_part);
+  a.part_dk = (float *)(ws + bp.off_part + bp.part_bytes);
+  if (hp.segmented) {
+    // incoming forward states of the segments: the forward's state pass and
+    // combine, exactly as in the forward call
+    a.slots = (float *)(ws + hp.off_slots);
+    a.cslots = (float *)(ws + bp.off_cslots);
+    FwdArgs f;
+    memset(&f, 0, sizeof(f));
+    f.q = a.q; f.k = a.k; f.v = a.v; f.s0 = a.s0; f.slots = a.slots;
+    f.scale = a.scale; f.H = a.H; f.dk = 96; f.dv = a.dv;
+    Plan ps = p;
+    ps.deal = 1;  // the state pass skips every last segment
+    if (launch_fwd(dt, true, true, ps, f, dec, 64, s) != hipSuccess) return GLA_ERR_HIP;
+    if (launch_combine(p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
+  }
+  if (launch_bwd_mfma(bp.dvt, p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
 }
 
 }  // namespace
@@ -376,7 +415,7 @@ size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
   if (check_common(dt, H, dk, dv, chunk) != GLA_OK || !bwd_supported(dt, dk, dv, chunk) ||
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
-  return plan_bwd(dt, B, T, H, dk, dv, chunk).ws_bytes;
+  return bwd_layout(plan_fixed(dt, B, T, H, dk, dv, chunk), (long long)B * T, H, dk, dv).ws_bytes;
 }
 
 gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
@@ -412,7 +451,7 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
     for (int b = a + 1; b < 4; ++b)
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
-  const BwdPlan bp = plan_bwd(dt, B, T, H, dk, dv, chunk);
+  const BwdPlan bp = bwd_layout(plan_fixed(dt, B, T, H, dk, dv, chunk), tok, H, dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
     for (int b = 0; b < 6; ++b)
@@ -431,27 +470,75 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.s0 = s0; a.ds_final = ds_final;
   a.dq = dq; a.dk = dk_out; a.dv_out = dv_out; a.ds0 = ds0;
-  char *ws = (char *)workspace;
-  a.part_dq = (float *)ws;
-  a.part_dk = (float *)(ws + bp.part_bytes);
-  a.scale = scale; a.H = H; a.dv = dv; a.nchp = bp.nchp;
-  const Decay dec = make_decay(decay_host, H);
-  if (bp.segmented) {
-    // incoming forward states of the segments: the forward's state pass
-    // and combine, exactly as in gla_chunk_fwd
-    a.slots = (float *)(ws + 2 * bp.part_bytes);
-    a.cslots = (float *)(ws + 2 * bp.part_bytes + bp.slot_bytes);
-    FwdArgs f;
-    memset(&f, 0, sizeof(f));
-    f.q = q; f.k = k; f.v = v; f.s0 = s0; f.slots = a.slots;
-    f.scale = scale; f.H = H; f.dk = dk; f.dv = dv;
-    Plan ps = bp.p;
-    ps.deal = 1;  // the state pass skips every last segment
-    if (launch_fwd(dt, true, true, ps, f, dec, 64, s) != hipSuccess) return GLA_ERR_HIP;
-    if (launch_combine(bp.p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
+  a.scale = scale; a.H = H; a.dv = dv;
+  return run_backward(dt, bp, a, make_decay(decay_host, H), workspace, s);
+}
+
+size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, int H,
+                                            int dk, int dv, int chunk) {
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || !bwd_supported(dt, dk, dv, chunk) ||
+      N < 1 || N > (1 << 28) || total_T < 0)
+    return 0;
+  return bwd_layout(plan_varlen(dt, N, total_T, H, dk, dv, chunk), total_T, H, dk, dv).ws_bytes;
+}
+
+gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
+                                int dv, int chunk, const int32_t *cu_seqlens,
+                                const void *q, const void *k, const void *v,
+                                const float *decay_host, float scale, const float *s0,
+                                const void *dout, const float *ds_final, void *dq,
+                                void *dk_out, void *dv_out, float *ds0, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  if (!bwd_supported(dt, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
+  if (N < 1 || N > (1 << 28) || total_T < 0) return GLA_ERR_SHAPE;
+  if (!isfinite(scale)) return GLA_ERR_SHAPE;
+  st = check_decay(decay_host, H);
+  if (st != GLA_OK) return st;
+  if (!cu_seqlens) return GLA_ERR_NULL;
+  if (total_T > 0 && (!q || !k || !v || !dout || !dq || !dk_out || !dv_out)) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) ||
+      misaligned(dq) || misaligned(dk_out) || misaligned(dv_out) || misaligned(s0) ||
+      misaligned(ds_final) || misaligned(ds0) || ((uintptr_t)cu_seqlens & 3u))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)total_T * H * dk * es, nv = (size_t)total_T * H * dv * es;
+  const size_t ns = (size_t)N * H * dk * dv * sizeof(float);
+  const size_t ncu = sizeof(int32_t) * ((size_t)N + 1);
+  const void *in[7] = {q, k, v, dout, s0, ds_final, cu_seqlens};
+  const size_t in_n[7] = {nqk, nqk, nv, nv, ns, ns, ncu};
+  const void *out[4] = {dq, dk_out, dv_out, ds0};
+  const size_t out_n[4] = {nqk, nqk, nv, ns};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 7; ++b)
+      if (overlap(out[a], out_n[a], in[b], in_n[b])) return GLA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
-  if (launch_bwd_mfma(bp.dvt, bp.p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
-  return GLA_OK;
+  HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk);
+  hp.p.cu = cu_seqlens;
+  const BwdPlan bp = bwd_layout(hp, total_T, H, dk, dv);
+  if (bp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
+    for (int b = 0; b < 7; ++b)
+      if (overlap(workspace, bp.ws_bytes, in[b], in_n[b])) return GLA_ERR_ALIAS;
+    for (int a = 0; a < 4; ++a)
+      if (overlap(workspace, bp.ws_bytes, out[a], out_n[a])) return GLA_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (total_T == 0) {  // no tokens: the gradient passes straight through
+    if (ds0 && launch_state_fill(N, H, dk, dv, ds_final, ds0, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    return GLA_OK;
+  }
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.s0 = s0; a.ds_final = ds_final;
+  a.dq = dq; a.dk = dk_out; a.dv_out = dv_out; a.ds0 = ds0;
+  a.scale = scale; a.H = H; a.dv = dv;
+  return run_backward(dt, bp, a, make_decay(decay_host, H), workspace, s);
 }
 
 gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,

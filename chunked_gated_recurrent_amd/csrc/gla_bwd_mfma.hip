@@ -23,20 +23,18 @@
 //     of its dv tile in MFMA accumulators: four "dv waves" form dv (complete:
 //     its contraction runs over dk) and advance Ch, four "dk waves" form the
 //     dk terms of this dv tile.
-// dq and dk contract over dv, so each dv tile yields a partial sum; the
-// partials go to the workspace in the MFMA output layout (one 16-byte store
-// per lane) and a small kernel adds the tiles and writes bf16 dq and dk.
+// dq and dk contract over dv, so each dv tile yields a partial sum: fp32 rows
+// [dv tile][H][token][96] in the workspace (each lane stores the 4
+// consecutive dk values of one token that it holds), which a streaming
+// kernel adds up into bf16 dq and dk.
 #include "gla_mfma.h"
 
 namespace gla {
 
-// fp32 partial-sum tile of one (sequence, head, chunk): 4 row blocks x 6 dk
-// tiles x 64 lanes x 4 values = 64 tokens x 96.
-constexpr int kPartTile = 64 * 96;
-
-__device__ __forceinline__ long long part_offset(int dtile, int n, int h, int ch,
-                                                 int n_seq, int H, int nchp) {
-  return ((((long long)dtile * n_seq + n) * H + h) * nchp + ch) * kPartTile;
+// fp32 partial-sum rows: [dv tile][H][total tokens][96]
+__device__ __forceinline__ float *part_row(float *part, int dtile, int h, long long t,
+                                           int H, long long total_T) {
+  return part + (((long long)dtile * H + h) * total_T + t) * 96;
 }
 
 // ---------------------------------------------------------------------------
@@ -45,7 +43,8 @@ __device__ __forceinline__ long long part_offset(int dtile, int n, int h, int ch
 template <int DVT>
 __device__ __forceinline__ void dq_role(
     const bf16 *__restrict__ dout, float *__restrict__ part, const Item &it,
-    int h, int H, int dv, int c0, float scale, int rt, int w, bf16 *sD,
+    int h, int H, int dv, int c0, int dtile, long long total_T, float scale,
+    int rt, int w, bf16 *sD,
     const bf16 *sK, const bf16 *sV, const bf16 *sSt0, const bf16 *sSt1,
     const float *sPow) {
   using M = MfCfg<DVT>;
@@ -150,13 +149,14 @@ __device__ __forceinline__ void dq_role(
         const bf16 *base = cK + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
         acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), pb[s], acc[dt]);
       }
-    // partial dq of this dv tile, in the MFMA output layout (the padding
-    // chunk past the item's end writes nothing: it may be the next item's)
-    if (ch < nch) {
-      float *dst = part + (long long)ch * kPartTile + (w * NDT * 64 + lane) * 4;
+    // partial dq of this dv tile: this lane holds dk values 16 dt + 4 g .. +3
+    // of token i_row (rows past the item's end are not written: they belong
+    // to the next item or sequence)
+    if (i_row < chunk_rows(it, ch)) {
+      float *dst = part_row(part, dtile, h, it.t0 + (long long)ch * C + i_row, H, total_T) + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4 *>(dst + dt * 64 * 4) = acc[dt] * scale;
+        *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt] * scale;
     }
   };
   for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ s0,
     float *__restrict__ slots, float *__restrict__ part_dq, Plan plan,
-    Decay dec, float scale, int H, int dv, int nchp) {
+    Decay dec, float scale, int H, int dv) {
   using M = MfCfg<DVT>;
   __shared__ __attribute__((aligned(16))) bf16 sD[2 * M::C * M::VS];
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
@@ -194,12 +194,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = dtile * DVT;
-  // chunk index of the item's first chunk within its sequence
-  const int ch0 = (it.t0 - it.n * plan.T) / M::C;
   if (role_wave < 4)
-    dq_role<DVT>(dout, part_dq + part_offset(dtile, it.n, h, ch0, plan.n_seq, H, nchp),
-                 it, h, H, dv, c0, scale, tid & 255, role_wave, sD, sK, sV, sSt0,
-                 sSt1, sPow);
+    dq_role<DVT>(dout, part_dq, it, h, H, dv, c0, dtile, plan.total_T, scale, tid & 255,
+                 role_wave, sD, sK, sV, sSt0, sSt1, sPow);
   else
     state_role<DVT, true>(k, v, s0, nullptr, slots, it, idx, h, H, dv, c0, 0,
                           tid & 255, role_wave - 4, sK, sKs, sV, sSt0, sSt1, sPow);
@@ -216,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const float *__restrict__ ds_final, const float *__restrict__ cslots,
     bf16 *__restrict__ dv_out, float *__restrict__ ds0,
     float *__restrict__ part_dk, Plan plan, Decay dec, float scale, int H,
-    int dv, int nchp) {
+    int dv) {
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NDT = M::NDT, NCT = M::NCT, NJS = M::NJS, NKS = M::NKS;
@@ -253,7 +250,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   const int nch = (it.t1 - it.t0 + C - 1) / C;
   const int i_row = 16 * w + l16;
   const long long state_off = ((long long)it.n * H + h) * DK * dv;
-  const int ch0 = (it.t0 - it.n * plan.T) / C;  // first chunk within the sequence
 
   // Chunk rows; chunks before the first (ch < 0) are empty.
   auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
@@ -525,11 +521,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           const bf16 *base = cQ + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
           acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), bm[s], acc[dt]);
         }
-      if (ch >= 0) {
-        float *dst = part_dk + part_offset(dtile, it.n, h, ch0 + ch, plan.n_seq, H, nchp) +
-                     (w * NDT * 64 + lane) * 4;
+      if (i_row < L) {  // rows past the item's end are not written
+        float *dst = part_row(part_dk, dtile, h, tb + i_row, H, plan.total_T) + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + dt * 64 * 4) = acc[dt];
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt];
       }
     }
   };
@@ -701,68 +696,33 @@ __global__ __launch_bounds__(256, 2) void bwd_carry_kernel(
 // ---------------------------------------------------------------------------
 // dq, dk <- sum of the dv-tile partials, as bf16 in [tokens, H, 96]
 // ---------------------------------------------------------------------------
-// One workgroup per (sequence, head, chunk). Each thread loads its 6 float4
-// of every partial tile (non-temporal: each partial is read once), sums them,
-// and writes the bf16 tile row-major into LDS; the rows then go out as
-// 16-byte segments.
+// One thread per 4 consecutive values of one (token, head) row; each partial
+// is read once (non-temporal loads).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(
     const float *__restrict__ part_dq, const float *__restrict__ part_dk,
-    bf16 *__restrict__ dq, bf16 *__restrict__ dk, Plan plan, int H, int ndt,
-    int nchp) {
-  constexpr int NDT = 6, PER = kPartTile / 4 / 256, RS = 96 + 8;
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, long long total_T, int H, int ndt) {
   typedef float f32x4n __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) bf16 sq[64 * RS];
-  __shared__ __attribute__((aligned(16))) bf16 sk[64 * RS];
-  const long long tile = blockIdx.x;  // (n, h, ch)
-  const int ch = (int)(tile % nchp);
-  const long long nh = tile / nchp;
-  const int h = (int)(nh % H);
-  const int n = (int)(nh / H);
-  if (n >= plan.n_seq) return;
-  // the sequence's token range: from its first item to its last
-  int first, last;
-  seq_items(plan, n, first, last);
-  Item a, b;
-  if (last <= first || !load_item(plan, first, a) || !load_item(plan, last - 1, b)) return;
-  const long long seq_t1 = b.t1;
-  const long long tok0 = (long long)a.t0 + (long long)ch * 64;
-  if (tok0 >= seq_t1) return;  // a padding chunk of the partial layout
-  const int tid = threadIdx.x;
-  f32x4n aq[PER], ak[PER];
-#pragma unroll
-  for (int m = 0; m < PER; ++m) aq[m] = ak[m] = (f32x4n){0.f, 0.f, 0.f, 0.f};
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  const long long n4 = total_T * H * 24;
+  if (e >= n4) return;
+  const long long row = e / 24;  // token * H + head
+  const int c4 = (int)(e - row * 24);
+  const long long t = row / H;
+  const int h = (int)(row - t * H);
+  f32x4n sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
   for (int d = 0; d < ndt; ++d) {
-    const long long off = part_offset(d, n, h, ch, plan.n_seq, H, nchp);
-    const f32x4n *pq = reinterpret_cast<const f32x4n *>(part_dq + off);
-    const f32x4n *pk = reinterpret_cast<const f32x4n *>(part_dk + off);
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      aq[m] += __builtin_nontemporal_load(pq + tid + 256 * m);
-      ak[m] += __builtin_nontemporal_load(pk + tid + 256 * m);
-    }
+    const long long off = (((long long)d * H + h) * total_T + t) * 96 + 4 * c4;
+    sq += __builtin_nontemporal_load(reinterpret_cast<const f32x4n *>(part_dq + off));
+    sk += __builtin_nontemporal_load(reinterpret_cast<const f32x4n *>(part_dk + off));
   }
+  bf16x4 oq, ok;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int j = tid + 256 * m;
-    const int w = j / (NDT * 64), dt = (j / 64) % NDT, lane = j & 63;
-    const int i = 16 * w + (lane & 15), col = 16 * dt + 4 * (lane >> 4);
-    bf16x4 oq, ok;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      oq[r] = (bf16)aq[m][r];
-      ok[r] = (bf16)ak[m][r];
-    }
-    *reinterpret_cast<bf16x4 *>(sq + i * RS + col) = oq;
-    *reinterpret_cast<bf16x4 *>(sk + i * RS + col) = ok;
+  for (int r = 0; r < 4; ++r) {
+    oq[r] = (bf16)sq[r];
+    ok[r] = (bf16)sk[r];
   }
-  __syncthreads();
-  const int rows = (int)min((long long)64, seq_t1 - tok0);
-  for (int e = tid; e < rows * 12; e += 256) {
-    const int i = e / 12, c = e - i * 12;
-    const long long o = ((tok0 + i) * H + h) * 96 + 8 * c;
-    *reinterpret_cast<u32x4 *>(dq + o) = *reinterpret_cast<const u32x4 *>(sq + i * RS + 8 * c);
-    *reinterpret_cast<u32x4 *>(dk + o) = *reinterpret_cast<const u32x4 *>(sk + i * RS + 8 * c);
-  }
+  *reinterpret_cast<bf16x4 *>(dq + row * 96 + 4 * c4) = oq;
+  *reinterpret_cast<bf16x4 *>(dk + row * 96 + 4 * c4) = ok;
 }
 
 template <int DVT>
@@ -780,21 +740,21 @@ static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
   }
   hipLaunchKernelGGL((bwd_dq_kernel<DVT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
-                     a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv, a.nchp);
+                     a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv);
   hipLaunchKernelGGL((bwd_dkdv_kernel<DVT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      (const bf16 *)a.dout, a.ds_final, a.cslots, (bf16 *)a.dv_out,
-                     a.ds0, a.part_dk, p, dec, a.scale, a.H, a.dv, a.nchp);
+                     a.ds0, a.part_dk, p, dec, a.scale, a.H, a.dv);
 }
 
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
                            const Decay &dec, hipStream_t s) {
   if (dvt == 96) launch_bwd_dvt<96>(p, a, dec, s);
   else launch_bwd_dvt<64>(p, a, dec, s);
-  const unsigned tiles = (unsigned)((long long)p.n_seq * a.H * a.nchp);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(tiles), dim3(256), 0, s,
-                     a.part_dq, a.part_dk, (bf16 *)a.dq, (bf16 *)a.dk, p, a.H,
-                     a.dv / dvt, a.nchp);
+  const long long n4 = (long long)p.total_T * a.H * 24;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     a.part_dq, a.part_dk, (bf16 *)a.dq, (bf16 *)a.dk, (long long)p.total_T,
+                     a.H, a.dv / dvt);
   return hipGetLastError();
 }
 

@@ -61,10 +61,9 @@ struct BwdArgs {
   float *ds0;
   float *slots;              // time segments: incoming states (forward combine)
   float *cslots;             // time segments: carried gradients (reverse combine)
-  float *part_dq, *part_dk;  // [dv tiles][sequences][H][nchp][64 * 96] fp32
+  float *part_dq, *part_dk;  // [dv tiles][H][tokens][96] fp32 partial sums
   float scale;
   int H, dv;
-  int nchp;  // chunks per sequence in the partial layout (rounded up to even)
 };
 
 // ---- launchers (gla_kernels.hip) -------------------------------------------

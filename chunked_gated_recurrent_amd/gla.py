@@ -12,6 +12,7 @@ Functions mirror the C entry points:
     gla_decode_step(q, k, v, decay, state, ...)  -> o   (state updated in place)
     gla_decode_step_pool(q, k, v, decay, state_pool, slots, ...) -> o
     gla_chunk_bwd(q, k, v, decay, dout, ...)    -> (dq, dk, dv, ds0)
+    gla_chunk_bwd_varlen(q, k, v, cu, decay, dout, ...) -> (dq, dk, dv, ds0)
 """
 from __future__ import annotations
 
@@ -37,6 +38,9 @@ _SIGS = {
     "gla_chunk_bwd_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_chunk_bwd": ([_I] * 7 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
                                   _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "gla_chunk_bwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
+    "gla_chunk_bwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "gla_chunk_fwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_chunk_fwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P], _I),
@@ -295,4 +299,52 @@ def gla_chunk_bwd(q, k, v, decay, dout, scale: float = 1.0, initial_state=None,
                          _stream(dev))
     if rc != 0:
         raise GlaError(rc, "gla_chunk_bwd")
+    return dq, dk, dv, ds0
+
+
+def gla_chunk_bwd_varlen(q, k, v, cu_seqlens, decay, dout, scale: float = 1.0,
+                         initial_state=None, ds_final=None, want_ds0: bool = True,
+                         chunk: int = 0, dq=None, dk=None, dv=None, ds0=None,
+                         workspace=None):
+    """Backward of gla_chunk_fwd_varlen: q, k [total_T, H, dk], v and dout
+    [total_T, H, dv] (bf16), cu_seqlens [N+1] int32 on the device,
+    initial_state and ds_final [N, H, dk, dv] fp32 or None. Returns
+    (dq, dk, dv, ds0)."""
+    import torch
+    dev = q.device
+    total, H, dk_ = q.shape
+    dv_ = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (total, H, dk_))
+    _check(v, "v", dev, q.dtype, (total, H, dv_))
+    _check(dout, "dout", dev, q.dtype, (total, H, dv_))
+    _check(cu_seqlens, "cu_seqlens", dev, torch.int32, (N + 1,))
+    dt = _dt(q)
+    for name, t in (("initial_state", initial_state), ("ds_final", ds_final)):
+        if t is not None:
+            _check(t, name, dev, torch.float32, (N, H, dk_, dv_))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(dq, "dq", dev, q.dtype, (total, H, dk_))
+    _check(dk, "dk", dev, q.dtype, (total, H, dk_))
+    _check(dv, "dv", dev, q.dtype, (total, H, dv_))
+    if ds0 is None and want_ds0:
+        ds0 = torch.empty((N, H, dk_, dv_), dtype=torch.float32, device=dev)
+    if ds0 is not None:
+        _check(ds0, "ds0", dev, torch.float32, (N, H, dk_, dv_))
+    L = lib()
+    need = L.gla_chunk_bwd_varlen_workspace_bytes(dt, N, total, H, dk_, dv_, chunk)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _d, dptr = _decay_array(decay, H)
+    rc = L.gla_chunk_bwd_varlen(dt, N, total, H, dk_, dv_, chunk, _ptr(cu_seqlens), _ptr(q),
+                                _ptr(k), _ptr(v), dptr, float(scale), _ptr(initial_state),
+                                _ptr(dout), _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(ds0), _ptr(ws), wsb, _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_chunk_bwd_varlen")
     return dq, dk, dv, ds0

@@ -162,6 +162,24 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
                          size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of gla_chunk_fwd_varlen: the arguments of gla_chunk_bwd in the
+ * packed layout of gla_chunk_fwd_varlen (q, k, dq, dk_grad [total_T, H, dk];
+ * v, dout, dv_grad [total_T, H, dv]; s0, ds_final, ds0 [N, H, dk, dv];
+ * cu_seqlens [N + 1] int32 on the device, as for the forward). Same support,
+ * checks and workspace rules; a zero-length sequence passes its ds_final
+ * (or zeros) straight to ds0.
+ */
+size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, int H,
+                                            int dk, int dv, int chunk);
+gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
+                                int dv, int chunk, const int32_t *cu_seqlens,
+                                const void *q, const void *k, const void *v,
+                                const float *decay_host, float scale, const float *s0,
+                                const void *dout, const float *ds_final, void *dq,
+                                void *dk_grad, void *dv_grad, float *ds0, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for N independent sequences (one token each):
  *   state[n,h] <- lambda_h * state[n,h] + k[n,h]^T v[n,h]    (in place)
  *   o[n,h]     <- scale * q[n,h] state[n,h]                  (after update)

@@ -189,10 +189,29 @@ def test_backward_argument_errors(L):
     d[3] = float("inf")
     assert bwd(decay=d) == DECAY
     need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 192, 0)
-    # dq and dk partials: 2 dv tiles x 8 x 16 heads x 32 chunks x 64 x 96 fp32, twice
-    assert need == 2 * 2 * 8 * 16 * 32 * 64 * 96 * 4
+    # dq and dk partials: 2 dv tiles x 16 heads x 16,384 tokens x 96 fp32, twice
+    assert need == 2 * 2 * 16 * 8 * 2048 * 96 * 4
     assert L.gla_chunk_bwd_workspace_bytes(F32, 8, 2048, 16, 96, 192, 0) == 0
     assert L.gla_chunk_bwd_workspace_bytes(BF16, 8, 0, 16, 96, 192, 0) == 0
+
+
+def test_backward_varlen_argument_errors(L):
+    def bwd(dt=BF16, N=3, total=300, H=4, dk=96, dv=192, chunk=0, cu=A[7], q=A[0], k=A[1],
+            v=A[2], do=A[3], dq=A[4], dk_=A[5], dv_=A[6], ds0=None, ws=None, wsb=0,
+            decay=GOOD):
+        return L.gla_chunk_bwd_varlen(dt, N, total, H, dk, dv, chunk, cu, q, k, v,
+                                      dptr(decay), 1.0, None, do, None, dq, dk_, dv_, ds0,
+                                      ws, wsb, None)
+    assert bwd(dt=F32) == UNSUP
+    assert bwd(N=0) == SHAPE
+    assert bwd(total=-2) == SHAPE
+    assert bwd(cu=None) == NULL
+    assert bwd(cu=ctypes.c_void_p(A[7].value + 2)) == ALIGN
+    assert bwd(dq=ctypes.c_void_p(A[7].value)) == ALIAS     # dq on top of cu_seqlens
+    assert bwd(dk_=A[4]) == ALIAS
+    assert bwd() == WS                                      # N > 1: the order needs scratch
+    assert L.gla_chunk_bwd_varlen_workspace_bytes(BF16, 3, 300, 4, 96, 192, 0) > 0
+    assert L.gla_chunk_bwd_varlen_workspace_bytes(F32, 3, 300, 4, 96, 192, 0) == 0
 
 
 def test_decode_pool_argument_errors(L):

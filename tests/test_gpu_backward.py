@@ -132,3 +132,56 @@ def test_backward_long_context_sampled_heads():
     ref = _oracle(x, do, dsf, heads=heads)
     sel = (got[0][:, :, heads], got[1][:, :, heads], got[2][:, :, heads], got[3][:, heads])
     _check("bwd long_context T65536 heads 0,15", sel, ref)
+
+
+def _varlen_case(seed, lengths, H=3, dv=192):
+    x = W.varlen_inputs(seed, len(lengths), 0, H, 96, dv, "bf16", 0.1,
+                        W.geometric_decays(H), lengths=lengths)
+    total = int(x["cu_seqlens"][-1])
+    rng = np.random.default_rng(seed + 1000)
+    do = W.bf16_bits(rng.standard_normal((total, H, dv), dtype=np.float32))
+    dsf = rng.standard_normal((len(lengths), H, 96, dv), dtype=np.float32) * np.float32(0.5)
+    return x, do, dsf
+
+
+def _run_varlen(x, do, dsf):
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    cu = dev(x["cu_seqlens"])
+    dq, dk, dv, ds0 = gla.gla_chunk_bwd_varlen(q, k, v, cu, x["decay"], dev(do), 1.0, s0,
+                                               dev(dsf))
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv), host(ds0)
+
+
+@pytest.mark.parametrize("lengths", [[5, 0, 130, 1, 64, 65, 300],
+                                     [2000, 1, 700]])
+def test_backward_varlen_matches_oracle(lengths):
+    """Packed sequences with empty, one-token, chunk-aligned and ragged
+    lengths (one workgroup per sequence), and a few long sequences (time
+    segments from the device planner)."""
+    x, do, dsf = _varlen_case(730 + len(lengths), lengths)
+    got = _run_varlen(x, do, dsf)
+    ref = O.gla_bwd_varlen(x["cu_seqlens"], x["q"], x["k"], x["v"], x["decay"], do, 1.0,
+                           x["s0"], dsf)
+    _check("bwd varlen %s" % lengths, got, ref)
+    for n, L in enumerate(lengths):
+        if L == 0:
+            np.testing.assert_array_equal(got[3][n], dsf[n].astype(np.float64))
+
+
+def test_backward_varlen_equals_fixed_batch():
+    """Equal lengths packed: bitwise the fixed-batch backward on the same
+    tokens (both split each sequence into the same two time segments)."""
+    B, T, H = 4, 300, 16
+    x, do, dsf = _inputs(740, B, T, H, 192)
+    got_f = _run(x, do, dsf)
+    cu = np.arange(B + 1, dtype=np.int32) * T
+    q, k, v = (dev(x[n].reshape(B * T, H, -1)) for n in ("q", "k", "v"))
+    dq, dk, dv, ds0 = gla.gla_chunk_bwd_varlen(q, k, v, dev(cu), x["decay"],
+                                               dev(do.reshape(B * T, H, -1)), 1.0,
+                                               dev(x["s0"]), dev(dsf))
+    torch.cuda.synchronize()
+    got_v = (host(dq).reshape(B, T, H, -1), host(dk).reshape(B, T, H, -1),
+             host(dv).reshape(B, T, H, -1), host(ds0))
+    for a, b in zip(got_f, got_v):
+        np.testing.assert_array_equal(a, b)
