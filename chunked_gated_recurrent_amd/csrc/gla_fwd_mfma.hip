@@ -227,8 +227,8 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     float *__restrict__ slots, Plan plan, Decay dec, int H, int dv) {
   using M = MfCfg<DVT>;
-  __shared__ __attribute__((aligned(16))) bf16 sKs[M::C * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[M::C * M::VS];
+  __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
   __shared__ float sPow[M::C + 4];
 
   const int ndt = dv / DVT;

@@ -92,7 +92,7 @@ __device__ __forceinline__ void state_role(
     float *__restrict__ slots, const Item &it, int idx, int h, int H, int dv,
     int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
     bf16 *sSt0, bf16 *sSt1, const float *sPow) {
-  // sK, sKs and sV hold two chunk buffers each (FUSED) or one (state pass)
+  // sK (FUSED only), sKs and sV hold two chunk buffers each
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
@@ -186,8 +186,7 @@ __device__ __forceinline__ void state_role(
       }
   };
 
-  // Chunk ch lives in LDS buffer ch & 1 (FUSED; the state pass has one
-  // buffer and a second barrier instead). Per chunk: one barrier, then the
+  // Chunk ch lives in LDS buffer ch & 1. Per chunk: one barrier, then the
   // loads of chunk ch+2 are issued, the registers holding chunk ch+1 are
   // written to the other buffer, and chunk ch is processed.
   u32x4 ka[QV], kb[QV], va[VV], vb[VV];
@@ -200,10 +199,10 @@ __device__ __forceinline__ void state_role(
   auto body = [&](int ch, u32x4(&rkn)[QV], u32x4(&rvn)[VV], const u32x4(&rkx)[QV],
                   const u32x4(&rvx)[VV], bf16 *st_pub) {
     const int L = chunk_rows(it, ch);
-    const int cur = FUSED ? (ch & 1) : 0;
+    const int cur = ch & 1;
     __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
     load_kv(ch + 2, rkn, rvn);
-    if (FUSED) store_kv(chunk_rows(it, ch + 1), cur ^ 1, rkx, rvx);
+    store_kv(chunk_rows(it, ch + 1), cur ^ 1, rkx, rvx);
     const bf16 *cKs = sKs + cur * KBUF, *cV = sV + cur * VBUF;
     const float lamL = sPow[L];
 #pragma unroll
@@ -229,12 +228,7 @@ __device__ __forceinline__ void state_role(
 #pragma unroll
         for (int b = 0; b < SCT; ++b) accS[a][b] = mfma(af[a], bfr[b], accS[a][b]);
     }
-    if (FUSED) {
-      publish(st_pub);  // S_ch for the next chunk's readout
-    } else {
-      __syncthreads();  // single buffer: all waves are done with chunk ch
-      store_kv(chunk_rows(it, ch + 1), 0, rkx, rvx);
-    }
+    if (FUSED) publish(st_pub);  // S_ch for the next chunk's readout
   };
   for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
     body(ch, ka, va, kb, vb, sSt0);

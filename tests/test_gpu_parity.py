@@ -141,6 +141,31 @@ def test_max_heads_and_lambda_one():
     check("H64 with lambda=1", o, ro, s, rs, TOL["bf16"])
 
 
+@pytest.mark.parametrize("T", [63, 300])
+def test_extreme_decays(T):
+    """Decays from nearly instant forgetting (powers underflow to zero within
+    a chunk) to none at all, with time segments forced so that the carried
+    state crosses segment boundaries; forward and backward."""
+    from gla_testutil import env
+    lam = np.array([1e-6, 1e-3, 0.25, 0.5, 0.9999, 1.0], np.float32)
+    x = W.prefill_inputs(56 + T, 2, T, 6, 96, 192, "bf16", 0.1, lam)
+    with env(GLA_TARGET_WGS=4096):
+        o, s = run_fixed(x)
+    ro, rs = oracle_fixed(x)
+    check("extreme decays T%d" % T, o, ro, s, rs, TOL["bf16"])
+    rng = np.random.default_rng(57 + T)
+    do = W.bf16_bits(rng.standard_normal((2, T, 6, 192), dtype=np.float32))
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    with env(GLA_TARGET_WGS=4096):
+        g = gla.gla_chunk_bwd(q, k, v, lam, dev(do), 1.0, s0)
+    torch.cuda.synchronize()
+    ref = O.gla_bwd(x["q"], x["k"], x["v"], lam, do, 1.0, x["s0"])
+    for name, a, b in zip(("dq", "dk", "dv", "dS0"), g, ref):
+        e = rel_err(host(a), b)
+        print("  bwd %s %.2e" % (name, e))
+        assert np.isfinite(host(a)).all() and e <= TOL["bf16"], (name, e)
+
+
 def test_empty_sequence_passes_state_through():
     x = W.prefill_inputs(3, 2, 0, 4, 96, 192, "bf16", 0.1, W.geometric_decays(4))
     s0 = dev(x["s0"])
