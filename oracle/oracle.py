@@ -5,7 +5,8 @@ CPU-baseline leg may use this module; the GPU library and its binding never
 import it. It takes numpy arrays, widens bf16 bit patterns to fp32 exactly,
 and calls the plain token-by-token fp64 recurrence of the Laplace 3B /
 Trainium2 page, section "GLA mixer" (S_t = lambda_h S_{t-1} + k_t^T v_t,
-o_t = scale * q_t S_t, readout after the update).
+o_t = scale * q_t S_t, readout after the update), its backward, and, in
+plain numpy, the short causal convolution in front of the mixer.
 """
 from __future__ import annotations
 
@@ -227,3 +228,45 @@ def gla_decode_pool(q, k, v, decay, pool, slots, scale=1.0, threads=None):
         o[valid] = gla_decode(q[valid], k[valid], v[valid], decay, pages, scale, threads)
         pool[slots[valid]] = pages
     return o
+
+
+def short_conv(x, w, bias=None, window=None):
+    """Causal depthwise convolution of width K followed by SiLU, in fp64
+    (Laplace 3B / Trainium2 page, section on the layer's normalisation and
+    convolution: every channel of the residual stream passes through a
+    causal Conv1d of width 4 with SiLU, a 4-gram summary per position).
+
+    x: [B, T, D]; w: [D, K] (tap j multiplies the input K-1-j tokens back,
+    so tap K-1 is the current token); bias: [D] or None; window: [B, K, D]
+    or None, the K most recent inputs before x, oldest first (zeros when
+    None). Returns (y [B, T, D], window_out [B, K, D]): y_t = SiLU(z_t),
+    z_t[c] = bias[c] + sum_j w[c, j] x_{t-K+1+j}[c], SiLU(z) = z / (1 + e^-z),
+    and window_out the K most recent inputs after x."""
+    x = widen(x).astype(np.float64)
+    w = np.asarray(w, np.float64)
+    B, T, D = x.shape
+    K = w.shape[1]
+    hist = np.zeros((B, K, D)) if window is None else np.asarray(window, np.float64)
+    X = np.concatenate([hist, x], axis=1)          # [B, K + T, D]
+    y = np.zeros((B, T, D))
+    for t in range(T):
+        z = np.zeros((B, D)) if bias is None else np.broadcast_to(
+            np.asarray(bias, np.float64), (B, D)).copy()
+        for j in range(K):
+            z += w[:, j] * X[:, t + 1 + j]
+        y[:, t] = z / (1.0 + np.exp(-z))
+    return y, X[:, T:T + K].copy()
+
+
+def short_conv_decode(x, w, bias, window):
+    """One decode step of short_conv: window [N, K, D] fp64 is shifted by one
+    token IN PLACE (the oldest input drops out, x enters last) and
+    y = SiLU(bias + sum_j w[:, j] window[:, j]) is returned, [N, D] fp64."""
+    x = widen(x).astype(np.float64)
+    w = np.asarray(w, np.float64)
+    window[:, :-1] = window[:, 1:].copy()
+    window[:, -1] = x
+    z = (window * w.T[None]).sum(axis=1)
+    if bias is not None:
+        z = z + np.asarray(bias, np.float64)
+    return z / (1.0 + np.exp(-z))
