@@ -261,6 +261,40 @@ def bench_backward(steps, warmup, workload="laplace_prefill"):
             "workspace_bytes": need}
 
 
+def bench_short_conv(steps, warmup):
+    """Short causal convolution + SiLU on the residual stream of the
+    Laplace-shaped batch (B8 T2048 D3072 bf16) and one decode step for 1,280
+    sequences."""
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    dev = torch.device("cuda")
+    B, T, D, N = 8, 2048, 3072, 1280
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    xs = [torch.randn(B, T, D, generator=g, device=dev).to(torch.bfloat16) for _ in range(2)]
+    w = torch.randn(D, 4, generator=g, device=dev) * 0.5
+    bias = torch.randn(D, generator=g, device=dev) * 0.1
+    y = torch.empty_like(xs[0])
+    wo = torch.empty(B, 4, D, dtype=torch.float32, device=dev)
+    wall, ev_ms = timed(lambda i: gla.short_conv_fwd(xs[i % 2], w, bias, None, out=y,
+                                                     window_out=wo), steps, warmup)
+    bytes_pre = B * T * D * 2 * 2 + B * 4 * D * 4
+    xd = torch.randn(N, D, generator=g, device=dev).to(torch.bfloat16)
+    win = torch.randn(N, 4, D, generator=g, device=dev)
+    yd = torch.empty_like(xd)
+    wall_d, ev_d = timed(lambda i: gla.short_conv_decode_step(xd, w, bias, win, out=yd),
+                         steps, warmup)
+    bytes_dec = N * D * (2 * 2 + 3 * 4 + 4 * 4)
+    return {"workload": "short_conv", "config": {"B": B, "T": T, "D": D, "decode_N": N},
+            "value": round(B * T * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_call": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(bytes_pre, ev_ms), kernel="short_conv_fwd_kernel<bf16>"),
+            "decode": {"value": round(N * steps / wall_d, 1), "unit": "seq-steps/s",
+                       "ms_per_step": round(wall_d / steps * 1e3, 4),
+                       "roofline": dict(roofline(bytes_dec, ev_d),
+                                        kernel="short_conv_decode_kernel<bf16>")}}
+
+
 def bench_varlen(steps, warmup):
     import torch
     from chunked_gated_recurrent_amd import gla
@@ -382,7 +416,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen",
-                                       "backward", "long_backward"])
+                                       "backward", "long_backward", "short_conv"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -400,6 +434,7 @@ def main():
               "decode": lambda: bench_decode(),
               "decode_pool": lambda: bench_decode_pool(),
               "backward": lambda: bench_backward(args.steps, args.warmup),
+              "short_conv": lambda: bench_short_conv(args.steps, args.warmup),
               "long_backward": lambda: bench_backward(args.steps, args.warmup, "long_context"),
               "varlen": lambda: bench_varlen(args.steps, args.warmup)}[args.only]
         r = fn()
@@ -421,6 +456,9 @@ def main():
         log("laplace_backward ...")
         secondary["laplace_backward"] = bench_backward(max(10, args.steps // 10),
                                                        max(3, args.warmup // 10))
+        log("short_conv ...")
+        secondary["short_conv"] = bench_short_conv(max(10, args.steps // 10),
+                                                   max(3, args.warmup // 10))
         log("varlen ...")
         secondary["varlen"] = bench_varlen(max(10, args.steps // 10), max(3, args.warmup // 10))
     copy_bw = copy_bandwidth()

@@ -541,6 +541,61 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
   return run_backward(dt, bp, a, make_decay(decay_host, H), workspace, s);
 }
 
+gla_status gla_short_conv_fwd(gla_dtype dt, int B, int T, int D, const void *x,
+                              const float *w, const float *bias, const float *window_in,
+                              void *y, float *window_out, void *stream) {
+  if (dt != GLA_F32 && dt != GLA_BF16) return GLA_ERR_DTYPE;
+  if (B < 1 || T < 0 || D < 1 || (long long)B * T > kMaxTokens) return GLA_ERR_SHAPE;
+  if (D % 8 != 0 || D > (1 << 20)) return GLA_ERR_UNSUPPORTED;
+  if (!w || (T > 0 && (!x || !y))) return GLA_ERR_NULL;
+  if (misaligned(x) || misaligned(y) || misaligned(window_in) || misaligned(window_out) ||
+      ((uintptr_t)w & 3u) || ((uintptr_t)bias & 3u))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nx = (size_t)B * T * D * es, nwin = (size_t)B * 4 * D * sizeof(float);
+  const size_t nw = (size_t)D * 4 * sizeof(float), nb = (size_t)D * sizeof(float);
+  const void *in[5] = {x, w, bias, window_in, nullptr};
+  const size_t in_n[5] = {nx, nw, nb, nwin, 0};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(y, nx, in[i], in_n[i]) || overlap(window_out, nwin, in[i], in_n[i]))
+      return GLA_ERR_ALIAS;
+  if (overlap(y, nx, window_out, nwin)) return GLA_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (T == 0) {  // no tokens: the window passes through
+    if (window_out && launch_state_fill(B, 1, 4, D, window_in, window_out, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    return GLA_OK;
+  }
+  if (launch_short_conv_fwd(dt, B, T, D, x, w, bias, window_in, y, window_out, s) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+gla_status gla_short_conv_decode_step(gla_dtype dt, int N, int D, const void *x,
+                                      const float *w, const float *bias, float *window,
+                                      void *y, void *stream) {
+  if (dt != GLA_F32 && dt != GLA_BF16) return GLA_ERR_DTYPE;
+  if (N < 0 || D < 1) return GLA_ERR_SHAPE;
+  if (D % 8 != 0 || D > (1 << 20)) return GLA_ERR_UNSUPPORTED;
+  if (N == 0) return GLA_OK;
+  if (!x || !w || !window || !y) return GLA_ERR_NULL;
+  if (misaligned(x) || misaligned(y) || misaligned(window) || ((uintptr_t)w & 3u) ||
+      ((uintptr_t)bias & 3u))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nx = (size_t)N * D * es, nwin = (size_t)N * 4 * D * sizeof(float);
+  const size_t nw = (size_t)D * 4 * sizeof(float), nb = (size_t)D * sizeof(float);
+  if (overlap(window, nwin, x, nx) || overlap(window, nwin, w, nw) ||
+      overlap(window, nwin, bias, nb) || overlap(window, nwin, y, nx) ||
+      overlap(y, nx, x, nx) || overlap(y, nx, w, nw) || overlap(y, nx, bias, nb))
+    return GLA_ERR_ALIAS;
+  (void)hipGetLastError();
+  if (launch_short_conv_decode(dt, N, D, x, w, bias, window, y, (hipStream_t)stream) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
                            const void *q, const void *k, const void *v,
                            const float *decay_host, float scale, float *state,

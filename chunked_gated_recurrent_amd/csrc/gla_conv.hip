@@ -1,0 +1,196 @@
+// gla_conv.hip -- the short causal convolution in front of the mixer: every
+// channel of the residual stream passes through a causal Conv1d of width 4
+// followed by SiLU (Laplace 3B / Trainium2 page, section on normalisation
+// and convolution), for prefill and for one decode step with a 4-row window
+// of the most recent inputs.
+//
+//   z_t[c] = bias[c] + sum_{j<4} w[c][j] x_{t-3+j}[c],   y_t = z_t / (1 + e^-z_t)
+//
+// Both kernels are HBM streams: every input and output element moves once
+// (prefill re-reads the 3 tokens before each run of tokens). A thread owns
+// 16 bytes of channels (8 bf16 or 4 fp32) and keeps the 4-token window in
+// registers in fp32.
+#include "gla_device.h"
+
+namespace gla {
+
+constexpr int kConvK = 4;     // taps
+constexpr int kConvRun = 32;  // tokens per prefill thread
+
+template <typename Tin>
+struct ConvVec {
+  static constexpr int N = 16 / sizeof(Tin);  // channels per thread
+};
+
+template <typename Tin>
+__device__ __forceinline__ void load_vec(const Tin *p, float (&out)[ConvVec<Tin>::N]) {
+  constexpr int N = ConvVec<Tin>::N;
+  typedef Tin vec_t __attribute__((ext_vector_type(N)));
+  const vec_t v = *reinterpret_cast<const vec_t *>(p);
+#pragma unroll
+  for (int e = 0; e < N; ++e) out[e] = (float)v[e];
+}
+
+template <typename Tin>
+__device__ __forceinline__ void store_vec(Tin *p, const float (&in)[ConvVec<Tin>::N]) {
+  constexpr int N = ConvVec<Tin>::N;
+  typedef Tin vec_t __attribute__((ext_vector_type(N)));
+  vec_t v;
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] = (Tin)in[e];
+  *reinterpret_cast<vec_t *>(p) = v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// One thread: channels [c, c + N) of batch entry b over tokens
+// [r * kConvRun, min(T, (r + 1) * kConvRun)).
+template <typename Tin>
+__global__ __launch_bounds__(256) void short_conv_fwd_kernel(
+    const Tin *__restrict__ x, const float *__restrict__ w,
+    const float *__restrict__ bias, const float *__restrict__ win_in,
+    Tin *__restrict__ y, float *__restrict__ win_out, int B, int T, int D) {
+  constexpr int N = ConvVec<Tin>::N;
+  const int groups = D / N;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int runs = (T + kConvRun - 1) / kConvRun;
+  if (gid >= (long long)B * runs * groups) return;
+  const int cg = (int)(gid % groups);
+  const long long br = gid / groups;
+  const int r = (int)(br % runs);
+  const int b = (int)(br / runs);
+  const int c = cg * N;
+  const int t0 = r * kConvRun, t1 = min(T, t0 + kConvRun);
+
+  float wt[kConvK][N], bs[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+#pragma unroll
+    for (int j = 0; j < kConvK; ++j) wt[j][e] = w[(long long)(c + e) * kConvK + j];
+    bs[e] = bias ? bias[c + e] : 0.f;
+  }
+  // window: the kConvK inputs before t0, oldest first
+  float win[kConvK][N];
+#pragma unroll
+  for (int j = 0; j < kConvK; ++j) {
+    const int t = t0 - kConvK + j;
+    if (t >= 0) {
+      load_vec(x + ((long long)b * T + t) * D + c, win[j]);
+    } else if (win_in) {
+      const float *src = win_in + ((long long)b * kConvK + (kConvK + t)) * D + c;
+#pragma unroll
+      for (int e = 0; e < N; ++e) win[j][e] = src[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) win[j][e] = 0.f;
+    }
+  }
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    float xt[N], out[N];
+    load_vec(x + ((long long)b * T + t) * D + c, xt);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      win[0][e] = win[1][e];
+      win[1][e] = win[2][e];
+      win[2][e] = win[3][e];
+      win[3][e] = xt[e];
+      float z = bs[e];
+#pragma unroll
+      for (int j = 0; j < kConvK; ++j) z = fmaf(wt[j][e], win[j][e], z);
+      out[e] = silu(z);
+    }
+    store_vec(y + ((long long)b * T + t) * D + c, out);
+  }
+  if (win_out && t1 == T) {  // the run holding the sequence's last token
+#pragma unroll
+    for (int j = 0; j < kConvK; ++j) {
+      float *dst = win_out + ((long long)b * kConvK + j) * D + c;
+#pragma unroll
+      for (int e = 0; e < N; ++e) dst[e] = win[j][e];
+    }
+  }
+}
+
+// One decode step: the window [N, kConvK, D] shifts by one token in place.
+template <typename Tin>
+__global__ __launch_bounds__(256) void short_conv_decode_kernel(
+    const Tin *__restrict__ x, const float *__restrict__ w,
+    const float *__restrict__ bias, float *__restrict__ window,
+    Tin *__restrict__ y, int Nseq, int D) {
+  constexpr int N = ConvVec<Tin>::N;
+  typedef float f32x4n __attribute__((ext_vector_type(4)));
+  const int groups = D / N;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)Nseq * groups) return;
+  const int cg = (int)(gid % groups);
+  const long long n = gid / groups;
+  const int c = cg * N;
+  float win[kConvK][N], xt[N], out[N];
+  load_vec(x + n * D + c, xt);
+#pragma unroll
+  for (int j = 1; j < kConvK; ++j) {
+    const float *src = window + (n * kConvK + j) * D + c;
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      const f32x4n v = __builtin_nontemporal_load(reinterpret_cast<const f32x4n *>(src + e));
+      win[j - 1][e] = v[0];
+      win[j - 1][e + 1] = v[1];
+      win[j - 1][e + 2] = v[2];
+      win[j - 1][e + 3] = v[3];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    win[kConvK - 1][e] = xt[e];
+    float z = bias ? bias[c + e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kConvK; ++j) z = fmaf(w[(long long)(c + e) * kConvK + j], win[j][e], z);
+    out[e] = silu(z);
+  }
+#pragma unroll
+  for (int j = 0; j < kConvK; ++j) {
+    float *dst = window + (n * kConvK + j) * D + c;
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      const f32x4n v = {win[j][e], win[j][e + 1], win[j][e + 2], win[j][e + 3]};
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4n *>(dst + e));
+    }
+  }
+  store_vec(y + n * D + c, out);
+}
+
+hipError_t launch_short_conv_fwd(int dt, int B, int T, int D, const void *x,
+                                 const float *w, const float *bias, const float *win_in,
+                                 void *y, float *win_out, hipStream_t s) {
+  const int runs = (T + kConvRun - 1) / kConvRun;
+  if (dt == 1) {
+    const long long n = (long long)B * runs * (D / ConvVec<bf16>::N);
+    hipLaunchKernelGGL(short_conv_fwd_kernel<bf16>, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, (const bf16 *)x, w, bias, win_in, (bf16 *)y,
+                       win_out, B, T, D);
+  } else {
+    const long long n = (long long)B * runs * (D / ConvVec<float>::N);
+    hipLaunchKernelGGL(short_conv_fwd_kernel<float>, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, (const float *)x, w, bias, win_in, (float *)y,
+                       win_out, B, T, D);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_short_conv_decode(int dt, int N, int D, const void *x, const float *w,
+                                    const float *bias, float *window, void *y,
+                                    hipStream_t s) {
+  if (dt == 1) {
+    const long long n = (long long)N * (D / ConvVec<bf16>::N);
+    hipLaunchKernelGGL(short_conv_decode_kernel<bf16>, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, (const bf16 *)x, w, bias, window, (bf16 *)y, N, D);
+  } else {
+    const long long n = (long long)N * (D / ConvVec<float>::N);
+    hipLaunchKernelGGL(short_conv_decode_kernel<float>, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, (const float *)x, w, bias, window, (float *)y, N, D);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -79,6 +79,12 @@ constexpr int kOrderMaxItems = 16384;
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s);
+hipError_t launch_short_conv_fwd(int dt, int B, int T, int D, const void *x,
+                                 const float *w, const float *bias, const float *win_in,
+                                 void *y, float *win_out, hipStream_t s);
+hipError_t launch_short_conv_decode(int dt, int N, int D, const void *x, const float *w,
+                                    const float *bias, float *window, void *y,
+                                    hipStream_t s);
 hipError_t launch_rcombine(const Plan &p, const float *ds_final, float *cslots,
                            const Decay &dec, int H, int dk, int dv, hipStream_t s);
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,

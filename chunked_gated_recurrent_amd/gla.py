@@ -13,6 +13,8 @@ Functions mirror the C entry points:
     gla_decode_step_pool(q, k, v, decay, state_pool, slots, ...) -> o
     gla_chunk_bwd(q, k, v, decay, dout, ...)    -> (dq, dk, dv, ds0)
     gla_chunk_bwd_varlen(q, k, v, cu, decay, dout, ...) -> (dq, dk, dv, ds0)
+    short_conv_fwd(x, w, bias, window_in, ...)  -> (y, window_out)
+    short_conv_decode_step(x, w, bias, window)  -> y   (window updated in place)
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ _SIGS = {
     "gla_chunk_fwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P], _I),
     "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
+    "gla_short_conv_fwd": ([_I] * 4 + [_P] * 7, _I),
+    "gla_short_conv_decode_step": ([_I] * 3 + [_P] * 6, _I),
     "gla_decode_step_pool": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _I, _P, _P, _P], _I),
 }
 EXPORTS = tuple(_SIGS)
@@ -348,3 +352,50 @@ def gla_chunk_bwd_varlen(q, k, v, cu_seqlens, decay, dout, scale: float = 1.0,
     if rc != 0:
         raise GlaError(rc, "gla_chunk_bwd_varlen")
     return dq, dk, dv, ds0
+
+
+def short_conv_fwd(x, w, bias=None, window_in=None, want_window: bool = True,
+                   out=None, window_out=None):
+    """Causal width-4 depthwise convolution + SiLU: x [B, T, D] (bf16 or
+    fp32), w [D, 4] fp32, bias [D] fp32 or None, window_in [B, 4, D] fp32 or
+    None. Returns (y [B, T, D], window_out [B, 4, D] fp32 or None)."""
+    import torch
+    dev = x.device
+    B, T, D = x.shape
+    _check(x, "x", dev)
+    _check(w, "w", dev, torch.float32, (D, 4))
+    if bias is not None:
+        _check(bias, "bias", dev, torch.float32, (D,))
+    if window_in is not None:
+        _check(window_in, "window_in", dev, torch.float32, (B, 4, D))
+    y = torch.empty_like(x) if out is None else out
+    _check(y, "out", dev, x.dtype, (B, T, D))
+    if window_out is None and want_window:
+        window_out = torch.empty((B, 4, D), dtype=torch.float32, device=dev)
+    if window_out is not None:
+        _check(window_out, "window_out", dev, torch.float32, (B, 4, D))
+    rc = lib().gla_short_conv_fwd(_dt(x), B, T, D, _ptr(x), _ptr(w), _ptr(bias),
+                                  _ptr(window_in), _ptr(y), _ptr(window_out), _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_short_conv_fwd")
+    return y, window_out
+
+
+def short_conv_decode_step(x, w, bias, window, out=None):
+    """One decode step of the convolution: x [N, D], window [N, 4, D] fp32
+    (shifted in place). Returns y [N, D]."""
+    import torch
+    dev = x.device
+    N, D = x.shape
+    _check(x, "x", dev)
+    _check(w, "w", dev, torch.float32, (D, 4))
+    if bias is not None:
+        _check(bias, "bias", dev, torch.float32, (D,))
+    _check(window, "window", dev, torch.float32, (N, 4, D))
+    y = torch.empty_like(x) if out is None else out
+    _check(y, "out", dev, x.dtype, (N, D))
+    rc = lib().gla_short_conv_decode_step(_dt(x), N, D, _ptr(x), _ptr(w), _ptr(bias),
+                                          _ptr(window), _ptr(y), _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_short_conv_decode_step")
+    return y

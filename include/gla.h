@@ -180,6 +180,38 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * The short causal convolution in front of the mixer (Laplace 3B / Trainium2
+ * page, section on normalisation and convolution): every channel passes
+ * through a causal Conv1d of width 4, then SiLU:
+ *   z_t[c] = bias[c] + sum_{j<4} w[c][j] x_{t-3+j}[c]     y_t[c] = z / (1 + e^-z)
+ *   x, y       : [B, T, D] dt (y written)
+ *   w          : [D, 4] fp32 DEVICE array, tap 3 on the current token
+ *   bias       : [D] fp32 device array or NULL (zero)
+ *   window_in  : [B, 4, D] fp32 or NULL: the 4 most recent inputs before x,
+ *                oldest first (zeros when NULL)
+ *   window_out : [B, 4, D] fp32 or NULL: the 4 most recent inputs after x
+ *                (the decode window to continue from); may not overlap
+ *                window_in
+ * D must be a multiple of 8 (GLA_ERR_UNSUPPORTED otherwise); 16-byte
+ * alignment for x, y and the windows, 4 bytes for w and bias; y and
+ * window_out may not overlap any input. T = 0 copies window_in (or zeros)
+ * to window_out.
+ */
+gla_status gla_short_conv_fwd(gla_dtype dt, int B, int T, int D, const void *x,
+                              const float *w, const float *bias, const float *window_in,
+                              void *y, float *window_out, void *stream);
+
+/*
+ * One decode step of the short convolution for N sequences (one token
+ * each): window [N, 4, D] fp32 shifts by one token in place (the oldest
+ * input drops out, x[n] enters last) and y[n] = SiLU(bias + sum_j w[:, j]
+ * window[n, j]). x, y : [N, D] dt. Checks as for gla_short_conv_fwd.
+ */
+gla_status gla_short_conv_decode_step(gla_dtype dt, int N, int D, const void *x,
+                                      const float *w, const float *bias, float *window,
+                                      void *y, void *stream);
+
+/*
  * One decode step for N independent sequences (one token each):
  *   state[n,h] <- lambda_h * state[n,h] + k[n,h]^T v[n,h]    (in place)
  *   o[n,h]     <- scale * q[n,h] state[n,h]                  (after update)

@@ -214,6 +214,30 @@ def test_backward_varlen_argument_errors(L):
     assert L.gla_chunk_bwd_varlen_workspace_bytes(F32, 3, 300, 4, 96, 192, 0) == 0
 
 
+def test_short_conv_argument_errors(L):
+    def conv(dt=BF16, B=2, T=10, D=3072, x=A[0], w=A[1], b=None, wi=None, y=A[2], wo=A[3]):
+        return L.gla_short_conv_fwd(dt, B, T, D, x, w, b, wi, y, wo, None)
+    assert conv(dt=4) == DTYPE
+    assert conv(B=0) == SHAPE
+    assert conv(T=-1) == SHAPE
+    assert conv(D=12) == UNSUP
+    assert conv(w=None) == NULL
+    assert conv(y=None) == NULL
+    assert conv(x=ctypes.c_void_p(A[0].value + 8)) == ALIGN
+    assert conv(b=ctypes.c_void_p(A[1].value + 2)) == ALIGN
+    assert conv(y=ctypes.c_void_p(A[0].value + 4096)) == ALIAS     # y inside x
+    assert conv(wo=A[2]) == ALIAS                                   # window_out on y
+    assert conv(wi=A[3]) == ALIAS                                   # window_in is window_out
+
+    def dec(dt=BF16, N=4, D=3072, x=A[0], w=A[1], b=None, win=A[3], y=A[2]):
+        return L.gla_short_conv_decode_step(dt, N, D, x, w, b, win, y, None)
+    assert dec(N=-1) == SHAPE
+    assert dec(N=0) == OK
+    assert dec(D=4) == UNSUP
+    assert dec(win=None) == NULL
+    assert dec(y=A[3]) == ALIAS                                     # y on the window
+
+
 def test_decode_pool_argument_errors(L):
     def pool(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], sl=A[5],
              P=8, st=A[3], o=A[4], decay=GOOD):
