@@ -549,7 +549,7 @@ gla_status gla_short_conv_fwd(gla_dtype dt, int B, int T, int D, const void *x,
   if (D % 8 != 0 || D > (1 << 20)) return GLA_ERR_UNSUPPORTED;
   if (!w || (T > 0 && (!x || !y))) return GLA_ERR_NULL;
   if (misaligned(x) || misaligned(y) || misaligned(window_in) || misaligned(window_out) ||
-      ((uintptr_t)w & 3u) || ((uintptr_t)bias & 3u))
+      misaligned(w) || ((uintptr_t)bias & 3u))
     return GLA_ERR_ALIGN;
   const size_t es = elem_size(dt);
   const size_t nx = (size_t)B * T * D * es, nwin = (size_t)B * 4 * D * sizeof(float);
@@ -580,7 +580,7 @@ gla_status gla_short_conv_decode_step(gla_dtype dt, int N, int D, const void *x,
   if (D % 8 != 0 || D > (1 << 20)) return GLA_ERR_UNSUPPORTED;
   if (N == 0) return GLA_OK;
   if (!x || !w || !window || !y) return GLA_ERR_NULL;
-  if (misaligned(x) || misaligned(y) || misaligned(window) || ((uintptr_t)w & 3u) ||
+  if (misaligned(x) || misaligned(y) || misaligned(window) || misaligned(w) ||
       ((uintptr_t)bias & 3u))
     return GLA_ERR_ALIGN;
   const size_t es = elem_size(dt);

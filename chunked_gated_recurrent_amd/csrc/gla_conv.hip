@@ -41,7 +41,12 @@ __device__ __forceinline__ void store_vec(Tin *p, const float (&in)[ConvVec<Tin>
   *reinterpret_cast<vec_t *>(p) = v;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU with the hardware exponential and reciprocal (about 1 ulp each); a
+// full-precision division would make the prefill ALU-bound. For z -> -inf
+// the reciprocal of inf is 0, so the result tends to (-)0 as it should.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // One thread: channels [c, c + N) of batch entry b over tokens
 // [r * kConvRun, min(T, (r + 1) * kConvRun)).
@@ -62,11 +67,13 @@ __global__ __launch_bounds__(256) void short_conv_fwd_kernel(
   const int c = cg * N;
   const int t0 = r * kConvRun, t1 = min(T, t0 + kConvRun);
 
+  typedef float f32x4n __attribute__((ext_vector_type(4)));
   float wt[kConvK][N], bs[N];
 #pragma unroll
   for (int e = 0; e < N; ++e) {
+    const f32x4n wv = *reinterpret_cast<const f32x4n *>(w + (long long)(c + e) * kConvK);
 #pragma unroll
-    for (int j = 0; j < kConvK; ++j) wt[j][e] = w[(long long)(c + e) * kConvK + j];
+    for (int j = 0; j < kConvK; ++j) wt[j][e] = wv[j];
     bs[e] = bias ? bias[c + e] : 0.f;
   }
   // window: the kConvK inputs before t0, oldest first
@@ -85,10 +92,8 @@ __global__ __launch_bounds__(256) void short_conv_fwd_kernel(
       for (int e = 0; e < N; ++e) win[j][e] = 0.f;
     }
   }
-#pragma unroll 8
-  for (int t = t0; t < t1; ++t) {
-    float xt[N], out[N];
-    load_vec(x + ((long long)b * T + t) * D + c, xt);
+  auto step = [&](const float (&xt)[N], int t) {
+    float out[N];
 #pragma unroll
     for (int e = 0; e < N; ++e) {
       win[0][e] = win[1][e];
@@ -101,6 +106,39 @@ __global__ __launch_bounds__(256) void short_conv_fwd_kernel(
       out[e] = silu(z);
     }
     store_vec(y + ((long long)b * T + t) * D + c, out);
+  };
+  if (t1 - t0 == kConvRun) {
+    // a full run: blocks of 8 tokens whose loads go out together, the next
+    // block's before the current one is computed (straight-line code)
+    constexpr int BLK = 8;
+    float xa[BLK][N], xb[BLK][N];
+    // (the scheduling barriers keep the compiler from sinking each block's
+    // loads down to their uses, which would leave one load in flight)
+#pragma unroll
+    for (int i = 0; i < BLK; ++i) load_vec(x + ((long long)b * T + t0 + i) * D + c, xa[i]);
+#pragma unroll
+    for (int blk = 0; blk < kConvRun; blk += 2 * BLK) {
+#pragma unroll
+      for (int i = 0; i < BLK; ++i)
+        load_vec(x + ((long long)b * T + t0 + blk + BLK + i) * D + c, xb[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) step(xa[i], t0 + blk + i);
+      if (blk + 2 * BLK < kConvRun) {
+#pragma unroll
+        for (int i = 0; i < BLK; ++i)
+          load_vec(x + ((long long)b * T + t0 + blk + 2 * BLK + i) * D + c, xa[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) step(xb[i], t0 + blk + BLK + i);
+    }
+  } else {
+    for (int t = t0; t < t1; ++t) {
+      float xt[N];
+      load_vec(x + ((long long)b * T + t) * D + c, xt);
+      step(xt, t);
+    }
   }
   if (win_out && t1 == T) {  // the run holding the sequence's last token
 #pragma unroll
@@ -140,12 +178,16 @@ __global__ __launch_bounds__(256) void short_conv_decode_kernel(
       win[j - 1][e + 3] = v[3];
     }
   }
+  // the taps of channel c + e are the 16 bytes at w + 4 (c + e)
+  f32x4n wt[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) wt[e] = *reinterpret_cast<const f32x4n *>(w + (long long)(c + e) * kConvK);
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     win[kConvK - 1][e] = xt[e];
     float z = bias ? bias[c + e] : 0.f;
 #pragma unroll
-    for (int j = 0; j < kConvK; ++j) z = fmaf(w[(long long)(c + e) * kConvK + j], win[j][e], z);
+    for (int j = 0; j < kConvK; ++j) z = fmaf(wt[e][j], win[j][e], z);
     out[e] = silu(z);
   }
 #pragma unroll

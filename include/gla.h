@@ -193,7 +193,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
  *                (the decode window to continue from); may not overlap
  *                window_in
  * D must be a multiple of 8 (GLA_ERR_UNSUPPORTED otherwise); 16-byte
- * alignment for x, y and the windows, 4 bytes for w and bias; y and
+ * alignment for x, y, w and the windows, 4 bytes for bias; y and
  * window_out may not overlap any input. T = 0 copies window_in (or zeros)
  * to window_out.
  */
