@@ -6,7 +6,8 @@ import it. It takes numpy arrays, widens bf16 bit patterns to fp32 exactly,
 and calls the plain token-by-token fp64 recurrence of the Laplace 3B /
 Trainium2 page, section "GLA mixer" (S_t = lambda_h S_{t-1} + k_t^T v_t,
 o_t = scale * q_t S_t, readout after the update), its backward, and, in
-plain numpy, the short causal convolution in front of the mixer.
+plain numpy, the short causal convolution in front of the mixer and the
+normalised causal linear attention of the linear-attention tutorial page.
 """
 from __future__ import annotations
 
@@ -270,3 +271,43 @@ def short_conv_decode(x, w, bias, window):
     if bias is not None:
         z = z + np.asarray(bias, np.float64)
     return z / (1.0 + np.exp(-z))
+
+
+LINEAR_ATTN_EPS = 1e-6
+
+
+def linear_attention(q, k, v, s0=None, z0=None, eps=LINEAR_ATTN_EPS):
+    """Normalised causal linear attention in fp64, token by token (the
+    tutorial page on RNNs without recurrence, section 6.1, "core logic of
+    linear attention"): with the non-negative feature map phi = ReLU,
+
+        S_t = S_{t-1} + phi(k_t)^T v_t,    z_t = z_{t-1} + phi(k_t),
+        o_t = phi(q_t) S_t / (phi(q_t) . z_t + eps),
+
+    eps = 1e-6 added to the denominator as in the page's demonstration
+    module (section 6.2); the page fixes no decay, so the state is a plain
+    running sum. Every head runs the recurrence on its own.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (fp32 values or bf16 bits as
+    uint16); s0: [B, H, dk, dv] and z0: [B, H, dk] or None (zeros): the
+    sums carried in from earlier tokens. Returns (o [B, T, H, dv],
+    s_final [B, H, dk, dv], z_final [B, H, dk]), all fp64."""
+    q = widen(q).astype(np.float64)
+    k = widen(k).astype(np.float64)
+    v = widen(v).astype(np.float64)
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H):
+        raise ValueError("shape mismatch")
+    S = np.zeros((B, H, dk, dv)) if s0 is None else np.array(s0, np.float64).reshape(B, H, dk, dv)
+    z = np.zeros((B, H, dk)) if z0 is None else np.array(z0, np.float64).reshape(B, H, dk)
+    fq = np.maximum(q, 0.0)
+    fk = np.maximum(k, 0.0)
+    o = np.zeros((B, T, H, dv))
+    for t in range(T):
+        S += fk[:, t, :, :, None] * v[:, t, :, None, :]
+        z += fk[:, t]
+        num = np.einsum("bhd,bhde->bhe", fq[:, t], S)
+        den = np.einsum("bhd,bhd->bh", fq[:, t], z) + eps
+        o[:, t] = num / den[:, :, None]
+    return o, S, z
