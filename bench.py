@@ -23,7 +23,8 @@ work, so the default warm-up (400 steps, about 30 ms) runs before the timed
 region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--no-secondary] [--only {prefill,long,decode,varlen}]
+       [--no-secondary] [--only {prefill,long,decode,decode_pool,varlen,backward,
+                                 long_backward,short_conv,linear_attn}]
 """
 import argparse
 import json
@@ -295,6 +296,40 @@ def bench_short_conv(steps, warmup):
                                         kernel="short_conv_decode_kernel<bf16>")}}
 
 
+def bench_linear_attn(steps, warmup):
+    """Normalised causal linear attention (ReLU features, no decay) on the
+    prefill batch shape B8 T2048 H16 dk96 dv192 bf16, final sums S and z
+    written."""
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    dev = torch.device("cuda")
+    B, T = 8, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    sets = []
+    for r in range(4):  # rotate buffer sets past the last-level cache
+        q, k = (torch.randn(B, T, H, DK, generator=g, device=dev).to(torch.bfloat16)
+                for _ in range(2))
+        v = torch.randn(B, T, H, DV, generator=g, device=dev).to(torch.bfloat16)
+        o = torch.empty(B, T, H, DV, dtype=torch.bfloat16, device=dev)
+        sf = torch.empty(B, H, DK, DV, dtype=torch.float32, device=dev)
+        zf = torch.empty(B, H, DK, dtype=torch.float32, device=dev)
+        sets.append((q, k, v, o, sf, zf))
+    assert gla.lib().gla_linear_attn_fwd_workspace_bytes(1, B, T, H, DK, DV, 64) == 0
+
+    def step(i):
+        q, k, v, o, sf, zf = sets[i % 4]
+        gla.linear_attn_fwd(q, k, v, chunk=64, out=o, final_state=sf, final_z=zf)
+
+    wall, ev_ms = timed(step, steps, warmup)
+    bytes_call = B * T * PREFILL_BYTES_PER_TOKEN + B * (STATE_BYTES + H * DK * 4)
+    return {"workload": "linear_attention", "config": {"B": B, "T": T, "H": H, "dk": DK,
+                                                       "dv": DV},
+            "value": round(B * T * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_call": round(wall / steps * 1e3, 4),
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true>")}
+
+
 def bench_varlen(steps, warmup):
     import torch
     from chunked_gated_recurrent_amd import gla
@@ -416,7 +451,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen",
-                                       "backward", "long_backward", "short_conv"])
+                                       "backward", "long_backward", "short_conv",
+                                       "linear_attn"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -435,6 +471,7 @@ def main():
               "decode_pool": lambda: bench_decode_pool(),
               "backward": lambda: bench_backward(args.steps, args.warmup),
               "short_conv": lambda: bench_short_conv(args.steps, args.warmup),
+              "linear_attn": lambda: bench_linear_attn(args.steps, args.warmup),
               "long_backward": lambda: bench_backward(args.steps, args.warmup, "long_context"),
               "varlen": lambda: bench_varlen(args.steps, args.warmup)}[args.only]
         r = fn()
@@ -459,6 +496,9 @@ def main():
         log("short_conv ...")
         secondary["short_conv"] = bench_short_conv(max(10, args.steps // 10),
                                                    max(3, args.warmup // 10))
+        log("linear_attention ...")
+        secondary["linear_attention"] = bench_linear_attn(max(10, args.steps // 10),
+                                                          max(3, args.warmup // 10))
         log("varlen ...")
         secondary["varlen"] = bench_varlen(max(10, args.steps // 10), max(3, args.warmup // 10))
     copy_bw = copy_bandwidth()

@@ -63,6 +63,7 @@ struct HostPlan {
   bool segmented; // at least one sequence has more than one item
   bool ordered;   // items are dispatched longest first (order in workspace)
   size_t off_index, off_items, off_order, off_slots, ws_bytes;
+  size_t off_zslots;  // normalised linear attention with time segments
 };
 
 void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk) {
@@ -172,10 +173,18 @@ gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
   p.deal = p.mode == kPlanFixed ? 0 : 1;
   if (hp.segmented) {
     a.slots = (float *)(ws + hp.off_slots);
+    if (a.norm) a.zslots = (float *)(ws + hp.off_zslots);
     Plan ps = p;
     ps.deal = 1;  // the state pass skips every last segment
     if (launch_fwd(dt, hp.fast, true, ps, a, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
     if (launch_combine(p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
+    if (a.norm) {  // the normaliser composes like a state with one column
+      FwdArgs az = a;
+      az.s0 = a.z0;
+      az.slots = a.zslots;
+      az.dv = 1;
+      if (launch_combine(p, az, dec, s) != hipSuccess) return GLA_ERR_HIP;
+    }
     // In place (s_final == s0): the first segment reads s0 while the last
     // writes the final state, so the last writes its own slot and a gather
     // copies it out afterwards.
@@ -187,6 +196,17 @@ gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
 }
 
 size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
+
+// Normalised linear attention: the fixed-batch plan plus, with time
+// segments, one z slot ([item][H][dk] fp32) per item after the state slots.
+HostPlan plan_linear_attn(int dt, int B, int T, int H, int dk, int dv, int chunk) {
+  HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
+  if (hp.segmented) {
+    hp.off_zslots = align256(hp.ws_bytes);
+    hp.ws_bytes = hp.off_zslots + (size_t)hp.p.max_items * H * dk * sizeof(float);
+  }
+  return hp;
+}
 
 // Backward layout: the forward's plan (work items, dispatch order, time
 // segments and their incoming-state slots, in the forward's workspace
@@ -340,6 +360,66 @@ gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
   a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
   return run_forward(dt, hp, a, make_decay(decay_host, H), workspace, s);
+}
+
+size_t gla_linear_attn_fwd_workspace_bytes(gla_dtype dt, int B, int T, int H,
+                                           int dk, int dv, int chunk) {
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || B < 1 || T < 0 ||
+      (long long)B * T > kMaxTokens)
+    return 0;
+  return plan_linear_attn(dt, B, T, H, dk, dv, chunk).ws_bytes;
+}
+
+gla_status gla_linear_attn_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                               int chunk, const void *q, const void *k, const void *v,
+                               const float *s0, const float *z0, void *o,
+                               float *s_final, float *z_final, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  if (B < 1 || T < 0 || (long long)B * T > kMaxTokens) return GLA_ERR_SHAPE;
+  const long long tok = (long long)B * T;
+  if (tok > 0 && (!q || !k || !v || !o)) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      misaligned(s0) || misaligned(s_final) || misaligned(z0) || misaligned(z_final))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)tok * H * dk * es, nv = (size_t)tok * H * dv * es;
+  const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
+  const size_t nz = (size_t)B * H * dk * sizeof(float);
+  // every output range (o, s_final, z_final) must be disjoint from every
+  // other range, inputs included (no in-place final state here)
+  const void *rp[7] = {q, k, v, s0, z0, o, s_final};
+  const size_t rn[7] = {nqk, nqk, nv, ns, nz, nv, ns};
+  for (int i = 0; i < 7; ++i) {
+    if (i != 5 && overlap(o, nv, rp[i], rn[i])) return GLA_ERR_ALIAS;
+    if (s_final && i != 6 && overlap(s_final, ns, rp[i], rn[i])) return GLA_ERR_ALIAS;
+    if (z_final && overlap(z_final, nz, rp[i], rn[i])) return GLA_ERR_ALIAS;
+  }
+  const HostPlan hp = plan_linear_attn(dt, B, T, H, dk, dv, chunk);
+  if (hp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    for (int i = 0; i < 7; ++i)
+      if (overlap(workspace, hp.ws_bytes, rp[i], rn[i])) return GLA_ERR_ALIAS;
+    if (overlap(workspace, hp.ws_bytes, z_final, nz)) return GLA_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (tok == 0) {
+    if (s_final || z_final) (void)hipGetLastError();
+    if (s_final && launch_state_fill(B, H, dk, dv, s0, s_final, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    if (z_final && launch_state_fill(B, H, dk, 1, z0, z_final, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    return GLA_OK;
+  }
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
+  a.scale = 1.0f; a.H = H; a.dk = dk; a.dv = dv;
+  a.norm = 1; a.z0 = z0; a.z_final = z_final;
+  Decay one;
+  for (int h = 0; h < kMaxHeads; ++h) one.lam[h] = 1.0f;
+  return run_forward(dt, hp, a, one, workspace, s);
 }
 
 size_t gla_chunk_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,

@@ -49,7 +49,7 @@ namespace gla {
 // ---------------------------------------------------------------------------
 // Output role: 4 waves (role wave w owns rows 16 w .. 16 w + 15 of a chunk).
 // ---------------------------------------------------------------------------
-template <int DVT>
+template <int DVT, bool NORM>
 __device__ __forceinline__ void output_role(
     const bf16 *__restrict__ q, bf16 *__restrict__ o, const Item &it, int h,
     int H, int dv, int c0, float scale, int rt, int w, bf16 *sQ,
@@ -82,7 +82,8 @@ __device__ __forceinline__ void output_role(
   auto store_q = [&](int buf, const u32x4(&r)[QV]) {
 #pragma unroll
     for (int m = 0; m < QV; ++m)
-      *reinterpret_cast<u32x4 *>(sQ + buf * KBUF + rowQ[m] * QS + 8 * colQ[m]) = r[m];
+      *reinterpret_cast<u32x4 *>(sQ + buf * KBUF + rowQ[m] * QS + 8 * colQ[m]) =
+          NORM ? relu_bf16x8(r[m]) : r[m];
   };
 
   u32x4 ra[QV], rb[QV];
@@ -153,6 +154,26 @@ __device__ __forceinline__ void output_role(
         const bf16x8 vf = cat8(tr4(base), tr4(base + 16 * VS));
         oacc[ct] = mfma(vf, pb[s], oacc[ct]);
       }
+    // the output coefficient: scale, or for normalised linear attention
+    // 1 / (phi(q_i) . z_i + eps) with the denominator formed like a 17th
+    // column tile: z_{ch-1} (row DVT of the state buffer, the same row for
+    // every lane) against Q^T, then a value tile of ones against P^T
+    float coef = scale;
+    if (NORM) {
+      f32x4 den = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8 zf = *reinterpret_cast<const bf16x8 *>(st + DVT * QS + 32 * s + 8 * g);
+        den = mfma(zf, qf[s], den);
+      }
+      den *= lam_i1;
+      const bf16x8 ones = ones_bf16x8();
+#pragma unroll
+      for (int s = 0; s < NJS; ++s) den = mfma(ones, pb[s], den);
+      // all four rows are equal; the hardware reciprocal (about 1 ulp) is
+      // far below the bf16 rounding of the output
+      coef = __builtin_amdgcn_rcpf(den[0] + kLinearAttnEps);
+    }
     // stage the 16 x DVT output tile of this wave in its own rows of the
     // current q buffer (only this wave reads them, and qf is already loaded),
     // then write 16-byte row segments
@@ -161,7 +182,7 @@ __device__ __forceinline__ void output_role(
     for (int ct = 0; ct < NCT; ++ct) {
       bf16x4 t;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] = (bf16)(scale * oacc[ct][r]);
+      for (int r = 0; r < 4; ++r) t[r] = (bf16)(coef * oacc[ct][r]);
       *reinterpret_cast<bf16x4 *>(so + l16 * QS + 16 * ct + 4 * g) = t;
     }
     const __amdgpu_buffer_rsrc_t bo =
@@ -183,20 +204,20 @@ __device__ __forceinline__ void output_role(
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
-template <int DVT>
+template <int DVT, bool NORM>
 __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, bf16 *__restrict__ o,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H, int dv,
-    int final_in_slot) {
+    int final_in_slot, NormPtrs np) {
   using M = MfCfg<DVT>;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
-  __shared__ __attribute__((aligned(16))) bf16 sSt0[DVT * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sSt1[DVT * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sSt0[M::SROWS * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sSt1[M::SROWS * M::QS];
   __shared__ float sPow[M::C + 4];
 
   const int ndt = dv / DVT;
@@ -214,18 +235,18 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = dtile * DVT;
   if (role_wave < 4)
-    output_role<DVT>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ, sK,
-                     sV, sSt0, sSt1, sPow);
+    output_role<DVT, NORM>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ,
+                           sK, sV, sSt0, sSt1, sPow);
   else
-    state_role<DVT, true>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
-                          final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
-                          sSt0, sSt1, sPow);
+    state_role<DVT, true, NORM>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
+                                final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
+                                sSt0, sSt1, sPow, np);
 }
 
-template <int DVT>
+template <int DVT, bool NORM>
 __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    float *__restrict__ slots, Plan plan, Decay dec, int H, int dv) {
+    float *__restrict__ slots, Plan plan, Decay dec, int H, int dv, NormPtrs np) {
   using M = MfCfg<DVT>;
   __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
@@ -244,29 +265,35 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
   if (it.flags & kLastSeg) return;  // no later segment reads it
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
-  state_role<DVT, false>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
-                         dtile * DVT, 0, tid, __builtin_amdgcn_readfirstlane(tid >> 6),
-                         nullptr, sKs, sV, nullptr, nullptr, sPow);
+  state_role<DVT, false, NORM>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
+                               dtile * DVT, 0, tid, __builtin_amdgcn_readfirstlane(tid >> 6),
+                               nullptr, sKs, sV, nullptr, nullptr, sPow, np);
 }
 
-template <int DVT>
+template <int DVT, bool NORM>
 static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
                        const Decay &dec, hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
+  const NormPtrs np = {a.z0, a.z_final, a.zslots};
   if (state_only)
-    hipLaunchKernelGGL((fwd_state_kernel<DVT>), dim3(grid), dim3(256), 0, s,
-                       (const bf16 *)a.k, (const bf16 *)a.v, a.slots, p, dec, a.H, a.dv);
+    hipLaunchKernelGGL((fwd_state_kernel<DVT, NORM>), dim3(grid), dim3(256), 0, s,
+                       (const bf16 *)a.k, (const bf16 *)a.v, a.slots, p, dec, a.H, a.dv, np);
   else
-    hipLaunchKernelGGL((fwd_out_kernel<DVT>), dim3(grid), dim3(512), 0, s,
+    hipLaunchKernelGGL((fwd_out_kernel<DVT, NORM>), dim3(grid), dim3(512), 0, s,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                        (bf16 *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
-                       a.H, a.dv, a.final_in_slot);
+                       a.H, a.dv, a.final_in_slot, np);
 }
 
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s) {
-  if (dvt == 96) launch_dvt<96>(state_only, p, a, dec, s);
-  else launch_dvt<64>(state_only, p, a, dec, s);
+  if (a.norm) {
+    if (dvt == 96) launch_dvt<96, true>(state_only, p, a, dec, s);
+    else launch_dvt<64, true>(state_only, p, a, dec, s);
+  } else {
+    if (dvt == 96) launch_dvt<96, false>(state_only, p, a, dec, s);
+    else launch_dvt<64, false>(state_only, p, a, dec, s);
+  }
 }
 
 }  // namespace gla

@@ -52,6 +52,22 @@ struct FwdArgs {
   float scale;
   int H, dk, dv;
   int final_in_slot;  // last segment writes its final state to its own slot
+  // Normalised linear attention (norm = 1): phi = ReLU on q and k, a
+  // normaliser sum z carried beside S, o = phi(q) S / (phi(q) . z + eps)
+  int norm;
+  const float *z0;  // [n_seq][H][dk] or nullptr
+  float *z_final;   // [n_seq][H][dk] or nullptr
+  float *zslots;    // [max_items][H][dk] with time segments
+};
+
+constexpr float kLinearAttnEps = 1e-6f;
+
+// Normalised linear attention: where the normaliser sum z enters and leaves
+// (all [.][H][dk] fp32, nullptr when absent); kernel argument.
+struct NormPtrs {
+  const float *z0;  // incoming z of each sequence
+  float *z_final;   // z after each sequence's last token
+  float *zslots;    // per-item z of time segments (local end, then combined)
 };
 
 struct BwdArgs {

@@ -35,6 +35,9 @@ namespace gla {
 // ===========================================================================
 // One workgroup per (item, head, 16-column dv tile). Everything in LDS as
 // fp32: the q/k/v chunk tiles, the masked score tile and the state tile.
+// NORM (normalised linear attention): q and k pass through ReLU on load, the
+// normaliser z (dk floats, carried like S with v = 1) gives each row its
+// denominator phi(q_i) . z_i + eps, which replaces the scale.
 constexpr int kValuDvt = 16;
 
 template <typename Tin>
@@ -47,20 +50,22 @@ __device__ __forceinline__ void st_out(Tin *p, float x) {
   *p = (Tin)x;
 }
 
-template <typename Tin, bool STATE_ONLY>
+template <typename Tin, bool STATE_ONLY, bool NORM>
 __global__ __launch_bounds__(256) void fwd_valu_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k,
     const Tin *__restrict__ v, Tin *__restrict__ o,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H,
-    int dk, int dv, int C, int final_in_slot) {
+    int dk, int dv, int C, int final_in_slot, NormPtrs np) {
   extern __shared__ float vsm[];
   float *sQ = vsm;                      // [C][dk]
   float *sK = sQ + C * dk;              // [C][dk]
   float *sV = sK + C * dk;              // [C][16]
   float *sP = sV + C * kValuDvt;        // [C][C]
   float *sS = sP + C * C;               // [dk][16]
-  float *sPow = sS + dk * kValuDvt;     // [C+1]
+  float *sPow = sS + dk * kValuDvt;     // [C+1] (+3)
+  float *sZ = sPow + C + 4;             // [dk]   NORM
+  float *sDen = sZ + dk;                // [C]    NORM
 
   const int ndt = dv / kValuDvt;
   int unit, dtile;
@@ -94,6 +99,16 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
       sS[e] = src ? src[(long long)d * dv + c0 + c] : 0.f;
     }
   }
+  if (NORM) {
+    const float *zsrc = nullptr;
+    if (!STATE_ONLY) {
+      if (it.flags & kFirstSeg)
+        zsrc = np.z0 ? np.z0 + ((long long)it.n * H + h) * dk : nullptr;
+      else
+        zsrc = np.zslots + ((long long)(idx - 1) * H + h) * dk;
+    }
+    for (int d = tid; d < dk; d += blockDim.x) sZ[d] = zsrc ? zsrc[d] : 0.f;
+  }
   __syncthreads();
 
   for (int ch = 0; ch < nch; ++ch) {
@@ -103,8 +118,12 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
       const int r = e / dk, d = e - r * dk;
       const bool ok = r < L;
       const long long off = (long long)(tb + r) * rowK + (long long)h * dk + d;
-      if (!STATE_ONLY) sQ[e] = ok ? ld_in(q + off) : 0.f;
-      sK[e] = ok ? ld_in(k + off) : 0.f;
+      if (!STATE_ONLY) {
+        const float x = ok ? ld_in(q + off) : 0.f;
+        sQ[e] = NORM ? fmaxf(x, 0.f) : x;
+      }
+      const float x = ok ? ld_in(k + off) : 0.f;
+      sK[e] = NORM ? fmaxf(x, 0.f) : x;
     }
     for (int e = tid; e < C * kValuDvt; e += blockDim.x) {
       const int r = e / kValuDvt, c = e - r * kValuDvt;
@@ -122,6 +141,16 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
         sP[e] = acc;
       }
       __syncthreads();
+      if (NORM) {  // per row: phi(q_i) . z_i + eps, z_i = lambda^(i+1) z_prev + sum_j P_ij
+        for (int i = tid; i < C; i += blockDim.x) {
+          float inter = 0.f;
+          for (int d = 0; d < dk; ++d) inter = fmaf(sQ[i * dk + d], sZ[d], inter);
+          float intra = 0.f;
+          for (int j = 0; j <= i; ++j) intra += sP[i * C + j];
+          sDen[i] = fmaf(sPow[i + 1], inter, intra) + kLinearAttnEps;
+        }
+        __syncthreads();
+      }
       for (int e = tid; e < C * kValuDvt; e += blockDim.x) {
         const int i = e / kValuDvt, c = e - i * kValuDvt;
         if (i < L) {
@@ -129,8 +158,9 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
           for (int d = 0; d < dk; ++d) inter = fmaf(sQ[i * dk + d], sS[d * kValuDvt + c], inter);
           float intra = 0.f;
           for (int j = 0; j <= i; ++j) intra = fmaf(sP[i * C + j], sV[j * kValuDvt + c], intra);
+          const float num = fmaf(sPow[i + 1], inter, intra);
           st_out(o + (long long)(tb + i) * rowV + (long long)h * dv + c0 + c,
-                 scale * fmaf(sPow[i + 1], inter, intra));
+                 NORM ? num / sDen[i] : scale * num);
         }
       }
       __syncthreads();
@@ -141,6 +171,13 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
       float acc = 0.f;
       for (int j = 0; j < L; ++j) acc = fmaf(sPow[L - 1 - j] * sK[j * dk + d], sV[j * kValuDvt + c], acc);
       sS[e] = fmaf(lamL, sS[e], acc);
+    }
+    if (NORM) {
+      for (int d = tid; d < dk; d += blockDim.x) {
+        float acc = 0.f;
+        for (int j = 0; j < L; ++j) acc = fmaf(sPow[L - 1 - j], sK[j * dk + d], acc);
+        sZ[d] = fmaf(lamL, sZ[d], acc);
+      }
     }
     __syncthreads();
   }
@@ -155,6 +192,15 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
       const int d = e / kValuDvt, c = e - d * kValuDvt;
       dst[(long long)d * dv + c0 + c] = sS[e];
     }
+  if (NORM && c0 == 0) {  // every dv tile holds the same z; the first stores it
+    float *zdst = nullptr;
+    if (STATE_ONLY)
+      zdst = np.zslots + ((long long)idx * H + h) * dk;
+    else if (it.flags & kLastSeg)
+      zdst = np.z_final ? np.z_final + ((long long)it.n * H + h) * dk : nullptr;
+    if (zdst)
+      for (int d = tid; d < dk; d += blockDim.x) zdst[d] = sZ[d];
+  }
 }
 
 // ===========================================================================
@@ -484,20 +530,29 @@ hipError_t launch_order(const Plan &p, int chunk, int32_t *order, hipStream_t s)
   return hipGetLastError();
 }
 
-template <typename Tin, bool SO>
-static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
-                        int C, hipStream_t s) {
+template <typename Tin, bool SO, bool NORM>
+static void launch_valu_n(const Plan &p, const FwdArgs &a, const Decay &dec,
+                          int C, hipStream_t s) {
   const int ndt = a.dv / kValuDvt;
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, ndt);
   const size_t lds = sizeof(float) * ((size_t)2 * C * a.dk + C * kValuDvt +
-                                      (size_t)C * C + a.dk * kValuDvt + C + 4);
+                                      (size_t)C * C + a.dk * kValuDvt + C + 4 +
+                                      a.dk + C);
   if (lds > 65536)  // beyond the default dynamic-LDS limit (gfx950 has 160 KB)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_valu_kernel<Tin, SO>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_valu_kernel<Tin, SO, NORM>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((fwd_valu_kernel<Tin, SO>), dim3(grid), dim3(256), lds, s,
+  const NormPtrs np = {a.z0, a.z_final, a.zslots};
+  hipLaunchKernelGGL((fwd_valu_kernel<Tin, SO, NORM>), dim3(grid), dim3(256), lds, s,
                      (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v,
                      (Tin *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
-                     a.H, a.dk, a.dv, C, a.final_in_slot);
+                     a.H, a.dk, a.dv, C, a.final_in_slot, np);
+}
+
+template <typename Tin, bool SO>
+static void launch_valu(const Plan &p, const FwdArgs &a, const Decay &dec,
+                        int C, hipStream_t s) {
+  if (a.norm) launch_valu_n<Tin, SO, true>(p, a, dec, C, s);
+  else launch_valu_n<Tin, SO, false>(p, a, dec, C, s);
 }
 
 hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,

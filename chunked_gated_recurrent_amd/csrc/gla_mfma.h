@@ -52,6 +52,24 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ReLU of eight bf16 packed in 16 bytes: every element whose sign bit is set
+// becomes +0 (per 32-bit word, m | (m - (m >> 15)) widens each set sign bit
+// to a 16-bit mask of its own half; no borrow crosses the halves).
+__device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    unsigned m = x[e] & 0x80008000u;
+    m |= m - (m >> 15);
+    x[e] &= ~m;
+  }
+  return x;
+}
+
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+  const bf16 one = (bf16)1.0f;
+  return (bf16x8){one, one, one, one, one, one, one, one};
+}
+
 template <int DVT>
 struct MfCfg {
   static constexpr int C = 64, DK = 96;
@@ -67,6 +85,9 @@ struct MfCfg {
   static constexpr int NJS = C / 32;     // 32-deep steps over the chunk
   static constexpr int SDT = NDT / 2, SCT = NCT / 2;  // state tiles per state wave
   static constexpr int NQV = DK / 8, NVV = DVT / 8;   // 16-byte vectors per row
+  // the published bf16 state: DVT rows of S^T, then (normalised linear
+  // attention) one row holding z, read by all lanes as a broadcast
+  static constexpr int SROWS = DVT + 1;
   static constexpr int QV = C * NQV / 256;  // q (or k) vectors per role thread
   static constexpr int VV = C * NVV / 256;  // v vectors per state thread
   static constexpr int OV = 16 * NVV / 64;  // output vectors per output lane
@@ -84,14 +105,20 @@ __device__ __forceinline__ int chunk_rows(const Item &it, int ch) {
 //   FUSED: runs beside the output role (also stores raw k for it and
 //          publishes the bf16 state each chunk); otherwise the state-only
 //          pass that computes a segment's local end state.
+//   NORM:  normalised linear attention: k passes through ReLU on its way to
+//          LDS, and the waves owning column tiles 0.. (w even) also carry
+//          z = sum of decay-weighted k over the chunk rows, as the MFMA of
+//          the Ks^T tile with a B operand of ones (every column of the
+//          result holds z); z is published in row DVT of the state buffer.
+//          Every dv tile's workgroup computes z; the one at c0 = 0 stores it.
 // ---------------------------------------------------------------------------
-template <int DVT, bool FUSED>
+template <int DVT, bool FUSED, bool NORM = false>
 __device__ __forceinline__ void state_role(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, const Item &it, int idx, int h, int H, int dv,
     int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
-    bf16 *sSt0, bf16 *sSt1, const float *sPow) {
+    bf16 *sSt0, bf16 *sSt1, const float *sPow, NormPtrs np = NormPtrs{}) {
   // sK (FUSED only), sKs and sV hold two chunk buffers each
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
@@ -127,6 +154,24 @@ __device__ __forceinline__ void state_role(
         accS[a][b] = x;
       }
   }
+  // the normaliser (NORM, waves with w even): z of d tiles dt0 .. dt0+SDT-1
+  const bool zw = NORM && !(w & 1);
+  f32x4 accZ[SDT];
+#pragma unroll
+  for (int a = 0; a < SDT; ++a) accZ[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (zw && FUSED) {
+    const float *src = nullptr;
+    if (it.flags & kFirstSeg)
+      src = np.z0 ? np.z0 + ((long long)it.n * H + h) * DK : nullptr;
+    else
+      src = np.zslots + ((long long)(idx - 1) * H + h) * DK;
+    if (src) {
+#pragma unroll
+      for (int a = 0; a < SDT; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accZ[a][r] = src[16 * (dt0 + a) + 4 * g + r];
+    }
+  }
 
   int rowK[QV], colK[QV], rowV[VV], colV[VV];
 #pragma unroll
@@ -160,10 +205,11 @@ __device__ __forceinline__ void state_role(
 #pragma unroll
     for (int m = 0; m < QV; ++m) {
       const int r = rowK[m];
-      if (FUSED) *reinterpret_cast<u32x4 *>(dK + r * QS + 8 * colK[m]) = rk[m];
+      const u32x4 kr = NORM ? relu_bf16x8(rk[m]) : rk[m];
+      if (FUSED) *reinterpret_cast<u32x4 *>(dK + r * QS + 8 * colK[m]) = kr;
       // decay-scaled copy lambda^(L-1-r) k_r; rows past the end are zero
       const float wgt = r < L ? sPow[max(L - 1 - r, 0)] : 0.f;
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, rk[m]);
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kr);
       bf16x8 ks;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ks[e] = (bf16)((float)kv[e] * wgt);
@@ -184,6 +230,15 @@ __device__ __forceinline__ void state_role(
         const int c = 16 * (ct0 + b) + l16;
         *reinterpret_cast<bf16x4 *>(dst + c * QS + 16 * (dt0 + a) + 4 * g) = t;
       }
+    if (zw && l16 == 0) {
+#pragma unroll
+      for (int a = 0; a < SDT; ++a) {
+        bf16x4 t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = (bf16)accZ[a][r];
+        *reinterpret_cast<bf16x4 *>(dst + DVT * QS + 16 * (dt0 + a) + 4 * g) = t;
+      }
+    }
   };
 
   // Chunk ch lives in LDS buffer ch & 1. Per chunk: one barrier, then the
@@ -209,6 +264,10 @@ __device__ __forceinline__ void state_role(
     for (int a = 0; a < SDT; ++a)
 #pragma unroll
       for (int b = 0; b < SCT; ++b) accS[a][b] *= lamL;
+    if (zw) {
+#pragma unroll
+      for (int a = 0; a < SDT; ++a) accZ[a] *= lamL;
+    }
 #pragma unroll
     for (int s = 0; s < M::NJS; ++s) {
       bf16x8 af[SDT], bfr[SCT];
@@ -227,6 +286,11 @@ __device__ __forceinline__ void state_role(
       for (int a = 0; a < SDT; ++a)
 #pragma unroll
         for (int b = 0; b < SCT; ++b) accS[a][b] = mfma(af[a], bfr[b], accS[a][b]);
+      if (zw) {
+        const bf16x8 ones = ones_bf16x8();
+#pragma unroll
+        for (int a = 0; a < SDT; ++a) accZ[a] = mfma(af[a], ones, accZ[a]);
+      }
     }
     if (FUSED) publish(st_pub);  // S_ch for the next chunk's readout
   };
@@ -250,6 +314,19 @@ __device__ __forceinline__ void state_role(
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(long long)(d + r) * dv + c] = accS[a][b][r];
       }
+  }
+  if (zw && l16 == 0 && c0 == 0) {
+    float *zdst = nullptr;
+    if (!FUSED)
+      zdst = np.zslots + ((long long)idx * H + h) * DK;
+    else if (it.flags & kLastSeg)
+      zdst = np.z_final ? np.z_final + ((long long)it.n * H + h) * DK : nullptr;
+    if (zdst) {
+#pragma unroll
+      for (int a = 0; a < SDT; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zdst[16 * (dt0 + a) + 4 * g + r] = accZ[a][r];
+    }
   }
 }
 

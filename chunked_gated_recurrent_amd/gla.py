@@ -46,6 +46,8 @@ _SIGS = {
     "gla_chunk_fwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_chunk_fwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "gla_linear_attn_fwd_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
+    "gla_linear_attn_fwd": ([_I] * 7 + [_P] * 9 + [ctypes.c_size_t, _P], _I),
     "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
     "gla_short_conv_fwd": ([_I] * 4 + [_P] * 7, _I),
     "gla_short_conv_decode_step": ([_I] * 3 + [_P] * 6, _I),
@@ -167,6 +169,55 @@ def gla_chunk_fwd(q, k, v, decay, scale: float = 1.0, initial_state=None,
     if rc != 0:
         raise GlaError(rc, "gla_chunk_fwd")
     return o, sf
+
+
+def linear_attn_fwd(q, k, v, initial_state=None, initial_z=None,
+                    output_final_state: bool = True, chunk: int = 0, out=None,
+                    final_state=None, final_z=None, workspace=None):
+    """Normalised causal linear attention with ReLU features (no decay):
+    o_t = phi(q_t) S_t / (phi(q_t) . z_t + 1e-6), S and z running sums of
+    phi(k)^T v and phi(k).
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32); initial_state
+    [B, H, dk, dv] and initial_z [B, H, dk] fp32 or None. Returns
+    (o, s_final or None, z_final or None).
+    """
+    import torch
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (B, T, H, dk))
+    _check(v, "v", dev, q.dtype, (B, T, H, dv))
+    dt = _dt(q)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, (B, H, dk, dv))
+    if initial_z is not None:
+        _check(initial_z, "initial_z", dev, torch.float32, (B, H, dk))
+    o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (B, T, H, dv))
+    sf, zf = final_state, final_z
+    if output_final_state:
+        if sf is None:
+            sf = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        if zf is None:
+            zf = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    if sf is not None:
+        _check(sf, "final_state", dev, torch.float32, (B, H, dk, dv))
+    if zf is not None:
+        _check(zf, "final_z", dev, torch.float32, (B, H, dk))
+    L = lib()
+    need = L.gla_linear_attn_fwd_workspace_bytes(dt, B, T, H, dk, dv, chunk)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = L.gla_linear_attn_fwd(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(initial_state), _ptr(initial_z), _ptr(o), _ptr(sf),
+                               _ptr(zf), _ptr(ws), wsb, _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_linear_attn_fwd")
+    return o, sf, zf
 
 
 def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,

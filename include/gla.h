@@ -180,6 +180,34 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Normalised causal linear attention (the tutorial page on RNNs without
+ * recurrence, section 6.1, with the 1e-6 denominator term of the module in
+ * its section 6.2). Per head, with the feature map phi = ReLU and no decay:
+ *   S_t = S_{t-1} + phi(k_t)^T v_t        z_t = z_{t-1} + phi(k_t)
+ *   o_t = phi(q_t) S_t / (phi(q_t) . z_t + 1e-6)
+ * computed chunkwise by the same kernels as gla_chunk_fwd at lambda = 1
+ * (the denominator is the readout of a value column of ones).
+ *   q, k    : [B, T, H, dk] dt, raw (phi is applied inside)
+ *   v, o    : [B, T, H, dv] dt (o written)
+ *   s0, z0  : [B, H, dk, dv] / [B, H, dk] fp32 running sums carried in from
+ *             earlier tokens, or NULL for zeros
+ *   s_final, z_final : the sums after the last token, or NULL to skip
+ *   workspace: device scratch of gla_linear_attn_fwd_workspace_bytes()
+ *             bytes (0 unless the batch is split into time segments).
+ * Shapes, dtypes and chunk as for gla_chunk_fwd (the matrix-core path for
+ * bf16 with dk = 96 and dv a multiple of 64). Every output must be disjoint
+ * from every other argument (no in-place final sums: GLA_ERR_ALIAS).
+ * T = 0 copies s0 and z0 (or zeros) to the final sums.
+ */
+size_t gla_linear_attn_fwd_workspace_bytes(gla_dtype dt, int B, int T, int H,
+                                           int dk, int dv, int chunk);
+gla_status gla_linear_attn_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                               int chunk, const void *q, const void *k, const void *v,
+                               const float *s0, const float *z0, void *o,
+                               float *s_final, float *z_final, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * The short causal convolution in front of the mixer (Laplace 3B / Trainium2
  * page, section on normalisation and convolution): every channel passes
  * through a causal Conv1d of width 4, then SiLU:

@@ -238,6 +238,36 @@ def test_short_conv_argument_errors(L):
     assert dec(y=A[3]) == ALIAS                                     # y on the window
 
 
+def test_linear_attn_argument_errors(L):
+    def la(dt=BF16, B=2, T=128, H=4, dk=96, dv=192, chunk=0, q=A[0], k=A[1], v=A[2],
+           s0=None, z0=None, o=A[3], sf=None, zf=None, ws=None, wsb=0):
+        return L.gla_linear_attn_fwd(dt, B, T, H, dk, dv, chunk, q, k, v, s0, z0, o,
+                                     sf, zf, ws, wsb, None)
+    assert la(dt=5) == DTYPE
+    assert la(B=0) == SHAPE
+    assert la(T=-1) == SHAPE
+    assert la(H=65) == UNSUP
+    assert la(dk=100) == UNSUP
+    assert la(chunk=48) == UNSUP
+    assert la(q=None) == NULL
+    assert la(o=None) == NULL
+    assert la(T=0, q=None, k=None, v=None, o=None) == OK   # nothing to launch
+    assert la(z0=ctypes.c_void_p(A[4].value + 4)) == ALIGN
+    assert la(o=ctypes.c_void_p(A[2].value + 4096)) == ALIAS    # o inside v
+    assert la(s0=A[4], sf=A[4]) == ALIAS                          # no in-place final sums
+    assert la(z0=A[5], zf=A[5]) == ALIAS
+    assert la(sf=A[4], zf=ctypes.c_void_p(A[4].value + 4096)) == ALIAS
+    assert la(zf=A[3]) == ALIAS                                   # z_final on o
+    # one batch entry of a long sequence is cut into time segments
+    need = L.gla_linear_attn_fwd_workspace_bytes(BF16, 1, 1 << 16, 4, 96, 192, 0)
+    plain = L.gla_chunk_fwd_workspace_bytes(BF16, 1, 1 << 16, 4, 96, 192, 0)
+    assert need > plain > 0
+    assert la(B=1, T=1 << 16) == WS
+    assert la(B=1, T=1 << 16, ws=A[6], wsb=need - 1) == WS
+    assert la(B=1, T=1 << 16, ws=A[0], wsb=need) == ALIAS         # workspace on q
+    assert L.gla_linear_attn_fwd_workspace_bytes(BF16, 64, 2048, 16, 96, 192, 0) == 0
+
+
 def test_decode_pool_argument_errors(L):
     def pool(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], sl=A[5],
              P=8, st=A[3], o=A[4], decay=GOOD):

@@ -1,0 +1,122 @@
+"""GPU parity of the normalised causal linear attention (ReLU features, no
+decay, eps = 1e-6 in the denominator) against the fp64 oracle on seeded
+inputs: the matrix-core path (bf16, dk = 96, dv tiles of 96 and 64), the
+vector-ALU path (the tutorial page's single-head d_k = 32 shape in fp32,
+bf16 dk = 64), time segments, carried sums, and the degenerate cases.
+
+Bar: max|gpu - oracle| <= 1e-2 * max|oracle| for bf16 inputs, 1e-4 for fp32,
+on the output and on the final sums S and z."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_recurrent_amd import gla
+from chunked_gated_recurrent_amd import workloads as W
+from oracle import oracle as O
+from gla_testutil import TOL, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, B, T, H, dk, dv, dtype):
+    rng = np.random.default_rng(seed)
+    xs = [rng.standard_normal((B, T, H, d), dtype=np.float32) for d in (dk, dk, dv)]
+    if dtype == "bf16":
+        xs = [W.bf16_bits(x) for x in xs]
+    return xs
+
+
+def _run(q, k, v, s0=None, z0=None, chunk=0):
+    o, sf, zf = gla.linear_attn_fwd(dev(q), dev(k), dev(v), dev(s0), dev(z0), chunk=chunk)
+    torch.cuda.synchronize()
+    return host(o), host(sf), host(zf)
+
+
+def _check(dtype, got, ref, what):
+    errs = [rel_err(g, r) for g, r in zip(got, ref)]
+    print("%s: o %.2e  S %.2e  z %.2e" % ((what,) + tuple(errs)))
+    assert max(errs) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dv", [192, 128])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 321])
+def test_matrix_core_path(T, dv):
+    q, k, v = _case(900 + T + dv, 2, T, 3, 96, dv, "bf16")
+    _check("bf16", _run(q, k, v), O.linear_attention(q, k, v), "mfma T%d dv%d" % (T, dv))
+
+
+@pytest.mark.parametrize("dtype,dk,dv,chunk", [("f32", 32, 32, 0), ("f32", 32, 32, 32),
+                                               ("bf16", 64, 64, 0), ("f32", 96, 48, 0)])
+def test_vector_alu_path(dtype, dk, dv, chunk):
+    """The page's demonstration shape (one head, d_k = 32 for q, k and v) and
+    other head sizes off the matrix-core path."""
+    q, k, v = _case(950 + dk + dv + chunk, 2, 150, 1 if dk == 32 else 2, dk, dv, dtype)
+    _check(dtype, _run(q, k, v, chunk=chunk), O.linear_attention(q, k, v),
+           "valu %s dk%d dv%d C%d" % (dtype, dk, dv, chunk))
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32)])
+def test_carried_sums_continue_the_sequence(dtype, dk, dv):
+    """First 100 tokens, then the remaining 133 from the returned (S, z):
+    equal to the oracle over all 233 tokens."""
+    q, k, v = _case(970 + dk, 2, 233, 2, dk, dv, dtype)
+    o1, s1, z1 = gla.linear_attn_fwd(dev(q[:, :100]), dev(k[:, :100]), dev(v[:, :100]))
+    o2, s2, z2 = gla.linear_attn_fwd(dev(q[:, 100:]), dev(k[:, 100:]), dev(v[:, 100:]), s1, z1)
+    torch.cuda.synchronize()
+    ro, rs, rz = O.linear_attention(q, k, v)
+    got = (np.concatenate([host(o1), host(o2)], axis=1), host(s2), host(z2))
+    _check(dtype, got, (ro, rs, rz), "carried %s" % dtype)
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T", [("bf16", 96, 192, 4000), ("f32", 32, 32, 1500)])
+def test_time_segments(dtype, dk, dv, T):
+    """One batch entry, few heads: the sequence is cut into time segments
+    whose local sums (S and z) are combined before the outputs."""
+    assert gla.lib().gla_linear_attn_fwd_workspace_bytes(
+        1 if dtype == "bf16" else 0, 1, T, 2, dk, dv, 0) > 0
+    q, k, v = _case(990 + T, 1, T, 2, dk, dv, dtype)
+    _, s0, z0 = O.linear_attention(*_case(992, 1, 50, 2, dk, dv, dtype))
+    got = _run(q, k, v, s0.astype(np.float32), z0.astype(np.float32))
+    ref = O.linear_attention(q, k, v, s0.astype(np.float32), z0.astype(np.float32))
+    _check(dtype, got, ref, "segments %s T%d" % (dtype, T))
+
+
+def test_laplace_shape_sampled():
+    """B8 T2048 H16 dk96 dv192 bf16 (the prefill batch shape): sampled
+    batch entries and heads against the oracle."""
+    B, T, H = 8, 2048, 16
+    q, k, v = _case(1000, B, T, H, 96, 192, "bf16")
+    o, sf, zf = _run(q, k, v)
+    for b, h in [(0, 0), (3, 7), (7, 15)]:
+        sel = np.s_[b:b + 1, :, h:h + 1]
+        ro, rs, rz = O.linear_attention(q[sel], k[sel], v[sel])
+        _check("bf16", (o[sel], sf[b:b + 1, h:h + 1], zf[b:b + 1, h:h + 1]),
+               (ro, rs, rz), "laplace b%d h%d" % (b, h))
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32)])
+def test_degenerate_features(dtype, dk, dv):
+    """phi(q) = 0 everywhere gives o = 0 exactly; phi(k) = 0 everywhere gives
+    S = z = 0 and o = 0 (the denominator is eps alone)."""
+    q, k, v = _case(1010, 2, 70, 2, dk, dv, dtype)
+    neg = (lambda x: x | np.uint16(0x8000)) if dtype == "bf16" else (lambda x: -np.abs(x))
+    o, sf, zf = _run(neg(q), k, v)
+    assert np.all(o == 0.0)
+    o, sf, zf = _run(q, neg(k), v)
+    assert np.all(o == 0.0) and np.all(sf == 0.0) and np.all(zf == 0.0)
+
+
+def test_empty_sequence_copies_the_sums():
+    B, H, dk, dv = 2, 3, 96, 192
+    rng = np.random.default_rng(1020)
+    s0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((B, H, dk))).astype(np.float32)
+    e = torch.empty((B, 0, H, dk), dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty((B, 0, H, dv), dtype=torch.bfloat16, device="cuda")
+    o, sf, zf = gla.linear_attn_fwd(e, e, ev, dev(s0), dev(z0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(sf), s0)
+    np.testing.assert_array_equal(host(zf), z0)
+    o, sf, zf = gla.linear_attn_fwd(e, e, ev)
+    torch.cuda.synchronize()
+    assert np.all(host(sf) == 0.0) and np.all(host(zf) == 0.0)
