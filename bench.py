@@ -381,8 +381,17 @@ def cpu_baseline(x, lam, budget_s=10.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(calls * B * T / el, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": "%d passes over the laplace_prefill workload (B=%d, T=%d, 16 heads), "
                       "fp64 token-by-token recurrence, %.1f s wall" % (calls, B, T, el)}
 
@@ -527,6 +536,7 @@ def main():
                          traffic=measured_traffic("fwd_out_kernel<96>@laplace_prefill"),
                          bytes_per_launch=pre["bytes"], launch_ms=round(pre["event_ms"], 5)),
         "hbm_copy_GBps": copy_bw,
+        "hbm_frac_of_copy": round(pre["roofline"]["achieved"] / copy_bw, 4) if copy_bw else None,
         "mfma_frac": round(pre["mfma_frac"], 4),
         "mfma_bf16_gemm_TFLOPs": mfma_tf,
         "mfma_frac_of_gemm": round(pre["mfma_frac"] * BF16_PEAK_TFLOPS / mfma_tf, 4),

@@ -22,7 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgla.so")
-SOURCES = ["gla_kernels.hip", "gla_fwd_mfma.hip", "gla_bwd_mfma.hip", "gla_conv.hip",
+SOURCES = ["gla_kernels.hip", "gla_fwd_mfma.hip", "gla_bwd_mfma.hip", "gla_bwd_valu.hip",
+           "gla_conv.hip",
            "gla_api.cpp"]
 ARCH = "gfx950"
 

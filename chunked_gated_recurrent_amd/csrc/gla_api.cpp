@@ -211,23 +211,20 @@ HostPlan plan_linear_attn(int dt, int B, int T, int H, int dk, int dv, int chunk
 // Backward layout: the forward's plan (work items, dispatch order, time
 // segments and their incoming-state slots, in the forward's workspace
 // layout), then, with time segments, the carried-gradient slots, then the
-// fp32 dv-tile partials of dq and dk ([dv tile][H][token][96] each). The
-// matrix-core path only.
+// fp32 dv-tile partials of dq and dk ([dv tile][H][token][dk] each). Dv
+// tiles of 96 or 64 columns on the matrix-core path, of up to 64 on the
+// vector-ALU path.
 struct BwdPlan {
   HostPlan hp;
   int ndt, dvt;
   size_t off_cslots, off_part, part_bytes, ws_bytes;
 };
 
-bool bwd_supported(int dt, int dk, int dv, int chunk) {
-  return fast_path_ok(dt, dk, dv, chunk);
-}
-
 BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv) {
   BwdPlan bp;
   memset(&bp, 0, sizeof(bp));
   bp.hp = hp;
-  bp.dvt = fast_dv_tile(dv);
+  bp.dvt = hp.fast ? fast_dv_tile(dv) : valu_bwd_tile(dv);
   bp.ndt = dv / bp.dvt;
   const size_t base = align256(hp.ws_bytes);
   const size_t slot_bytes =
@@ -270,13 +267,15 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     FwdArgs f;
     memset(&f, 0, sizeof(f));
     f.q = a.q; f.k = a.k; f.v = a.v; f.s0 = a.s0; f.slots = a.slots;
-    f.scale = a.scale; f.H = a.H; f.dk = 96; f.dv = a.dv;
+    f.scale = a.scale; f.H = a.H; f.dk = a.dk_dim; f.dv = a.dv;
     Plan ps = p;
     ps.deal = 1;  // the state pass skips every last segment
-    if (launch_fwd(dt, true, true, ps, f, dec, 64, s) != hipSuccess) return GLA_ERR_HIP;
+    if (launch_fwd(dt, hp.fast, true, ps, f, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
     if (launch_combine(p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
   }
-  if (launch_bwd_mfma(bp.dvt, p, a, dec, s) != hipSuccess) return GLA_ERR_HIP;
+  const hipError_t e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s)
+                               : launch_bwd_valu(dt, p, a, dec, s);
+  if (e != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
 
@@ -492,7 +491,7 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
 
 size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
                                      int dv, int chunk) {
-  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || !bwd_supported(dt, dk, dv, chunk) ||
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK ||
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
   return bwd_layout(plan_fixed(dt, B, T, H, dk, dv, chunk), (long long)B * T, H, dk, dv).ws_bytes;
@@ -506,7 +505,6 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
                          size_t workspace_bytes, void *stream) {
   gla_status st = check_common(dt, H, dk, dv, chunk);
   if (st != GLA_OK) return st;
-  if (!bwd_supported(dt, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
   if (B < 1 || T < 0 || (long long)B * T > kMaxTokens) return GLA_ERR_SHAPE;
   if (!isfinite(scale)) return GLA_ERR_SHAPE;
   st = check_decay(decay_host, H);
@@ -550,13 +548,13 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.s0 = s0; a.ds_final = ds_final;
   a.dq = dq; a.dk = dk_out; a.dv_out = dv_out; a.ds0 = ds0;
-  a.scale = scale; a.H = H; a.dv = dv;
+  a.scale = scale; a.H = H; a.dv = dv; a.dk_dim = dk;
   return run_backward(dt, bp, a, make_decay(decay_host, H), workspace, s);
 }
 
 size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, int H,
                                             int dk, int dv, int chunk) {
-  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || !bwd_supported(dt, dk, dv, chunk) ||
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK ||
       N < 1 || N > (1 << 28) || total_T < 0)
     return 0;
   return bwd_layout(plan_varlen(dt, N, total_T, H, dk, dv, chunk), total_T, H, dk, dv).ws_bytes;
@@ -571,7 +569,6 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
                                 size_t workspace_bytes, void *stream) {
   gla_status st = check_common(dt, H, dk, dv, chunk);
   if (st != GLA_OK) return st;
-  if (!bwd_supported(dt, dk, dv, chunk)) return GLA_ERR_UNSUPPORTED;
   if (N < 1 || N > (1 << 28) || total_T < 0) return GLA_ERR_SHAPE;
   if (!isfinite(scale)) return GLA_ERR_SHAPE;
   st = check_decay(decay_host, H);
@@ -617,7 +614,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.s0 = s0; a.ds_final = ds_final;
   a.dq = dq; a.dk = dk_out; a.dv_out = dv_out; a.ds0 = ds0;
-  a.scale = scale; a.H = H; a.dv = dv;
+  a.scale = scale; a.H = H; a.dv = dv; a.dk_dim = dk;
   return run_backward(dt, bp, a, make_decay(decay_host, H), workspace, s);
 }
 

@@ -80,6 +80,7 @@ struct BwdArgs {
   float *part_dq, *part_dk;  // [dv tiles][H][tokens][96] fp32 partial sums
   float scale;
   int H, dv;
+  int dk_dim;  // dk (96 on the matrix-core path)
 };
 
 // ---- launchers (gla_kernels.hip) -------------------------------------------
@@ -105,6 +106,11 @@ hipError_t launch_rcombine(const Plan &p, const float *ds_final, float *cslots,
                            const Decay &dec, int H, int dk, int dv, hipStream_t s);
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
                            const Decay &dec, hipStream_t s);
+// vector-ALU backward (gla_bwd_valu.hip): dv tiles of valu_bwd_tile(dv)
+// columns, fp32 partial rows [dv tile][H][token][dk]
+int valu_bwd_tile(int dv);
+hipError_t launch_bwd_valu(int dt, const Plan &p, const BwdArgs &a, const Decay &dec,
+                           hipStream_t s);
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,

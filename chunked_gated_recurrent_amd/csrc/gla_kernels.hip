@@ -511,8 +511,11 @@ __global__ __launch_bounds__(512) void decode_kernel(
 // ===========================================================================
 // launchers
 // ===========================================================================
+// The matrix-core path always runs 64-token chunks; a request for 128 is
+// served with 64 (results do not depend on the chunk beyond rounding), and
+// only an explicit 32 selects the vector-ALU path for these shapes.
 bool fast_path_ok(int dt, int dk, int dv, int chunk) {
-  return dt == 1 && dk == 96 && (dv % 64 == 0) && (chunk == 0 || chunk == 64);
+  return dt == 1 && dk == 96 && (dv % 64 == 0) && chunk != 32;
 }
 
 int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }

@@ -31,7 +31,9 @@
  *     initial states are always fp32.
  *   - Shapes: 1 <= H <= 64; dk and dv multiples of 16 with dk <= 128 and
  *     dv <= 256. `chunk` is 0 (library default) or 32, 64 or 128; results do
- *     not depend on it beyond rounding.
+ *     not depend on it beyond rounding. It is a hint: the kernels run 64-token
+ *     chunks for 0, 64 and 128, and 32-token chunks (on the vector ALUs) for
+ *     32.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued on it; no call synchronises.
  *   - Arguments are validated on the host before any HIP call. On an error
@@ -147,10 +149,12 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
  *              sums of dq and dk over dv tiles and, when sequences are split
  *              into time segments, the segments' incoming states and carried
  *              gradients); NULL allowed when that is 0.
- * Supported: bf16 with dk = 96, dv a multiple of 64 and chunk 0 or 64
- * (GLA_ERR_UNSUPPORTED otherwise). Checks as for gla_chunk_fwd; no output may
- * overlap an input or another output. T = 0 is valid: ds0 receives ds_final
- * (or zeros).
+ * Shapes, dtypes and chunk as for gla_chunk_fwd: bf16 with dk = 96 and dv a
+ * multiple of 64 runs on the matrix cores; fp32, other head sizes and
+ * chunk = 32 run on the vector ALUs (fp32 arithmetic). The workspace is
+ * never 0 for tokens > 0 unless dv fits one dv tile. Checks as for
+ * gla_chunk_fwd; no output may overlap an input or another output. T = 0 is
+ * valid: ds0 receives ds_final (or zeros).
  */
 size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
                                      int dv, int chunk);

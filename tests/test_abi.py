@@ -171,9 +171,13 @@ def test_backward_argument_errors(L):
         return L.gla_chunk_bwd(dt, B, T, H, dk, dv, chunk, q, k, v, dptr(decay), 1.0, s0,
                                do, dsf, dq, dk_, dv_, ds0, ws, wsb, None)
     assert bwd(dt=7) == DTYPE
-    assert bwd(dt=F32) == UNSUP              # the backward runs on the bf16 matrix-core path
-    assert bwd(dk=64) == UNSUP
-    assert bwd(chunk=32) == UNSUP
+    # fp32, other head sizes and 32-token chunks run on the vector ALUs: valid
+    # shapes, so here they fail only for want of workspace
+    assert bwd(dt=F32, wsb=16) == WS
+    assert bwd(dk=64, ws=None) == WS
+    assert bwd(chunk=32, ws=None) == WS
+    assert bwd(chunk=48) == UNSUP
+    assert bwd(dk=100) == UNSUP
     assert bwd(B=0) == SHAPE
     assert bwd(T=-1) == SHAPE
     assert bwd(do=None) == NULL
@@ -191,7 +195,9 @@ def test_backward_argument_errors(L):
     need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 192, 0)
     # dq and dk partials: 2 dv tiles x 16 heads x 16,384 tokens x 96 fp32, twice
     assert need == 2 * 2 * 16 * 8 * 2048 * 96 * 4
-    assert L.gla_chunk_bwd_workspace_bytes(F32, 8, 2048, 16, 96, 192, 0) == 0
+    # vector-ALU path: dv tiles of 64 columns, dk = 32
+    assert L.gla_chunk_bwd_workspace_bytes(F32, 8, 2048, 16, 32, 192, 0) == \
+        2 * 3 * 16 * 8 * 2048 * 32 * 4
     assert L.gla_chunk_bwd_workspace_bytes(BF16, 8, 0, 16, 96, 192, 0) == 0
 
 
@@ -202,7 +208,8 @@ def test_backward_varlen_argument_errors(L):
         return L.gla_chunk_bwd_varlen(dt, N, total, H, dk, dv, chunk, cu, q, k, v,
                                       dptr(decay), 1.0, None, do, None, dq, dk_, dv_, ds0,
                                       ws, wsb, None)
-    assert bwd(dt=F32) == UNSUP
+    assert bwd(dt=F32) == WS                                # vector-ALU path, no workspace given
+    assert bwd(chunk=96) == UNSUP
     assert bwd(N=0) == SHAPE
     assert bwd(total=-2) == SHAPE
     assert bwd(cu=None) == NULL
@@ -211,7 +218,7 @@ def test_backward_varlen_argument_errors(L):
     assert bwd(dk_=A[4]) == ALIAS
     assert bwd() == WS                                      # N > 1: the order needs scratch
     assert L.gla_chunk_bwd_varlen_workspace_bytes(BF16, 3, 300, 4, 96, 192, 0) > 0
-    assert L.gla_chunk_bwd_varlen_workspace_bytes(F32, 3, 300, 4, 96, 192, 0) == 0
+    assert L.gla_chunk_bwd_varlen_workspace_bytes(F32, 3, 300, 4, 96, 192, 0) > 0
 
 
 def test_short_conv_argument_errors(L):
