@@ -317,7 +317,7 @@ def gla_chunk_bwd(q, k, v, decay, dout, scale: float = 1.0, initial_state=None,
                   ds_final=None, want_ds0: bool = True, chunk: int = 0,
                   dq=None, dk=None, dv=None, ds0=None, workspace=None):
     """Backward of gla_chunk_fwd: q, k [B, T, H, dk], v and dout [B, T, H, dv]
-    (bf16), decay H floats, initial_state and ds_final [B, H, dk, dv] fp32 or
+    (bf16 or fp32), decay H floats, initial_state and ds_final [B, H, dk, dv] fp32 or
     None. Returns (dq, dk, dv, ds0) with ds0 None unless want_ds0 or given."""
     import torch
     dev = q.device
@@ -362,7 +362,7 @@ def gla_chunk_bwd_varlen(q, k, v, cu_seqlens, decay, dout, scale: float = 1.0,
                          chunk: int = 0, dq=None, dk=None, dv=None, ds0=None,
                          workspace=None):
     """Backward of gla_chunk_fwd_varlen: q, k [total_T, H, dk], v and dout
-    [total_T, H, dv] (bf16), cu_seqlens [N+1] int32 on the device,
+    [total_T, H, dv] (bf16 or fp32), cu_seqlens [N+1] int32 on the device,
     initial_state and ds_final [N, H, dk, dv] fp32 or None. Returns
     (dq, dk, dv, ds0)."""
     import torch
