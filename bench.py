@@ -323,11 +323,28 @@ def bench_linear_attn(steps, warmup):
 
     wall, ev_ms = timed(step, steps, warmup)
     bytes_call = B * T * PREFILL_BYTES_PER_TOKEN + B * (STATE_BYTES + H * DK * 4)
+    del sets
+    # one decode step for 1,280 sequences from running sums (S, z), in place
+    N = 1280
+    st = torch.randn(N, H, DK, DV, generator=g, device=dev) * 0.3
+    zs = torch.rand(N, H, DK, generator=g, device=dev) * 10.0
+    qd, kd = (torch.randn(N, H, DK, generator=g, device=dev).to(torch.bfloat16)
+              for _ in range(2))
+    vd = torch.randn(N, H, DV, generator=g, device=dev).to(torch.bfloat16)
+    od = torch.empty(N, H, DV, dtype=torch.bfloat16, device=dev)
+    dsteps = max(10, steps // 10)
+    wall_d, ev_d = timed(lambda i: gla.linear_attn_decode_step(qd, kd, vd, st, zs, out=od),
+                         dsteps, max(3, warmup // 10))
+    bytes_dec = N * (DECODE_BYTES_PER_SEQSTEP + 2 * H * DK * 4)
     return {"workload": "linear_attention", "config": {"B": B, "T": T, "H": H, "dk": DK,
-                                                       "dv": DV},
+                                                       "dv": DV, "decode_N": N},
             "value": round(B * T * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
-            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true>")}
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true>"),
+            "decode": {"value": round(N * dsteps / wall_d, 1), "unit": "seq-steps/s",
+                       "ms_per_step": round(wall_d / dsteps * 1e3, 4),
+                       "roofline": dict(roofline(bytes_dec, ev_d),
+                                        kernel="decode_kernel<bf16,16,true>")}}
 
 
 def bench_varlen(steps, warmup):

@@ -701,6 +701,34 @@ gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
   return GLA_OK;
 }
 
+gla_status gla_linear_attn_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
+                                       const void *q, const void *k, const void *v,
+                                       float *state, float *z, void *o, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, 0);
+  if (st != GLA_OK) return st;
+  if (N < 0 || (long long)N * H > kMaxTokens) return GLA_ERR_SHAPE;
+  if (N == 0) return GLA_OK;
+  if (!q || !k || !v || !o || !state || !z) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(state) ||
+      misaligned(z))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)N * H * dk * es, nv = (size_t)N * H * dv * es;
+  const size_t ns = (size_t)N * H * dk * dv * sizeof(float), nz = (size_t)N * H * dk * 4;
+  const void *rp[6] = {q, k, v, o, state, z};
+  const size_t rn[6] = {nqk, nqk, nv, nv, ns, nz};
+  for (int a = 3; a < 6; ++a)  // o, state, z: disjoint from everything else
+    for (int b = 0; b < 6; ++b)
+      if (a != b && overlap(rp[a], rn[a], rp[b], rn[b])) return GLA_ERR_ALIAS;
+  Decay one;
+  for (int h = 0; h < kMaxHeads; ++h) one.lam[h] = 1.0f;
+  (void)hipGetLastError();
+  if (launch_decode(dt, N, H, dk, dv, q, k, v, one, 1.0f, state, o, (hipStream_t)stream,
+                    nullptr, 0, z) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
 gla_status gla_decode_step_pool(gla_dtype dt, int N, int H, int dk, int dv,
                                 const void *q, const void *k, const void *v,
                                 const float *decay_host, float scale,

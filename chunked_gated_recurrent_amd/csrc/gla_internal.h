@@ -121,6 +121,7 @@ hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
 hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
                          const void *k, const void *v, const Decay &dec,
                          float scale, float *state, void *o, hipStream_t s,
-                         const int32_t *slots = nullptr, int n_slots = 0);
+                         const int32_t *slots = nullptr, int n_slots = 0,
+                         float *zsum = nullptr);
 
 }  // namespace gla

@@ -430,12 +430,15 @@ typedef float f32x4n __attribute__((ext_vector_type(4)));
 // With a slot table (state pool), row n reads and writes pool entry
 // slots[n]; a slot outside [0, n_slots) marks a padding row, whose output
 // is written as zeros and which touches no state.
-template <typename Tin, int RPT>
+// NORM (normalised linear attention, lambda = 1 from the host): q and k
+// pass through ReLU, the normaliser z [rows][dk] is updated in place beside
+// the state, and the output is the readout over phi(q) . z + eps.
+template <typename Tin, int RPT, bool NORM>
 __global__ __launch_bounds__(512) void decode_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k,
     const Tin *__restrict__ v, Decay dec, float scale, float *__restrict__ state,
     Tin *__restrict__ o, int H, int dk, int dv, int rpt_rt,
-    const int32_t *__restrict__ slots, int n_slots) {
+    const int32_t *__restrict__ slots, int n_slots, float *__restrict__ zsum) {
   extern __shared__ float dsm[];
   const int quads = dv / 4;
   const int rpt = RPT > 0 ? RPT : rpt_rt;
@@ -444,6 +447,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
   float *sk = sq + dk;    // [dk]
   float *sv = sk + dk;    // [dv]
   float *part = sv + dv;  // [rg_n][dv]
+  float *zt = part + rg_n * dv;  // [dk] (NORM): phi(q)[r] z_new[r]
   const long long unit = blockIdx.x;
   const int h = (int)(unit % H);
   const int tid = threadIdx.x;
@@ -461,12 +465,21 @@ __global__ __launch_bounds__(512) void decode_kernel(
   float *base = state + srow * (long long)dk * dv + 4 * cq;
   const int r0 = rg * rpt;
   for (int e = tid; e < dk; e += blockDim.x) {
-    sq[e] = (float)q[unit * dk + e];
-    sk[e] = (float)k[unit * dk + e];
+    const float qe = (float)q[unit * dk + e], ke = (float)k[unit * dk + e];
+    sq[e] = NORM ? fmaxf(qe, 0.f) : qe;
+    sk[e] = NORM ? fmaxf(ke, 0.f) : ke;
   }
   for (int e = tid; e < dv; e += blockDim.x) sv[e] = (float)v[unit * dv + e];
   __syncthreads();
   const float lam = dec.lam[h];
+  if (NORM) {
+    for (int e = tid; e < dk; e += blockDim.x) {
+      float *zp = zsum + srow * dk + e;
+      const float zn = fmaf(lam, *zp, sk[e]);
+      *zp = zn;
+      zt[e] = sq[e] * zn;
+    }
+  }
   f32x4n s[RPT > 0 ? RPT : 1];
   if constexpr (RPT > 0) {
     if (active) {
@@ -501,10 +514,16 @@ __global__ __launch_bounds__(512) void decode_kernel(
     *reinterpret_cast<f32x4n *>(part + rg * dv + 4 * cq) = acc;
   }
   __syncthreads();
+  float coef = scale;
+  if (NORM) {
+    float den = 0.f;
+    for (int r = 0; r < dk; ++r) den += zt[r];
+    coef = 1.0f / (den + kLinearAttnEps);
+  }
   for (int c = tid; c < dv; c += blockDim.x) {
     float sum = 0.f;
     for (int r = 0; r < rg_n; ++r) sum += part[r * dv + c];
-    o[unit * dv + c] = (Tin)(scale * sum);
+    o[unit * dv + c] = (Tin)(coef * sum);
   }
 }
 
@@ -616,7 +635,7 @@ hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
 hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
                          const void *k, const void *v, const Decay &dec,
                          float scale, float *state, void *o, hipStream_t s,
-                         const int32_t *slots, int n_slots) {
+                         const int32_t *slots, int n_slots, float *zsum) {
   const int quads = dv / 4;
   // row groups: the largest divisor of dk with quads * groups <= 320 threads
   // (for dk 96, dv 192: 6 groups of 16 rows, 288 threads)
@@ -625,18 +644,26 @@ hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
     if (dk % c == 0 && quads * c <= 320) rg = c;
   const int rpt = dk / rg;
   const unsigned threads = (unsigned)(quads * rg);
-  const size_t lds = sizeof(float) * (size_t)(2 * dk + dv + rg * dv);
+  const size_t lds = sizeof(float) * (size_t)(2 * dk + dv + rg * dv + (zsum ? dk : 0));
   const unsigned grid = (unsigned)((long long)N * H);
-#define GLA_DECODE(T, R)                                                       \
-  hipLaunchKernelGGL((decode_kernel<T, R>), dim3(grid), dim3(threads), lds, s, \
-                     (const T *)q, (const T *)k, (const T *)v, dec, scale,     \
-                     state, (T *)o, H, dk, dv, rpt, slots, n_slots)
-  if (dt == 1) {
-    if (rpt == 16) GLA_DECODE(bf16, 16);
-    else GLA_DECODE(bf16, 0);
+#define GLA_DECODE(T, R, NORM)                                                       \
+  hipLaunchKernelGGL((decode_kernel<T, R, NORM>), dim3(grid), dim3(threads), lds, s, \
+                     (const T *)q, (const T *)k, (const T *)v, dec, scale,           \
+                     state, (T *)o, H, dk, dv, rpt, slots, n_slots, zsum)
+  if (zsum) {
+    if (dt == 1) {
+      if (rpt == 16) GLA_DECODE(bf16, 16, true);
+      else GLA_DECODE(bf16, 0, true);
+    } else {
+      if (rpt == 16) GLA_DECODE(float, 16, true);
+      else GLA_DECODE(float, 0, true);
+    }
+  } else if (dt == 1) {
+    if (rpt == 16) GLA_DECODE(bf16, 16, false);
+    else GLA_DECODE(bf16, 0, false);
   } else {
-    if (rpt == 16) GLA_DECODE(float, 16);
-    else GLA_DECODE(float, 0);
+    if (rpt == 16) GLA_DECODE(float, 16, false);
+    else GLA_DECODE(float, 0, false);
   }
 #undef GLA_DECODE
   return hipGetLastError();

@@ -48,6 +48,7 @@ _SIGS = {
                                          _P, _P, _P, ctypes.c_size_t, _P], _I),
     "gla_linear_attn_fwd_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_linear_attn_fwd": ([_I] * 7 + [_P] * 9 + [ctypes.c_size_t, _P], _I),
+    "gla_linear_attn_decode_step": ([_I] * 5 + [_P] * 7, _I),
     "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
     "gla_short_conv_fwd": ([_I] * 4 + [_P] * 7, _I),
     "gla_short_conv_decode_step": ([_I] * 3 + [_P] * 6, _I),
@@ -218,6 +219,28 @@ def linear_attn_fwd(q, k, v, initial_state=None, initial_z=None,
     if rc != 0:
         raise GlaError(rc, "gla_linear_attn_fwd")
     return o, sf, zf
+
+
+def linear_attn_decode_step(q, k, v, state, z, out=None):
+    """One decode step of the normalised linear attention: q, k [N, H, dk],
+    v [N, H, dv]; state [N, H, dk, dv] and z [N, H, dk] fp32, updated in
+    place. Returns o [N, H, dv]."""
+    import torch
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (N, H, dk))
+    _check(v, "v", dev, q.dtype, (N, H, dv))
+    _check(state, "state", dev, torch.float32, (N, H, dk, dv))
+    _check(z, "z", dev, torch.float32, (N, H, dk))
+    o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (N, H, dv))
+    rc = lib().gla_linear_attn_decode_step(_dt(q), N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(state), _ptr(z), _ptr(o), _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_linear_attn_decode_step")
+    return o
 
 
 def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,

@@ -212,6 +212,18 @@ gla_status gla_linear_attn_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv
                                size_t workspace_bytes, void *stream);
 
 /*
+ * One decode step of the normalised linear attention for N sequences (one
+ * token each), continuing from the sums gla_linear_attn_fwd returns:
+ *   S += phi(k)^T v,   z += phi(k),   o = phi(q) S / (phi(q) . z + 1e-6)
+ *   q, k : [N, H, dk] dt   v, o : [N, H, dv] dt (o written)
+ *   state: [N, H, dk, dv] fp32 and z: [N, H, dk] fp32, both updated in place
+ * Checks as for gla_decode_step; o, state and z overlap nothing else.
+ */
+gla_status gla_linear_attn_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
+                                       const void *q, const void *k, const void *v,
+                                       float *state, float *z, void *o, void *stream);
+
+/*
  * The short causal convolution in front of the mixer (Laplace 3B / Trainium2
  * page, section on normalisation and convolution): every channel passes
  * through a causal Conv1d of width 4, then SiLU:

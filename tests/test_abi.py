@@ -275,6 +275,19 @@ def test_linear_attn_argument_errors(L):
     assert L.gla_linear_attn_fwd_workspace_bytes(BF16, 64, 2048, 16, 96, 192, 0) == 0
 
 
+def test_linear_attn_decode_argument_errors(L):
+    def la(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], st=A[3], z=A[4], o=A[5]):
+        return L.gla_linear_attn_decode_step(dt, N, H, dk, dv, q, k, v, st, z, o, None)
+    assert la(dt=2) == DTYPE
+    assert la(N=-1) == SHAPE
+    assert la(N=0) == OK                                          # nothing launched
+    assert la(dk=24) == UNSUP
+    assert la(z=None) == NULL
+    assert la(z=ctypes.c_void_p(A[4].value + 8)) == ALIGN
+    assert la(z=ctypes.c_void_p(A[3].value + 4096)) == ALIAS      # z inside the state
+    assert la(o=A[0]) == ALIAS                                    # o on q
+
+
 def test_decode_pool_argument_errors(L):
     def pool(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], sl=A[5],
              P=8, st=A[3], o=A[4], decay=GOOD):

@@ -120,3 +120,22 @@ def test_empty_sequence_copies_the_sums():
     o, sf, zf = gla.linear_attn_fwd(e, e, ev)
     torch.cuda.synchronize()
     assert np.all(host(sf) == 0.0) and np.all(host(zf) == 0.0)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32), ("bf16", 64, 128)])
+def test_decode_steps_continue_the_prefill(dtype, dk, dv):
+    """Prefill 37 tokens, then 5 decode steps from the returned (S, z): equal
+    to the oracle over all 42 tokens, outputs and final sums."""
+    B, T0, T, H = 3, 37, 42, 2
+    q, k, v = _case(1030 + dk, B, T, H, dk, dv, dtype)
+    o, sf, zf = gla.linear_attn_fwd(dev(q[:, :T0]), dev(k[:, :T0]), dev(v[:, :T0]))
+    outs = [host(o)]
+    for t in range(T0, T):
+        ot = gla.linear_attn_decode_step(dev(np.ascontiguousarray(q[:, t])),
+                                         dev(np.ascontiguousarray(k[:, t])),
+                                         dev(np.ascontiguousarray(v[:, t])), sf, zf)
+        outs.append(host(ot)[:, None])
+    torch.cuda.synchronize()
+    ro, rs, rz = O.linear_attention(q, k, v)
+    _check(dtype, (np.concatenate(outs, axis=1), host(sf), host(zf)), (ro, rs, rz),
+           "decode after prefill %s dk%d" % (dtype, dk))
