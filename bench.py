@@ -289,11 +289,14 @@ def bench_short_conv(steps, warmup):
     return {"workload": "short_conv", "config": {"B": B, "T": T, "D": D, "decode_N": N},
             "value": round(B * T * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
-            "roofline": dict(roofline(bytes_pre, ev_ms), kernel="short_conv_fwd_kernel<bf16>"),
+            "roofline": dict(roofline(bytes_pre, ev_ms), kernel="short_conv_fwd_kernel<bf16>",
+                             traffic=measured_traffic("short_conv_fwd_kernel<bf16>@short_conv")),
             "decode": {"value": round(N * steps / wall_d, 1), "unit": "seq-steps/s",
                        "ms_per_step": round(wall_d / steps * 1e3, 4),
                        "roofline": dict(roofline(bytes_dec, ev_d),
-                                        kernel="short_conv_decode_kernel<bf16>")}}
+                                        kernel="short_conv_decode_kernel<bf16>",
+                                        traffic=measured_traffic(
+                                            "short_conv_decode_kernel<bf16>@short_conv"))}}
 
 
 def bench_linear_attn(steps, warmup):
@@ -340,11 +343,14 @@ def bench_linear_attn(steps, warmup):
                                                        "dv": DV, "decode_N": N},
             "value": round(B * T * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
-            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true>"),
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true>",
+                             traffic=measured_traffic("fwd_out_kernel<96, true>@linear_attention")),
             "decode": {"value": round(N * dsteps / wall_d, 1), "unit": "seq-steps/s",
                        "ms_per_step": round(wall_d / dsteps * 1e3, 4),
                        "roofline": dict(roofline(bytes_dec, ev_d),
-                                        kernel="decode_kernel<bf16,16,true>")}}
+                                        kernel="decode_kernel<bf16,16,true>",
+                                        traffic=measured_traffic(
+                                            "decode_kernel<bf16,16,true>@linear_attention"))}}
 
 
 def bench_varlen(steps, warmup):
@@ -462,7 +468,7 @@ def measured_traffic(key):
         from chunked_gated_recurrent_amd.profiling import source_sha256
         with open(f) as fh:
             rec = json.load(fh).get(key)
-        if rec and rec.get("source_sha256") == source_sha256():
+        if rec and rec.get("source_sha256") == source_sha256(rec.get("source_files")):
             return int(rec["traffic_bytes"])
     except (OSError, ValueError, KeyError):
         pass
@@ -549,8 +555,8 @@ def main():
         "config": {"workload": "laplace_prefill", "B": 8, "T": 2048, "H": H, "dk": DK,
                    "dv": DV, "chunk": 64, "decays": "geometric, memory 32..4096 tokens",
                    "initial_state": "zero", "buffer_sets": 4},
-        "roofline": dict(pre["roofline"], kernel="fwd_out_kernel<96>",
-                         traffic=measured_traffic("fwd_out_kernel<96>@laplace_prefill"),
+        "roofline": dict(pre["roofline"], kernel="fwd_out_kernel<96, false>",
+                         traffic=measured_traffic("fwd_out_kernel<96, false>@laplace_prefill"),
                          bytes_per_launch=pre["bytes"], launch_ms=round(pre["event_ms"], 5)),
         "hbm_copy_GBps": copy_bw,
         "hbm_frac_of_copy": round(pre["roofline"]["achieved"] / copy_bw, 4) if copy_bw else None,

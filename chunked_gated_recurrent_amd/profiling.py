@@ -14,10 +14,15 @@
         FETCH_SIZE / WRITE_SIZE readings calibrate the HBM byte counters
     python -m chunked_gated_recurrent_amd.profiling traffic FETCH_DIR WRITE_DIR
             CAL_FETCH_DIR CAL_WRITE_DIR --kernel SUBSTR [--kernel SUBSTR ...] [--gib 1]
+            [--sources GROUP] [--key NAME --into FILE]
         HBM bytes per dispatch of a kernel: each counter divided by the ratio
         counter / true bytes that the same counter shows for the copy kernel.
         With several --kernel names, the per-dispatch figures are summed: the
-        bytes of one call that launches each of those kernels once.
+        bytes of one call that launches each of those kernels once. The
+        record carries a sha256 of the library sources the kernels are built
+        from (the files of GROUP in SOURCE_GROUPS, default all), so a later
+        change to those files marks it stale; --key/--into merge it into a
+        JSON file under NAME.
 """
 from __future__ import annotations
 
@@ -91,12 +96,25 @@ def copy_kernel(gib=1.0):
     print("copied %d bytes three times" % (n * 4))
 
 
-def source_sha256():
-    """sha256 over every source file of the HIP library (names and bytes), so
-    that any change to the kernels invalidates recorded counter readings."""
+# The library sources each measured path is built from (host dispatch,
+# shared device headers and the kernel files it launches).
+_COMMON = ["gla_api.cpp", "gla_device.h", "gla_internal.h"]
+SOURCE_GROUPS = {
+    "forward": _COMMON + ["gla_kernels.hip", "gla_mfma.h", "gla_fwd_mfma.hip"],
+    "decode": _COMMON + ["gla_kernels.hip"],
+    "backward": _COMMON + ["gla_kernels.hip", "gla_mfma.h", "gla_fwd_mfma.hip",
+                           "gla_bwd_mfma.hip"],
+    "conv": _COMMON + ["gla_conv.hip"],
+}
+
+
+def source_sha256(files=None):
+    """sha256 over source files of the HIP library (names and bytes): the
+    given csrc file names, or every file. Any change to them invalidates
+    recorded counter readings."""
     h = hashlib.sha256()
     d = os.path.join(HERE, "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in sorted(files if files is not None else os.listdir(d)):
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read() + b"\0")
     return h.hexdigest()
@@ -148,6 +166,9 @@ def main(argv=None):
     t.add_argument("cal_write_dir")
     t.add_argument("--kernel", required=True, action="append")
     t.add_argument("--gib", type=float, default=1.0)
+    t.add_argument("--sources", choices=sorted(SOURCE_GROUPS))
+    t.add_argument("--key")
+    t.add_argument("--into")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         rows = kernel_stats(a.dir, a.kernel)
@@ -169,8 +190,22 @@ def main(argv=None):
         copy_kernel(a.gib)
     elif a.cmd == "traffic":
         r = traffic(a.fetch_dir, a.write_dir, a.cal_fetch_dir, a.cal_write_dir, a.kernel, a.gib)
-        r["source_sha256"] = source_sha256()
+        files = SOURCE_GROUPS[a.sources] if a.sources else None
+        r["source_sha256"] = source_sha256(files)
+        r["source"] = ("chunked_gated_recurrent_amd/csrc/{%s}" % ",".join(files)
+                       if files else "chunked_gated_recurrent_amd/csrc/*")
+        if files:
+            r["source_files"] = files
         print(json.dumps(r, indent=1))
+        if a.key and a.into:
+            db = {}
+            if os.path.exists(a.into):
+                with open(a.into) as f:
+                    db = json.load(f)
+            db[a.key] = r
+            with open(a.into, "w") as f:
+                json.dump(db, f, indent=1, sort_keys=True)
+                f.write("\n")
 
 
 if __name__ == "__main__":
