@@ -197,15 +197,29 @@ gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
 
 size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
 
-// Normalised linear attention: the fixed-batch plan plus, with time
-// segments, one z slot ([item][H][dk] fp32) per item after the state slots.
-HostPlan plan_linear_attn(int dt, int B, int T, int H, int dk, int dv, int chunk) {
-  HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
+// Normalised linear attention: the forward's plan plus, with time segments,
+// one z slot ([item][H][dk] fp32) per item after the state slots.
+HostPlan with_zslots(HostPlan hp, int H, int dk) {
   if (hp.segmented) {
     hp.off_zslots = align256(hp.ws_bytes);
     hp.ws_bytes = hp.off_zslots + (size_t)hp.p.max_items * H * dk * sizeof(float);
   }
   return hp;
+}
+
+HostPlan plan_linear_attn(int dt, int B, int T, int H, int dk, int dv, int chunk) {
+  return with_zslots(plan_fixed(dt, B, T, H, dk, dv, chunk), H, dk);
+}
+
+HostPlan plan_linear_attn_varlen(int dt, int N, int total_T, int H, int dk, int dv,
+                                 int chunk) {
+  return with_zslots(plan_varlen(dt, N, total_T, H, dk, dv, chunk), H, dk);
+}
+
+Decay unit_decay() {
+  Decay one;
+  for (int h = 0; h < kMaxHeads; ++h) one.lam[h] = 1.0f;
+  return one;
 }
 
 // Backward layout: the forward's plan (work items, dispatch order, time
@@ -416,9 +430,65 @@ gla_status gla_linear_attn_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv
   a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
   a.scale = 1.0f; a.H = H; a.dk = dk; a.dv = dv;
   a.norm = 1; a.z0 = z0; a.z_final = z_final;
-  Decay one;
-  for (int h = 0; h < kMaxHeads; ++h) one.lam[h] = 1.0f;
-  return run_forward(dt, hp, a, one, workspace, s);
+  return run_forward(dt, hp, a, unit_decay(), workspace, s);
+}
+
+size_t gla_linear_attn_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,
+                                                  int H, int dk, int dv, int chunk) {
+  if (check_common(dt, H, dk, dv, chunk) != GLA_OK || N < 1 || total_T < 0) return 0;
+  return plan_linear_attn_varlen(dt, N, total_T, H, dk, dv, chunk).ws_bytes;
+}
+
+gla_status gla_linear_attn_fwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
+                                      int dv, int chunk, const int32_t *cu_seqlens,
+                                      const void *q, const void *k, const void *v,
+                                      const float *s0, const float *z0, void *o,
+                                      float *s_final, float *z_final, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  if (N < 1 || total_T < 0 || N > (1 << 28)) return GLA_ERR_SHAPE;
+  if (!cu_seqlens) return GLA_ERR_NULL;
+  if (total_T > 0 && (!q || !k || !v || !o)) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      misaligned(s0) || misaligned(s_final) || misaligned(z0) || misaligned(z_final) ||
+      ((uintptr_t)cu_seqlens & 3u))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dt);
+  const size_t nqk = (size_t)total_T * H * dk * es, nv = (size_t)total_T * H * dv * es;
+  const size_t ns = (size_t)N * H * dk * dv * sizeof(float);
+  const size_t nz = (size_t)N * H * dk * sizeof(float);
+  const size_t ncu = sizeof(int32_t) * ((size_t)N + 1);
+  const void *rp[8] = {q, k, v, s0, z0, cu_seqlens, o, s_final};
+  const size_t rn[8] = {nqk, nqk, nv, ns, nz, ncu, nv, ns};
+  for (int i = 0; i < 8; ++i) {
+    if (i != 6 && overlap(o, nv, rp[i], rn[i])) return GLA_ERR_ALIAS;
+    if (s_final && i != 7 && overlap(s_final, ns, rp[i], rn[i])) return GLA_ERR_ALIAS;
+    if (z_final && overlap(z_final, nz, rp[i], rn[i])) return GLA_ERR_ALIAS;
+  }
+  HostPlan hp = plan_linear_attn_varlen(dt, N, total_T, H, dk, dv, chunk);
+  if (hp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    for (int i = 0; i < 8; ++i)
+      if (overlap(workspace, hp.ws_bytes, rp[i], rn[i])) return GLA_ERR_ALIAS;
+    if (overlap(workspace, hp.ws_bytes, z_final, nz)) return GLA_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (total_T == 0) {
+    if (s_final || z_final) (void)hipGetLastError();
+    if (s_final && launch_state_fill(N, H, dk, dv, s0, s_final, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    if (z_final && launch_state_fill(N, H, dk, 1, z0, z_final, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    return GLA_OK;
+  }
+  hp.p.cu = cu_seqlens;
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
+  a.scale = 1.0f; a.H = H; a.dk = dk; a.dv = dv;
+  a.norm = 1; a.z0 = z0; a.z_final = z_final;
+  return run_forward(dt, hp, a, unit_decay(), workspace, s);
 }
 
 size_t gla_chunk_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,
@@ -720,10 +790,8 @@ gla_status gla_linear_attn_decode_step(gla_dtype dt, int N, int H, int dk, int d
   for (int a = 3; a < 6; ++a)  // o, state, z: disjoint from everything else
     for (int b = 0; b < 6; ++b)
       if (a != b && overlap(rp[a], rn[a], rp[b], rn[b])) return GLA_ERR_ALIAS;
-  Decay one;
-  for (int h = 0; h < kMaxHeads; ++h) one.lam[h] = 1.0f;
   (void)hipGetLastError();
-  if (launch_decode(dt, N, H, dk, dv, q, k, v, one, 1.0f, state, o, (hipStream_t)stream,
+  if (launch_decode(dt, N, H, dk, dv, q, k, v, unit_decay(), 1.0f, state, o, (hipStream_t)stream,
                     nullptr, 0, z) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;

@@ -49,6 +49,8 @@ _SIGS = {
     "gla_linear_attn_fwd_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_linear_attn_fwd": ([_I] * 7 + [_P] * 9 + [ctypes.c_size_t, _P], _I),
     "gla_linear_attn_decode_step": ([_I] * 5 + [_P] * 7, _I),
+    "gla_linear_attn_fwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
+    "gla_linear_attn_fwd_varlen": ([_I] * 7 + [_P] * 10 + [ctypes.c_size_t, _P], _I),
     "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
     "gla_short_conv_fwd": ([_I] * 4 + [_P] * 7, _I),
     "gla_short_conv_decode_step": ([_I] * 3 + [_P] * 6, _I),
@@ -218,6 +220,54 @@ def linear_attn_fwd(q, k, v, initial_state=None, initial_z=None,
                                _ptr(zf), _ptr(ws), wsb, _stream(dev))
     if rc != 0:
         raise GlaError(rc, "gla_linear_attn_fwd")
+    return o, sf, zf
+
+
+def linear_attn_fwd_varlen(q, k, v, cu_seqlens, initial_state=None, initial_z=None,
+                           output_final_state: bool = True, chunk: int = 0, out=None,
+                           final_state=None, final_z=None, workspace=None):
+    """linear_attn_fwd over packed sequences: q, k [total_T, H, dk], v
+    [total_T, H, dv], cu_seqlens [N+1] int32 on the device; initial_state
+    [N, H, dk, dv], initial_z [N, H, dk] fp32 or None. Returns
+    (o, s_final or None, z_final or None)."""
+    import torch
+    dev = q.device
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (total, H, dk))
+    _check(v, "v", dev, q.dtype, (total, H, dv))
+    _check(cu_seqlens, "cu_seqlens", dev, torch.int32, (N + 1,))
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, (N, H, dk, dv))
+    if initial_z is not None:
+        _check(initial_z, "initial_z", dev, torch.float32, (N, H, dk))
+    o = torch.empty((total, H, dv), dtype=q.dtype, device=dev) if out is None else out
+    _check(o, "out", dev, q.dtype, (total, H, dv))
+    sf, zf = final_state, final_z
+    if output_final_state:
+        if sf is None:
+            sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        if zf is None:
+            zf = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    if sf is not None:
+        _check(sf, "final_state", dev, torch.float32, (N, H, dk, dv))
+    if zf is not None:
+        _check(zf, "final_z", dev, torch.float32, (N, H, dk))
+    L = lib()
+    dt = _dt(q)
+    need = L.gla_linear_attn_fwd_varlen_workspace_bytes(dt, N, total, H, dk, dv, chunk)
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = L.gla_linear_attn_fwd_varlen(dt, N, total, H, dk, dv, chunk, _ptr(cu_seqlens),
+                                      _ptr(q), _ptr(k), _ptr(v), _ptr(initial_state),
+                                      _ptr(initial_z), _ptr(o), _ptr(sf), _ptr(zf), _ptr(ws),
+                                      wsb, _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_linear_attn_fwd_varlen")
     return o, sf, zf
 
 

@@ -212,6 +212,24 @@ gla_status gla_linear_attn_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv
                                size_t workspace_bytes, void *stream);
 
 /*
+ * gla_linear_attn_fwd over N packed variable-length sequences bounded by
+ * cu_seqlens (as for gla_chunk_fwd_varlen): q, k [total_T, H, dk], v, o
+ * [total_T, H, dv]; s0, s_final [N, H, dk, dv]; z0, z_final [N, H, dk].
+ * Workspace: gla_linear_attn_fwd_varlen_workspace_bytes() bytes (never 0
+ * for N > 1: it holds the dispatch order). Same checks as
+ * gla_linear_attn_fwd; a zero-length sequence copies its s0 and z0 (or
+ * zeros) to the final sums.
+ */
+size_t gla_linear_attn_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,
+                                                  int H, int dk, int dv, int chunk);
+gla_status gla_linear_attn_fwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
+                                      int dv, int chunk, const int32_t *cu_seqlens,
+                                      const void *q, const void *k, const void *v,
+                                      const float *s0, const float *z0, void *o,
+                                      float *s_final, float *z_final, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
  * One decode step of the normalised linear attention for N sequences (one
  * token each), continuing from the sums gla_linear_attn_fwd returns:
  *   S += phi(k)^T v,   z += phi(k),   o = phi(q) S / (phi(q) . z + 1e-6)

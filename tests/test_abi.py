@@ -275,6 +275,26 @@ def test_linear_attn_argument_errors(L):
     assert L.gla_linear_attn_fwd_workspace_bytes(BF16, 64, 2048, 16, 96, 192, 0) == 0
 
 
+def test_linear_attn_varlen_argument_errors(L):
+    def la(dt=BF16, N=3, total=300, H=4, dk=96, dv=192, chunk=0, cu=A[7], q=A[0], k=A[1],
+           v=A[2], s0=None, z0=None, o=A[3], sf=None, zf=None, ws=None, wsb=0):
+        return L.gla_linear_attn_fwd_varlen(dt, N, total, H, dk, dv, chunk, cu, q, k, v,
+                                            s0, z0, o, sf, zf, ws, wsb, None)
+    assert la(dt=3) == DTYPE
+    assert la(N=0) == SHAPE
+    assert la(cu=None) == NULL
+    assert la(cu=ctypes.c_void_p(A[7].value + 2)) == ALIGN
+    assert la(o=ctypes.c_void_p(A[7].value)) == ALIAS      # o on cu_seqlens
+    assert la(s0=A[4], sf=A[4]) == ALIAS
+    assert la(zf=A[2]) == ALIAS                            # z_final on v
+    assert la() == WS                                      # N > 1: the order needs scratch
+    assert L.gla_linear_attn_fwd_varlen_workspace_bytes(BF16, 3, 300, 4, 96, 192, 0) > 0
+    # a few long sequences: time segments with their z slots
+    a = L.gla_linear_attn_fwd_varlen_workspace_bytes(BF16, 2, 1 << 16, 4, 96, 192, 0)
+    b = L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 2, 1 << 16, 4, 96, 192, 0)
+    assert a > b > 0
+
+
 def test_linear_attn_decode_argument_errors(L):
     def la(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], st=A[3], z=A[4], o=A[5]):
         return L.gla_linear_attn_decode_step(dt, N, H, dk, dv, q, k, v, st, z, o, None)

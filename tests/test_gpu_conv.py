@@ -65,3 +65,37 @@ def test_short_conv_decode_steps_continue_the_prefill(dtype):
     ry, rwo = O.short_conv(x, w, b, win)
     assert rel_err(np.concatenate(ys, axis=1), ry) <= TOL[dtype]
     np.testing.assert_array_equal(host(wo), rwo)
+
+
+def test_short_conv_decode_full_size_sampled():
+    """One decode step for 1,280 sequences x 3,072 channels (the decode
+    workload's width): every 7th sequence against the oracle; the window is
+    shifted exactly."""
+    N, D = 1280, 3072
+    rng = np.random.default_rng(830)
+    x = W.bf16_bits(rng.standard_normal((N, D), dtype=np.float32))
+    w = (rng.standard_normal((D, 4)) * 0.5).astype(np.float32)
+    b = (rng.standard_normal(D) * 0.1).astype(np.float32)
+    win = rng.standard_normal((N, 4, D)).astype(np.float32)
+    wd = _t(win)
+    y = gla.short_conv_decode_step(dev(x), _t(w), _t(b), wd)
+    torch.cuda.synchronize()
+    sel = slice(0, N, 7)
+    rw = win[sel].astype(np.float64)
+    ry = O.short_conv_decode(x[sel], w, b, rw)
+    assert rel_err(host(y)[sel], ry) <= TOL["bf16"]
+    np.testing.assert_array_equal(host(wd)[sel], rw)
+
+
+def test_short_conv_causality_and_determinism():
+    x, w, b, win = _case(840, 2, 200, 3072, "bf16")
+    y1, w1 = gla.short_conv_fwd(dev(x), _t(w), _t(b), _t(win))
+    y2, w2 = gla.short_conv_fwd(dev(x), _t(w), _t(b), _t(win))
+    x3 = x.copy()
+    x3[:, 120:] ^= np.uint16(0x0040)          # perturb every later token
+    y3, _ = gla.short_conv_fwd(dev(x3), _t(w), _t(b), _t(win))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(y1), host(y2))
+    np.testing.assert_array_equal(host(w1), host(w2))
+    np.testing.assert_array_equal(host(y3)[:, :120], host(y1)[:, :120])
+    assert not np.array_equal(host(y3)[:, 120:], host(y1)[:, 120:])

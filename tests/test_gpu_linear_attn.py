@@ -139,3 +139,55 @@ def test_decode_steps_continue_the_prefill(dtype, dk, dv):
     ro, rs, rz = O.linear_attention(q, k, v)
     _check(dtype, (np.concatenate(outs, axis=1), host(sf), host(zf)), (ro, rs, rz),
            "decode after prefill %s dk%d" % (dtype, dk))
+
+
+def test_causality_and_determinism():
+    """Changing tokens after position 100 leaves outputs 0..100 bitwise
+    unchanged; two identical calls agree bitwise (no atomics feed an
+    output)."""
+    q, k, v = _case(1040, 2, 200, 3, 96, 192, "bf16")
+    a = _run(q, k, v)
+    b = _run(q, k, v)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    rng = np.random.default_rng(1041)
+    for arr in (q2, k2, v2):
+        arr[:, 101:] = W.bf16_bits(rng.standard_normal(arr[:, 101:].shape, dtype=np.float32))
+    c = _run(q2, k2, v2)
+    np.testing.assert_array_equal(c[0][:, :101], a[0][:, :101])
+    assert not np.array_equal(c[0][:, 101:], a[0][:, 101:])
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32)])
+@pytest.mark.parametrize("lengths", [[5, 0, 130, 1, 64, 65, 300], [3000, 1, 700]])
+def test_packed_sequences(dtype, dk, dv, lengths):
+    """Packed sequences (empty, one-token, chunk-aligned, ragged; a few long
+    ones cut into time segments by the device planner), each from its own
+    carried sums: every sequence equals the oracle run on it alone."""
+    H = 2
+    N = len(lengths)
+    cu = np.zeros(N + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    total = int(cu[-1])
+    q, k, v = (x[0] for x in _case(1050 + total, 1, total, H, dk, dv, dtype))
+    rng = np.random.default_rng(1051)
+    s0 = (rng.standard_normal((N, H, dk, dv)) * 0.3).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((N, H, dk))).astype(np.float32)
+    o, sf, zf = gla.linear_attn_fwd_varlen(dev(q), dev(k), dev(v), dev(cu), dev(s0), dev(z0))
+    torch.cuda.synchronize()
+    o, sf, zf = host(o), host(sf), host(zf)
+    worst = [0.0, 0.0, 0.0]
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        ro, rs, rz = O.linear_attention(q[None, a:b], k[None, a:b], v[None, a:b],
+                                        s0[n:n + 1], z0[n:n + 1])
+        if b > a:
+            worst[0] = max(worst[0], rel_err(o[a:b], ro[0]))
+        worst[1] = max(worst[1], rel_err(sf[n], rs[0]))
+        worst[2] = max(worst[2], rel_err(zf[n], rz[0]))
+        if b == a:
+            np.testing.assert_array_equal(sf[n], s0[n])
+            np.testing.assert_array_equal(zf[n], z0[n])
+    print("packed %s %s: o %.2e  S %.2e  z %.2e" % ((dtype, lengths) + tuple(worst)))
+    assert max(worst) <= TOL[dtype], worst
