@@ -314,6 +314,46 @@ __global__ __launch_bounds__(1024) void order_kernel(Plan p, int chunk,
 // ===========================================================================
 // Slot i holds U_i (local end state of item i) on entry and S_in(i+1) on
 // exit. One thread per 4 consecutive state elements of one (sequence, head).
+// The scan is a chain of scaled adds, but its inputs are not: the slots are
+// read in batches of kScanBatch before any of them is rewritten, so a thread
+// has that many loads in flight instead of one per step.
+constexpr int kScanBatch = 8;
+
+// S <- a S + U over the items of one (sequence, head), forward (REV false:
+// items first .. last-2, S starting from s_in) or backward (REV true: items
+// last-1 .. first+1); each item's slot receives the running S.
+template <bool REV>
+__device__ __forceinline__ void scan_slots(const Plan &p, int first, int last, float lam,
+                                           float4 S, float *slots, long long stride,
+                                           long long off) {
+  const int n_steps = last - first - 1;
+  for (int b = 0; b < n_steps; b += kScanBatch) {
+    float4 U[kScanBatch];
+    float a[kScanBatch];
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      if (b + j < n_steps) {
+        const int i = REV ? last - 1 - (b + j) : first + b + j;
+        Item it = {0, 0, 0, 0};  // stays empty (a = 1) only for an invalid plan
+        load_item(p, i, it);
+        a[j] = pow_f64(lam, it.t1 - it.t0);
+        U[j] = *reinterpret_cast<const float4 *>(slots + i * stride + off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      if (b + j < n_steps) {
+        const int i = REV ? last - 1 - (b + j) : first + b + j;
+        S.x = fmaf(a[j], S.x, U[j].x);
+        S.y = fmaf(a[j], S.y, U[j].y);
+        S.z = fmaf(a[j], S.z, U[j].z);
+        S.w = fmaf(a[j], S.w, U[j].w);
+        *reinterpret_cast<float4 *>(slots + i * stride + off) = S;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(
     Plan p, const float *__restrict__ s0, float *__restrict__ slots, Decay dec,
     int H, int dk, int dv) {
@@ -328,21 +368,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
   int first, last;
   seq_items(p, n, first, last);
   if (last - first < 2) return;
-  const float lam = dec.lam[h];
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
   if (s0) S = *reinterpret_cast<const float4 *>(s0 + ((long long)n * H + h) * per_state + e);
-  for (int i = first; i < last - 1; ++i) {
-    Item it;
-    if (!load_item(p, i, it)) break;
-    const float a = pow_f64(lam, it.t1 - it.t0);
-    float4 *slot = reinterpret_cast<float4 *>(slots + ((long long)i * H + h) * per_state + e);
-    const float4 U = *slot;
-    S.x = fmaf(a, S.x, U.x);
-    S.y = fmaf(a, S.y, U.y);
-    S.z = fmaf(a, S.z, U.z);
-    S.w = fmaf(a, S.w, U.w);
-    *slot = S;
-  }
+  scan_slots<false>(p, first, last, dec.lam[h], S, slots, (long long)H * per_state,
+                    (long long)h * per_state + e);
 }
 
 // Reverse combine of carried gradients over a sequence's items: slot i
@@ -364,22 +393,11 @@ __global__ __launch_bounds__(256) void rcombine_kernel(
   int first, last;
   seq_items(p, n, first, last);
   if (last - first < 2) return;
-  const float lam = dec.lam[h];
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
   if (ds_final)
     S = *reinterpret_cast<const float4 *>(ds_final + ((long long)n * H + h) * per_state + e);
-  for (int i = last - 1; i > first; --i) {
-    Item it;
-    if (!load_item(p, i, it)) break;
-    const float a = pow_f64(lam, it.t1 - it.t0);
-    float4 *slot = reinterpret_cast<float4 *>(slots + ((long long)i * H + h) * per_state + e);
-    const float4 U = *slot;
-    S.x = fmaf(a, S.x, U.x);
-    S.y = fmaf(a, S.y, U.y);
-    S.z = fmaf(a, S.z, U.z);
-    S.w = fmaf(a, S.w, U.w);
-    *slot = S;
-  }
+  scan_slots<true>(p, first, last, dec.lam[h], S, slots, (long long)H * per_state,
+                   (long long)h * per_state + e);
 }
 
 // s_final[n] <- slot of sequence n's last item (in-place final state with
