@@ -65,6 +65,13 @@ def test_backward_ragged_lengths(T, dv):
     _check("bwd T%d dv%d" % (T, dv), _run(x, do, dsf), _oracle(x, do, dsf))
 
 
+def test_backward_widest_value_head():
+    """dv = 256, the widest head: four dv tiles of 64 columns, four
+    partial sums per dq and dk element."""
+    x, do, dsf = _inputs(705, 2, 150, 2, 256)
+    _check("bwd dv256", _run(x, do, dsf), _oracle(x, do, dsf))
+
+
 def test_backward_without_initial_state_or_final_gradient():
     x, do, dsf = _inputs(710, 2, 150, 4, 192, with_s0=False, with_dsf=False)
     _check("bwd no s0 / dS_final", _run(x, do, dsf), _oracle(x, do, dsf))

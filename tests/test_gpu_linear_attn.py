@@ -38,7 +38,7 @@ def _check(dtype, got, ref, what):
     assert max(errs) <= TOL[dtype], errs
 
 
-@pytest.mark.parametrize("dv", [192, 128])
+@pytest.mark.parametrize("dv", [192, 128, 256])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 321])
 def test_matrix_core_path(T, dv):
     q, k, v = _case(900 + T + dv, 2, T, 3, 96, dv, "bf16")

@@ -125,7 +125,7 @@ def test_ragged_lengths_mfma(T, with_s0):
 @pytest.mark.parametrize("dtype,dk,dv,T,chunk", [
     ("bf16", 16, 32, 100, 32), ("f32", 32, 64, 130, 64), ("f32", 128, 256, 70, 0),
     ("bf16", 64, 128, 129, 0), ("f32", 96, 192, 257, 128), ("bf16", 96, 128, 150, 0),
-    ("bf16", 96, 64, 150, 0)])
+    ("bf16", 96, 64, 150, 0), ("bf16", 96, 256, 150, 0), ("bf16", 128, 256, 90, 0)])
 def test_shapes(dtype, dk, dv, T, chunk):
     x = W.prefill_inputs(7 + dk + T, 2, T, 2, dk, dv, dtype, 0.1, np.array([0.9, 0.995], np.float32))
     o, s = run_fixed(x, chunk=chunk)
