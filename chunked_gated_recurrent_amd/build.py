@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgla.so")
 SOURCES = ["gla_kernels.hip", "gla_fwd_mfma.hip", "gla_bwd_mfma.hip", "gla_bwd_valu.hip",
-           "gla_conv.hip",
+           "gla_bwd_wide.hip", "gla_conv.hip",
            "gla_api.cpp"]
 ARCH = "gfx950"
 

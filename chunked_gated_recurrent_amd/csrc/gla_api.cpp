@@ -73,11 +73,15 @@ void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk) {
   hp.ndt = hp.fast ? dv / fast_dv_tile(dv) : dv / 16;
 }
 
-HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk) {
+// plan_ndt (when > 0) replaces the forward's dv tiles per unit in the
+// decision to split sequences into time segments (the wide backward runs
+// one workgroup per unit).
+HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk,
+                    int plan_ndt = 0) {
   HostPlan hp;
   base_plan(hp, dt, dk, dv, chunk);
   const int C = hp.chunk;
-  const long long chains = (long long)B * H * hp.ndt;
+  const long long chains = (long long)B * H * (plan_ndt > 0 ? plan_ndt : hp.ndt);
   const long long target = target_workgroups();
   int G = 1;
   if (T > 2 * C && chains < target) {
@@ -103,11 +107,12 @@ HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk) {
   return hp;
 }
 
-HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk) {
+HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk,
+                     int plan_ndt = 0) {
   HostPlan hp;
   base_plan(hp, dt, dk, dv, chunk);
   const int C = hp.chunk;
-  const long long chains = (long long)N * H * hp.ndt;
+  const long long chains = (long long)N * H * (plan_ndt > 0 ? plan_ndt : hp.ndt);
   const long long target = target_workgroups();
   Plan &p = hp.p;
   p.n_seq = N;
@@ -228,24 +233,37 @@ Decay unit_decay() {
 // fp32 dv-tile partials of dq and dk ([dv tile][H][token][dk] each). Dv
 // tiles of 96 or 64 columns on the matrix-core path, of up to 64 on the
 // vector-ALU path.
+// The wide matrix-core backward (dk 96, dv 192: one workgroup per unit over
+// all of dv) writes dq and dk directly: no partials.
 struct BwdPlan {
   HostPlan hp;
   int ndt, dvt;
+  bool wide;
   size_t off_cslots, off_part, part_bytes, ws_bytes;
 };
+
+bool bwd_wide_path(int dt, int dk, int dv, int chunk) {
+  return fast_path_ok(dt, dk, dv, chunk) && bwd_wide_ok(dk, dv);
+}
+
+// dv tiles per unit the backward plans its time segments for
+int bwd_plan_ndt(int dt, int dk, int dv, int chunk) {
+  return bwd_wide_path(dt, dk, dv, chunk) ? 1 : 0;
+}
 
 BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv) {
   BwdPlan bp;
   memset(&bp, 0, sizeof(bp));
   bp.hp = hp;
-  bp.dvt = hp.fast ? fast_dv_tile(dv) : valu_bwd_tile(dv);
+  bp.wide = hp.fast && bwd_wide_ok(dk, dv);
+  bp.dvt = bp.wide ? dv : hp.fast ? fast_dv_tile(dv) : valu_bwd_tile(dv);
   bp.ndt = dv / bp.dvt;
   const size_t base = align256(hp.ws_bytes);
   const size_t slot_bytes =
       hp.segmented ? align256((size_t)hp.p.max_items * H * dk * dv * sizeof(float)) : 0;
   bp.off_cslots = base;
   bp.off_part = base + slot_bytes;
-  bp.part_bytes = align256((size_t)bp.ndt * H * total_T * dk * sizeof(float));
+  bp.part_bytes = bp.wide ? 0 : align256((size_t)bp.ndt * H * total_T * dk * sizeof(float));
   bp.ws_bytes = total_T > 0 ? bp.off_part + 2 * bp.part_bytes : 0;
   return bp;
 }
@@ -287,8 +305,14 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     if (launch_fwd(dt, hp.fast, true, ps, f, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
     if (launch_combine(p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
   }
-  const hipError_t e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s)
-                               : launch_bwd_valu(dt, p, a, dec, s);
+  hipError_t e;
+  if (bp.wide) {
+    if (a.cslots && launch_bwd_carry(fast_dv_tile(a.dv), p, a, dec, s) != hipSuccess)
+      return GLA_ERR_HIP;
+    e = launch_bwd_wide(p, a, dec, s);
+  } else {
+    e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
+  }
   if (e != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
@@ -564,7 +588,8 @@ size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
   if (check_common(dt, H, dk, dv, chunk) != GLA_OK ||
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
-  return bwd_layout(plan_fixed(dt, B, T, H, dk, dv, chunk), (long long)B * T, H, dk, dv).ws_bytes;
+  const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+  return bwd_layout(hp, (long long)B * T, H, dk, dv).ws_bytes;
 }
 
 gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
@@ -599,7 +624,8 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
     for (int b = a + 1; b < 4; ++b)
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
-  const BwdPlan bp = bwd_layout(plan_fixed(dt, B, T, H, dk, dv, chunk), tok, H, dk, dv);
+  const BwdPlan bp = bwd_layout(
+      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk)), tok, H, dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
     for (int b = 0; b < 6; ++b)
@@ -627,7 +653,9 @@ size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, in
   if (check_common(dt, H, dk, dv, chunk) != GLA_OK ||
       N < 1 || N > (1 << 28) || total_T < 0)
     return 0;
-  return bwd_layout(plan_varlen(dt, N, total_T, H, dk, dv, chunk), total_T, H, dk, dv).ws_bytes;
+  const HostPlan hp =
+      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+  return bwd_layout(hp, total_T, H, dk, dv).ws_bytes;
 }
 
 gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
@@ -663,7 +691,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
     for (int b = a + 1; b < 4; ++b)
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
-  HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk);
+  HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
   hp.p.cu = cu_seqlens;
   const BwdPlan bp = bwd_layout(hp, total_T, H, dk, dv);
   if (bp.ws_bytes > 0) {

@@ -725,19 +725,31 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(
   *reinterpret_cast<bf16x4 *>(dk + row * 96 + 4 * c4) = ok;
 }
 
+// Time segments: every segment's local carry, then the reverse combine.
+template <int DVT>
+static void launch_carry_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
+                             hipStream_t s) {
+  Plan pc = p;
+  pc.deal = 1;  // the carry pass skips every first segment
+  const unsigned gc = xcd_grid(1, (long long)p.max_items * a.H, a.dv / DVT);
+  hipLaunchKernelGGL((bwd_carry_kernel<DVT>), dim3(gc), dim3(256), 0, s,
+                     (const bf16 *)a.q, (const bf16 *)a.dout, a.cslots, pc, dec,
+                     a.scale, a.H, a.dv);
+  (void)launch_rcombine(p, a.ds_final, a.cslots, dec, a.H, 96, a.dv, s);  // errors surface below
+}
+
+hipError_t launch_bwd_carry(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
+                            hipStream_t s) {
+  if (dvt == 96) launch_carry_dvt<96>(p, a, dec, s);
+  else launch_carry_dvt<64>(p, a, dec, s);
+  return hipGetLastError();
+}
+
 template <int DVT>
 static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
-  if (a.cslots) {  // time segments: local carries, combined in reverse
-    Plan pc = p;
-    pc.deal = 1;  // the carry pass skips every first segment
-    const unsigned gc = xcd_grid(1, (long long)p.max_items * a.H, a.dv / DVT);
-    hipLaunchKernelGGL((bwd_carry_kernel<DVT>), dim3(gc), dim3(256), 0, s,
-                       (const bf16 *)a.q, (const bf16 *)a.dout, a.cslots, pc, dec,
-                       a.scale, a.H, a.dv);
-    (void)launch_rcombine(p, a.ds_final, a.cslots, dec, a.H, 96, a.dv, s);  // errors surface below
-  }
+  if (a.cslots) launch_carry_dvt<DVT>(p, a, dec, s);
   hipLaunchKernelGGL((bwd_dq_kernel<DVT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
                      a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv);
