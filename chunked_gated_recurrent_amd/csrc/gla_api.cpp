@@ -292,27 +292,34 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
   a.part_dq = (float *)(ws + bp.off_part);
   a.part_dk = (float *)(ws + bp.off_part + bp.part_bytes);
   if (hp.segmented) {
-    // incoming forward states of the segments: the forward's state pass and
-    // combine, exactly as in the forward call
+    // the segments' incoming forward states (the forward's state pass and
+    // combine) and, on the matrix cores, their incoming carried gradients
+    // (local carries and the reverse combine); the vector-ALU backward runs
+    // its own carry pass
     a.slots = (float *)(ws + hp.off_slots);
     a.cslots = (float *)(ws + bp.off_cslots);
-    FwdArgs f;
-    memset(&f, 0, sizeof(f));
-    f.q = a.q; f.k = a.k; f.v = a.v; f.s0 = a.s0; f.slots = a.slots;
-    f.scale = a.scale; f.H = a.H; f.dk = a.dk_dim; f.dv = a.dv;
-    Plan ps = p;
-    ps.deal = 1;  // the state pass skips every last segment
-    if (launch_fwd(dt, hp.fast, true, ps, f, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
-    if (launch_combine(p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
+    if (hp.fast) {
+      if (launch_bwd_boundary(fast_dv_tile(a.dv), p, a, dec, s) != hipSuccess)
+        return GLA_ERR_HIP;
+      if (launch_bicombine(p, a.s0, a.slots, a.ds_final, a.cslots, dec, a.H, a.dk_dim, a.dv,
+                           s) != hipSuccess)
+        return GLA_ERR_HIP;
+    } else {
+      FwdArgs f;
+      memset(&f, 0, sizeof(f));
+      f.q = a.q; f.k = a.k; f.v = a.v; f.s0 = a.s0; f.slots = a.slots;
+      f.scale = a.scale; f.H = a.H; f.dk = a.dk_dim; f.dv = a.dv;
+      Plan ps = p;
+      ps.deal = 1;  // the state pass skips every last segment
+      if (launch_fwd(dt, false, true, ps, f, dec, hp.chunk, s) != hipSuccess) return GLA_ERR_HIP;
+      if (launch_combine(p, f, dec, s) != hipSuccess) return GLA_ERR_HIP;
+    }
   }
   hipError_t e;
-  if (bp.wide) {
-    if (a.cslots && launch_bwd_carry(fast_dv_tile(a.dv), p, a, dec, s) != hipSuccess)
-      return GLA_ERR_HIP;
+  if (bp.wide)
     e = launch_bwd_wide(p, a, dec, s);
-  } else {
+  else
     e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
-  }
   if (e != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }

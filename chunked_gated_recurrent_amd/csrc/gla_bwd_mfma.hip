@@ -554,31 +554,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 // reverse chunk walk as the dv waves of bwd_dkdv_kernel, into slot g.
 // ---------------------------------------------------------------------------
 template <int DVT>
-__global__ __launch_bounds__(256, 2) void bwd_carry_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ dout,
-    float *__restrict__ cslots, Plan plan, Decay dec, float scale, int H, int dv) {
+__device__ __forceinline__ void carry_role(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ dout, float *__restrict__ cslots,
+    const Item &it, int idx, int h, int dtile, float scale, int H, int dv, int tid,
+    bf16 *sQ, bf16 *sD, const float *sPow) {
   using M = MfCfg<DVT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NJS = M::NJS, SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
   constexpr int NVV = M::NVV;
   constexpr int KBUF = C * QS, VBUF = C * VS;
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2 * C * QS];
-  __shared__ __attribute__((aligned(16))) bf16 sD[2 * C * VS];
-  __shared__ float sPow[C + 4];
-
-  const int ndt = dv / DVT;
-  int unit, dtile;
-  xcd_unit(plan, ndt, plan.max_items * H, unit, dtile);
-  if (unit >= plan.max_items * H) return;
-  const int slot = unit / H;
-  const int h = unit - slot * H;
-  int idx;
-  Item it;
-  if (!slot_item(plan, slot, idx, it)) return;
-  make_uniform(idx, it);
-  if (it.flags & kFirstSeg) return;  // no earlier item reads it
-  const int tid = threadIdx.x;
-  if (tid <= C) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
@@ -694,6 +678,48 @@ __global__ __launch_bounds__(256, 2) void bwd_carry_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Time segments, both directions in one launch: workgroups [0, n_state) run
+// the forward's state pass (local end state of every segment but a
+// sequence's last, into `slots`), the rest the local carries (every segment
+// but a sequence's first, into `cslots`). The two halves read different
+// arrays (k, v and q, dO) and each leaves half of the unit slots idle, so
+// together they fill the GPU once instead of half-filling it twice.
+// ---------------------------------------------------------------------------
+template <int DVT>
+__global__ __launch_bounds__(256, 2) void bwd_boundary_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, float *__restrict__ slots, float *__restrict__ cslots,
+    Plan plan, Decay dec, float scale, int H, int dv, int n_state) {
+  using M = MfCfg<DVT>;
+  __shared__ __attribute__((aligned(16))) bf16 sA[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2 * M::C * M::VS];
+  __shared__ float sPow[M::C + 4];
+  const bool state = (int)blockIdx.x < n_state;
+  const int P = state ? (int)blockIdx.x : (int)blockIdx.x - n_state;
+  const int ndt = dv / DVT;
+  int unit, dtile;
+  xcd_unit_at(plan, P, ndt, plan.max_items * H, unit, dtile);
+  if (unit >= plan.max_items * H) return;
+  const int slot = unit / H;
+  const int h = unit - slot * H;
+  int idx;
+  Item it;
+  if (!slot_item(plan, slot, idx, it)) return;
+  make_uniform(idx, it);
+  // no later segment reads a last segment's state, no earlier one a first
+  // segment's carry
+  if (it.flags & (state ? kLastSeg : kFirstSeg)) return;
+  const int tid = threadIdx.x;
+  if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
+  if (state)
+    state_role<DVT, false>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv, dtile * DVT, 0,
+                           tid, __builtin_amdgcn_readfirstlane(tid >> 6), nullptr, sA, sB,
+                           nullptr, nullptr, sPow);
+  else
+    carry_role<DVT>(q, dout, cslots, it, idx, h, dtile, scale, H, dv, tid, sA, sB, sPow);
+}
+
+// ---------------------------------------------------------------------------
 // dq, dk <- sum of the dv-tile partials, as bf16 in [tokens, H, 96]
 // ---------------------------------------------------------------------------
 // One thread per 4 consecutive values of one (token, head) row; each partial
@@ -725,23 +751,22 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(
   *reinterpret_cast<bf16x4 *>(dk + row * 96 + 4 * c4) = ok;
 }
 
-// Time segments: every segment's local carry, then the reverse combine.
 template <int DVT>
-static void launch_carry_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
-                             hipStream_t s) {
-  Plan pc = p;
-  pc.deal = 1;  // the carry pass skips every first segment
-  const unsigned gc = xcd_grid(1, (long long)p.max_items * a.H, a.dv / DVT);
-  hipLaunchKernelGGL((bwd_carry_kernel<DVT>), dim3(gc), dim3(256), 0, s,
-                     (const bf16 *)a.q, (const bf16 *)a.dout, a.cslots, pc, dec,
-                     a.scale, a.H, a.dv);
-  (void)launch_rcombine(p, a.ds_final, a.cslots, dec, a.H, 96, a.dv, s);  // errors surface below
+static void launch_boundary_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
+                                hipStream_t s) {
+  Plan pb = p;
+  pb.deal = 1;  // both halves skip a segment of every sequence
+  const unsigned g = xcd_grid(1, (long long)p.max_items * a.H, a.dv / DVT);
+  hipLaunchKernelGGL((bwd_boundary_kernel<DVT>), dim3(2 * g), dim3(256), 0, s,
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                     (const bf16 *)a.dout, a.slots, a.cslots, pb, dec, a.scale, a.H, a.dv,
+                     (int)g);
 }
 
-hipError_t launch_bwd_carry(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
-                            hipStream_t s) {
-  if (dvt == 96) launch_carry_dvt<96>(p, a, dec, s);
-  else launch_carry_dvt<64>(p, a, dec, s);
+hipError_t launch_bwd_boundary(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
+                               hipStream_t s) {
+  if (dvt == 96) launch_boundary_dvt<96>(p, a, dec, s);
+  else launch_boundary_dvt<64>(p, a, dec, s);
   return hipGetLastError();
 }
 
@@ -749,7 +774,6 @@ template <int DVT>
 static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
-  if (a.cslots) launch_carry_dvt<DVT>(p, a, dec, s);
   hipLaunchKernelGGL((bwd_dq_kernel<DVT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
                      a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv);

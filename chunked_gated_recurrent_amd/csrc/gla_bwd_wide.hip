@@ -333,51 +333,61 @@ __device__ __forceinline__ void wide_rev_role(
     bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow) {
   constexpr int C = kWC, DK = 96, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
   constexpr int NDT = MW::NDT, NCT = MW::NCT, NJS = MW::NJS, NKS = MW::NKS;
-  // loads: the dv role brings q and k (QV each), the dk role v and dO (VV each)
-  constexpr int NL = DV_ROLE ? QV : VV;
+  // loads, 9 vectors per role thread and register stage: the dv role brings
+  // q and k (3 each) and dO rows 0-31 (3), the dk role v (6) and dO rows
+  // 32-63 (3)
+  constexpr int NA = DV_ROLE ? QV : VV;  // q then k, or v
+  constexpr int NL = (DV_ROLE ? 2 * QV : VV) + 3;
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
   const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
   const unsigned rowKb = (unsigned)(H * DK * 2), rowVb = (unsigned)(H * kWideDv * 2);
   const int nch = (it.t1 - it.t0 + C - 1) / C;
   const int i_row = 16 * w + l16;
   const long long state_off = ((long long)it.n * H + h) * DK * kWideDv;
-  const TileIdx<NL> ix(rt, DV_ROLE ? MW::NQV : MW::NVV);
+  const TileIdx<NA> ia(rt, DV_ROLE ? MW::NQV : MW::NVV);
+  const TileIdx<3> idh(rt, MW::NVV);  // rows 0-31 of the dO tile
+  const int drow0 = DV_ROLE ? 0 : 32;
   auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
 
-  auto load = [&](int ch, u32x4(&r1)[NL], u32x4(&r2)[NL]) {
+  auto load = [&](int ch, u32x4(&r)[NL]) {
     const unsigned L = (unsigned)rows_of(ch);
     const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
+    const __amdgpu_buffer_rsrc_t bd = buf_rsrc(dout + (tb * H + h) * kWideDv, L * rowVb);
     if (DV_ROLE) {
       const __amdgpu_buffer_rsrc_t bq = buf_rsrc(q + (tb * H + h) * DK, L * rowKb);
       const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, L * rowKb);
 #pragma unroll
-      for (int m = 0; m < NL; ++m)
-        r1[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, ix.row[m] * rowKb + ix.col[m] * 16, 0, 0);
+      for (int m = 0; m < QV; ++m)
+        r[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
 #pragma unroll
-      for (int m = 0; m < NL; ++m)
-        r2[m] = __builtin_amdgcn_raw_buffer_load_b128(bk, ix.row[m] * rowKb + ix.col[m] * 16, 0, 0);
+      for (int m = 0; m < QV; ++m)
+        r[QV + m] = __builtin_amdgcn_raw_buffer_load_b128(bk, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t bv = buf_rsrc(v + (tb * H + h) * kWideDv, L * rowVb);
-      const __amdgpu_buffer_rsrc_t bd = buf_rsrc(dout + (tb * H + h) * kWideDv, L * rowVb);
 #pragma unroll
-      for (int m = 0; m < NL; ++m)
-        r1[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, ix.row[m] * rowVb + ix.col[m] * 16, 0, 0);
-#pragma unroll
-      for (int m = 0; m < NL; ++m)
-        r2[m] = __builtin_amdgcn_raw_buffer_load_b128(bd, ix.row[m] * rowVb + ix.col[m] * 16, 0, 0);
+      for (int m = 0; m < VV; ++m)
+        r[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, ia.row[m] * rowVb + ia.col[m] * 16, 0, 0);
     }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      r[NL - 3 + m] = __builtin_amdgcn_raw_buffer_load_b128(
+          bd, (drow0 + idh.row[m]) * rowVb + idh.col[m] * 16, 0, 0);
   };
-  auto store = [&](const u32x4(&r1)[NL], const u32x4(&r2)[NL]) {
+  auto store = [&](const u32x4(&r)[NL]) {
+    if (DV_ROLE) {
 #pragma unroll
-    for (int m = 0; m < NL; ++m) {
-      if (DV_ROLE) {
-        *reinterpret_cast<u32x4 *>(sQ + ix.row[m] * QS + 8 * ix.col[m]) = r1[m];
-        *reinterpret_cast<u32x4 *>(sK + ix.row[m] * QS + 8 * ix.col[m]) = r2[m];
-      } else {
-        *reinterpret_cast<u32x4 *>(sV + ix.row[m] * VS + 8 * ix.col[m]) = r1[m];
-        *reinterpret_cast<u32x4 *>(sD + ix.row[m] * VS + 8 * ix.col[m]) = r2[m];
+      for (int m = 0; m < QV; ++m) {
+        *reinterpret_cast<u32x4 *>(sQ + ia.row[m] * QS + 8 * ia.col[m]) = r[m];
+        *reinterpret_cast<u32x4 *>(sK + ia.row[m] * QS + 8 * ia.col[m]) = r[QV + m];
       }
+    } else {
+#pragma unroll
+      for (int m = 0; m < VV; ++m)
+        *reinterpret_cast<u32x4 *>(sV + ia.row[m] * VS + 8 * ia.col[m]) = r[m];
     }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      *reinterpret_cast<u32x4 *>(sD + (drow0 + idh.row[m]) * VS + 8 * idh.col[m]) = r[NL - 3 + m];
   };
 
   // this wave's 3 x 3 tiles of the carried gradient Ch: d tiles dt0.., column
@@ -415,9 +425,9 @@ __device__ __forceinline__ void wide_rev_role(
       }
   };
 
-  u32x4 a1[NL], a2[NL], b1[NL], b2[NL];
-  load(nch - 1, a1, a2);
-  load(nch - 2, b1, b2);
+  u32x4 ra[NL], rb[NL];
+  load(nch - 1, ra);
+  load(nch - 2, rb);
   __syncthreads();  // sPow ready
   // scores mask: scale * lambda^(t-i) for t >= i, else 0 (column i of this lane)
   float maskA[4][4];
@@ -437,15 +447,14 @@ __device__ __forceinline__ void wide_rev_role(
       fq[s][e] = scale * sPow[32 * s + 4 * g + e + 1];
       fq[s][4 + e] = scale * sPow[32 * s + 16 + 4 * g + e + 1];
     }
-  store(a1, a2);
+  store(ra);
   publish();
 
-  auto body = [&](int ch, u32x4(&n1)[NL], u32x4(&n2)[NL], const u32x4(&x1)[NL],
-                  const u32x4(&x2)[NL]) {
+  auto body = [&](int ch, u32x4(&rn)[NL], const u32x4(&rx)[NL]) {
     const int L = rows_of(ch);
     const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
     __syncthreads();  // A: chunk ch and Ch_in are in LDS
-    load(ch - 2, n1, n2);
+    load(ch - 2, rn);
     const float lam_rev = sPow[clampi(L - 1 - i_row, 0, C)];  // lambda^(L-1-i)
     if (DV_ROLE) {
       // scores A[t][i] = q_t . k_i (natural k-set over d)
@@ -589,12 +598,12 @@ __device__ __forceinline__ void wide_rev_role(
         for (int b = 0; b < 3; ++b) accC[a][b] = mfma(qa[a], dfr[b], accC[a][b]);
     }
     __syncthreads();  // B: every read of chunk ch and Ch_in is done
-    store(x1, x2);
+    store(rx);
     publish();
   };
   for (int p = 0; p < nch; p += 2) {  // a chunk before the first is all zeros
-    body(nch - 1 - p, a1, a2, b1, b2);
-    body(nch - 2 - p, b1, b2, a1, a2);
+    body(nch - 1 - p, ra, rb);
+    body(nch - 2 - p, rb, ra);
   }
   // after the first chunk Ch is dL/dS0 (an extra empty step leaves it as is:
   // lambda^0 = 1 and no rows)

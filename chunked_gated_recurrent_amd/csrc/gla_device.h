@@ -121,9 +121,10 @@ __device__ __forceinline__ void make_uniform(int &idx, Item &it) {
 //    dealt round-robin over the XCDs, so every XCD gets an equal share of
 //    every item. Used when units differ in length (packed sequences, a state
 //    pass that skips last segments).
-__device__ __forceinline__ void xcd_unit(const Plan &p, int ndt, int units,
-                                         int &unit, int &dtile) {
-  const int P = blockIdx.x;
+// (xcd_unit_at takes the workgroup id P explicitly: a launch that runs two
+// kind of work gives each its own id range starting at a multiple of 8.)
+__device__ __forceinline__ void xcd_unit_at(const Plan &p, int P, int ndt, int units,
+                                            int &unit, int &dtile) {
   const int xcd = P & 7;
   const int r = P >> 3;
   if (p.deal == 0) {
@@ -138,6 +139,11 @@ __device__ __forceinline__ void xcd_unit(const Plan &p, int ndt, int units,
     unit = (pr * 8 + xcd) * 2 + rem / ndt;
     dtile = rem - (rem / ndt) * ndt;
   }
+}
+
+__device__ __forceinline__ void xcd_unit(const Plan &p, int ndt, int units,
+                                         int &unit, int &dtile) {
+  xcd_unit_at(p, (int)blockIdx.x, ndt, units, unit, dtile);
 }
 
 // Workgroups xcd_unit needs to cover `units` units of `ndt` dv tiles.

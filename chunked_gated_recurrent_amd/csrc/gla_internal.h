@@ -106,9 +106,13 @@ hipError_t launch_rcombine(const Plan &p, const float *ds_final, float *cslots,
                            const Decay &dec, int H, int dk, int dv, hipStream_t s);
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
                            const Decay &dec, hipStream_t s);
-// time segments of the matrix-core backward: local carries + reverse combine
-hipError_t launch_bwd_carry(int dvt, const Plan &p, const BwdArgs &a,
-                            const Decay &dec, hipStream_t s);
+// time segments of the matrix-core backward: the forward's local end states
+// (slots) and the local carries (cslots) in one launch, then both scans
+hipError_t launch_bwd_boundary(int dvt, const Plan &p, const BwdArgs &a,
+                               const Decay &dec, hipStream_t s);
+hipError_t launch_bicombine(const Plan &p, const float *s0, float *slots,
+                            const float *ds_final, float *cslots, const Decay &dec, int H,
+                            int dk, int dv, hipStream_t s);
 // matrix-core backward with one workgroup per (item, head) over all of dv
 // (gla_bwd_wide.hip): dk 96, dv 192, no partial sums
 bool bwd_wide_ok(int dk, int dv);

@@ -400,6 +400,37 @@ __global__ __launch_bounds__(256) void rcombine_kernel(
                    (long long)h * per_state + e);
 }
 
+// Both scans of a segmented backward in one launch: workgroups [0, nb)
+// combine the forward states (as combine_kernel), the rest the carried
+// gradients in reverse (as rcombine_kernel).
+__global__ __launch_bounds__(256) void bicombine_kernel(
+    Plan p, const float *__restrict__ s0, float *__restrict__ slots,
+    const float *__restrict__ ds_final, float *__restrict__ cslots, Decay dec, int H,
+    int dk, int dv, int nb) {
+  const bool fwd = (int)blockIdx.x < nb;
+  const int b = fwd ? (int)blockIdx.x : (int)blockIdx.x - nb;
+  const int per_state = dk * dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const int unit = b / blocks_per;
+  const int part = b - unit * blocks_per;
+  const int n = unit / H, h = unit - (unit / H) * H;
+  if (n >= p.n_seq) return;
+  const int e = (part * 256 + threadIdx.x) * 4;
+  if (e >= per_state) return;
+  int first, last;
+  seq_items(p, n, first, last);
+  if (last - first < 2) return;
+  const float *init = fwd ? s0 : ds_final;
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (init) S = *reinterpret_cast<const float4 *>(init + ((long long)n * H + h) * per_state + e);
+  if (fwd)
+    scan_slots<false>(p, first, last, dec.lam[h], S, slots, (long long)H * per_state,
+                      (long long)h * per_state + e);
+  else
+    scan_slots<true>(p, first, last, dec.lam[h], S, cslots, (long long)H * per_state,
+                     (long long)h * per_state + e);
+}
+
 // s_final[n] <- slot of sequence n's last item (in-place final state with
 // segments: the last segment cannot write s_final while the first segment of
 // the same sequence may still be reading it as s0).
@@ -630,6 +661,17 @@ hipError_t launch_rcombine(const Plan &p, const float *ds_final, float *cslots,
   const unsigned grid = (unsigned)((long long)p.n_seq * H * blocks_per);
   hipLaunchKernelGGL(rcombine_kernel, dim3(grid), dim3(256), 0, s, p, ds_final,
                      cslots, dec, H, dk, dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_bicombine(const Plan &p, const float *s0, float *slots,
+                            const float *ds_final, float *cslots, const Decay &dec, int H,
+                            int dk, int dv, hipStream_t s) {
+  const int per_state = dk * dv;
+  const int blocks_per = (per_state / 4 + 255) / 256;
+  const int nb = p.n_seq * H * blocks_per;
+  hipLaunchKernelGGL(bicombine_kernel, dim3((unsigned)(2 * nb)), dim3(256), 0, s, p, s0,
+                     slots, ds_final, cslots, dec, H, dk, dv, nb);
   return hipGetLastError();
 }
 
