@@ -257,7 +257,7 @@ def bench_backward(steps, warmup, workload="laplace_prefill"):
             "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
             "roofline": dict(roofline(bytes_call, ev_ms),
-                             kernel="whole call (dq pass + dk/dv pass + partial sums)",
+                             kernel="whole call (segment boundaries + scans + dq pass + dk/dv pass)",
                              traffic=measured_traffic("whole call@" + name)),
             "workspace_bytes": need}
 
