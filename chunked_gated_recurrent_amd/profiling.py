@@ -103,7 +103,7 @@ SOURCE_GROUPS = {
     "forward": _COMMON + ["gla_kernels.hip", "gla_mfma.h", "gla_fwd_mfma.hip"],
     "decode": _COMMON + ["gla_kernels.hip"],
     "backward": _COMMON + ["gla_kernels.hip", "gla_mfma.h", "gla_fwd_mfma.hip",
-                           "gla_bwd_mfma.hip"],
+                           "gla_bwd_mfma.hip", "gla_bwd_wide.hip"],
     "conv": _COMMON + ["gla_conv.hip"],
 }
 
