@@ -10,17 +10,17 @@ inputs in the 256 MB last-level cache.
 
 The same JSON line also carries:
   roofline      the dominant kernel (the MFMA chunk kernel; HBM-bound):
-                algorithmic bytes per launch / mean launch duration from HIP
-                events recorded on the launch stream around every timed step;
+                algorithmic bytes per launch / mean launch duration from one
+                HIP event pair on the launch stream around the timed steps;
   cpu_baseline  the fp64 oracle timed on this host's cores on a bounded
                 sample of the same workload;
   secondary     long_context (B1 T65536), batched_decode (1,280 sequences,
                 100 consecutive steps) and varlen (32 packed sequences),
                 each with its own throughput and HBM roofline.
 
-The GPU reaches its steady clocks only after some tens of milliseconds of
-work, so the default warm-up (400 steps, about 30 ms) runs before the timed
-region.
+The GPU reaches its steady clocks only after a while under load, so every
+timed region follows the W warm-up steps (400 by default for the headline)
+and, if those took less, untimed steps up to at least 0.5 s of work.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--no-secondary] [--only {prefill,long,decode,decode_pool,varlen,backward,
@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 METRIC = "GLA fwd tokens/s (H16,dk96,dv192) + decode seq-steps/s; % MFMA / HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MIN_WARM_S = 0.5               # untimed work before every timed region, at least
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 H, DK, DV = 16, 96, 192
 # algorithmic bytes per token (all heads): q, k, v read once, o written once, bf16
@@ -65,6 +66,18 @@ def timed(fn, steps, warmup):
     import torch
     for i in range(warmup):
         fn(i)
+    # The W warm-up steps can be as short as a few tens of milliseconds; a GPU
+    # coming out of idle (e.g. after the process's own start-up) has been seen
+    # to need longer to reach its steady clocks, so keep warming (untimed)
+    # until at least MIN_WARM_S of the workload has run.
+    torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t_w < MIN_WARM_S:
+        for j in range(8):
+            fn(warmup + n + j)
+        n += 8
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
