@@ -228,7 +228,9 @@ def bench_decode_pool(warmup_runs=1, pool_pages=2048):
             "value": round(N * steps / wall, 1), "unit": "seq-steps/s",
             "ms_per_step": round(wall / steps * 1e3, 4),
             "roofline": dict(roofline(N * DECODE_BYTES_PER_SEQSTEP, ev_ms),
-                             kernel="decode_kernel<bf16,16> (slot table)")}
+                             kernel="decode_kernel<bf16,16> (slot table)",
+                             traffic=measured_traffic(
+                                 "decode_kernel<bf16,16> (slot table)@batched_decode_pool"))}
 
 
 BACKWARD_BYTES_PER_TOKEN = 16 * (96 + 96 + 192 + 192) * 2 + 16 * (96 + 96 + 192) * 2
