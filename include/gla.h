@@ -39,7 +39,7 @@
  *   - Environment: GLA_TARGET_WGS (default 256, one per compute unit) is the
  *     number of workgroups below which a call splits its sequences into time
  *     segments; it changes the workspace size, never the results beyond
- *     rounding. Set it before the process starts (it is read at every call).
+ *     rounding. It is read at every call.
  *   - Arguments are validated on the host before any HIP call. On an error
  *     nothing is launched and no output is touched. A launch failure returns
  *     GLA_ERR_HIP; faults inside kernels surface at the caller's next
