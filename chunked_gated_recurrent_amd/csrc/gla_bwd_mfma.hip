@@ -26,7 +26,10 @@
 // dq and dk contract over dv, so each dv tile yields a partial sum: fp32 rows
 // [dv tile][H][token][96] in the workspace (each lane stores the 4
 // consecutive dk values of one token that it holds), which a streaming
-// kernel adds up into bf16 dq and dk.
+// kernel adds up into bf16 dq and dk. (dv = 192 takes the workgroup-per-head
+// kernels of gla_bwd_wide.hip instead; this file also holds the boundary
+// pass that gives time segments their incoming states and carries, used by
+// both.)
 #include "gla_mfma.h"
 
 namespace gla {

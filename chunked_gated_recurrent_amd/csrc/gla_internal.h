@@ -1,5 +1,6 @@
 // gla_internal.h -- types shared by the host dispatch (gla_api.cpp) and the
-// HIP kernels (gla_kernels.hip). Not part of the public ABI.
+// HIP kernels (gla_*.hip), and the launchers the dispatch calls. Not part of
+// the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
