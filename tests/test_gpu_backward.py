@@ -72,6 +72,17 @@ def test_backward_widest_value_head():
     _check("bwd dv256", _run(x, do, dsf), _oracle(x, do, dsf))
 
 
+def test_backward_max_heads_with_lambda_one():
+    """64 heads, one of them without decay."""
+    H = 64
+    lam = np.concatenate([[1.0], W.geometric_decays(H - 1)]).astype(np.float32)
+    x = W.prefill_inputs(706, 1, 90, H, 96, 192, "bf16", 0.1, lam)
+    rng = np.random.default_rng(1706)
+    do = W.bf16_bits(rng.standard_normal((1, 90, H, 192), dtype=np.float32))
+    dsf = rng.standard_normal((1, H, 96, 192), dtype=np.float32) * np.float32(0.5)
+    _check("bwd H64", _run(x, do, dsf), _oracle(x, do, dsf))
+
+
 def test_backward_without_initial_state_or_final_gradient():
     x, do, dsf = _inputs(710, 2, 150, 4, 192, with_s0=False, with_dsf=False)
     _check("bwd no s0 / dS_final", _run(x, do, dsf), _oracle(x, do, dsf))

@@ -191,3 +191,8 @@ def test_packed_sequences(dtype, dk, dv, lengths):
             np.testing.assert_array_equal(zf[n], z0[n])
     print("packed %s %s: o %.2e  S %.2e  z %.2e" % ((dtype, lengths) + tuple(worst)))
     assert max(worst) <= TOL[dtype], worst
+
+
+def test_max_heads():
+    q, k, v = _case(1060, 1, 90, 64, 96, 192, "bf16")
+    _check("bf16", _run(q, k, v), O.linear_attention(q, k, v), "H64")
