@@ -291,6 +291,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
   p.deal = p.mode == kPlanFixed ? 0 : 1;
   a.part_dq = (float *)(ws + bp.off_part);
   a.part_dk = (float *)(ws + bp.off_part + bp.part_bytes);
+  bool pair = false;
   if (hp.segmented) {
     // the segments' incoming forward states (the forward's state pass and
     // combine) and, on the matrix cores, their incoming carried gradients
@@ -301,8 +302,10 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     if (hp.fast) {
       if (launch_bwd_boundary(fast_dv_tile(a.dv), p, a, dec, s) != hipSuccess)
         return GLA_ERR_HIP;
-      if (launch_bicombine(p, a.s0, a.slots, a.ds_final, a.cslots, dec, a.H, a.dk_dim, a.dv,
-                           s) != hipSuccess)
+      // two segments per sequence: the wide kernels join them on load
+      pair = bp.wide && p.mode == kPlanFixed && p.G == 2;
+      if (!pair && launch_bicombine(p, a.s0, a.slots, a.ds_final, a.cslots, dec, a.H,
+                                    a.dk_dim, a.dv, s) != hipSuccess)
         return GLA_ERR_HIP;
     } else {
       FwdArgs f;
@@ -317,7 +320,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
   }
   hipError_t e;
   if (bp.wide)
-    e = launch_bwd_wide(p, a, dec, s);
+    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, s);
   else
     e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
   if (e != hipSuccess) return GLA_ERR_HIP;

@@ -170,10 +170,14 @@ __device__ __forceinline__ void wide_dq_role(
   }
 }
 
+// With `pair` set (every sequence is cut into exactly two segments and the
+// slots hold the raw local quantities, not yet scanned), the incoming value
+// of the second segment is formed here: U_0 + lambda^len0 S0.
 __device__ __forceinline__ void wide_state_role(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const float *__restrict__ s0,
     const float *__restrict__ slots, const Item &it, int idx, int h, int H, int rt, int w,
-    bf16 *sK, bf16 *sKs, bf16 *sV, bf16 *sSt, const float *sPow) {
+    bf16 *sK, bf16 *sKs, bf16 *sV, bf16 *sSt, const float *sPow, const float *pair_add,
+    float pair_scale) {
   constexpr int C = kWC, DK = 96, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
   constexpr int SDT = MW::SDT, SCT = MW::SCT, NJS = MW::NJS;
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
@@ -194,11 +198,16 @@ __device__ __forceinline__ void wide_state_role(
 #pragma unroll
       for (int b = 0; b < SCT; ++b) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        const int d = 16 * (dt0 + a) + 4 * g;
+        const int c = 16 * (ct0 + b) + l16;
         if (src) {
-          const int d = 16 * (dt0 + a) + 4 * g;
-          const int c = 16 * (ct0 + b) + l16;
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[r] = src[(long long)(d + r) * kWideDv + c];
+        }
+        if (pair_add) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[r] = fmaf(pair_scale, pair_add[(long long)(d + r) * kWideDv + c], x[r]);
         }
         accS[a][b] = x;
       }
@@ -294,7 +303,7 @@ __device__ __forceinline__ void wide_state_role(
 __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
     const float *__restrict__ s0, const float *__restrict__ slots, bf16 *__restrict__ dq,
-    Plan plan, Decay dec, float scale, int H) {
+    Plan plan, Decay dec, float scale, int H, int pair) {
   __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sKs[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sV[kWC * kWVS];
@@ -314,11 +323,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
   const int tid = threadIdx.x;
   if (tid <= kWC) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (role_wave < 4)
+  if (role_wave < 4) {
     wide_dq_role(dout, dq, it, h, H, scale, tid & 255, role_wave, sD, sK, sV, sSt, sPow);
-  else
+  } else {
+    const float *pair_add = nullptr;
+    float pair_scale = 0.f;
+    if (pair && !(it.flags & kFirstSeg) && s0) {  // second of two segments
+      Item prev;
+      load_item(plan, idx - 1, prev);
+      pair_add = s0 + ((long long)it.n * H + h) * 96 * kWideDv;
+      pair_scale = pow_f64(dec.lam[h], prev.t1 - prev.t0);
+    }
     wide_state_role(k, v, s0, slots, it, idx, h, H, tid & 255, role_wave - 4, sK, sKs, sV,
-                    sSt, sPow);
+                    sSt, sPow, pair_add, pair_scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -330,7 +348,8 @@ __device__ __forceinline__ void wide_rev_role(
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ out, float *__restrict__ ds0,
     const Item &it, int idx, int h, int H, float scale, int rt, int w, bf16 *sQ, bf16 *sK,
-    bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow) {
+    bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow, const float *pair_add,
+    float pair_scale) {
   constexpr int C = kWC, DK = 96, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
   constexpr int NDT = MW::NDT, NCT = MW::NCT, NJS = MW::NJS, NKS = MW::NKS;
   // loads, 9 vectors per role thread and register stage: the dv role brings
@@ -404,11 +423,16 @@ __device__ __forceinline__ void wide_rev_role(
 #pragma unroll
     for (int b = 0; b < 3; ++b) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      const int d = 16 * (dt0 + a) + 4 * g;
+      const int c = 16 * (ct0 + b) + l16;
       if (cin) {
-        const int d = 16 * (dt0 + a) + 4 * g;
-        const int c = 16 * (ct0 + b) + l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = cin[(long long)(d + r) * kWideDv + c];
+      }
+      if (pair_add) {  // first of two segments: U'_1 + lambda^len1 dL/dS_final
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[r] = fmaf(pair_scale, pair_add[(long long)(d + r) * kWideDv + c], x[r]);
       }
       accC[a][b] = x;
     }
@@ -624,7 +648,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
-    float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H) {
+    float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H, int pair) {
   __shared__ __attribute__((aligned(16))) bf16 sQ[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sV[kWC * kWVS];
@@ -644,25 +668,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
   const int tid = threadIdx.x;
   if (tid <= kWC) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const float *pair_add = nullptr;
+  float pair_scale = 0.f;
+  if (pair && !(it.flags & kLastSeg) && ds_final) {  // first of two segments
+    Item next;
+    load_item(plan, idx + 1, next);
+    pair_add = ds_final + ((long long)it.n * H + h) * 96 * kWideDv;
+    pair_scale = pow_f64(dec.lam[h], next.t1 - next.t0);
+  }
   if (wave < 4)
     wide_rev_role<true>(q, k, v, dout, ds_final, cslots, dv_out, ds0, it, idx, h, H, scale,
-                        tid & 255, wave, sQ, sK, sV, sD, sCt, sPow);
+                        tid & 255, wave, sQ, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
   else
     wide_rev_role<false>(q, k, v, dout, ds_final, cslots, dk_out, ds0, it, idx, h, H, scale,
-                         tid & 255, wave - 4, sQ, sK, sV, sD, sCt, sPow);
+                         tid & 255, wave - 4, sQ, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
 }
 
 bool bwd_wide_ok(int dk, int dv) { return dk == 96 && dv == kWideDv; }
 
-hipError_t launch_bwd_wide(const Plan &p, const BwdArgs &a, const Decay &dec,
+// pair: the segment slots hold unscanned local quantities and every sequence
+// has exactly two segments (the kernels join them on load).
+hipError_t launch_bwd_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, 1);
   hipLaunchKernelGGL(bwd_dq_wide_kernel, dim3(grid), dim3(512), 0, s, (const bf16 *)a.k,
                      (const bf16 *)a.v, (const bf16 *)a.dout, a.s0, a.slots, (bf16 *)a.dq, p,
-                     dec, a.scale, a.H);
+                     dec, a.scale, a.H, pair);
   hipLaunchKernelGGL(bwd_dkdv_wide_kernel, dim3(grid), dim3(512), 0, s, (const bf16 *)a.q,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.ds_final,
-                     a.cslots, (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H);
+                     a.cslots, (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H,
+                     pair);
   return hipGetLastError();
 }
 

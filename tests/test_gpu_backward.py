@@ -72,6 +72,16 @@ def test_backward_widest_value_head():
     _check("bwd dv256", _run(x, do, dsf), _oracle(x, do, dsf))
 
 
+def test_backward_two_segments_joined_on_load():
+    """8 x 16 units of 256 tokens: two time segments per sequence, whose
+    local states and carries the wide kernels join with S0 and dL/dS_final
+    as they load them (no scan launch)."""
+    x, do, dsf = _inputs(707, 8, 256, 16, 192)
+    need = gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 16, 96, 192, 0)
+    assert need == 2 * (8 * 2 * 16 * 96 * 192 * 4)  # two segments' states and carries
+    _check("bwd two segments", _run(x, do, dsf), _oracle(x, do, dsf))
+
+
 def test_backward_max_heads_with_lambda_one():
     """64 heads, one of them without decay."""
     H = 64
