@@ -196,3 +196,17 @@ def test_packed_sequences(dtype, dk, dv, lengths):
 def test_max_heads():
     q, k, v = _case(1060, 1, 90, 64, 96, 192, "bf16")
     _check("bf16", _run(q, k, v), O.linear_attention(q, k, v), "H64")
+
+
+def test_packed_all_empty_copies_the_sums():
+    N, H, dk, dv = 3, 2, 96, 192
+    rng = np.random.default_rng(1070)
+    s0 = rng.standard_normal((N, H, dk, dv)).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((N, H, dk))).astype(np.float32)
+    e = torch.empty((0, H, dk), dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty((0, H, dv), dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    o, sf, zf = gla.linear_attn_fwd_varlen(e, e, ev, cu, dev(s0), dev(z0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(sf), s0)
+    np.testing.assert_array_equal(host(zf), z0)
