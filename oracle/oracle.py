@@ -60,7 +60,7 @@ def _load():
 
 def default_threads() -> int:
     """Threads for the oracle: OMP_NUM_THREADS when set, else the visible
-    cores capped at 16 (a GPU machine's CPU share)."""
+    cores capped at 16."""
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit() and int(env) > 0:
         return int(env)
