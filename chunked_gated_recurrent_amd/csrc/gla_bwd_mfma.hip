@@ -293,6 +293,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int m = 0; m < VV; ++m)
         r2[m] = __builtin_amdgcn_raw_buffer_load_b128(bd, rowB[m] * rowVb + colB[m] * 16, 0, 0);
+      // define the slots this role leaves unused (d_v tiles narrower than
+      // d_k), so that both roles fill every register of the stage arrays
+#pragma unroll
+      for (int m = VV; m < QV; ++m) r1[m] = r2[m] = (u32x4){0u, 0u, 0u, 0u};
     }
   };
   auto store = [&](int buf, const u32x4(&r1)[QV], const u32x4(&r2)[VV > QV ? VV : QV]) {
@@ -476,26 +480,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         __builtin_amdgcn_raw_buffer_store_b128(val, bo, (16 * w + row) * rowVb + col * 16, 0, 0);
       }
     } else {
-      // scores Bm[t][i] = dO_t . v_i over this dv tile (P k-set over c)
-      bf16x8 vf[NCS];
-#pragma unroll
-      for (int s = 0; s < NCS; ++s) {
-        const bf16 *row = cV + i_row * VS + 32 * s;
-        vf[s] = cat8(*reinterpret_cast<const bf16x4 *>(row + 4 * g),
-                     *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * g));
-      }
+      // scores Bm[t][i] = dO_t . v_i over this dv tile (natural k-set over
+      // c: both operands are 16-byte row reads)
       f32x4 sc[4];
 #pragma unroll
       for (int T = 0; T < 4; ++T) sc[T] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NCS; ++s)
+      for (int s = 0; s < NCS; ++s) {
+        const bf16x8 vn = *reinterpret_cast<const bf16x8 *>(cV + i_row * VS + 32 * s + 8 * g);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
-          const bf16 *row = cD + (16 * T + l16) * VS + 32 * s;
-          const bf16x8 df = cat8(*reinterpret_cast<const bf16x4 *>(row + 4 * g),
-                                 *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * g));
-          sc[T] = mfma(df, vf[s], sc[T]);
+          const bf16x8 df =
+              *reinterpret_cast<const bf16x8 *>(cD + (16 * T + l16) * VS + 32 * s + 8 * g);
+          sc[T] = mfma(df, vn, sc[T]);
         }
+      }
       bf16x8 bm[NJS];
 #pragma unroll
       for (int s = 0; s < NJS; ++s)
@@ -509,12 +508,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NCS; ++s)
+      for (int s = 0; s < NCS; ++s) {
+        // v_i in the P k-set over c, matching the transposed reads of Ch
+        const bf16 *vrow = cV + i_row * VS + 32 * s;
+        const bf16x8 vf = cat8(*reinterpret_cast<const bf16x4 *>(vrow + 4 * g),
+                               *reinterpret_cast<const bf16x4 *>(vrow + 16 + 4 * g));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const bf16 *base = ct_in + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
-          acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), vf[s], acc[dt]);
+          acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), vf, acc[dt]);
         }
+      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] *= lam_rev;
 #pragma unroll

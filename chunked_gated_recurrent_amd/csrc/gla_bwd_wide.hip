@@ -38,6 +38,13 @@ static_assert(kWC * kWQS * 2 * 2 + kWC * kWVS * 2 * 2 + kWideDv * kWQS * 2 + 4 *
                   160 * 1024,
               "LDS budget of the wide backward");
 
+// The state S^T published by the dq pass's state waves keeps its 8-column
+// blocks XOR-swizzled by bit 3 of the row: element (c, d) sits at
+// c * QS + (d ^ (c & 8)). Its only readers are transposing reads of aligned
+// 4-column groups, which the swizzle keeps whole; it halves the LDS bank
+// conflicts of the publish (16 rows written at one column offset).
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ (r & 8); }
+
 // One tile load pattern: `n` 16-byte vectors per role thread over a chunk
 // tile of `per_row` vectors per row.
 template <int N>
@@ -138,7 +145,8 @@ __device__ __forceinline__ void wide_dq_role(
     for (int s = 0; s < kWNCS; ++s)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16 *base = sSt + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
+        const int row = 32 * s + 4 * g + tr_row;  // row + 16 has the same bit 3
+        const bf16 *base = sSt + row * QS + swz8(row, 16 * dt + tr_col);
         acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), dfp[s], acc[dt]);
       }
 #pragma unroll
@@ -250,7 +258,7 @@ __device__ __forceinline__ void wide_state_role(
 #pragma unroll
         for (int r = 0; r < 4; ++r) t[r] = (bf16)accS[a][b][r];
         const int c = 16 * (ct0 + b) + l16;
-        *reinterpret_cast<bf16x4 *>(sSt + c * QS + 16 * (dt0 + a) + 4 * g) = t;
+        *reinterpret_cast<bf16x4 *>(sSt + c * QS + swz8(c, 16 * (dt0 + a) + 4 * g)) = t;
       }
   };
 
@@ -535,26 +543,21 @@ __device__ __forceinline__ void wide_rev_role(
         }
       }
     } else {
-      // scores Bm[t][i] = dO_t . v_i over dv (P k-set over c)
-      bf16x8 vf[kWNCS];
-#pragma unroll
-      for (int s = 0; s < kWNCS; ++s) {
-        const bf16 *row = sV + i_row * VS + 32 * s;
-        vf[s] = cat8(*reinterpret_cast<const bf16x4 *>(row + 4 * g),
-                     *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * g));
-      }
+      // scores Bm[t][i] = dO_t . v_i over dv (natural k-set over c: both
+      // operands are 16-byte row reads)
       f32x4 sc[4];
 #pragma unroll
       for (int T = 0; T < 4; ++T) sc[T] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < kWNCS; ++s)
+      for (int s = 0; s < kWNCS; ++s) {
+        const bf16x8 vn = *reinterpret_cast<const bf16x8 *>(sV + i_row * VS + 32 * s + 8 * g);
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
-          const bf16 *row = sD + (16 * T + l16) * VS + 32 * s;
-          const bf16x8 df = cat8(*reinterpret_cast<const bf16x4 *>(row + 4 * g),
-                                 *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * g));
-          sc[T] = mfma(df, vf[s], sc[T]);
+          const bf16x8 df =
+              *reinterpret_cast<const bf16x8 *>(sD + (16 * T + l16) * VS + 32 * s + 8 * g);
+          sc[T] = mfma(df, vn, sc[T]);
         }
+      }
       bf16x8 bm[NJS];
 #pragma unroll
       for (int s = 0; s < NJS; ++s)
@@ -568,12 +571,17 @@ __device__ __forceinline__ void wide_rev_role(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < kWNCS; ++s)
+      for (int s = 0; s < kWNCS; ++s) {
+        // v_i in the P k-set over c, matching the transposed reads of Ch
+        const bf16 *vrow = sV + i_row * VS + 32 * s;
+        const bf16x8 vf = cat8(*reinterpret_cast<const bf16x4 *>(vrow + 4 * g),
+                               *reinterpret_cast<const bf16x4 *>(vrow + 16 + 4 * g));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const bf16 *base = sCt + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
-          acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), vf[s], acc[dt]);
+          acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), vf, acc[dt]);
         }
+      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] *= lam_rev;
 #pragma unroll
