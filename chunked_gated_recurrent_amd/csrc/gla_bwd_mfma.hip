@@ -108,10 +108,9 @@ __device__ __forceinline__ void dq_role(
     bf16x8 dfn[NCS], dfp[NCS];
 #pragma unroll
     for (int s = 0; s < NCS; ++s) {
-      const bf16 *row = cD + i_row * VS + 32 * s;
-      dfn[s] = *reinterpret_cast<const bf16x8 *>(row + 8 * g);
-      dfp[s] = cat8(*reinterpret_cast<const bf16x4 *>(row + 4 * g),
-                    *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * g));
+      const int row = i_row * VS + 32 * s;
+      dfn[s] = *reinterpret_cast<const bf16x8 *>(cD + row + 8 * g);
+      dfp[s] = cat8(lds8_apart(cD, row + 4 * g), lds8_apart(cD, row + 16 + 4 * g));
     }
     // P'^T[j][i] = v_j . dO_i over the tile, for j blocks 0..3
     f32x4 p[4];
@@ -510,9 +509,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int s = 0; s < NCS; ++s) {
         // v_i in the P k-set over c, matching the transposed reads of Ch
-        const bf16 *vrow = cV + i_row * VS + 32 * s;
-        const bf16x8 vf = cat8(*reinterpret_cast<const bf16x4 *>(vrow + 4 * g),
-                               *reinterpret_cast<const bf16x4 *>(vrow + 16 + 4 * g));
+        const int vrow = i_row * VS + 32 * s;
+        const bf16x8 vf = cat8(lds8_apart(cV, vrow + 4 * g), lds8_apart(cV, vrow + 16 + 4 * g));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const bf16 *base = ct_in + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;

@@ -113,10 +113,9 @@ __device__ __forceinline__ void wide_dq_role(
     bf16x8 dfn[kWNCS], dfp[kWNCS];  // dO row i: natural and P k-sets over dv
 #pragma unroll
     for (int s = 0; s < kWNCS; ++s) {
-      const bf16 *row = sD + i_row * VS + 32 * s;
-      dfn[s] = *reinterpret_cast<const bf16x8 *>(row + 8 * g);
-      dfp[s] = cat8(*reinterpret_cast<const bf16x4 *>(row + 4 * g),
-                    *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * g));
+      const int row = i_row * VS + 32 * s;
+      dfn[s] = *reinterpret_cast<const bf16x8 *>(sD + row + 8 * g);
+      dfp[s] = cat8(lds8_apart(sD, row + 4 * g), lds8_apart(sD, row + 16 + 4 * g));
     }
     // P'^T[j][i] = v_j . dO_i over all of dv, j blocks 0..3
     f32x4 p[4];
@@ -573,9 +572,8 @@ __device__ __forceinline__ void wide_rev_role(
 #pragma unroll
       for (int s = 0; s < kWNCS; ++s) {
         // v_i in the P k-set over c, matching the transposed reads of Ch
-        const bf16 *vrow = sV + i_row * VS + 32 * s;
-        const bf16x8 vf = cat8(*reinterpret_cast<const bf16x4 *>(vrow + 4 * g),
-                               *reinterpret_cast<const bf16x4 *>(vrow + 16 + 4 * g));
+        const int vrow = i_row * VS + 32 * s;
+        const bf16x8 vf = cat8(lds8_apart(sV, vrow + 4 * g), lds8_apart(sV, vrow + 16 + 4 * g));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const bf16 *base = sCt + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;

@@ -48,6 +48,16 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Eight bytes of an LDS tile at element offset `off`. The offset is hidden
+// from the compiler so that neighbouring reads of the same row are not fused
+// into one two-address read (ds_read2_b64): for 16 rows at one column
+// offset, that form conflicts many times more on gfx950 LDS than two plain
+// 8-byte reads.
+__device__ __forceinline__ bf16x4 lds8_apart(const bf16 *tile, int off) {
+  asm("" : "+v"(off));
+  return *reinterpret_cast<const bf16x4 *>(tile + off);
+}
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
