@@ -34,7 +34,7 @@ constexpr int kWideDv = 192;
 using MW = MfCfg<kWideDv>;  // C 64, DK 96, QS 112, VS 208, NCT 12, NDT 6
 constexpr int kWC = MW::C, kWQS = MW::QS, kWVS = MW::VS;
 constexpr int kWNCS = kWideDv / 32;  // 32-deep steps over dv
-static_assert(kWC * kWQS * 2 * 2 + kWC * kWVS * 2 * 2 + kWideDv * kWQS * 2 + 4 * (kWC + 4) <=
+static_assert(kWC * kWQS * 2 * 3 + kWC * kWVS * 2 * 2 + kWideDv * kWQS * 2 + 4 * (kWC + 4) <=
                   160 * 1024,
               "LDS budget of the wide backward");
 
@@ -354,7 +354,8 @@ __device__ __forceinline__ void wide_rev_role(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ out, float *__restrict__ ds0,
-    const Item &it, int idx, int h, int H, float scale, int rt, int w, bf16 *sQ, bf16 *sK,
+    const Item &it, int idx, int h, int H, float scale, int rt, int w, bf16 *sQ, bf16 *sQs,
+    bf16 *sK,
     bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow, const float *pair_add,
     float pair_scale) {
   constexpr int C = kWC, DK = 96, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
@@ -399,12 +400,19 @@ __device__ __forceinline__ void wide_rev_role(
       r[NL - 3 + m] = __builtin_amdgcn_raw_buffer_load_b128(
           bd, (drow0 + idh.row[m]) * rowVb + idh.col[m] * 16, 0, 0);
   };
+  float fqr[NA];  // dv role: scale * lambda^(t+1) of the q rows this thread stores
   auto store = [&](const u32x4(&r)[NL]) {
     if (DV_ROLE) {
 #pragma unroll
       for (int m = 0; m < QV; ++m) {
         *reinterpret_cast<u32x4 *>(sQ + ia.row[m] * QS + 8 * ia.col[m]) = r[m];
         *reinterpret_cast<u32x4 *>(sK + ia.row[m] * QS + 8 * ia.col[m]) = r[QV + m];
+        // the carry's decay-scaled copy of q, made once per chunk
+        const bf16x8 qv = __builtin_bit_cast(bf16x8, r[m]);
+        bf16x8 qs;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)qv[e] * fqr[m]);
+        *reinterpret_cast<bf16x8 *>(sQs + ia.row[m] * QS + 8 * ia.col[m]) = qs;
       }
     } else {
 #pragma unroll
@@ -469,15 +477,8 @@ __device__ __forceinline__ void wide_rev_role(
       const int diff = (16 * T + 4 * g + r) - i_row;
       maskA[T][r] = diff >= 0 ? scale * sPow[max(diff, 0)] : 0.f;
     }
-  // carry scaling of q_t: scale * lambda^(t+1) for this lane's P k-set rows t
-  float fq[NJS][8];
 #pragma unroll
-  for (int s = 0; s < NJS; ++s)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      fq[s][e] = scale * sPow[32 * s + 4 * g + e + 1];
-      fq[s][4 + e] = scale * sPow[32 * s + 16 + 4 * g + e + 1];
-    }
+  for (int m = 0; m < NA; ++m) fqr[m] = DV_ROLE ? scale * sPow[ia.row[m] + 1] : 0.f;
   store(ra);
   publish();
 
@@ -608,14 +609,12 @@ __device__ __forceinline__ void wide_rev_role(
       for (int b = 0; b < 3; ++b) accC[a][b] *= lamL;
 #pragma unroll
     for (int s = 0; s < NJS; ++s) {
-      bf16x8 qa[3], dfr[3];
+      bf16x8 qa[3], dfr[3];  // scale lambda^(t+1) q_t (P k-set over t) and dO
       const int row = 32 * s + 4 * g + tr_row;
 #pragma unroll
       for (int a = 0; a < 3; ++a) {
-        const bf16 *base = sQ + row * QS + 16 * (dt0 + a) + tr_col;
-        const bf16x8 raw = cat8(tr4(base), tr4(base + 16 * QS));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qa[a][e] = (bf16)((float)raw[e] * fq[s][e]);
+        const bf16 *base = sQs + row * QS + 16 * (dt0 + a) + tr_col;
+        qa[a] = cat8(tr4(base), tr4(base + 16 * QS));
       }
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
@@ -656,6 +655,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
     const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
     float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H, int pair) {
   __shared__ __attribute__((aligned(16))) bf16 sQ[kWC * kWQS];
+  __shared__ __attribute__((aligned(16))) bf16 sQs[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sV[kWC * kWVS];
   __shared__ __attribute__((aligned(16))) bf16 sD[kWC * kWVS];
@@ -684,10 +684,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
   }
   if (wave < 4)
     wide_rev_role<true>(q, k, v, dout, ds_final, cslots, dv_out, ds0, it, idx, h, H, scale,
-                        tid & 255, wave, sQ, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
+                        tid & 255, wave, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
   else
     wide_rev_role<false>(q, k, v, dout, ds_final, cslots, dk_out, ds0, it, idx, h, H, scale,
-                         tid & 255, wave - 4, sQ, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
+                         tid & 255, wave - 4, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
 }
 
 bool bwd_wide_ok(int dk, int dv) { return dk == 96 && dv == kWideDv; }
