@@ -59,7 +59,7 @@ def _check(name, got, ref):
 
 
 @pytest.mark.parametrize("T", [1, 17, 64, 65, 130, 200])
-@pytest.mark.parametrize("dv", [192, 128])
+@pytest.mark.parametrize("dv", [192, 128, 64])
 def test_backward_ragged_lengths(T, dv):
     x, do, dsf = _inputs(700 + T, 2, T, 3, dv)
     _check("bwd T%d dv%d" % (T, dv), _run(x, do, dsf), _oracle(x, do, dsf))
