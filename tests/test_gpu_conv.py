@@ -67,24 +67,27 @@ def test_short_conv_decode_steps_continue_the_prefill(dtype):
     np.testing.assert_array_equal(host(wo), rwo)
 
 
-def test_short_conv_decode_full_size_sampled():
-    """One decode step for 1,280 sequences x 3,072 channels (the decode
-    workload's width): every 7th sequence against the oracle; the window is
-    shifted exactly."""
-    N, D = 1280, 3072
-    rng = np.random.default_rng(830)
-    x = W.bf16_bits(rng.standard_normal((N, D), dtype=np.float32))
+@pytest.mark.parametrize("dtype,N", [("bf16", 1280), ("f32", 1280), ("bf16", 700)])
+def test_short_conv_decode_full_size(dtype, N):
+    """One decode step at the decode workload's width (3,072 channels) for
+    1,280 sequences and a ragged 700: every sequence against the oracle
+    (each thread walks several sequences of one channel group, so every row
+    is checked), and the window is shifted exactly."""
+    D = 3072
+    rng = np.random.default_rng(830 + N)
+    x = rng.standard_normal((N, D), dtype=np.float32)
+    if dtype == "bf16":
+        x = W.bf16_bits(x)
     w = (rng.standard_normal((D, 4)) * 0.5).astype(np.float32)
     b = (rng.standard_normal(D) * 0.1).astype(np.float32)
     win = rng.standard_normal((N, 4, D)).astype(np.float32)
     wd = _t(win)
     y = gla.short_conv_decode_step(dev(x), _t(w), _t(b), wd)
     torch.cuda.synchronize()
-    sel = slice(0, N, 7)
-    rw = win[sel].astype(np.float64)
-    ry = O.short_conv_decode(x[sel], w, b, rw)
-    assert rel_err(host(y)[sel], ry) <= TOL["bf16"]
-    np.testing.assert_array_equal(host(wd)[sel], rw)
+    rw = win.astype(np.float64)
+    ry = O.short_conv_decode(x, w, b, rw)
+    assert rel_err(host(y), ry) <= TOL[dtype]
+    np.testing.assert_array_equal(host(wd), rw)
 
 
 def test_short_conv_causality_and_determinism():
