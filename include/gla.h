@@ -35,7 +35,9 @@
  *     chunks for 0, 64 and 128, and 32-token chunks (on the vector ALUs) for
  *     32.
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
- *     enqueued on it; no call synchronises.
+ *     enqueued on it as kernel launches; no call synchronises, allocates or
+ *     records a memset, so a sequence of calls may be captured into a HIP
+ *     graph and replayed (the decay values and sizes are fixed at capture).
  *   - Environment: GLA_TARGET_WGS (default 256, one per compute unit) is the
  *     number of workgroups below which a call splits its sequences into time
  *     segments; it changes the workspace size, never the results beyond
