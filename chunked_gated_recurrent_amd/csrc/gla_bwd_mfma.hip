@@ -603,10 +603,17 @@ __device__ __forceinline__ void carry_role(
     for (int m = 0; m < VV; ++m)
       rd[m] = __builtin_amdgcn_raw_buffer_load_b128(bd, rowB[m] * rowVb + colB[m] * 16, 0, 0);
   };
+  // q enters the carry only as scale * lambda^(t+1) q_t: it is stored scaled
+  float fqr[QV];
   auto store = [&](int buf, const u32x4(&rq)[QV], const u32x4(&rd)[VV]) {
 #pragma unroll
-    for (int m = 0; m < QV; ++m)
-      *reinterpret_cast<u32x4 *>(sQ + buf * KBUF + rowA[m] * QS + 8 * colA[m]) = rq[m];
+    for (int m = 0; m < QV; ++m) {
+      const bf16x8 qv = __builtin_bit_cast(bf16x8, rq[m]);
+      bf16x8 qs;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)qv[e] * fqr[m]);
+      *reinterpret_cast<bf16x8 *>(sQ + buf * KBUF + rowA[m] * QS + 8 * colA[m]) = qs;
+    }
 #pragma unroll
     for (int m = 0; m < VV; ++m)
       *reinterpret_cast<u32x4 *>(sD + buf * VBUF + rowB[m] * VS + 8 * colB[m]) = rd[m];
@@ -621,14 +628,8 @@ __device__ __forceinline__ void carry_role(
   load(nch - 1, qa_, da_);
   load(nch - 2, qb_, db_);
   __syncthreads();  // sPow ready
-  float fq[NJS][8];
 #pragma unroll
-  for (int s = 0; s < NJS; ++s)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      fq[s][e] = scale * sPow[32 * s + 4 * g + e + 1];
-      fq[s][4 + e] = scale * sPow[32 * s + 16 + 4 * g + e + 1];
-    }
+  for (int m = 0; m < QV; ++m) fqr[m] = scale * sPow[rowA[m] + 1];
   store((nch - 1) & 1, qa_, da_);
 
   auto body = [&](int ch, u32x4(&nq)[QV], u32x4(&nd)[VV], const u32x4(&xq)[QV],
@@ -651,9 +652,7 @@ __device__ __forceinline__ void carry_role(
 #pragma unroll
       for (int a = 0; a < SDT; ++a) {
         const bf16 *base = cQ + row * QS + 16 * (dt0 + a) + tr_col;
-        const bf16x8 raw = cat8(tr4(base), tr4(base + 16 * QS));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qs[a][e] = (bf16)((float)raw[e] * fq[s][e]);
+        qs[a] = cat8(tr4(base), tr4(base + 16 * QS));
       }
 #pragma unroll
       for (int b = 0; b < SCT; ++b) {

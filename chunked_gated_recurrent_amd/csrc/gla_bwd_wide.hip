@@ -7,11 +7,12 @@
 // contract over dv split into two tiles and leave fp32 partial rows for a
 // third pass to add (about 0.8 GB of extra traffic at the Laplace batch);
 // here a workgroup holds the whole dv, so dq and dk come out complete and
-// go straight to their bf16 rows. The price is LDS: the tiles of a chunk,
-// 124,928 bytes, fit only once, so every chunk takes two barriers (tiles
-// and published state ready / all reads done) instead of double buffers,
-// and the batch's parallelism comes from time segments (the planner splits
-// sequences when batch x heads cannot fill the GPU).
+// go straight to their bf16 rows. The price is LDS: the tiles of a chunk
+// (125 KB in the dq pass, 140 KB in the reverse walk) fit only once, so
+// every chunk takes two barriers (tiles and published state ready / all
+// reads done) instead of double buffers, and the batch's parallelism comes
+// from time segments (the planner splits sequences when batch x heads
+// cannot fill the GPU).
 //
 //   bwd_dq_wide_kernel   forward walk. Waves 0-3 ("dq waves", rows 16 w ..
 //                        16 w + 15 of each chunk) form dq; waves 4-7 rebuild
