@@ -358,8 +358,8 @@ def bench_linear_attn(steps, warmup):
                                                        "dv": DV, "decode_N": N},
             "value": round(B * T * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
-            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true>",
-                             traffic=measured_traffic("fwd_out_kernel<96, true>@linear_attention")),
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel="fwd_out_kernel<96, true, 96>",
+                             traffic=measured_traffic("fwd_out_kernel<96, true, 96>@linear_attention")),
             "decode": {"value": round(N * dsteps / wall_d, 1), "unit": "seq-steps/s",
                        "ms_per_step": round(wall_d / dsteps * 1e3, 4),
                        "roofline": dict(roofline(bytes_dec, ev_d),
@@ -570,8 +570,8 @@ def main():
         "config": {"workload": "laplace_prefill", "B": 8, "T": 2048, "H": H, "dk": DK,
                    "dv": DV, "chunk": 64, "decays": "geometric, memory 32..4096 tokens",
                    "initial_state": "zero", "buffer_sets": 4},
-        "roofline": dict(pre["roofline"], kernel="fwd_out_kernel<96, false>",
-                         traffic=measured_traffic("fwd_out_kernel<96, false>@laplace_prefill"),
+        "roofline": dict(pre["roofline"], kernel="fwd_out_kernel<96, false, 96>",
+                         traffic=measured_traffic("fwd_out_kernel<96, false, 96>@laplace_prefill"),
                          bytes_per_launch=pre["bytes"], launch_ms=round(pre["event_ms"], 5)),
         "hbm_copy_GBps": copy_bw,
         "hbm_frac_of_copy": round(pre["roofline"]["achieved"] / copy_bw, 4) if copy_bw else None,

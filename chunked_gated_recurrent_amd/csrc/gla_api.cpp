@@ -66,20 +66,21 @@ struct HostPlan {
   size_t off_zslots;  // normalised linear attention with time segments
 };
 
-void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk) {
+// bwd: the plan of a backward call (its matrix-core kernels take dk 96 only)
+void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk, bool bwd) {
   memset(&hp, 0, sizeof(hp));
-  hp.fast = fast_path_ok(dt, dk, dv, chunk);
+  hp.fast = bwd ? bwd_fast_path_ok(dt, dk, dv, chunk) : fast_path_ok(dt, dk, dv, chunk);
   hp.chunk = hp.fast ? 64 : generic_chunk(chunk);
-  hp.ndt = hp.fast ? dv / fast_dv_tile(dv) : dv / 16;
+  hp.ndt = hp.fast ? dv / (bwd ? fast_dv_tile(dv) : fwd_dv_tile(dk, dv)) : dv / 16;
 }
 
 // plan_ndt (when > 0) replaces the forward's dv tiles per unit in the
 // decision to split sequences into time segments (the wide backward runs
 // one workgroup per unit).
 HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk,
-                    int plan_ndt = 0) {
+                    int plan_ndt = 0, bool bwd = false) {
   HostPlan hp;
-  base_plan(hp, dt, dk, dv, chunk);
+  base_plan(hp, dt, dk, dv, chunk, bwd);
   const int C = hp.chunk;
   const long long chains = (long long)B * H * (plan_ndt > 0 ? plan_ndt : hp.ndt);
   const long long target = target_workgroups();
@@ -108,9 +109,9 @@ HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk,
 }
 
 HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk,
-                     int plan_ndt = 0) {
+                     int plan_ndt = 0, bool bwd = false) {
   HostPlan hp;
-  base_plan(hp, dt, dk, dv, chunk);
+  base_plan(hp, dt, dk, dv, chunk, bwd);
   const int C = hp.chunk;
   const long long chains = (long long)N * H * (plan_ndt > 0 ? plan_ndt : hp.ndt);
   const long long target = target_workgroups();
@@ -598,7 +599,8 @@ size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
   if (check_common(dt, H, dk, dv, chunk) != GLA_OK ||
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
-  const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+  const HostPlan hp =
+      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true);
   return bwd_layout(hp, (long long)B * T, H, dk, dv).ws_bytes;
 }
 
@@ -635,7 +637,8 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
   const BwdPlan bp = bwd_layout(
-      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk)), tok, H, dk, dv);
+      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true), tok, H,
+      dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
     for (int b = 0; b < 6; ++b)
@@ -664,7 +667,7 @@ size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, in
       N < 1 || N > (1 << 28) || total_T < 0)
     return 0;
   const HostPlan hp =
-      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true);
   return bwd_layout(hp, total_T, H, dk, dv).ws_bytes;
 }
 
@@ -701,7 +704,8 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
     for (int b = a + 1; b < 4; ++b)
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
-  HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+  HostPlan hp =
+      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true);
   hp.p.cu = cu_seqlens;
   const BwdPlan bp = bwd_layout(hp, total_T, H, dk, dv);
   if (bp.ws_bytes > 0) {

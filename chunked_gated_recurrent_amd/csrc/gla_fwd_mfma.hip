@@ -1,5 +1,5 @@
 // gla_fwd_mfma.hip -- chunked Simple GLA forward for bf16 inputs with dk = 96
-// on the gfx950 matrix cores.
+// (the Laplace head) or 64 on the gfx950 matrix cores.
 //
 // A workgroup owns one (work item, head, dv tile) and walks the item's chunks
 // in order; the fp32 state tile lives in MFMA accumulators for the whole
@@ -49,15 +49,16 @@ namespace gla {
 // ---------------------------------------------------------------------------
 // Output role: 4 waves (role wave w owns rows 16 w .. 16 w + 15 of a chunk).
 // ---------------------------------------------------------------------------
-template <int DVT, bool NORM>
+template <int DVT, bool NORM, int DKT>
 __device__ __forceinline__ void output_role(
     const bf16 *__restrict__ q, bf16 *__restrict__ o, const Item &it, int h,
     int H, int dv, int c0, float scale, int rt, int w, bf16 *sQ,
     const bf16 *sK, const bf16 *sV, const bf16 *sSt0, const bf16 *sSt1,
     const float *sPow) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NCT = M::NCT, NKS = M::NKS, NJS = M::NJS, QV = M::QV;
+  static_assert(DVT <= QS, "a wave stages its 16 x DVT output rows in its own q rows");
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
   const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
   const unsigned rowKb = (unsigned)(H * DK * 2), rowVb = (unsigned)(H * dv * 2);
@@ -204,14 +205,14 @@ __device__ __forceinline__ void output_role(
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
-template <int DVT, bool NORM>
+template <int DVT, bool NORM, int DKT>
 __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, bf16 *__restrict__ o,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H, int dv,
     int final_in_slot, NormPtrs np) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
@@ -235,19 +236,19 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = dtile * DVT;
   if (role_wave < 4)
-    output_role<DVT, NORM>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ,
-                           sK, sV, sSt0, sSt1, sPow);
+    output_role<DVT, NORM, DKT>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ,
+                                sK, sV, sSt0, sSt1, sPow);
   else
-    state_role<DVT, true, NORM>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
-                                final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
-                                sSt0, sSt1, sPow, np);
+    state_role<DVT, true, NORM, DKT>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
+                                     final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
+                                     sSt0, sSt1, sPow, np);
 }
 
-template <int DVT, bool NORM>
+template <int DVT, bool NORM, int DKT>
 __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     float *__restrict__ slots, Plan plan, Decay dec, int H, int dv, NormPtrs np) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
   __shared__ float sPow[M::C + 4];
@@ -265,34 +266,39 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
   if (it.flags & kLastSeg) return;  // no later segment reads it
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
-  state_role<DVT, false, NORM>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
+  state_role<DVT, false, NORM, DKT>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
                                dtile * DVT, 0, tid, __builtin_amdgcn_readfirstlane(tid >> 6),
                                nullptr, sKs, sV, nullptr, nullptr, sPow, np);
 }
 
-template <int DVT, bool NORM>
+template <int DVT, bool NORM, int DKT>
 static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
                        const Decay &dec, hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
   const NormPtrs np = {a.z0, a.z_final, a.zslots};
   if (state_only)
-    hipLaunchKernelGGL((fwd_state_kernel<DVT, NORM>), dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((fwd_state_kernel<DVT, NORM, DKT>), dim3(grid), dim3(256), 0, s,
                        (const bf16 *)a.k, (const bf16 *)a.v, a.slots, p, dec, a.H, a.dv, np);
   else
-    hipLaunchKernelGGL((fwd_out_kernel<DVT, NORM>), dim3(grid), dim3(512), 0, s,
+    hipLaunchKernelGGL((fwd_out_kernel<DVT, NORM, DKT>), dim3(grid), dim3(512), 0, s,
                        (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                        (bf16 *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
                        a.H, a.dv, a.final_in_slot, np);
 }
 
+// dk 96 runs d_v tiles of 96 or 64 columns, dk 64 tiles of 64 (a wave
+// stages its output rows in its q rows, dk + 16 elements wide)
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s) {
-  if (a.norm) {
-    if (dvt == 96) launch_dvt<96, true>(state_only, p, a, dec, s);
-    else launch_dvt<64, true>(state_only, p, a, dec, s);
+  if (a.dk == 64) {
+    if (a.norm) launch_dvt<64, true, 64>(state_only, p, a, dec, s);
+    else launch_dvt<64, false, 64>(state_only, p, a, dec, s);
+  } else if (a.norm) {
+    if (dvt == 96) launch_dvt<96, true, 96>(state_only, p, a, dec, s);
+    else launch_dvt<64, true, 96>(state_only, p, a, dec, s);
   } else {
-    if (dvt == 96) launch_dvt<96, false>(state_only, p, a, dec, s);
-    else launch_dvt<64, false>(state_only, p, a, dec, s);
+    if (dvt == 96) launch_dvt<96, false, 96>(state_only, p, a, dec, s);
+    else launch_dvt<64, false, 96>(state_only, p, a, dec, s);
   }
 }
 

@@ -87,7 +87,9 @@ struct BwdArgs {
 // ---- launchers (gla_kernels.hip) -------------------------------------------
 // All return the hipGetLastError() of their launches.
 bool fast_path_ok(int dt, int dk, int dv, int chunk);
+bool bwd_fast_path_ok(int dt, int dk, int dv, int chunk);
 int fast_dv_tile(int dv);
+int fwd_dv_tile(int dk, int dv);
 int generic_chunk(int chunk);
 hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items, hipStream_t s);
 hipError_t launch_order(const Plan &p, int chunk, int32_t *order, hipStream_t s);

@@ -581,12 +581,19 @@ __global__ __launch_bounds__(512) void decode_kernel(
 // ===========================================================================
 // The matrix-core path always runs 64-token chunks; a request for 128 is
 // served with 64 (results do not depend on the chunk beyond rounding), and
-// only an explicit 32 selects the vector-ALU path for these shapes.
+// only an explicit 32 selects the vector-ALU path for these shapes. The
+// forward takes dk 96 or 64, the backward's matrix-core kernels dk 96.
 bool fast_path_ok(int dt, int dk, int dv, int chunk) {
-  return dt == 1 && dk == 96 && (dv % 64 == 0) && chunk != 32;
+  return dt == 1 && (dk == 96 || dk == 64) && (dv % 64 == 0) && chunk != 32;
+}
+
+bool bwd_fast_path_ok(int dt, int dk, int dv, int chunk) {
+  return fast_path_ok(dt, dk, dv, chunk) && dk == 96;
 }
 
 int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }
+
+int fwd_dv_tile(int dk, int dv) { return dk == 64 ? 64 : fast_dv_tile(dv); }
 
 int generic_chunk(int chunk) { return chunk == 32 ? 32 : 64; }
 
@@ -630,7 +637,7 @@ hipError_t launch_fwd(int dt, bool fast, bool state_only, const Plan &p,
                       const FwdArgs &a, const Decay &dec, int chunk,
                       hipStream_t s) {
   if (fast) {
-    launch_fwd_mfma(state_only, fast_dv_tile(a.dv), p, a, dec, s);
+    launch_fwd_mfma(state_only, fwd_dv_tile(a.dk, a.dv), p, a, dec, s);
   } else {
     const int C = generic_chunk(chunk);
     if (dt == 1) {

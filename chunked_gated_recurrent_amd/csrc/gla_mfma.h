@@ -80,9 +80,9 @@ __device__ __forceinline__ bf16x8 ones_bf16x8() {
   return (bf16x8){one, one, one, one, one, one, one, one};
 }
 
-template <int DVT>
+template <int DVT, int DKT = 96>
 struct MfCfg {
-  static constexpr int C = 64, DK = 96;
+  static constexpr int C = 64, DK = DKT;
   // LDS row strides (elements). A stride of 8 mod 16 dwords (112 bf16 for 96
   // columns, 80 for 64) keeps both the 16-byte fragment reads (16 rows, one
   // column block) and the transpose reads (rows 4g + l16/4) free of bank
@@ -122,7 +122,7 @@ __device__ __forceinline__ int chunk_rows(const Item &it, int ch) {
 //          result holds z); z is published in row DVT of the state buffer.
 //          Every dv tile's workgroup computes z; the one at c0 = 0 stores it.
 // ---------------------------------------------------------------------------
-template <int DVT, bool FUSED, bool NORM = false>
+template <int DVT, bool FUSED, bool NORM = false, int DKT = 96>
 __device__ __forceinline__ void state_role(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ s0, float *__restrict__ s_final,
@@ -130,7 +130,7 @@ __device__ __forceinline__ void state_role(
     int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
     bf16 *sSt0, bf16 *sSt1, const float *sPow, NormPtrs np = NormPtrs{}) {
   // sK (FUSED only), sKs and sV hold two chunk buffers each
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;

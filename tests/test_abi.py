@@ -335,3 +335,13 @@ def test_decode_pool_argument_errors(L):
     d = GOOD.copy()
     d[2] = -0.5
     assert pool(decay=d) == DECAY
+
+
+def test_dk64_forward_plans_on_matrix_cores():
+    """bf16 with d_k 64 plans the matrix-core forward (d_v tiles of 64
+    columns: 3 per head at d_v 192, 12 units for 4 heads, so 22 time
+    segments of 192 tokens for one 4,096-token sequence); fp32 plans the
+    vector-ALU forward (16-column tiles: 48 units, 6 segments)."""
+    L = gla.lib()
+    assert L.gla_chunk_fwd_workspace_bytes(1, 1, 4096, 4, 64, 192, 0) == 22 * 4 * 64 * 192 * 4
+    assert L.gla_chunk_fwd_workspace_bytes(0, 1, 4096, 4, 64, 192, 0) == 6 * 4 * 64 * 192 * 4

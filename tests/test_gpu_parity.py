@@ -122,6 +122,37 @@ def test_ragged_lengths_mfma(T, with_s0):
     check("mfma T%d s0=%s" % (T, with_s0), o, ro, s, rs, TOL["bf16"])
 
 
+@pytest.mark.parametrize("T", [1, 63, 65, 200])
+@pytest.mark.parametrize("dv", [64, 192, 256])
+def test_ragged_lengths_mfma_dk64(T, dv):
+    """d_k = 64 on the matrix cores (d_v tiles of 64 columns)."""
+    x = W.prefill_inputs(140 + T + dv, 2, T, 3, 64, dv, "bf16", 0.1, W.geometric_decays(3))
+    o, s = run_fixed(x)
+    ro, rs = oracle_fixed(x)
+    check("mfma dk64 dv%d T%d" % (dv, T), o, ro, s, rs, TOL["bf16"])
+
+
+def test_dk64_time_segments_and_packed_sequences():
+    """d_k = 64: one long sequence cut into time segments (state pass,
+    combine, output pass), and packed sequences with and without segments."""
+    x = W.prefill_inputs(160, 1, 3000, 2, 64, 128, "bf16", 0.1, W.geometric_decays(2))
+    assert gla.lib().gla_chunk_fwd_workspace_bytes(1, 1, 3000, 2, 64, 128, 0) > 0
+    o, s = run_fixed(x)
+    ro, rs = oracle_fixed(x)
+    check("mfma dk64 segmented T3000", o, ro, s, rs, TOL["bf16"])
+    lens = [0, 1, 63, 65, 300, 1000]
+    x = W.varlen_inputs(161, 0, 0, 4, 64, 192, "bf16", 0.1, W.geometric_decays(4), lengths=lens)
+    ro, rs = oracle_varlen(x)
+    for knob in ({}, dict(GLA_TARGET_WGS=100000)):
+        with env(**knob):
+            q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+            o, sf = gla.gla_chunk_fwd_varlen(q, k, v, dev(x["cu_seqlens"]), x["decay"],
+                                             initial_state=s0)
+            torch.cuda.synchronize()
+            check("mfma dk64 varlen %s" % knob, host(o), ro, host(sf), rs, TOL["bf16"],
+                  head_axis_o=1)
+
+
 @pytest.mark.parametrize("dtype,dk,dv,T,chunk", [
     ("bf16", 16, 32, 100, 32), ("f32", 32, 64, 130, 64), ("f32", 128, 256, 70, 0),
     ("bf16", 64, 128, 129, 0), ("f32", 96, 192, 257, 128), ("bf16", 96, 128, 150, 0),
