@@ -1,5 +1,5 @@
 // gla_fwd_mfma.hip -- chunked Simple GLA forward for bf16 inputs with dk = 96
-// (the Laplace head) or 64 on the gfx950 matrix cores.
+// (the Laplace head), 64 or 128 on the gfx950 matrix cores.
 //
 // A workgroup owns one (work item, head, dv tile) and walks the item's chunks
 // in order; the fp32 state tile lives in MFMA accumulators for the whole
@@ -287,12 +287,17 @@ static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
 }
 
 // dk 96 runs d_v tiles of 96 or 64 columns, dk 64 tiles of 64 (a wave
-// stages its output rows in its q rows, dk + 16 elements wide)
+// stages its output rows in its q rows, dk + 16 elements wide), dk 128
+// tiles of 32 (three double-buffered 64 x 128 q/k tiles leave LDS room for
+// no wider state)
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s) {
   if (a.dk == 64) {
     if (a.norm) launch_dvt<64, true, 64>(state_only, p, a, dec, s);
     else launch_dvt<64, false, 64>(state_only, p, a, dec, s);
+  } else if (a.dk == 128) {
+    if (a.norm) launch_dvt<32, true, 128>(state_only, p, a, dec, s);
+    else launch_dvt<32, false, 128>(state_only, p, a, dec, s);
   } else if (a.norm) {
     if (dvt == 96) launch_dvt<96, true, 96>(state_only, p, a, dec, s);
     else launch_dvt<64, true, 96>(state_only, p, a, dec, s);

@@ -582,9 +582,9 @@ __global__ __launch_bounds__(512) void decode_kernel(
 // The matrix-core path always runs 64-token chunks; a request for 128 is
 // served with 64 (results do not depend on the chunk beyond rounding), and
 // only an explicit 32 selects the vector-ALU path for these shapes. The
-// forward takes dk 96 or 64, the backward's matrix-core kernels dk 96.
+// forward takes dk 96, 64 or 128, the backward's matrix-core kernels dk 96.
 bool fast_path_ok(int dt, int dk, int dv, int chunk) {
-  return dt == 1 && (dk == 96 || dk == 64) && (dv % 64 == 0) && chunk != 32;
+  return dt == 1 && (dk == 96 || dk == 64 || dk == 128) && (dv % 64 == 0) && chunk != 32;
 }
 
 bool bwd_fast_path_ok(int dt, int dk, int dv, int chunk) {
@@ -593,7 +593,7 @@ bool bwd_fast_path_ok(int dt, int dk, int dv, int chunk) {
 
 int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }
 
-int fwd_dv_tile(int dk, int dv) { return dk == 64 ? 64 : fast_dv_tile(dv); }
+int fwd_dv_tile(int dk, int dv) { return dk == 64 ? 64 : dk == 128 ? 32 : fast_dv_tile(dv); }
 
 int generic_chunk(int chunk) { return chunk == 32 ? 32 : 64; }
 

@@ -95,8 +95,8 @@ const char *gla_status_str(gla_status s);
  *             bytes (NULL allowed when that is 0); its contents on entry
  *             are ignored, and it must not be used by other work on other
  *             streams while the call's kernels run.
- * bf16 with dk = 96 or 64 and dv a multiple of 64 runs on the matrix cores
- * (64-token chunks); fp32, other head sizes and chunk = 32 run on the vector
+ * bf16 with dk = 96, 64 or 128 and dv a multiple of 64 runs on the matrix
+ * cores (64-token chunks); fp32, other head sizes and chunk = 32 run on the vector
  * ALUs (fp32 arithmetic, 32- or 64-token chunks).
  * T = 0 is valid: o is untouched and s_final receives s0 (or zeros).
  * B * T must stay below 2^31 tokens.
@@ -159,7 +159,7 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
  *              into time segments, the segments' incoming states and carried
  *              gradients); NULL allowed when that is 0.
  * Shapes, dtypes and chunk as for gla_chunk_fwd: bf16 with dk = 96 and dv a
- * multiple of 64 runs on the matrix cores (dk = 64 only in the forward); fp32,
+ * multiple of 64 runs on the matrix cores (dk = 64 and 128 only in the forward); fp32,
  * other head sizes and
  * chunk = 32 run on the vector ALUs (fp32 arithmetic). The workspace is
  * never 0 for tokens > 0 unless dv fits one dv tile. Checks as for
@@ -209,7 +209,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
  *   workspace: device scratch of gla_linear_attn_fwd_workspace_bytes()
  *             bytes (0 unless the batch is split into time segments).
  * Shapes, dtypes and chunk as for gla_chunk_fwd (the matrix-core path for
- * bf16 with dk = 96 or 64 and dv a multiple of 64). Every output must be disjoint
+ * bf16 with dk = 96, 64 or 128 and dv a multiple of 64). Every output must be disjoint
  * from every other argument (no in-place final sums: GLA_ERR_ALIAS).
  * T = 0 copies s0 and z0 (or zeros) to the final sums.
  */

@@ -122,7 +122,8 @@ def test_empty_sequence_copies_the_sums():
     assert np.all(host(sf) == 0.0) and np.all(host(zf) == 0.0)
 
 
-@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32), ("bf16", 64, 128)])
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32), ("bf16", 64, 128),
+                                         ("bf16", 128, 64)])
 def test_decode_steps_continue_the_prefill(dtype, dk, dv):
     """Prefill 37 tokens, then 5 decode steps from the returned (S, z): equal
     to the oracle over all 42 tokens, outputs and final sums."""

@@ -123,25 +123,29 @@ def test_ragged_lengths_mfma(T, with_s0):
 
 
 @pytest.mark.parametrize("T", [1, 63, 65, 200])
-@pytest.mark.parametrize("dv", [64, 192, 256])
-def test_ragged_lengths_mfma_dk64(T, dv):
-    """d_k = 64 on the matrix cores (d_v tiles of 64 columns)."""
-    x = W.prefill_inputs(140 + T + dv, 2, T, 3, 64, dv, "bf16", 0.1, W.geometric_decays(3))
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 192), (64, 256), (128, 64), (128, 192)])
+def test_ragged_lengths_mfma_dk64_dk128(T, dk, dv):
+    """d_k = 64 (d_v tiles of 64 columns) and 128 (tiles of 32) on the
+    matrix cores."""
+    x = W.prefill_inputs(140 + T + dk + dv, 2, T, 3, dk, dv, "bf16", 0.1, W.geometric_decays(3))
     o, s = run_fixed(x)
     ro, rs = oracle_fixed(x)
-    check("mfma dk64 dv%d T%d" % (dv, T), o, ro, s, rs, TOL["bf16"])
+    check("mfma dk%d dv%d T%d" % (dk, dv, T), o, ro, s, rs, TOL["bf16"])
 
 
-def test_dk64_time_segments_and_packed_sequences():
-    """d_k = 64: one long sequence cut into time segments (state pass,
-    combine, output pass), and packed sequences with and without segments."""
-    x = W.prefill_inputs(160, 1, 3000, 2, 64, 128, "bf16", 0.1, W.geometric_decays(2))
-    assert gla.lib().gla_chunk_fwd_workspace_bytes(1, 1, 3000, 2, 64, 128, 0) > 0
+@pytest.mark.parametrize("dk", [64, 128])
+def test_dk64_dk128_time_segments_and_packed_sequences(dk):
+    """d_k = 64 and 128: one long sequence cut into time segments (state
+    pass, combine, output pass), and packed sequences with and without
+    segments."""
+    x = W.prefill_inputs(160 + dk, 1, 3000, 2, dk, 128, "bf16", 0.1, W.geometric_decays(2))
+    assert gla.lib().gla_chunk_fwd_workspace_bytes(1, 1, 3000, 2, dk, 128, 0) > 0
     o, s = run_fixed(x)
     ro, rs = oracle_fixed(x)
-    check("mfma dk64 segmented T3000", o, ro, s, rs, TOL["bf16"])
+    check("mfma dk%d segmented T3000" % dk, o, ro, s, rs, TOL["bf16"])
     lens = [0, 1, 63, 65, 300, 1000]
-    x = W.varlen_inputs(161, 0, 0, 4, 64, 192, "bf16", 0.1, W.geometric_decays(4), lengths=lens)
+    x = W.varlen_inputs(161 + dk, 0, 0, 4, dk, 192, "bf16", 0.1, W.geometric_decays(4),
+                        lengths=lens)
     ro, rs = oracle_varlen(x)
     for knob in ({}, dict(GLA_TARGET_WGS=100000)):
         with env(**knob):
@@ -149,7 +153,7 @@ def test_dk64_time_segments_and_packed_sequences():
             o, sf = gla.gla_chunk_fwd_varlen(q, k, v, dev(x["cu_seqlens"]), x["decay"],
                                              initial_state=s0)
             torch.cuda.synchronize()
-            check("mfma dk64 varlen %s" % knob, host(o), ro, host(sf), rs, TOL["bf16"],
+            check("mfma dk%d varlen %s" % (dk, knob), host(o), ro, host(sf), rs, TOL["bf16"],
                   head_axis_o=1)
 
 
