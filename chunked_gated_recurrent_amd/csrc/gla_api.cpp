@@ -66,21 +66,20 @@ struct HostPlan {
   size_t off_zslots;  // normalised linear attention with time segments
 };
 
-// bwd: the plan of a backward call (its matrix-core kernels take dk 96 only)
-void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk, bool bwd) {
+void base_plan(HostPlan &hp, int dt, int dk, int dv, int chunk) {
   memset(&hp, 0, sizeof(hp));
-  hp.fast = bwd ? bwd_fast_path_ok(dt, dk, dv, chunk) : fast_path_ok(dt, dk, dv, chunk);
+  hp.fast = fast_path_ok(dt, dk, dv, chunk);
   hp.chunk = hp.fast ? 64 : generic_chunk(chunk);
-  hp.ndt = hp.fast ? dv / (bwd ? fast_dv_tile(dv) : fwd_dv_tile(dk, dv)) : dv / 16;
+  hp.ndt = hp.fast ? dv / fwd_dv_tile(dk, dv) : dv / 16;
 }
 
 // plan_ndt (when > 0) replaces the forward's dv tiles per unit in the
 // decision to split sequences into time segments (the wide backward runs
 // one workgroup per unit).
 HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk,
-                    int plan_ndt = 0, bool bwd = false) {
+                    int plan_ndt = 0) {
   HostPlan hp;
-  base_plan(hp, dt, dk, dv, chunk, bwd);
+  base_plan(hp, dt, dk, dv, chunk);
   const int C = hp.chunk;
   const long long chains = (long long)B * H * (plan_ndt > 0 ? plan_ndt : hp.ndt);
   const long long target = target_workgroups();
@@ -109,9 +108,9 @@ HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk,
 }
 
 HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk,
-                     int plan_ndt = 0, bool bwd = false) {
+                     int plan_ndt = 0) {
   HostPlan hp;
-  base_plan(hp, dt, dk, dv, chunk, bwd);
+  base_plan(hp, dt, dk, dv, chunk);
   const int C = hp.chunk;
   const long long chains = (long long)N * H * (plan_ndt > 0 ? plan_ndt : hp.ndt);
   const long long target = target_workgroups();
@@ -257,7 +256,7 @@ BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv)
   memset(&bp, 0, sizeof(bp));
   bp.hp = hp;
   bp.wide = hp.fast && bwd_wide_ok(dk, dv);
-  bp.dvt = bp.wide ? dv : hp.fast ? fast_dv_tile(dv) : valu_bwd_tile(dv);
+  bp.dvt = bp.wide ? dv : hp.fast ? fwd_dv_tile(dk, dv) : valu_bwd_tile(dv);
   bp.ndt = dv / bp.dvt;
   const size_t base = align256(hp.ws_bytes);
   const size_t slot_bytes =
@@ -301,7 +300,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     a.slots = (float *)(ws + hp.off_slots);
     a.cslots = (float *)(ws + bp.off_cslots);
     if (hp.fast) {
-      if (launch_bwd_boundary(fast_dv_tile(a.dv), p, a, dec, s) != hipSuccess)
+      if (launch_bwd_boundary(fwd_dv_tile(a.dk_dim, a.dv), p, a, dec, s) != hipSuccess)
         return GLA_ERR_HIP;
       // two segments per sequence: the wide kernels join them on load
       pair = bp.wide && p.mode == kPlanFixed && p.G == 2;
@@ -600,7 +599,7 @@ size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
   const HostPlan hp =
-      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true);
+      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
   return bwd_layout(hp, (long long)B * T, H, dk, dv).ws_bytes;
 }
 
@@ -637,7 +636,7 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
   const BwdPlan bp = bwd_layout(
-      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true), tok, H,
+      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk)), tok, H,
       dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
@@ -667,7 +666,7 @@ size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, in
       N < 1 || N > (1 << 28) || total_T < 0)
     return 0;
   const HostPlan hp =
-      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true);
+      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
   return bwd_layout(hp, total_T, H, dk, dv).ws_bytes;
 }
 
@@ -705,7 +704,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
   HostPlan hp =
-      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk), true);
+      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
   hp.p.cu = cu_seqlens;
   const BwdPlan bp = bwd_layout(hp, total_T, H, dk, dv);
   if (bp.ws_bytes > 0) {

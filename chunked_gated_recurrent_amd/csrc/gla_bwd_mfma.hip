@@ -1,5 +1,6 @@
 // gla_bwd_mfma.hip -- backward of the chunked Simple GLA forward for bf16
-// inputs with dk = 96 on the gfx950 matrix cores.
+// inputs with dk = 96, 64 or 128 on the gfx950 matrix cores (d_v tiles as
+// the forward's: 96 or 64 columns at dk 96, 64 at dk 64, 32 at dk 128).
 //
 // The gradients of S_t = lambda S_{t-1} + k_t^T v_t, o_t = scale q_t S_t
 // (Laplace 3B / Trainium2 page, sections "GLA mixer" and "Challenge 3":
@@ -24,7 +25,7 @@
 //     its contraction runs over dk) and advance Ch, four "dk waves" form the
 //     dk terms of this dv tile.
 // dq and dk contract over dv, so each dv tile yields a partial sum: fp32 rows
-// [dv tile][H][token][96] in the workspace (each lane stores the 4
+// [dv tile][H][token][dk] in the workspace (each lane stores the 4
 // consecutive dk values of one token that it holds), which a streaming
 // kernel adds up into bf16 dq and dk. (dv = 192 takes the workgroup-per-head
 // kernels of gla_bwd_wide.hip instead; this file also holds the boundary
@@ -34,23 +35,23 @@
 
 namespace gla {
 
-// fp32 partial-sum rows: [dv tile][H][total tokens][96]
+// fp32 partial-sum rows: [dv tile][H][total tokens][dk]
 __device__ __forceinline__ float *part_row(float *part, int dtile, int h, long long t,
-                                           int H, long long total_T) {
-  return part + (((long long)dtile * H + h) * total_T + t) * 96;
+                                           int H, long long total_T, int dk) {
+  return part + (((long long)dtile * H + h) * total_T + t) * dk;
 }
 
 // ---------------------------------------------------------------------------
 // dq role: 4 waves (role wave w owns rows 16 w .. 16 w + 15 of a chunk).
 // ---------------------------------------------------------------------------
-template <int DVT>
+template <int DVT, int DKT>
 __device__ __forceinline__ void dq_role(
     const bf16 *__restrict__ dout, float *__restrict__ part, const Item &it,
     int h, int H, int dv, int c0, int dtile, long long total_T, float scale,
     int rt, int w, bf16 *sD,
     const bf16 *sK, const bf16 *sV, const bf16 *sSt0, const bf16 *sSt1,
     const float *sPow) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   constexpr int C = M::C, QS = M::QS, VS = M::VS;
   constexpr int NDT = M::NDT, NJS = M::NJS, NVV = M::NVV, VV = M::VV;
   constexpr int NCS = DVT / 32;  // 32-deep steps over the dv tile
@@ -155,7 +156,7 @@ __device__ __forceinline__ void dq_role(
     // of token i_row (rows past the item's end are not written: they belong
     // to the next item or sequence)
     if (i_row < chunk_rows(it, ch)) {
-      float *dst = part_row(part, dtile, h, it.t0 + (long long)ch * C + i_row, H, total_T) + 4 * g;
+      float *dst = part_row(part, dtile, h, it.t0 + (long long)ch * C + i_row, H, total_T, M::DK) + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt] * scale;
@@ -167,13 +168,13 @@ __device__ __forceinline__ void dq_role(
   }
 }
 
-template <int DVT>
+template <int DVT, int DKT>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ s0,
     float *__restrict__ slots, float *__restrict__ part_dq, Plan plan,
     Decay dec, float scale, int H, int dv) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   __shared__ __attribute__((aligned(16))) bf16 sD[2 * M::C * M::VS];
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
@@ -197,10 +198,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = dtile * DVT;
   if (role_wave < 4)
-    dq_role<DVT>(dout, part_dq, it, h, H, dv, c0, dtile, plan.total_T, scale, tid & 255,
+    dq_role<DVT, DKT>(dout, part_dq, it, h, H, dv, c0, dtile, plan.total_T, scale, tid & 255,
                  role_wave, sD, sK, sV, sSt0, sSt1, sPow);
   else
-    state_role<DVT, true>(k, v, s0, nullptr, slots, it, idx, h, H, dv, c0, 0,
+    state_role<DVT, true, false, DKT>(k, v, s0, nullptr, slots, it, idx, h, H, dv, c0, 0,
                           tid & 255, role_wave - 4, sK, sKs, sV, sSt0, sSt1, sPow);
 }
 
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 // Reverse walk: dv waves (dv of 16 rows + the carried gradient Ch) and dk
 // waves (partial dk of 16 rows), chunks from the last to the first.
 // ---------------------------------------------------------------------------
-template <int DVT>
+template <int DVT, int DKT>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     bf16 *__restrict__ dv_out, float *__restrict__ ds0,
     float *__restrict__ part_dk, Plan plan, Decay dec, float scale, int H,
     int dv) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NDT = M::NDT, NCT = M::NCT, NJS = M::NJS, NKS = M::NKS;
   constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV, NVV = M::NVV;
@@ -270,35 +271,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     rowB[m] = vi / NVV;
     colB[m] = vi - rowB[m] * NVV;
   }
-  auto load = [&](int ch, u32x4(&r1)[QV], u32x4(&r2)[VV > QV ? VV : QV]) {
+  // Per-lane byte offsets of the role's 16-byte loads. Both roles issue the
+  // same QV loads per operand into the same stage registers (a role-dependent
+  // count makes the compiler keep the stage arrays in private memory); the
+  // slots the dk role does not need (d_v tiles narrower than d_k) point past
+  // every buffer's end, where a buffer load returns zeros and reads nothing.
+  static_assert(VV <= QV, "a d_v tile is at most d_k wide");
+  unsigned offs[QV];
+#pragma unroll
+  for (int m = 0; m < QV; ++m) {
+    unsigned ob = 0x80000000u;
+    if (m < VV) ob = rowB[m < VV ? m : 0] * rowVb + colB[m < VV ? m : 0] * 16;
+    offs[m] = dv_role ? rowA[m] * rowKb + colA[m] * 16 : ob;
+  }
+  auto load = [&](int ch, u32x4(&r1)[QV], u32x4(&r2)[QV]) {
     const int L = rows_of(ch);
     const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
-    if (dv_role) {
-      const __amdgpu_buffer_rsrc_t bq = buf_rsrc(q + (tb * H + h) * DK, (unsigned)L * rowKb);
-      const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, (unsigned)L * rowKb);
+    const long long vo = tb * H * dv + (long long)h * dv + c0;
+    const long long ko = (tb * H + h) * DK;
+    const __amdgpu_buffer_rsrc_t b1 =
+        buf_rsrc(dv_role ? q + ko : v + vo, (unsigned)L * (dv_role ? rowKb : rowVb));
+    const __amdgpu_buffer_rsrc_t b2 =
+        buf_rsrc(dv_role ? k + ko : dout + vo, (unsigned)L * (dv_role ? rowKb : rowVb));
 #pragma unroll
-      for (int m = 0; m < QV; ++m)
-        r1[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, rowA[m] * rowKb + colA[m] * 16, 0, 0);
+    for (int m = 0; m < QV; ++m) r1[m] = __builtin_amdgcn_raw_buffer_load_b128(b1, offs[m], 0, 0);
 #pragma unroll
-      for (int m = 0; m < QV; ++m)
-        r2[m] = __builtin_amdgcn_raw_buffer_load_b128(bk, rowA[m] * rowKb + colA[m] * 16, 0, 0);
-    } else {
-      const long long vo = tb * H * dv + (long long)h * dv + c0;
-      const __amdgpu_buffer_rsrc_t bv = buf_rsrc(v + vo, (unsigned)L * rowVb);
-      const __amdgpu_buffer_rsrc_t bd = buf_rsrc(dout + vo, (unsigned)L * rowVb);
-#pragma unroll
-      for (int m = 0; m < VV; ++m)
-        r1[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, rowB[m] * rowVb + colB[m] * 16, 0, 0);
-#pragma unroll
-      for (int m = 0; m < VV; ++m)
-        r2[m] = __builtin_amdgcn_raw_buffer_load_b128(bd, rowB[m] * rowVb + colB[m] * 16, 0, 0);
-      // define the slots this role leaves unused (d_v tiles narrower than
-      // d_k), so that both roles fill every register of the stage arrays
-#pragma unroll
-      for (int m = VV; m < QV; ++m) r1[m] = r2[m] = (u32x4){0u, 0u, 0u, 0u};
-    }
+    for (int m = 0; m < QV; ++m) r2[m] = __builtin_amdgcn_raw_buffer_load_b128(b2, offs[m], 0, 0);
   };
-  auto store = [&](int buf, const u32x4(&r1)[QV], const u32x4(&r2)[VV > QV ? VV : QV]) {
+  auto store = [&](int buf, const u32x4(&r1)[QV], const u32x4(&r2)[QV]) {
     if (dv_role) {
 #pragma unroll
       for (int m = 0; m < QV; ++m) {
@@ -348,8 +348,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
       }
   };
 
-  constexpr int R2 = VV > QV ? VV : QV;
-  u32x4 a1[QV], a2[R2], b1[QV], b2[R2];
+  u32x4 a1[QV], a2[QV], b1[QV], b2[QV];
   load(nch - 1, a1, a2);
   load(nch - 2, b1, b2);
   __syncthreads();  // sPow ready
@@ -376,8 +375,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 
   // step p processes chunk ch = nch - 1 - p: reads Ch from sCt[p & 1] and
   // publishes the advanced Ch into sCt[(p + 1) & 1]
-  auto body = [&](int ch, u32x4(&n1)[QV], u32x4(&n2)[R2], const u32x4(&x1)[QV],
-                  const u32x4(&x2)[R2], const bf16 *ct_in, bf16 *ct_out) {
+  auto body = [&](int ch, u32x4(&n1)[QV], u32x4(&n2)[QV], const u32x4(&x1)[QV],
+                  const u32x4(&x2)[QV], const bf16 *ct_in, bf16 *ct_out) {
     const int L = rows_of(ch);
     const int cur = ch & 1;
     const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
@@ -527,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
           acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), bm[s], acc[dt]);
         }
       if (i_row < L) {  // rows past the item's end are not written
-        float *dst = part_row(part_dk, dtile, h, tb + i_row, H, plan.total_T) + 4 * g;
+        float *dst = part_row(part_dk, dtile, h, tb + i_row, H, plan.total_T, M::DK) + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(dst + 16 * dt) = acc[dt];
       }
@@ -558,12 +557,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 // gradient the item passes back when nothing flows into it), by the same
 // reverse chunk walk as the dv waves of bwd_dkdv_kernel, into slot g.
 // ---------------------------------------------------------------------------
-template <int DVT>
+template <int DVT, int DKT>
 __device__ __forceinline__ void carry_role(
     const bf16 *__restrict__ q, const bf16 *__restrict__ dout, float *__restrict__ cslots,
     const Item &it, int idx, int h, int dtile, float scale, int H, int dv, int tid,
     bf16 *sQ, bf16 *sD, const float *sPow) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int NJS = M::NJS, SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
   constexpr int NVV = M::NVV;
@@ -689,12 +688,12 @@ __device__ __forceinline__ void carry_role(
 // arrays (k, v and q, dO) and each leaves half of the unit slots idle, so
 // together they fill the GPU once instead of half-filling it twice.
 // ---------------------------------------------------------------------------
-template <int DVT>
+template <int DVT, int DKT>
 __global__ __launch_bounds__(256, 2) void bwd_boundary_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, float *__restrict__ slots, float *__restrict__ cslots,
     Plan plan, Decay dec, float scale, int H, int dv, int n_state) {
-  using M = MfCfg<DVT>;
+  using M = MfCfg<DVT, DKT>;
   __shared__ __attribute__((aligned(16))) bf16 sA[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sB[2 * M::C * M::VS];
   __shared__ float sPow[M::C + 4];
@@ -716,32 +715,34 @@ __global__ __launch_bounds__(256, 2) void bwd_boundary_kernel(
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
   if (state)
-    state_role<DVT, false>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv, dtile * DVT, 0,
+    state_role<DVT, false, false, DKT>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv, dtile * DVT, 0,
                            tid, __builtin_amdgcn_readfirstlane(tid >> 6), nullptr, sA, sB,
                            nullptr, nullptr, sPow);
   else
-    carry_role<DVT>(q, dout, cslots, it, idx, h, dtile, scale, H, dv, tid, sA, sB, sPow);
+    carry_role<DVT, DKT>(q, dout, cslots, it, idx, h, dtile, scale, H, dv, tid, sA, sB, sPow);
 }
 
 // ---------------------------------------------------------------------------
-// dq, dk <- sum of the dv-tile partials, as bf16 in [tokens, H, 96]
+// dq, dk <- sum of the dv-tile partials, as bf16 in [tokens, H, dk]
 // ---------------------------------------------------------------------------
 // One thread per 4 consecutive values of one (token, head) row; each partial
 // is read once (non-temporal loads).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(
     const float *__restrict__ part_dq, const float *__restrict__ part_dk,
-    bf16 *__restrict__ dq, bf16 *__restrict__ dk, long long total_T, int H, int ndt) {
+    bf16 *__restrict__ dq, bf16 *__restrict__ dk, long long total_T, int H, int ndt,
+    int dkd) {
   typedef float f32x4n __attribute__((ext_vector_type(4)));
+  const int q4 = dkd / 4;  // float4s per (token, head) row
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // float4 index
-  const long long n4 = total_T * H * 24;
+  const long long n4 = total_T * H * q4;
   if (e >= n4) return;
-  const long long row = e / 24;  // token * H + head
-  const int c4 = (int)(e - row * 24);
+  const long long row = e / q4;  // token * H + head
+  const int c4 = (int)(e - row * q4);
   const long long t = row / H;
   const int h = (int)(row - t * H);
   f32x4n sq = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
   for (int d = 0; d < ndt; ++d) {
-    const long long off = (((long long)d * H + h) * total_T + t) * 96 + 4 * c4;
+    const long long off = (((long long)d * H + h) * total_T + t) * dkd + 4 * c4;
     sq += __builtin_nontemporal_load(reinterpret_cast<const f32x4n *>(part_dq + off));
     sk += __builtin_nontemporal_load(reinterpret_cast<const f32x4n *>(part_dk + off));
   }
@@ -751,37 +752,41 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(
     oq[r] = (bf16)sq[r];
     ok[r] = (bf16)sk[r];
   }
-  *reinterpret_cast<bf16x4 *>(dq + row * 96 + 4 * c4) = oq;
-  *reinterpret_cast<bf16x4 *>(dk + row * 96 + 4 * c4) = ok;
+  *reinterpret_cast<bf16x4 *>(dq + row * dkd + 4 * c4) = oq;
+  *reinterpret_cast<bf16x4 *>(dk + row * dkd + 4 * c4) = ok;
 }
 
-template <int DVT>
+template <int DVT, int DKT>
 static void launch_boundary_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
                                 hipStream_t s) {
   Plan pb = p;
   pb.deal = 1;  // both halves skip a segment of every sequence
   const unsigned g = xcd_grid(1, (long long)p.max_items * a.H, a.dv / DVT);
-  hipLaunchKernelGGL((bwd_boundary_kernel<DVT>), dim3(2 * g), dim3(256), 0, s,
+  hipLaunchKernelGGL((bwd_boundary_kernel<DVT, DKT>), dim3(2 * g), dim3(256), 0, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      (const bf16 *)a.dout, a.slots, a.cslots, pb, dec, a.scale, a.H, a.dv,
                      (int)g);
 }
 
+// d_v tiles as the forward's: 96 or 64 columns at dk 96, 64 at dk 64, 32 at
+// dk 128
 hipError_t launch_bwd_boundary(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
                                hipStream_t s) {
-  if (dvt == 96) launch_boundary_dvt<96>(p, a, dec, s);
-  else launch_boundary_dvt<64>(p, a, dec, s);
+  if (a.dk_dim == 64) launch_boundary_dvt<64, 64>(p, a, dec, s);
+  else if (a.dk_dim == 128) launch_boundary_dvt<32, 128>(p, a, dec, s);
+  else if (dvt == 96) launch_boundary_dvt<96, 96>(p, a, dec, s);
+  else launch_boundary_dvt<64, 96>(p, a, dec, s);
   return hipGetLastError();
 }
 
-template <int DVT>
+template <int DVT, int DKT>
 static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
-  hipLaunchKernelGGL((bwd_dq_kernel<DVT>), dim3(grid), dim3(512), 0, s,
+  hipLaunchKernelGGL((bwd_dq_kernel<DVT, DKT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
                      a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DVT>), dim3(grid), dim3(512), 0, s,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DVT, DKT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      (const bf16 *)a.dout, a.ds_final, a.cslots, (bf16 *)a.dv_out,
                      a.ds0, a.part_dk, p, dec, a.scale, a.H, a.dv);
@@ -789,12 +794,14 @@ static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
 
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
                            const Decay &dec, hipStream_t s) {
-  if (dvt == 96) launch_bwd_dvt<96>(p, a, dec, s);
-  else launch_bwd_dvt<64>(p, a, dec, s);
-  const long long n4 = (long long)p.total_T * a.H * 24;
+  if (a.dk_dim == 64) launch_bwd_dvt<64, 64>(p, a, dec, s);
+  else if (a.dk_dim == 128) launch_bwd_dvt<32, 128>(p, a, dec, s);
+  else if (dvt == 96) launch_bwd_dvt<96, 96>(p, a, dec, s);
+  else launch_bwd_dvt<64, 96>(p, a, dec, s);
+  const long long n4 = (long long)p.total_T * a.H * (a.dk_dim / 4);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
                      a.part_dq, a.part_dk, (bf16 *)a.dq, (bf16 *)a.dk, (long long)p.total_T,
-                     a.H, a.dv / dvt);
+                     a.H, a.dv / dvt, a.dk_dim);
   return hipGetLastError();
 }
 

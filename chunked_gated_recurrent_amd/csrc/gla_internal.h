@@ -81,13 +81,12 @@ struct BwdArgs {
   float *part_dq, *part_dk;  // [dv tiles][H][tokens][96] fp32 partial sums
   float scale;
   int H, dv;
-  int dk_dim;  // dk (96 on the matrix-core path)
+  int dk_dim;  // dk
 };
 
 // ---- launchers (gla_kernels.hip) -------------------------------------------
 // All return the hipGetLastError() of their launches.
 bool fast_path_ok(int dt, int dk, int dv, int chunk);
-bool bwd_fast_path_ok(int dt, int dk, int dv, int chunk);
 int fast_dv_tile(int dv);
 int fwd_dv_tile(int dk, int dv);
 int generic_chunk(int chunk);

@@ -581,14 +581,10 @@ __global__ __launch_bounds__(512) void decode_kernel(
 // ===========================================================================
 // The matrix-core path always runs 64-token chunks; a request for 128 is
 // served with 64 (results do not depend on the chunk beyond rounding), and
-// only an explicit 32 selects the vector-ALU path for these shapes. The
-// forward takes dk 96, 64 or 128, the backward's matrix-core kernels dk 96.
+// only an explicit 32 selects the vector-ALU path for these shapes. Forward
+// and backward take dk 96, 64 or 128.
 bool fast_path_ok(int dt, int dk, int dv, int chunk) {
   return dt == 1 && (dk == 96 || dk == 64 || dk == 128) && (dv % 64 == 0) && chunk != 32;
-}
-
-bool bwd_fast_path_ok(int dt, int dk, int dv, int chunk) {
-  return fast_path_ok(dt, dk, dv, chunk) && dk == 96;
 }
 
 int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }

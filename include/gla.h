@@ -158,10 +158,9 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
  *              sums of dq and dk over dv tiles and, when sequences are split
  *              into time segments, the segments' incoming states and carried
  *              gradients); NULL allowed when that is 0.
- * Shapes, dtypes and chunk as for gla_chunk_fwd: bf16 with dk = 96 and dv a
- * multiple of 64 runs on the matrix cores (dk = 64 and 128 only in the forward); fp32,
- * other head sizes and
- * chunk = 32 run on the vector ALUs (fp32 arithmetic). The workspace is
+ * Shapes, dtypes and chunk as for gla_chunk_fwd: bf16 with dk = 64, 96 or
+ * 128 and dv a multiple of 64 runs on the matrix cores; fp32, other head
+ * sizes and chunk = 32 run on the vector ALUs (fp32 arithmetic). The workspace is
  * never 0 for tokens > 0 unless dv fits one dv tile. Checks as for
  * gla_chunk_fwd; no output may overlap an input or another output. T = 0 is
  * valid: ds0 receives ds_final (or zeros).

@@ -21,12 +21,12 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _inputs(seed, B, T, H, dv, with_s0=True, with_dsf=True):
-    x = W.prefill_inputs(seed, B, T, H, 96, dv, "bf16", 0.1 if with_s0 else None,
+def _inputs(seed, B, T, H, dv, with_s0=True, with_dsf=True, dk=96):
+    x = W.prefill_inputs(seed, B, T, H, dk, dv, "bf16", 0.1 if with_s0 else None,
                          W.geometric_decays(H))
     rng = np.random.default_rng(seed + 1000)
     do = W.bf16_bits(rng.standard_normal((B, T, H, dv), dtype=np.float32))
-    dsf = (rng.standard_normal((B, H, 96, dv), dtype=np.float32) * np.float32(0.5)
+    dsf = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(0.5)
            if with_dsf else None)
     return x, do, dsf
 
@@ -134,6 +134,37 @@ def test_backward_is_bitwise_deterministic():
         np.testing.assert_array_equal(u, w)
 
 
+DK_DV_OFF96 = [(64, 64), (64, 192), (64, 256), (128, 64), (128, 128), (128, 192)]
+
+
+@pytest.mark.parametrize("T", [17, 130])
+@pytest.mark.parametrize("dk,dv", DK_DV_OFF96)
+def test_backward_dk64_dk128(dk, dv, T):
+    """Key heads of 64 and 128 on the matrix cores: d_v tiles of 64 columns
+    at dk 64 and of 32 at dk 128 (as the forward), one partial per tile."""
+    x, do, dsf = _inputs(760 + dk + dv + T, 2, T, 3, dv, dk=dk)
+    _check("bwd dk%d dv%d T%d" % (dk, dv, T), _run(x, do, dsf), _oracle(x, do, dsf))
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_backward_dk64_dk128_time_segments_and_packed(dk, dv):
+    """dk 64 and 128: a fixed batch cut into time segments (boundary pass
+    and both scans), then packed sequences with empty, short and long
+    lengths (device planner)."""
+    from gla_testutil import env
+    x, do, dsf = _inputs(770 + dk, 2, 700, 3, dv, dk=dk)
+    with env(GLA_TARGET_WGS=4096):
+        got = _run(x, do, dsf)
+    _check("bwd segmented dk%d dv%d" % (dk, dv), got, _oracle(x, do, dsf))
+    lengths = [5, 0, 130, 1, 2000, 65, 300]
+    x, do, dsf = _varlen_case(780 + dk, lengths, dv=dv, dk=dk)
+    got = _run_varlen(x, do, dsf)
+    ref = O.gla_bwd_varlen(x["cu_seqlens"], x["q"], x["k"], x["v"], x["decay"], do, 1.0,
+                           x["s0"], dsf)
+    _check("bwd varlen dk%d dv%d" % (dk, dv), got, ref)
+    np.testing.assert_array_equal(got[3][1], dsf[1].astype(np.float64))
+
+
 @pytest.mark.parametrize("T", [700, 1000])
 def test_backward_time_segments(T):
     """Few chains and a high workgroup target force time segments: the
@@ -162,13 +193,13 @@ def test_backward_long_context_sampled_heads():
     _check("bwd long_context T65536 heads 0,15", sel, ref)
 
 
-def _varlen_case(seed, lengths, H=3, dv=192):
-    x = W.varlen_inputs(seed, len(lengths), 0, H, 96, dv, "bf16", 0.1,
+def _varlen_case(seed, lengths, H=3, dv=192, dk=96):
+    x = W.varlen_inputs(seed, len(lengths), 0, H, dk, dv, "bf16", 0.1,
                         W.geometric_decays(H), lengths=lengths)
     total = int(x["cu_seqlens"][-1])
     rng = np.random.default_rng(seed + 1000)
     do = W.bf16_bits(rng.standard_normal((total, H, dv), dtype=np.float32))
-    dsf = rng.standard_normal((len(lengths), H, 96, dv), dtype=np.float32) * np.float32(0.5)
+    dsf = rng.standard_normal((len(lengths), H, dk, dv), dtype=np.float32) * np.float32(0.5)
     return x, do, dsf
 
 
