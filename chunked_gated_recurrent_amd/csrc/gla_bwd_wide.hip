@@ -1,6 +1,6 @@
 // gla_bwd_wide.hip -- backward of the chunked Simple GLA forward for bf16
-// inputs with dk = 96 and dv = 192 (the Laplace 3B head), one workgroup per
-// (work item, head) owning all 192 value columns.
+// inputs with dk = 96 and dv = 192 (the Laplace 3B head), 128 or 64, one
+// workgroup per (work item, head) owning all value columns.
 //
 // Same gradients and chunk formulas as gla_bwd_mfma.hip (Laplace 3B /
 // Trainium2 page, sections "GLA mixer" and "Challenge 3"). There, dq and dk
@@ -8,7 +8,8 @@
 // third pass to add (about 0.8 GB of extra traffic at the Laplace batch);
 // here a workgroup holds the whole dv, so dq and dk come out complete and
 // go straight to their bf16 rows. The price is LDS: the tiles of a chunk
-// (125 KB in the dq pass, 140 KB in the reverse walk) fit only once, so
+// (at dv 192, 125 KB in the dq pass and 140 KB in the reverse walk; 94 and
+// 109 KB at dv 128) fit only once, so
 // every chunk takes two barriers (tiles and published state ready / all
 // reads done) instead of double buffers, and the batch's parallelism comes
 // from time segments (the planner splits sequences when batch x heads
@@ -16,13 +17,13 @@
 //
 //   bwd_dq_wide_kernel   forward walk. Waves 0-3 ("dq waves", rows 16 w ..
 //                        16 w + 15 of each chunk) form dq; waves 4-7 rebuild
-//                        S (a 3 x 6 block of 16 x 16 tiles each) and
+//                        S (a 3 x dv/32 block of 16 x 16 tiles each) and
 //                        publish its bf16 transpose every chunk.
 //   bwd_dkdv_wide_kernel reverse walk. Waves 0-3 form dv, waves 4-7 dk, and
-//                        each wave also advances a 3 x 3 block of tiles of
-//                        the carried gradient Ch (column tiles 0-5 on the dv
-//                        waves, 6-11 on the dk waves), published as bf16
-//                        Ch^T every chunk.
+//                        each wave also advances a 3 x dv/64 block of tiles
+//                        of the carried gradient Ch (the first half of the
+//                        column tiles on the dv waves, the second on the dk
+//                        waves), published as bf16 Ch^T every chunk.
 // Outputs are written from registers: each lane stores the 4 consecutive
 // values of one row that an MFMA result tile gives it (8-byte stores).
 #include "gla_mfma.h"
@@ -31,13 +32,27 @@ namespace gla {
 
 namespace {
 
-constexpr int kWideDv = 192;
-using MW = MfCfg<kWideDv>;  // C 64, DK 96, QS 112, VS 208, NCT 12, NDT 6
-constexpr int kWC = MW::C, kWQS = MW::QS, kWVS = MW::VS;
-constexpr int kWNCS = kWideDv / 32;  // 32-deep steps over dv
-static_assert(kWC * kWQS * 2 * 3 + kWC * kWVS * 2 * 2 + kWideDv * kWQS * 2 + 4 * (kWC + 4) <=
-                  160 * 1024,
-              "LDS budget of the wide backward");
+// LDS of the reverse walk (the larger pass): q, scaled q and k tiles, v and
+// dO tiles, the published Ch^T and the decay powers.
+constexpr int wide_lds(int dk, int dv) {
+  return 64 * (dk + 16) * 2 * 3 + 64 * (dv + 16) * 2 * 2 + dv * (dk + 16) * 2 + 4 * 68;
+}
+// The head shapes these kernels take: each reverse wave owns a quarter of
+// the column tiles of Ch, and the reverse walk's tiles must fit the LDS
+// (dk 128 with dv 192 does not).
+constexpr bool wide_shape(int dk, int dv) {
+  return (dk == 64 || dk == 96 || dk == 128) && (dv == 64 || dv == 128 || dv == 192) &&
+         wide_lds(dk, dv) <= 160 * 1024;
+}
+
+// Per-shape constants, declared inside every templated function; at dk 96,
+// dv 192: C 64, QS 112, VS 208, NCT 12, NDT 6.
+#define WIDE_CONSTS(DK_, DV_)                                                 \
+  using MW = MfCfg<DV_, DK_>;                                                 \
+  constexpr int kWideDv = DV_;                                                \
+  constexpr int kWC = MW::C, kWQS = MW::QS, kWVS = MW::VS;                    \
+  constexpr int kWNCS = DV_ / 32; /* 32-deep steps over dv */                 \
+  static_assert(wide_shape(DK_, DV_), "head shape of the wide backward")
 
 // The state S^T published by the dq pass's state waves keeps its 8-column
 // blocks XOR-swizzled by bit 3 of the row: element (c, d) sits at
@@ -66,10 +81,12 @@ struct TileIdx {
 // ---------------------------------------------------------------------------
 // dq pass
 // ---------------------------------------------------------------------------
+template <int DKT, int DV>
 __device__ __forceinline__ void wide_dq_role(
     const bf16 *__restrict__ dout, bf16 *__restrict__ dq, const Item &it, int h, int H,
     float scale, int rt, int w, bf16 *sD, const bf16 *sK, const bf16 *sV, const bf16 *sSt,
     const float *sPow) {
+  WIDE_CONSTS(DKT, DV);
   constexpr int C = kWC, QS = kWQS, VS = kWVS, VV = MW::VV, NDT = MW::NDT, NJS = MW::NJS;
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
   const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
@@ -160,7 +177,7 @@ __device__ __forceinline__ void wide_dq_role(
       }
     // dq row i: this lane holds dk values 16 dt + 4 g .. + 3
     if (i_row < chunk_rows(it, ch)) {
-      bf16 *dst = dq + ((it.t0 + (long long)ch * C + i_row) * H + h) * 96 + 4 * g;
+      bf16 *dst = dq + ((it.t0 + (long long)ch * C + i_row) * H + h) * DKT + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         bf16x4 t;
@@ -181,12 +198,14 @@ __device__ __forceinline__ void wide_dq_role(
 // With `pair` set (every sequence is cut into exactly two segments and the
 // slots hold the raw local quantities, not yet scanned), the incoming value
 // of the second segment is formed here: U_0 + lambda^len0 S0.
+template <int DKT, int DV>
 __device__ __forceinline__ void wide_state_role(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const float *__restrict__ s0,
     const float *__restrict__ slots, const Item &it, int idx, int h, int H, int rt, int w,
     bf16 *sK, bf16 *sKs, bf16 *sV, bf16 *sSt, const float *sPow, const float *pair_add,
     float pair_scale) {
-  constexpr int C = kWC, DK = 96, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
+  WIDE_CONSTS(DKT, DV);
+  constexpr int C = kWC, DK = DKT, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
   constexpr int SDT = MW::SDT, SCT = MW::SCT, NJS = MW::NJS;
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
   const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
@@ -308,10 +327,12 @@ __device__ __forceinline__ void wide_state_role(
   }
 }
 
+template <int DKT, int DV>
 __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
     const float *__restrict__ s0, const float *__restrict__ slots, bf16 *__restrict__ dq,
     Plan plan, Decay dec, float scale, int H, int pair) {
+  WIDE_CONSTS(DKT, DV);
   __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sKs[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sV[kWC * kWVS];
@@ -332,17 +353,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
   if (tid <= kWC) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (role_wave < 4) {
-    wide_dq_role(dout, dq, it, h, H, scale, tid & 255, role_wave, sD, sK, sV, sSt, sPow);
+    wide_dq_role<DKT, DV>(dout, dq, it, h, H, scale, tid & 255, role_wave, sD, sK, sV, sSt, sPow);
   } else {
     const float *pair_add = nullptr;
     float pair_scale = 0.f;
     if (pair && !(it.flags & kFirstSeg) && s0) {  // second of two segments
       Item prev;
       load_item(plan, idx - 1, prev);
-      pair_add = s0 + ((long long)it.n * H + h) * 96 * kWideDv;
+      pair_add = s0 + ((long long)it.n * H + h) * DKT * DV;
       pair_scale = pow_f64(dec.lam[h], prev.t1 - prev.t0);
     }
-    wide_state_role(k, v, s0, slots, it, idx, h, H, tid & 255, role_wave - 4, sK, sKs, sV,
+    wide_state_role<DKT, DV>(k, v, s0, slots, it, idx, h, H, tid & 255, role_wave - 4, sK, sKs, sV,
                     sSt, sPow, pair_add, pair_scale);
   }
 }
@@ -350,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
 // ---------------------------------------------------------------------------
 // Reverse walk: dv and dk rows, Ch split over both roles
 // ---------------------------------------------------------------------------
-template <bool DV_ROLE>
+template <int DKT, int DV, bool DV_ROLE>
 __device__ __forceinline__ void wide_rev_role(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
@@ -359,13 +380,19 @@ __device__ __forceinline__ void wide_rev_role(
     bf16 *sK,
     bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow, const float *pair_add,
     float pair_scale) {
-  constexpr int C = kWC, DK = 96, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
+  WIDE_CONSTS(DKT, DV);
+  constexpr int C = kWC, DK = DKT, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
   constexpr int NDT = MW::NDT, NCT = MW::NCT, NJS = MW::NJS, NKS = MW::NKS;
-  // loads, 9 vectors per role thread and register stage: the dv role brings
-  // q and k (3 each) and dO rows 0-31 (3), the dk role v (6) and dO rows
-  // 32-63 (3)
+  // loads per role thread and register stage: the dv role brings q and k
+  // (QV each) and dO rows 0-31 (ND), the dk role v (VV) and dO rows 32-63
+  // (ND); at d_v 192 that is 9 vectors for either role
+  constexpr int ND = 32 * MW::NVV / 256;
   constexpr int NA = DV_ROLE ? QV : VV;  // q then k, or v
-  constexpr int NL = (DV_ROLE ? 2 * QV : VV) + 3;
+  constexpr int NL = (DV_ROLE ? 2 * QV : VV) + ND;
+  // Ch: each wave owns RB d tiles (half of them) x CB column tiles (a
+  // quarter of them)
+  constexpr int RB = NDT / 2, CB = NCT / 4;
+  static_assert(NDT % 2 == 0 && NCT % 4 == 0 && 32 * MW::NVV % 256 == 0, "reverse split");
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
   const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
   const unsigned rowKb = (unsigned)(H * DK * 2), rowVb = (unsigned)(H * kWideDv * 2);
@@ -373,7 +400,7 @@ __device__ __forceinline__ void wide_rev_role(
   const int i_row = 16 * w + l16;
   const long long state_off = ((long long)it.n * H + h) * DK * kWideDv;
   const TileIdx<NA> ia(rt, DV_ROLE ? MW::NQV : MW::NVV);
-  const TileIdx<3> idh(rt, MW::NVV);  // rows 0-31 of the dO tile
+  const TileIdx<ND> idh(rt, MW::NVV);  // rows 0-31 of the dO tile
   const int drow0 = DV_ROLE ? 0 : 32;
   auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
 
@@ -397,8 +424,8 @@ __device__ __forceinline__ void wide_rev_role(
         r[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, ia.row[m] * rowVb + ia.col[m] * 16, 0, 0);
     }
 #pragma unroll
-    for (int m = 0; m < 3; ++m)
-      r[NL - 3 + m] = __builtin_amdgcn_raw_buffer_load_b128(
+    for (int m = 0; m < ND; ++m)
+      r[NL - ND + m] = __builtin_amdgcn_raw_buffer_load_b128(
           bd, (drow0 + idh.row[m]) * rowVb + idh.col[m] * 16, 0, 0);
   };
   float fqr[NA];  // dv role: scale * lambda^(t+1) of the q rows this thread stores
@@ -421,23 +448,24 @@ __device__ __forceinline__ void wide_rev_role(
         *reinterpret_cast<u32x4 *>(sV + ia.row[m] * VS + 8 * ia.col[m]) = r[m];
     }
 #pragma unroll
-    for (int m = 0; m < 3; ++m)
-      *reinterpret_cast<u32x4 *>(sD + (drow0 + idh.row[m]) * VS + 8 * idh.col[m]) = r[NL - 3 + m];
+    for (int m = 0; m < ND; ++m)
+      *reinterpret_cast<u32x4 *>(sD + (drow0 + idh.row[m]) * VS + 8 * idh.col[m]) = r[NL - ND + m];
   };
 
-  // this wave's 3 x 3 tiles of the carried gradient Ch: d tiles dt0.., column
-  // tiles ct0.. (0-5 on the dv role, 6-11 on the dk role). Ch starts as
+  // this wave's RB x CB tiles of the carried gradient Ch: d tiles dt0..,
+  // column tiles ct0.. (the first half on the dv role, the second half on
+  // the dk role; 0-5 and 6-11 at d_v 192). Ch starts as
   // dL/dS_final for a sequence's last item, else as the combined carry
   // flowing out of the next item (its slot)
-  const int dt0 = 3 * (w >> 1), ct0 = (DV_ROLE ? 0 : 6) + 3 * (w & 1);
+  const int dt0 = RB * (w >> 1), ct0 = (DV_ROLE ? 0 : NCT / 2) + CB * (w & 1);
   const float *cin = (it.flags & kLastSeg)
                          ? (ds_final ? ds_final + state_off : nullptr)
                          : cslots + ((long long)(idx + 1) * H + h) * DK * kWideDv;
-  f32x4 accC[3][3];
+  f32x4 accC[RB][CB];
 #pragma unroll
-  for (int a = 0; a < 3; ++a)
+  for (int a = 0; a < RB; ++a)
 #pragma unroll
-    for (int b = 0; b < 3; ++b) {
+    for (int b = 0; b < CB; ++b) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
       const int d = 16 * (dt0 + a) + 4 * g;
       const int c = 16 * (ct0 + b) + l16;
@@ -454,9 +482,9 @@ __device__ __forceinline__ void wide_rev_role(
     }
   auto publish = [&]() {  // Ch^T as bf16, row c, columns d
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
+      for (int b = 0; b < CB; ++b) {
         bf16x4 t;
 #pragma unroll
         for (int r = 0; r < 4; ++r) t[r] = (bf16)accC[a][b][r];
@@ -605,27 +633,27 @@ __device__ __forceinline__ void wide_rev_role(
     // Ch <- lambda^L Ch + scale sum_t lambda^(t+1) q_t^T dO_t (this wave's tiles)
     const float lamL = sPow[L];
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
-      for (int b = 0; b < 3; ++b) accC[a][b] *= lamL;
+      for (int b = 0; b < CB; ++b) accC[a][b] *= lamL;
 #pragma unroll
     for (int s = 0; s < NJS; ++s) {
-      bf16x8 qa[3], dfr[3];  // scale lambda^(t+1) q_t (P k-set over t) and dO
+      bf16x8 qa[RB], dfr[CB];  // scale lambda^(t+1) q_t (P k-set over t) and dO
       const int row = 32 * s + 4 * g + tr_row;
 #pragma unroll
-      for (int a = 0; a < 3; ++a) {
+      for (int a = 0; a < RB; ++a) {
         const bf16 *base = sQs + row * QS + 16 * (dt0 + a) + tr_col;
         qa[a] = cat8(tr4(base), tr4(base + 16 * QS));
       }
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
+      for (int b = 0; b < CB; ++b) {
         const bf16 *base = sD + row * VS + 16 * (ct0 + b) + tr_col;
         dfr[b] = cat8(tr4(base), tr4(base + 16 * VS));
       }
 #pragma unroll
-      for (int a = 0; a < 3; ++a)
+      for (int a = 0; a < RB; ++a)
 #pragma unroll
-        for (int b = 0; b < 3; ++b) accC[a][b] = mfma(qa[a], dfr[b], accC[a][b]);
+        for (int b = 0; b < CB; ++b) accC[a][b] = mfma(qa[a], dfr[b], accC[a][b]);
     }
     __syncthreads();  // B: every read of chunk ch and Ch_in is done
     store(rx);
@@ -639,9 +667,9 @@ __device__ __forceinline__ void wide_rev_role(
   // lambda^0 = 1 and no rows)
   if (ds0 && (it.flags & kFirstSeg)) {
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < RB; ++a)
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
+      for (int b = 0; b < CB; ++b) {
         const int d = 16 * (dt0 + a) + 4 * g;
         const int c = 16 * (ct0 + b) + l16;
 #pragma unroll
@@ -650,11 +678,13 @@ __device__ __forceinline__ void wide_rev_role(
   }
 }
 
+template <int DKT, int DV>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
     float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H, int pair) {
+  WIDE_CONSTS(DKT, DV);
   __shared__ __attribute__((aligned(16))) bf16 sQ[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sQs[kWC * kWQS];
   __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
@@ -680,31 +710,49 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
   if (pair && !(it.flags & kLastSeg) && ds_final) {  // first of two segments
     Item next;
     load_item(plan, idx + 1, next);
-    pair_add = ds_final + ((long long)it.n * H + h) * 96 * kWideDv;
+    pair_add = ds_final + ((long long)it.n * H + h) * DKT * DV;
     pair_scale = pow_f64(dec.lam[h], next.t1 - next.t0);
   }
   if (wave < 4)
-    wide_rev_role<true>(q, k, v, dout, ds_final, cslots, dv_out, ds0, it, idx, h, H, scale,
+    wide_rev_role<DKT, DV, true>(q, k, v, dout, ds_final, cslots, dv_out, ds0, it, idx, h, H, scale,
                         tid & 255, wave, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
   else
-    wide_rev_role<false>(q, k, v, dout, ds_final, cslots, dk_out, ds0, it, idx, h, H, scale,
+    wide_rev_role<DKT, DV, false>(q, k, v, dout, ds_final, cslots, dk_out, ds0, it, idx, h, H, scale,
                          tid & 255, wave - 4, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
 }
 
-bool bwd_wide_ok(int dk, int dv) { return dk == 96 && dv == kWideDv; }
+bool bwd_wide_ok(int dk, int dv) { return wide_shape(dk, dv); }
+
+// One head shape; see launch_bwd_wide.
+template <int DKT, int DV>
+static void launch_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
+                           hipStream_t s) {
+  const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, 1);
+  hipLaunchKernelGGL((bwd_dq_wide_kernel<DKT, DV>), dim3(grid), dim3(512), 0, s, (const bf16 *)a.k,
+                     (const bf16 *)a.v, (const bf16 *)a.dout, a.s0, a.slots, (bf16 *)a.dq, p,
+                     dec, a.scale, a.H, pair);
+  hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DKT, DV>), dim3(grid), dim3(512), 0, s, (const bf16 *)a.q,
+                     (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.ds_final,
+                     a.cslots, (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H,
+                     pair);
+}
 
 // pair: the segment slots hold unscanned local quantities and every sequence
 // has exactly two segments (the kernels join them on load).
 hipError_t launch_bwd_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
                            hipStream_t s) {
-  const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, 1);
-  hipLaunchKernelGGL(bwd_dq_wide_kernel, dim3(grid), dim3(512), 0, s, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (const bf16 *)a.dout, a.s0, a.slots, (bf16 *)a.dq, p,
-                     dec, a.scale, a.H, pair);
-  hipLaunchKernelGGL(bwd_dkdv_wide_kernel, dim3(grid), dim3(512), 0, s, (const bf16 *)a.q,
-                     (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.ds_final,
-                     a.cslots, (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H,
-                     pair);
+  // the shapes wide_shape() admits
+  switch (a.dk_dim * 1000 + a.dv) {
+    case 96192: launch_wide<96, 192>(p, a, dec, pair, s); break;
+    case 96128: launch_wide<96, 128>(p, a, dec, pair, s); break;
+    case 96064: launch_wide<96, 64>(p, a, dec, pair, s); break;
+    case 64192: launch_wide<64, 192>(p, a, dec, pair, s); break;
+    case 64128: launch_wide<64, 128>(p, a, dec, pair, s); break;
+    case 64064: launch_wide<64, 64>(p, a, dec, pair, s); break;
+    case 128128: launch_wide<128, 128>(p, a, dec, pair, s); break;
+    case 128064: launch_wide<128, 64>(p, a, dec, pair, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

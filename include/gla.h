@@ -161,7 +161,9 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
  * Shapes, dtypes and chunk as for gla_chunk_fwd: bf16 with dk = 64, 96 or
  * 128 and dv a multiple of 64 runs on the matrix cores; fp32, other head
  * sizes and chunk = 32 run on the vector ALUs (fp32 arithmetic). The workspace is
- * never 0 for tokens > 0 unless dv fits one dv tile. Checks as for
+ * 0 when one workgroup covers all of dv (bf16 with dv = 64, 128 or 192 at
+ * dk = 64 or 96, dv = 64 or 128 at dk = 128) and no sequence is cut into
+ * time segments. Checks as for
  * gla_chunk_fwd; no output may overlap an input or another output. T = 0 is
  * valid: ds0 receives ds_final (or zeros).
  */

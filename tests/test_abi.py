@@ -165,8 +165,8 @@ def test_decode_argument_errors(L):
 
 
 def test_backward_argument_errors(L):
-    # dv = 128: two dv tiles whose partial sums need workspace at any size
-    def bwd(dt=BF16, B=2, T=100, H=4, dk=96, dv=128, chunk=0, q=A[0], k=A[1], v=A[2],
+    # dv = 256: four dv tiles whose partial sums need workspace at any size
+    def bwd(dt=BF16, B=2, T=100, H=4, dk=96, dv=256, chunk=0, q=A[0], k=A[1], v=A[2],
             s0=None, do=A[3], dsf=None, dq=A[4], dk_=A[5], dv_=A[6], ds0=None,
             ws=A[7], wsb=1 << 40, decay=GOOD):
         return L.gla_chunk_bwd(dt, B, T, H, dk, dv, chunk, q, k, v, dptr(decay), 1.0, s0,
@@ -193,9 +193,15 @@ def test_backward_argument_errors(L):
     d = GOOD.copy()
     d[3] = float("inf")
     assert bwd(decay=d) == DECAY
-    need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 128, 0)
-    # dq and dk partials: 2 dv tiles x 16 heads x 16,384 tokens x 96 fp32, twice
-    assert need == 2 * 2 * 16 * 8 * 2048 * 96 * 4
+    need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 256, 0)
+    # dq and dk partials: 4 dv tiles x 16 heads x 16,384 tokens x 96 fp32, twice
+    assert need == 2 * 4 * 16 * 8 * 2048 * 96 * 4
+    # dv = 128 and 64 take the workgroup-per-head kernels as dv = 192 does:
+    # no partials; 8 x 16 units in 2 time segments (states and carries)
+    for dv in (128, 64):
+        need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, dv, 0)
+        assert need == 2 * (8 * 2 * 16 * 96 * dv * 4), dv
+    assert L.gla_chunk_bwd_workspace_bytes(BF16, 2, 100, 4, 96, 128, 0) == 0
     # dv = 192: one workgroup per (sequence, head) over all of dv, no partials;
     # 8 x 16 units are split into 2 time segments, whose incoming states and
     # carried gradients (fp32 96 x 192 per segment and head) are the workspace

@@ -72,14 +72,15 @@ def test_backward_widest_value_head():
     _check("bwd dv256", _run(x, do, dsf), _oracle(x, do, dsf))
 
 
-def test_backward_two_segments_joined_on_load():
+@pytest.mark.parametrize("dv", [192, 128, 64])
+def test_backward_two_segments_joined_on_load(dv):
     """8 x 16 units of 256 tokens: two time segments per sequence, whose
-    local states and carries the wide kernels join with S0 and dL/dS_final
-    as they load them (no scan launch)."""
-    x, do, dsf = _inputs(707, 8, 256, 16, 192)
-    need = gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 16, 96, 192, 0)
-    assert need == 2 * (8 * 2 * 16 * 96 * 192 * 4)  # two segments' states and carries
-    _check("bwd two segments", _run(x, do, dsf), _oracle(x, do, dsf))
+    local states and carries the wide kernels (one workgroup over all of
+    d_v) join with S0 and dL/dS_final as they load them (no scan launch)."""
+    x, do, dsf = _inputs(707 + dv, 8, 256, 16, dv)
+    need = gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 16, 96, dv, 0)
+    assert need == 2 * (8 * 2 * 16 * 96 * dv * 4)  # two segments' states and carries
+    _check("bwd two segments dv%d" % dv, _run(x, do, dsf), _oracle(x, do, dsf))
 
 
 def test_backward_max_heads_with_lambda_one():
@@ -140,13 +141,15 @@ DK_DV_OFF96 = [(64, 64), (64, 192), (64, 256), (128, 64), (128, 128), (128, 192)
 @pytest.mark.parametrize("T", [17, 130])
 @pytest.mark.parametrize("dk,dv", DK_DV_OFF96)
 def test_backward_dk64_dk128(dk, dv, T):
-    """Key heads of 64 and 128 on the matrix cores: d_v tiles of 64 columns
-    at dk 64 and of 32 at dk 128 (as the forward), one partial per tile."""
+    """Key heads of 64 and 128 on the matrix cores: one workgroup over all
+    of d_v where its tiles fit the LDS (d_v 64 and 128, and 192 at dk 64),
+    else d_v tiles of 64 columns at dk 64 and of 32 at dk 128 (as the
+    forward) with one partial sum per tile."""
     x, do, dsf = _inputs(760 + dk + dv + T, 2, T, 3, dv, dk=dk)
     _check("bwd dk%d dv%d T%d" % (dk, dv, T), _run(x, do, dsf), _oracle(x, do, dsf))
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (128, 192)])
 def test_backward_dk64_dk128_time_segments_and_packed(dk, dv):
     """dk 64 and 128: a fixed batch cut into time segments (boundary pass
     and both scans), then packed sequences with empty, short and long
@@ -165,16 +168,16 @@ def test_backward_dk64_dk128_time_segments_and_packed(dk, dv):
     np.testing.assert_array_equal(got[3][1], dsf[1].astype(np.float64))
 
 
-@pytest.mark.parametrize("T", [700, 1000])
-def test_backward_time_segments(T):
+@pytest.mark.parametrize("T,dv", [(700, 192), (1000, 192), (700, 128), (1000, 64)])
+def test_backward_time_segments(T, dv):
     """Few chains and a high workgroup target force time segments: the
     forward state pass and combine give each segment its incoming state,
     the carry pass and reverse combine its incoming gradient."""
     from gla_testutil import env
-    x, do, dsf = _inputs(720 + T, 2, T, 3, 192)
+    x, do, dsf = _inputs(720 + T + dv, 2, T, 3, dv)
     with env(GLA_TARGET_WGS=4096):
         got = _run(x, do, dsf)
-    _check("bwd segmented T%d" % T, got, _oracle(x, do, dsf))
+    _check("bwd segmented T%d dv%d" % (T, dv), got, _oracle(x, do, dsf))
 
 
 def test_backward_long_context_sampled_heads():
@@ -212,13 +215,14 @@ def _run_varlen(x, do, dsf):
     return host(dq), host(dk), host(dv), host(ds0)
 
 
-@pytest.mark.parametrize("lengths", [[5, 0, 130, 1, 64, 65, 300],
-                                     [2000, 1, 700]])
-def test_backward_varlen_matches_oracle(lengths):
+@pytest.mark.parametrize("lengths,dv", [([5, 0, 130, 1, 64, 65, 300], 192),
+                                        ([2000, 1, 700], 192),
+                                        ([5, 0, 130, 1, 2000, 65, 300], 128)])
+def test_backward_varlen_matches_oracle(lengths, dv):
     """Packed sequences with empty, one-token, chunk-aligned and ragged
     lengths (one workgroup per sequence), and a few long sequences (time
     segments from the device planner)."""
-    x, do, dsf = _varlen_case(730 + len(lengths), lengths)
+    x, do, dsf = _varlen_case(730 + len(lengths), lengths, dv=dv)
     got = _run_varlen(x, do, dsf)
     ref = O.gla_bwd_varlen(x["cu_seqlens"], x["q"], x["k"], x["v"], x["decay"], do, 1.0,
                            x["s0"], dsf)
