@@ -768,8 +768,8 @@ static void launch_boundary_dvt(const Plan &p, const BwdArgs &a, const Decay &de
                      (int)g);
 }
 
-// d_v tiles as the forward's: 96 or 64 columns at dk 96, 64 at dk 64, 32 at
-// dk 128
+// d_v tiles: 96 or 64 columns at dk 96, 64 at dk 64, 32 at dk 128 (where
+// the forward, without a decay-scaled k copy in LDS, runs 64)
 hipError_t launch_bwd_boundary(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
                                hipStream_t s) {
   if (a.dk_dim == 64) launch_boundary_dvt<64, 64>(p, a, dec, s);

@@ -213,9 +213,12 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H, int dv,
     int final_in_slot, NormPtrs np) {
   using M = MfCfg<DVT, DKT>;
+  // dk 128: the state waves scale k in registers (no third 64 x 144 tile),
+  // which leaves LDS room for 64-column d_v tiles
+  constexpr bool KSR = DKT == 128;
   __shared__ __attribute__((aligned(16))) bf16 sQ[2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
-  __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sKs[KSR ? 8 : 2 * M::C * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
   __shared__ __attribute__((aligned(16))) bf16 sSt0[M::SROWS * M::QS];
   __shared__ __attribute__((aligned(16))) bf16 sSt1[M::SROWS * M::QS];
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
     output_role<DVT, NORM, DKT>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ,
                                 sK, sV, sSt0, sSt1, sPow);
   else
-    state_role<DVT, true, NORM, DKT>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
+    state_role<DVT, true, NORM, DKT, KSR>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
                                      final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
                                      sSt0, sSt1, sPow, np);
 }
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
   if (it.flags & kLastSeg) return;  // no later segment reads it
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
-  state_role<DVT, false, NORM, DKT>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
+  state_role<DVT, false, NORM, DKT, DKT == 128>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
                                dtile * DVT, 0, tid, __builtin_amdgcn_readfirstlane(tid >> 6),
                                nullptr, sKs, sV, nullptr, nullptr, sPow, np);
 }
@@ -288,16 +291,16 @@ static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
 
 // dk 96 runs d_v tiles of 96 or 64 columns, dk 64 tiles of 64 (a wave
 // stages its output rows in its q rows, dk + 16 elements wide), dk 128
-// tiles of 32 (three double-buffered 64 x 128 q/k tiles leave LDS room for
-// no wider state)
+// tiles of 64 (with k scaled in registers: two double-buffered 64 x 128
+// q/k tiles, 132 KB of LDS)
 void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s) {
   if (a.dk == 64) {
     if (a.norm) launch_dvt<64, true, 64>(state_only, p, a, dec, s);
     else launch_dvt<64, false, 64>(state_only, p, a, dec, s);
   } else if (a.dk == 128) {
-    if (a.norm) launch_dvt<32, true, 128>(state_only, p, a, dec, s);
-    else launch_dvt<32, false, 128>(state_only, p, a, dec, s);
+    if (a.norm) launch_dvt<64, true, 128>(state_only, p, a, dec, s);
+    else launch_dvt<64, false, 128>(state_only, p, a, dec, s);
   } else if (a.norm) {
     if (dvt == 96) launch_dvt<96, true, 96>(state_only, p, a, dec, s);
     else launch_dvt<64, true, 96>(state_only, p, a, dec, s);

@@ -589,7 +589,9 @@ bool fast_path_ok(int dt, int dk, int dv, int chunk) {
 
 int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }
 
-int fwd_dv_tile(int dk, int dv) { return dk == 64 ? 64 : dk == 128 ? 32 : fast_dv_tile(dv); }
+int fwd_dv_tile(int dk, int dv) { return dk == 64 || dk == 128 ? 64 : fast_dv_tile(dv); }
+
+int bwd_dv_tile(int dk, int dv) { return dk == 64 ? 64 : dk == 128 ? 32 : fast_dv_tile(dv); }
 
 int generic_chunk(int chunk) { return chunk == 32 ? 32 : 64; }
 

@@ -122,14 +122,17 @@ __device__ __forceinline__ int chunk_rows(const Item &it, int ch) {
 //          result holds z); z is published in row DVT of the state buffer.
 //          Every dv tile's workgroup computes z; the one at c0 = 0 stores it.
 // ---------------------------------------------------------------------------
-template <int DVT, bool FUSED, bool NORM = false, int DKT = 96>
+template <int DVT, bool FUSED, bool NORM = false, int DKT = 96, bool KSR = false>
 __device__ __forceinline__ void state_role(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, const Item &it, int idx, int h, int H, int dv,
     int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
     bf16 *sSt0, bf16 *sSt1, const float *sPow, NormPtrs np = NormPtrs{}) {
-  // sK (FUSED only), sKs and sV hold two chunk buffers each
+  // sK (FUSED only), sKs and sV hold two chunk buffers each. KSR: no
+  // decay-scaled copy of k in LDS (it frees a third q/k-sized tile); the
+  // raw k tile (sK when FUSED, else sKs) is scaled as its fragments are
+  // read, with the same rounding as the copy
   using M = MfCfg<DVT, DKT>;
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
@@ -211,12 +214,17 @@ __device__ __forceinline__ void state_role(
   };
   constexpr int KBUF = C * QS, VBUF = C * VS;  // elements per chunk buffer
   auto store_kv = [&](int L, int buf, const u32x4(&rk)[QV], const u32x4(&rv)[VV]) {
-    bf16 *dK = sK + buf * KBUF, *dKs = sKs + buf * KBUF, *dV = sV + buf * VBUF;
+    bf16 *dK = sK + buf * KBUF, *dV = sV + buf * VBUF;
+    bf16 *dKs = KSR && FUSED ? nullptr : sKs + buf * KBUF;
 #pragma unroll
     for (int m = 0; m < QV; ++m) {
       const int r = rowK[m];
       const u32x4 kr = NORM ? relu_bf16x8(rk[m]) : rk[m];
       if (FUSED) *reinterpret_cast<u32x4 *>(dK + r * QS + 8 * colK[m]) = kr;
+      if (KSR) {
+        if (!FUSED) *reinterpret_cast<u32x4 *>(dKs + r * QS + 8 * colK[m]) = kr;
+        continue;
+      }
       // decay-scaled copy lambda^(L-1-r) k_r; rows past the end are zero
       const float wgt = r < L ? sPow[max(L - 1 - r, 0)] : 0.f;
       const bf16x8 kv = __builtin_bit_cast(bf16x8, kr);
@@ -268,8 +276,21 @@ __device__ __forceinline__ void state_role(
     __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
     load_kv(ch + 2, rkn, rvn);
     store_kv(chunk_rows(it, ch + 1), cur ^ 1, rkx, rvx);
-    const bf16 *cKs = sKs + cur * KBUF, *cV = sV + cur * VBUF;
+    const bf16 *cKs = (KSR && FUSED ? sK : sKs) + cur * KBUF, *cV = sV + cur * VBUF;
     const float lamL = sPow[L];
+    // KSR: lambda^(L-1-t) for the rows t of this lane's fragments (P k-set),
+    // 0 past the chunk's end
+    float wk[M::NJS][8];
+    if (KSR) {
+#pragma unroll
+      for (int s = 0; s < M::NJS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t0 = 32 * s + 4 * g + e, t1 = t0 + 16;
+          wk[s][e] = t0 < L ? sPow[max(L - 1 - t0, 0)] : 0.f;
+          wk[s][4 + e] = t1 < L ? sPow[max(L - 1 - t1, 0)] : 0.f;
+        }
+    }
 #pragma unroll
     for (int a = 0; a < SDT; ++a)
 #pragma unroll
@@ -286,6 +307,10 @@ __device__ __forceinline__ void state_role(
       for (int a = 0; a < SDT; ++a) {
         const bf16 *base = cKs + row * QS + 16 * (dt0 + a) + tr_col;
         af[a] = cat8(tr4(base), tr4(base + 16 * QS));
+        if (KSR) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) af[a][e] = (bf16)((float)af[a][e] * wk[s][e]);
+        }
       }
 #pragma unroll
       for (int b = 0; b < SCT; ++b) {

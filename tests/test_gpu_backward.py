@@ -135,7 +135,7 @@ def test_backward_is_bitwise_deterministic():
         np.testing.assert_array_equal(u, w)
 
 
-DK_DV_OFF96 = [(64, 64), (64, 192), (64, 256), (128, 64), (128, 128), (128, 192)]
+DK_DV_OFF96 = [(64, 64), (64, 192), (64, 256), (128, 64), (128, 128), (128, 192), (128, 256)]
 
 
 @pytest.mark.parametrize("T", [17, 130])

@@ -123,7 +123,7 @@ def test_ragged_lengths_mfma(T, with_s0):
 
 
 @pytest.mark.parametrize("T", [1, 63, 65, 200])
-@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 192), (64, 256), (128, 64), (128, 192)])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 192), (64, 256), (128, 64), (128, 192), (128, 256)])
 def test_ragged_lengths_mfma_dk64_dk128(T, dk, dv):
     """d_k = 64 (d_v tiles of 64 columns) and 128 (tiles of 32) on the
     matrix cores."""
