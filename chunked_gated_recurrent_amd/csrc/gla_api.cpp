@@ -249,7 +249,7 @@ bool bwd_wide_path(int dt, int dk, int dv, int chunk) {
 // dv tiles per unit the backward plans its time segments for
 int bwd_plan_ndt(int dt, int dk, int dv, int chunk) {
   if (bwd_wide_path(dt, dk, dv, chunk)) return 1;
-  return fast_path_ok(dt, dk, dv, chunk) ? dv / bwd_dv_tile(dk, dv) : 0;
+  return fast_path_ok(dt, dk, dv, chunk) ? dv / fwd_dv_tile(dk, dv) : 0;
 }
 
 BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv) {
@@ -257,7 +257,7 @@ BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv)
   memset(&bp, 0, sizeof(bp));
   bp.hp = hp;
   bp.wide = hp.fast && bwd_wide_ok(dk, dv);
-  bp.dvt = bp.wide ? dv : hp.fast ? bwd_dv_tile(dk, dv) : valu_bwd_tile(dv);
+  bp.dvt = bp.wide ? dv : hp.fast ? fwd_dv_tile(dk, dv) : valu_bwd_tile(dv);
   bp.ndt = dv / bp.dvt;
   const size_t base = align256(hp.ws_bytes);
   const size_t slot_bytes =
@@ -301,7 +301,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     a.slots = (float *)(ws + hp.off_slots);
     a.cslots = (float *)(ws + bp.off_cslots);
     if (hp.fast) {
-      if (launch_bwd_boundary(bwd_dv_tile(a.dk_dim, a.dv), p, a, dec, s) != hipSuccess)
+      if (launch_bwd_boundary(fwd_dv_tile(a.dk_dim, a.dv), p, a, dec, s) != hipSuccess)
         return GLA_ERR_HIP;
       // two segments per sequence: the wide kernels join them on load
       pair = bp.wide && p.mode == kPlanFixed && p.G == 2;

@@ -1,6 +1,7 @@
 // gla_bwd_mfma.hip -- backward of the chunked Simple GLA forward for bf16
 // inputs with dk = 96, 64 or 128 on the gfx950 matrix cores (d_v tiles as
-// the forward's: 96 or 64 columns at dk 96, 64 at dk 64, 32 at dk 128).
+// the forward's: 96 or 64 columns at dk 96, 64 at dk 64 and 128), for the
+// heads whose whole d_v does not fit one workgroup of gla_bwd_wide.hip.
 //
 // The gradients of S_t = lambda S_{t-1} + k_t^T v_t, o_t = scale q_t S_t
 // (Laplace 3B / Trainium2 page, sections "GLA mixer" and "Challenge 3":
@@ -768,12 +769,12 @@ static void launch_boundary_dvt(const Plan &p, const BwdArgs &a, const Decay &de
                      (int)g);
 }
 
-// d_v tiles: 96 or 64 columns at dk 96, 64 at dk 64, 32 at dk 128 (where
-// the forward, without a decay-scaled k copy in LDS, runs 64)
+// d_v tiles as the forward's: 96 or 64 columns at dk 96, 64 at dk 64 and
+// 128
 hipError_t launch_bwd_boundary(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
                                hipStream_t s) {
   if (a.dk_dim == 64) launch_boundary_dvt<64, 64>(p, a, dec, s);
-  else if (a.dk_dim == 128) launch_boundary_dvt<32, 128>(p, a, dec, s);
+  else if (a.dk_dim == 128) launch_boundary_dvt<64, 128>(p, a, dec, s);
   else if (dvt == 96) launch_boundary_dvt<96, 96>(p, a, dec, s);
   else launch_boundary_dvt<64, 96>(p, a, dec, s);
   return hipGetLastError();
@@ -795,7 +796,7 @@ static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,
                            const Decay &dec, hipStream_t s) {
   if (a.dk_dim == 64) launch_bwd_dvt<64, 64>(p, a, dec, s);
-  else if (a.dk_dim == 128) launch_bwd_dvt<32, 128>(p, a, dec, s);
+  else if (a.dk_dim == 128) launch_bwd_dvt<64, 128>(p, a, dec, s);
   else if (dvt == 96) launch_bwd_dvt<96, 96>(p, a, dec, s);
   else launch_bwd_dvt<64, 96>(p, a, dec, s);
   const long long n4 = (long long)p.total_T * a.H * (a.dk_dim / 4);

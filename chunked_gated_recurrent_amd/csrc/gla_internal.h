@@ -89,9 +89,6 @@ struct BwdArgs {
 bool fast_path_ok(int dt, int dk, int dv, int chunk);
 int fast_dv_tile(int dv);
 int fwd_dv_tile(int dk, int dv);
-// d_v tile of the d_v-tiled matrix-core backward (its dk 128 kernels keep a
-// decay-scaled q/k copy in LDS and run 32 columns)
-int bwd_dv_tile(int dk, int dv);
 int generic_chunk(int chunk);
 hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items, hipStream_t s);
 hipError_t launch_order(const Plan &p, int chunk, int32_t *order, hipStream_t s);

@@ -591,8 +591,6 @@ int fast_dv_tile(int dv) { return dv % 96 == 0 ? 96 : 64; }
 
 int fwd_dv_tile(int dk, int dv) { return dk == 64 || dk == 128 ? 64 : fast_dv_tile(dv); }
 
-int bwd_dv_tile(int dk, int dv) { return dk == 64 ? 64 : dk == 128 ? 32 : fast_dv_tile(dv); }
-
 int generic_chunk(int chunk) { return chunk == 32 ? 32 : 64; }
 
 hipError_t launch_planner(const Plan &p, int32_t *index, int4 *items,

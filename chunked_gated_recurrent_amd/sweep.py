@@ -147,7 +147,7 @@ def sweep_backward():
     cases = [("bf16", 8, 2048, 16, 96, 192), ("bf16", 32, 2048, 16, 96, 192),
              ("bf16", 8, 2048, 16, 96, 128), ("bf16", 8, 2048, 16, 96, 256),
              ("bf16", 8, 2048, 16, 64, 128), ("bf16", 8, 2048, 16, 128, 128),
-             ("f32", 8, 2048, 16, 96, 192)]
+             ("bf16", 8, 2048, 16, 128, 256), ("f32", 8, 2048, 16, 96, 192)]
     for dtype, B, T, H, dk, dv in cases:
         lam = W.geometric_decays(H)
         e = _elt(dtype)
