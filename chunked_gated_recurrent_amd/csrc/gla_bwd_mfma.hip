@@ -769,11 +769,15 @@ static void launch_boundary_dvt(const Plan &p, const BwdArgs &a, const Decay &de
                      (int)g);
 }
 
-// d_v tiles as the forward's: 96 or 64 columns at dk 96, 64 at dk 64 and
-// 128
+// d_v tiles as the forward's (96 or 64 columns at dk 96, 64 at dk 64 and
+// 128), except dk 96 with dv 128 (always the per-head backward): one tile
+// of all 128 columns, so q and k are requested once per token instead of
+// once per tile (66 KB of LDS, two workgroups per CU). The same at dv 192
+// (82 KB, one workgroup per CU) measured slower than two 96-column tiles.
 hipError_t launch_bwd_boundary(int dvt, const Plan &p, const BwdArgs &a, const Decay &dec,
                                hipStream_t s) {
-  if (a.dk_dim == 64) launch_boundary_dvt<64, 64>(p, a, dec, s);
+  if (a.dk_dim == 96 && a.dv == 128) launch_boundary_dvt<128, 96>(p, a, dec, s);
+  else if (a.dk_dim == 64) launch_boundary_dvt<64, 64>(p, a, dec, s);
   else if (a.dk_dim == 128) launch_boundary_dvt<64, 128>(p, a, dec, s);
   else if (dvt == 96) launch_boundary_dvt<96, 96>(p, a, dec, s);
   else launch_boundary_dvt<64, 96>(p, a, dec, s);
