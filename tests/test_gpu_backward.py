@@ -149,7 +149,7 @@ def test_backward_dk64_dk128(dk, dv, T):
     _check("bwd dk%d dv%d T%d" % (dk, dv, T), _run(x, do, dsf), _oracle(x, do, dsf))
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (128, 192)])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (64, 192), (128, 64), (128, 192)])
 def test_backward_dk64_dk128_time_segments_and_packed(dk, dv):
     """dk 64 and 128: a fixed batch cut into time segments (boundary pass
     and both scans), then packed sequences with empty, short and long

@@ -100,6 +100,38 @@ def test_graph_long_sequence_forward_and_backward():
     _capture_and_replay(run, [o, S, dq, dk, dvv, ds0])
 
 
+@pytest.mark.parametrize("dk,dv", [(96, 128), (128, 128), (64, 192)])
+def test_graph_other_head_shapes(dk, dv):
+    """Time segments at other head shapes: the forward's state pass (d_k 128
+    scales k in registers), the backward's boundary pass and the per-head
+    backward kernels."""
+    dev = torch.device("cuda")
+    B, T, H = 1, 3000, 4
+    lam = W.geometric_decays(H)
+    q, k, v, s0 = W.device_normal_inputs(1530 + dk, (B, T), H, dk, dv, dev, (B, H, dk, dv), 0.1)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1531)
+    do = torch.randn(B, T, H, dv, generator=g, device=dev).to(torch.bfloat16)
+    dsf = torch.randn(B, H, dk, dv, generator=g, device=dev)
+    L = gla.lib()
+    wf = torch.empty(max(L.gla_chunk_fwd_workspace_bytes(1, B, T, H, dk, dv, 0), 1),
+                     dtype=torch.uint8, device=dev)
+    wb = torch.empty(max(L.gla_chunk_bwd_workspace_bytes(1, B, T, H, dk, dv, 0), 1),
+                     dtype=torch.uint8, device=dev)
+    assert wf.numel() > 1 and wb.numel() > 1, "expected the segmented paths"
+    o = torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, dk, dv, device=dev)
+    dq, dk_, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds0 = torch.empty(B, H, dk, dv, device=dev)
+
+    def run():
+        gla.gla_chunk_fwd(q, k, v, lam, initial_state=s0, out=o, final_state=S, workspace=wf)
+        gla.gla_chunk_bwd(q, k, v, lam, do, 1.0, s0, dsf, dq=dq, dk=dk_, dv=dvv, ds0=ds0,
+                          workspace=wb)
+
+    _capture_and_replay(run, [o, S, dq, dk_, dvv, ds0])
+
+
 def test_graph_packed_sequences():
     """Packed input with device-side planning (order kernel) and its
     backward, plus the short convolution's prefill and decode step."""
