@@ -22,7 +22,9 @@ gla_status check_common(int dt, int H, int dk, int dv, int chunk) {
   if (H < 1 || dk < 1 || dv < 1) return GLA_ERR_SHAPE;
   if (H > GLA_MAX_HEADS) return GLA_ERR_UNSUPPORTED;
   if (dk % 16 != 0 || dv % 16 != 0 || dk > 128 || dv > 256) return GLA_ERR_UNSUPPORTED;
-  if (chunk != 0 && chunk != 32 && chunk != 64 && chunk != 128) return GLA_ERR_UNSUPPORTED;
+  // 0 (the library default, 64), 32 (vector ALUs) or 64; no kernel runs
+  // 128-token chunks, so 128 is refused rather than served with 64
+  if (chunk != 0 && chunk != 32 && chunk != 64) return GLA_ERR_UNSUPPORTED;
   return GLA_OK;
 }
 
@@ -390,6 +392,7 @@ gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GLA_ERR_ALIGN;
     if (overlap(workspace, hp.ws_bytes, q, nqk) || overlap(workspace, hp.ws_bytes, k, nqk) ||
         overlap(workspace, hp.ws_bytes, v, nv) || overlap(workspace, hp.ws_bytes, o, nv) ||
         overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns))
@@ -447,6 +450,7 @@ gla_status gla_linear_attn_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv
   const HostPlan hp = plan_linear_attn(dt, B, T, H, dk, dv, chunk);
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GLA_ERR_ALIGN;
     for (int i = 0; i < 7; ++i)
       if (overlap(workspace, hp.ws_bytes, rp[i], rn[i])) return GLA_ERR_ALIAS;
     if (overlap(workspace, hp.ws_bytes, z_final, nz)) return GLA_ERR_ALIAS;
@@ -504,6 +508,7 @@ gla_status gla_linear_attn_fwd_varlen(gla_dtype dt, int N, int total_T, int H, i
   HostPlan hp = plan_linear_attn_varlen(dt, N, total_T, H, dk, dv, chunk);
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GLA_ERR_ALIGN;
     for (int i = 0; i < 8; ++i)
       if (overlap(workspace, hp.ws_bytes, rp[i], rn[i])) return GLA_ERR_ALIAS;
     if (overlap(workspace, hp.ws_bytes, z_final, nz)) return GLA_ERR_ALIAS;
@@ -569,6 +574,7 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
   const HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk);
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GLA_ERR_ALIGN;
     if (overlap(workspace, hp.ws_bytes, q, nqk) || overlap(workspace, hp.ws_bytes, k, nqk) ||
         overlap(workspace, hp.ws_bytes, v, nv) || overlap(workspace, hp.ws_bytes, o, nv) ||
         overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns) ||
@@ -641,6 +647,7 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
       dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GLA_ERR_ALIGN;
     for (int b = 0; b < 6; ++b)
       if (overlap(workspace, bp.ws_bytes, in[b], in_n[b])) return GLA_ERR_ALIAS;
     for (int a = 0; a < 4; ++a)
@@ -710,6 +717,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
   const BwdPlan bp = bwd_layout(hp, total_T, H, dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GLA_ERR_ALIGN;
     for (int b = 0; b < 7; ++b)
       if (overlap(workspace, bp.ws_bytes, in[b], in_n[b])) return GLA_ERR_ALIAS;
     for (int a = 0; a < 4; ++a)

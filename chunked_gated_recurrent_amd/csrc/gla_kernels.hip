@@ -579,10 +579,9 @@ __global__ __launch_bounds__(512) void decode_kernel(
 // ===========================================================================
 // launchers
 // ===========================================================================
-// The matrix-core path always runs 64-token chunks; a request for 128 is
-// served with 64 (results do not depend on the chunk beyond rounding), and
-// only an explicit 32 selects the vector-ALU path for these shapes. Forward
-// and backward take dk 96, 64 or 128.
+// The matrix-core path runs 64-token chunks (chunk 0 or 64); an explicit 32
+// selects the vector-ALU path for these shapes (the host refuses any other
+// chunk). Forward and backward take dk 96, 64 or 128.
 bool fast_path_ok(int dt, int dk, int dv, int chunk) {
   return dt == 1 && (dk == 96 || dk == 64 || dk == 128) && (dv % 64 == 0) && chunk != 32;
 }

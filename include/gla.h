@@ -23,17 +23,22 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers to caller-owned memory, dense and
- *     row-major in the documented layout, 16-byte aligned. The library never
- *     allocates, frees or keeps a pointer after it returns.
+ *     row-major in the documented layout, 16-byte aligned (the workspace
+ *     too; GLA_ERR_ALIGN otherwise). The library never allocates, frees or
+ *     keeps a pointer after it returns.
  *   - `decay_host` is a HOST array of H floats, read during the call only.
  *     Every lambda must be finite with 0 < lambda <= 1.
  *   - `dt` is the dtype of q, k, v and o (GLA_F32 or GLA_BF16). States and
  *     initial states are always fp32.
  *   - Shapes: 1 <= H <= 64; dk and dv multiples of 16 with dk <= 128 and
- *     dv <= 256. `chunk` is 0 (library default) or 32, 64 or 128; results do
- *     not depend on it beyond rounding. It is a hint: the kernels run 64-token
- *     chunks for 0, 64 and 128, and 32-token chunks (on the vector ALUs) for
- *     32.
+ *     dv <= 256. `chunk` is the number of tokens per chunk: 0 (the library
+ *     default, 64), 64 or 32; results do not depend on it beyond rounding.
+ *     64 runs on the matrix cores where the shape allows, 32 always on the
+ *     vector ALUs. Any other value, 128 included, returns
+ *     GLA_ERR_UNSUPPORTED: no kernel here runs 128-token chunks (the
+ *     Laplace 3B page's 128 matches the 128 partitions of a Trainium2
+ *     on-chip buffer; on gfx950 two double-buffered 128-token tiles of q,
+ *     k and v do not fit the 160 KB LDS beside the published state).
  *   - `stream` is a hipStream_t (NULL = the default stream). All work is
  *     enqueued on it as kernel launches; no call synchronises, allocates or
  *     records a memset, so a sequence of calls may be captured into a HIP

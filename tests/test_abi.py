@@ -83,6 +83,9 @@ def test_fwd_argument_errors(L):
     assert fwd(L, dv=512) == UNSUP
     assert fwd(L, dk=144) == UNSUP
     assert fwd(L, chunk=48) == UNSUP
+    # no kernel runs 128-token chunks: refused, not served with 64
+    assert fwd(L, chunk=128) == UNSUP
+    assert L.gla_chunk_fwd_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 128) == 0
     assert fwd(L, decay=False) == NULL
     assert fwd(L, q=None) == NULL
     assert fwd(L, o=None) == NULL
@@ -108,6 +111,9 @@ def test_fwd_workspace_contract(L):
     assert fwd(L, B=1, T=65536, H=16, decay=dec, ws=A[5], wsb=need - 1) == WS
     # scratch overlapping an input is rejected
     assert fwd(L, B=1, T=65536, H=16, decay=dec, ws=A[0], wsb=need) == ALIAS
+    # the workspace follows the 16-byte alignment of every other pointer
+    assert fwd(L, B=1, T=65536, H=16, decay=dec, ws=ctypes.c_void_p(A[5].value + 8),
+               wsb=need) == ALIGN
     # Laplace-shaped batch: enough chains, no scratch
     assert L.gla_chunk_fwd_workspace_bytes(BF16, 8, 2048, 16, 96, 192, 0) == 0
     assert L.gla_chunk_fwd_workspace_bytes(BF16, 0, 2048, 16, 96, 192, 0) == 0
@@ -142,6 +148,9 @@ def test_varlen_argument_errors(L):
     # is the dispatch order alone (32 int32, rounded up to 256 bytes)
     assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 32, 131072, 16, 96, 192, 0) == 256
     assert varlen(L, N=32, total=131072, H=16, decay=dec) == WS
+    assert varlen(L, N=32, total=131072, H=16, decay=dec,
+                  ws=ctypes.c_void_p(A[5].value + 4), wsb=4096) == ALIGN
+    assert varlen(L, chunk=128) == UNSUP
     # one short sequence needs no scratch at all
     assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 1, 100, 16, 96, 192, 0) == 0
 
