@@ -104,8 +104,8 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def _qkv(rng, lead, H, dk, dv, dtype):
-    sc = np.float32(1.0 / np.sqrt(dk))
+def _qkv(rng, lead, H, dk, dv, dtype, prescale=True):
+    sc = np.float32(1.0 / np.sqrt(dk)) if prescale else np.float32(1.0)
     q = rng.standard_normal(lead + (H, dk), dtype=np.float32) * sc
     k = rng.standard_normal(lead + (H, dk), dtype=np.float32) * sc
     v = rng.standard_normal(lead + (H, dv), dtype=np.float32)
@@ -113,11 +113,13 @@ def _qkv(rng, lead, H, dk, dv, dtype):
 
 
 def prefill_inputs(seed: int, B: int, T: int, H: int, dk: int, dv: int,
-                   dtype: str = "bf16", s0_sigma=None, decays=None) -> dict:
+                   dtype: str = "bf16", s0_sigma=None, decays=None,
+                   prescale: bool = True) -> dict:
     """q, k: [B, T, H, dk]; v: [B, T, H, dv] (uint16 bf16 bits or fp32);
-    s0: [B, H, dk, dv] fp32 or None; decay: [H] fp32."""
+    s0: [B, H, dk, dv] fp32 or None; decay: [H] fp32. prescale=False leaves
+    q and k at N(0, 1) (for a caller that passes dk**-0.5 as the scale)."""
     rng = np.random.default_rng(seed)
-    q, k, v = _qkv(rng, (B, T), H, dk, dv, dtype)
+    q, k, v = _qkv(rng, (B, T), H, dk, dv, dtype, prescale)
     s0 = None
     if s0_sigma is not None:
         s0 = rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(s0_sigma)
@@ -131,7 +133,7 @@ def varlen_lengths(seed: int, N: int, max_len: int) -> np.ndarray:
 
 def varlen_inputs(seed: int, N: int, max_len: int, H: int, dk: int, dv: int,
                   dtype: str = "bf16", s0_sigma=0.1, decays=None,
-                  lengths=None) -> dict:
+                  lengths=None, prescale: bool = True) -> dict:
     """Lengths are drawn first (uniform integers in [1, max_len]) unless
     given; q, k: [total, H, dk]; v: [total, H, dv]; cu_seqlens: [N+1] int32;
     s0: [N, H, dk, dv] fp32 or None."""
@@ -143,7 +145,7 @@ def varlen_inputs(seed: int, N: int, max_len: int, H: int, dk: int, dv: int,
     cu = np.zeros(N + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     total = int(cu[-1])
-    q, k, v = _qkv(rng, (total,), H, dk, dv, dtype)
+    q, k, v = _qkv(rng, (total,), H, dk, dv, dtype, prescale)
     s0 = None
     if s0_sigma is not None:
         s0 = rng.standard_normal((N, H, dk, dv), dtype=np.float32) * np.float32(s0_sigma)
@@ -159,10 +161,10 @@ def decode_state(seed: int, N: int, H: int, dk: int, dv: int,
 
 
 def decode_tokens(seed: int, step: int, N: int, H: int, dk: int, dv: int,
-                  dtype: str = "bf16"):
+                  dtype: str = "bf16", prescale: bool = True):
     """q, k: [N, H, dk]; v: [N, H, dv] for decode step `step`."""
     rng = np.random.default_rng([seed, step + 1])
-    return _qkv(rng, (N,), H, dk, dv, dtype)
+    return _qkv(rng, (N,), H, dk, dv, dtype, prescale)
 
 
 def spec_inputs(name: str, **overrides) -> dict:

@@ -81,17 +81,13 @@ def test_time_segments(dtype, dk, dv, T):
     _check(dtype, got, ref, "segments %s T%d" % (dtype, T))
 
 
-def test_laplace_shape_sampled():
-    """B8 T2048 H16 dk96 dv192 bf16 (the prefill batch shape): sampled
-    batch entries and heads against the oracle."""
+def test_laplace_shape_full():
+    """B8 T2048 H16 dk96 dv192 bf16 (the prefill batch shape): every head of
+    every batch entry against the oracle."""
     B, T, H = 8, 2048, 16
     q, k, v = _case(1000, B, T, H, 96, 192, "bf16")
     o, sf, zf = _run(q, k, v)
-    for b, h in [(0, 0), (3, 7), (7, 15)]:
-        sel = np.s_[b:b + 1, :, h:h + 1]
-        ro, rs, rz = O.linear_attention(q[sel], k[sel], v[sel])
-        _check("bf16", (o[sel], sf[b:b + 1, h:h + 1], zf[b:b + 1, h:h + 1]),
-               (ro, rs, rz), "laplace b%d h%d" % (b, h))
+    _check("bf16", (o, sf, zf), O.linear_attention(q, k, v), "laplace B8 T2048 all heads")
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("bf16", 96, 192), ("f32", 32, 32)])

@@ -2,10 +2,9 @@
 same seeded inputs. Bar: max|gpu - oracle| <= 1e-2 * max|oracle| for bf16
 inputs and <= 1e-4 for fp32 inputs, for outputs and final states.
 
-Full-size workloads are run in full on the GPU; where the oracle would take
-too long, it checks a sample of heads or sequences (each (sequence, head)
-chain is independent, so a sampled chain is checked exactly as in the full
-run)."""
+Full-size workloads are run in full on the GPU and compared in full: every
+head of every sequence, every decode row at every step (the threaded fp64
+oracle takes seconds for each of them)."""
 import numpy as np
 import pytest
 import torch
@@ -64,47 +63,47 @@ def test_laplace_prefill_full():
     check("laplace_prefill B8 T2048", o, ro, s, rs, TOL["bf16"])
 
 
-def test_long_context_sampled_heads():
-    """B1 T65536: all heads on the GPU (segmented carry), the oracle on the
-    fastest, a middle and the slowest head over the whole sequence."""
+def test_long_context_full():
+    """B1 T65536 from a random initial state (segmented carry on the GPU):
+    every head over the whole sequence, outputs and final states."""
     x = W.spec_inputs("long_context")
     o, s = run_fixed(x, chunk=64)
-    heads = [0, 7, 15]
-    ro, rs = oracle_fixed(x, heads=heads)
-    check("long_context T65536 heads 0,7,15", o[:, :, heads], ro, s[:, heads], rs, TOL["bf16"])
+    ro, rs = oracle_fixed(x)
+    check("long_context T65536 all heads", o, ro, s, rs, TOL["bf16"])
 
 
-def test_varlen_workload_sampled_heads():
+def test_varlen_workload_full():
+    """32 packed sequences with lengths uniform in [1, 8192]: every head of
+    every sequence."""
     x = W.spec_inputs("varlen")
     q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
     cu = dev(x["cu_seqlens"])
     o, sf = gla.gla_chunk_fwd_varlen(q, k, v, cu, x["decay"], initial_state=s0)
     torch.cuda.synchronize()
-    heads = [0, 9, 15]
-    ro, rs = oracle_varlen(x, heads=heads)
-    check("varlen N32 heads 0,9,15", host(o)[:, heads], ro, host(sf)[:, heads], rs,
-          TOL["bf16"], head_axis_o=1)
+    ro, rs = oracle_varlen(x)
+    check("varlen N32 all heads", host(o), ro, host(sf), rs, TOL["bf16"], head_axis_o=1)
 
 
-def test_batched_decode_100_steps_sampled():
+def test_batched_decode_100_steps_full():
+    """1,280 sequences x 16 heads, 100 consecutive steps in place: every
+    output row at every step, and every state after the last step."""
     spec = W.WORKLOADS["batched_decode"]
     N, H, dk, dv, steps = spec["N"], spec["H"], spec["dk"], spec["dv"], spec["steps"]
     seed = spec["seed"]
     lam = W.decays_for(spec)
     S = W.decode_state(seed, N, H, dk, dv, spec["state_sigma"])
-    sample = np.unique(np.linspace(0, N - 1, 24).astype(int))
-    ref_state = S[sample].astype(np.float64)
+    ref_state = S.astype(np.float64)
     state = dev(S)
     del S
     worst = 0.0
     for t in range(steps):
         q, k, v = W.decode_tokens(seed, t, N, H, dk, dv)
         o = gla.gla_decode_step(dev(q), dev(k), dev(v), lam, state)
-        ro = O.gla_decode(q[sample], k[sample], v[sample], lam, ref_state)
-        e = rel_err(host(o)[sample], ro)
+        ro = O.gla_decode(q, k, v, lam, ref_state)
+        e = rel_err(host(o), ro)
         worst = max(worst, e)
         assert e <= TOL["bf16"], (t, e)
-    es = rel_err(host(state)[sample], ref_state)
+    es = rel_err(host(state), ref_state)
     print("decode N1280 x100: worst o err %.3e, S err %.3e" % (worst, es))
     assert es <= TOL["bf16"]
 
@@ -159,7 +158,7 @@ def test_dk64_dk128_time_segments_and_packed_sequences(dk):
 
 @pytest.mark.parametrize("dtype,dk,dv,T,chunk", [
     ("bf16", 16, 32, 100, 32), ("f32", 32, 64, 130, 64), ("f32", 128, 256, 70, 0),
-    ("bf16", 64, 128, 129, 0), ("f32", 96, 192, 257, 128), ("bf16", 96, 128, 150, 0),
+    ("bf16", 64, 128, 129, 0), ("f32", 96, 192, 257, 64), ("bf16", 96, 128, 150, 0),
     ("bf16", 96, 64, 150, 0), ("bf16", 96, 256, 150, 0), ("bf16", 128, 256, 90, 0)])
 def test_shapes(dtype, dk, dv, T, chunk):
     x = W.prefill_inputs(7 + dk + T, 2, T, 2, dk, dv, dtype, 0.1, np.array([0.9, 0.995], np.float32))
@@ -230,11 +229,19 @@ def test_segmented_carry_matches_oracle_and_in_place_state():
 
 
 def test_chunk_sizes_agree():
+    """The two chunk sizes the library runs (32 on the vector ALUs, 64 on
+    the matrix cores) both meet the bar; 0 is the default 64 (bitwise the
+    same call) and 128, which no kernel runs, is refused."""
     x = W.prefill_inputs(31, 1, 300, 2, 96, 192, "bf16", 0.1, np.array([0.97, 0.999], np.float32))
     ro, rs = oracle_fixed(x)
-    for c in (0, 32, 64, 128):
-        o, s = run_fixed(x, chunk=c)
-        check("chunk %d" % c, o, ro, s, rs, TOL["bf16"])
+    res = {}
+    for c in (0, 32, 64):
+        res[c] = run_fixed(x, chunk=c)
+        check("chunk %d" % c, res[c][0], ro, res[c][1], rs, TOL["bf16"])
+    assert np.array_equal(res[0][0], res[64][0]) and np.array_equal(res[0][1], res[64][1])
+    with pytest.raises(gla.GlaError) as e:
+        run_fixed(x, chunk=128)
+    assert e.value.code == 6  # GLA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("T1", [1, 63, 64, 65, 255])
@@ -472,9 +479,10 @@ def test_decode_pool_is_bitwise_the_direct_step():
     assert torch.equal(pool[torch.from_numpy(slots).long().cuda()], direct)
 
 
-def test_decode_pool_full_size_sampled():
+def test_decode_pool_full_size():
     """1,280 rows (128 of them padding) against a pool of 2,048 pages at the
-    Laplace head shape; sampled rows against the oracle."""
+    Laplace head shape: every row's output and every page against the
+    oracle's pooled step (untouched pages bit-identical)."""
     rng = np.random.default_rng(42)
     spec = W.WORKLOADS["batched_decode"]
     N, H, dk, dv = spec["N"], spec["H"], spec["dk"], spec["dv"]
@@ -483,14 +491,17 @@ def test_decode_pool_full_size_sampled():
     pool = torch.randn(P, H, dk, dv, device="cuda").mul_(spec["state_sigma"])
     slots = _pool_slots(rng, N, P, 128)
     valid = np.nonzero((slots >= 0) & (slots < P))[0]
-    sample = valid[np.linspace(0, valid.size - 1, 24).astype(int)]
-    ref = host(pool[torch.from_numpy(slots[sample]).long().cuda()])
+    before = W.to_numpy_bits(pool)  # fp32 copy of the whole pool
+    ref = before.astype(np.float64)
     q, k, v = W.decode_tokens(spec["seed"], 0, N, H, dk, dv)
     o = host(gla.gla_decode_step_pool(dev(q), dev(k), dev(v), lam, pool, dev(slots)))
-    ro = O.gla_decode(q[sample], k[sample], v[sample], lam, ref)
-    e = rel_err(o[sample], ro)
-    es = rel_err(host(pool[torch.from_numpy(slots[sample]).long().cuda()]), ref)
+    ro = O.gla_decode_pool(q, k, v, lam, ref, slots)
+    got = W.to_numpy_bits(pool)
+    e = rel_err(o, ro)
+    es = rel_err(got[slots[valid]], ref[slots[valid]])
     print("pool decode N1280 P2048: o err %.3e  S err %.3e" % (e, es))
     pad = np.setdiff1d(np.arange(N), valid)
     assert not o[pad].any()
+    untouched = np.setdiff1d(np.arange(P), slots[valid])
+    np.testing.assert_array_equal(got[untouched], before[untouched])
     assert e <= TOL["bf16"] and es <= TOL["bf16"]
