@@ -24,7 +24,10 @@ and, if those took less, untimed steps up to at least 0.5 s of work.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--no-secondary] [--only {prefill,long,decode,decode_pool,varlen,backward,
-                                 long_backward,short_conv,linear_attn}]
+                                 long_backward,short_conv,linear_attn,sweep,cpu}]
+       [--sweep-part {forward,decode,backward}]
+(--only sweep: the shape sweep, one JSON line per case; --only cpu: the
+oracle's CPU baseline alone.)
 """
 import argparse
 import json
@@ -404,12 +407,206 @@ def bench_varlen(steps, warmup):
             "workspace_bytes": need}
 
 
-def cpu_baseline(x, lam, budget_s=10.0):
-    """The fp64 oracle on this host, on the whole headline workload (8
-    sequences x 2,048 tokens x 16 heads), repeated until about `budget_s`
-    seconds have passed."""
+# ---------------------------------------------------------------------------
+# Shape sweep (--only sweep): the same calls across head shapes, dtypes, head
+# counts, batch sizes and sequence lengths; for each case the time per call
+# and its HBM roofline fraction (algorithmic bytes per call / time / 8 TB/s;
+# every call is HBM-bound at these shapes), one JSON line per case. Inputs
+# are seeded synthetic draws on the device (q, k, v ~ N(0, 1), q and k
+# scaled by dk^-1/2, geometric decays); two or more input sets are rotated so
+# that small cases do not run out of the last-level cache, and every timed
+# region follows at least SWEEP_WARM_S of untimed calls.
+SWEEP_WARM_S = 0.3
+
+
+def _sweep_elt(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+def _sweep_time(fn, n_sets, min_calls=20):
+    import torch
+    i = 0
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    while time.perf_counter() - t < SWEEP_WARM_S or i < 3:
+        fn(i % n_sets)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t) / i
+    calls = max(min_calls, int(0.5 / max(per, 1e-6)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for j in range(calls):
+        fn(j % n_sets)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls * 1e3  # microseconds
+
+
+def _sweep_inputs(lead, H, dk, dv, dtype, seed):
+    import torch
+    from chunked_gated_recurrent_amd import workloads as W
+    dev = torch.device("cuda")
+    q, k, v, _ = W.device_normal_inputs(seed, lead, H, dk, dv, dev)
+    if dtype == "f32":
+        q, k, v = q.float(), k.float(), v.float()
+    return q, k, v
+
+
+def _sweep_sets(nbytes):
+    """Input sets to rotate: enough to exceed the 256 MB last-level cache."""
+    return max(2, min(8, int(1.2e9 // max(nbytes, 1)) + 1))
+
+
+def _sweep_line(call, dtype, shape, us, nbytes, **extra):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    d = {"call": call, "dtype": dtype}
+    d.update(shape)
+    d.update({"us": round(us, 1), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 3)})
+    d.update(extra)
+    print(json.dumps(d), flush=True)
+
+
+def sweep_forward():
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    cases = [  # dtype, B, T, H, dk, dv
+        ("bf16", 8, 2048, 16, 96, 192), ("bf16", 1, 2048, 16, 96, 192),
+        ("bf16", 8, 512, 16, 96, 192), ("bf16", 32, 2048, 16, 96, 192),
+        ("bf16", 8, 8192, 16, 96, 192), ("bf16", 1, 65536, 16, 96, 192),
+        ("bf16", 8, 2048, 8, 96, 192), ("bf16", 8, 2048, 32, 96, 192),
+        ("bf16", 8, 2048, 16, 96, 64), ("bf16", 8, 2048, 16, 96, 128),
+        ("bf16", 8, 2048, 16, 96, 256),
+        ("bf16", 8, 2048, 16, 64, 128), ("bf16", 8, 2048, 16, 128, 128),
+        ("f32", 8, 2048, 16, 96, 192),
+    ]
+    for dtype, B, T, H, dk, dv in cases:
+        lam = W.geometric_decays(H)
+        e = _sweep_elt(dtype)
+        nbytes = B * T * H * (2 * dk + 2 * dv) * e + B * H * dk * dv * 4
+        sets = []
+        for r in range(_sweep_sets(nbytes)):
+            q, k, v = _sweep_inputs((B, T), H, dk, dv, dtype, 40 + r)
+            o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+            sf = torch.empty(B, H, dk, dv, device=q.device)
+            sets.append((q, k, v, o, sf))
+        need = gla.lib().gla_chunk_fwd_workspace_bytes(1 if dtype == "bf16" else 0, B, T, H,
+                                                       dk, dv, 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=sets[0][0].device)
+
+        def call(i):
+            q, k, v, o, sf = sets[i]
+            gla.gla_chunk_fwd(q, k, v, lam, out=o, final_state=sf, workspace=ws)
+
+        us = _sweep_time(call, len(sets))
+        _sweep_line("gla_chunk_fwd", dtype, dict(B=B, T=T, H=H, dk=dk, dv=dv), us, nbytes,
+              tokens_per_s=round(B * T / (us * 1e-6), 1), workspace_bytes=need)
+        del sets, ws
+        torch.cuda.empty_cache()
+
+
+def sweep_decode():
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    cases = [("bf16", 1280, 16, 96, 192), ("bf16", 64, 16, 96, 192),
+             ("bf16", 1280, 16, 96, 128), ("bf16", 1280, 16, 64, 128),
+             ("f32", 1280, 16, 96, 192)]
+    for dtype, N, H, dk, dv in cases:
+        lam = W.geometric_decays(H)
+        e = _sweep_elt(dtype)
+        nbytes = N * H * (2 * dk * dv * 4 + (2 * dk + 2 * dv) * e)
+        n_sets = _sweep_sets(nbytes)
+        dev = torch.device("cuda")
+        states = [torch.randn(N, H, dk, dv, device=dev) * 0.3 for _ in range(n_sets)]
+        q, k, v = _sweep_inputs((n_sets, N), H, dk, dv, dtype, 60)
+        o = torch.empty(N, H, dv, dtype=q.dtype, device=dev)
+
+        def call(i):
+            gla.gla_decode_step(q[i], k[i], v[i], lam, states[i], out=o)
+
+        us = _sweep_time(call, n_sets)
+        _sweep_line("gla_decode_step", dtype, dict(N=N, H=H, dk=dk, dv=dv), us, nbytes,
+              seq_steps_per_s=round(N / (us * 1e-6), 1))
+        del states
+        torch.cuda.empty_cache()
+
+
+def sweep_backward():
+    import torch
+    from chunked_gated_recurrent_amd import gla
+    from chunked_gated_recurrent_amd import workloads as W
+    cases = [("bf16", 8, 2048, 16, 96, 192), ("bf16", 32, 2048, 16, 96, 192),
+             ("bf16", 8, 2048, 16, 96, 128), ("bf16", 8, 2048, 16, 96, 256),
+             ("bf16", 8, 2048, 16, 64, 128), ("bf16", 8, 2048, 16, 128, 128),
+             ("bf16", 8, 2048, 16, 128, 256), ("f32", 8, 2048, 16, 96, 192)]
+    for dtype, B, T, H, dk, dv in cases:
+        lam = W.geometric_decays(H)
+        e = _sweep_elt(dtype)
+        nbytes = B * T * H * (4 * dk + 3 * dv) * e + 2 * B * H * dk * dv * 4
+        sets = []
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(70)
+        for r in range(_sweep_sets(nbytes)):
+            q, k, v = _sweep_inputs((B, T), H, dk, dv, dtype, 80 + r)
+            do = torch.randn(B, T, H, dv, generator=gen, device=q.device).to(q.dtype)
+            dsf = torch.randn(B, H, dk, dv, generator=gen, device=q.device)
+            outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                    torch.empty(B, H, dk, dv, device=q.device))
+            sets.append((q, k, v, do, dsf, outs))
+        need = gla.lib().gla_chunk_bwd_workspace_bytes(1 if dtype == "bf16" else 0, B, T, H,
+                                                       dk, dv, 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=sets[0][0].device)
+
+        def call(i):
+            q, k, v, do, dsf, (dq, dk_, dv_, ds0) = sets[i]
+            gla.gla_chunk_bwd(q, k, v, lam, do, 1.0, None, dsf, dq=dq, dk=dk_, dv=dv_, ds0=ds0,
+                              workspace=ws)
+
+        us = _sweep_time(call, len(sets))
+        _sweep_line("gla_chunk_bwd", dtype, dict(B=B, T=T, H=H, dk=dk, dv=dv), us, nbytes,
+              tokens_per_s=round(B * T / (us * 1e-6), 1), workspace_bytes=need)
+        del sets, ws
+        torch.cuda.empty_cache()
+
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(x, lam, budget_s=8.0, decode_budget_s=4.0):
+    """The fp64 oracle on this host's cores, untuned, parallel only across
+    independent (sequence, head) chains:
+      * the headline: the whole Laplace-shaped prefill workload (8 x 2,048
+        tokens x 16 heads), repeated for about `budget_s` seconds;
+      * decode: steps of the batched-decode recipe (fp32 states N(0, 0.1),
+        fresh bf16 tokens per step) on the first 160 of its 1,280 sequences
+        (all 16 heads), for about `decode_budget_s` seconds;
+      * one pass over the long-context workload (1 x 65,536 tokens) and one
+        over the packed 32-sequence workload.
+    `threads` is what the oracle ran with: OMP_NUM_THREADS when set, else
+    the visible cores capped at 16, the CPU share a job on one GPU gets on
+    these hosts; `host_cores` is what the operating system reports."""
+    import numpy as np
+    from chunked_gated_recurrent_amd import workloads as W
     from oracle import oracle as O
     threads = O.default_threads()
+    host_cores = os.cpu_count()
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = host_cores
     B, T = x["q"].shape[0], x["q"].shape[1]
     t0 = time.perf_counter()
     calls = 0
@@ -419,19 +616,51 @@ def cpu_baseline(x, lam, budget_s=10.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            for ln in f:
-                if ln.startswith("model name"):
-                    model = ln.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(calls * B * T / el, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "cpu_model": model,
-            "sample": "%d passes over the laplace_prefill workload (B=%d, T=%d, 16 heads), "
-                      "fp64 token-by-token recurrence, %.1f s wall" % (calls, B, T, el)}
+    out = {"value": round(calls * B * T / el, 1), "unit": "tokens/s", "cores": threads,
+           "threads": threads, "host_cores": host_cores, "usable_cores": usable,
+           "kind": "oracle", "cpu_model": _cpu_model(),
+           "sample": "%d passes over the laplace_prefill workload (B=%d, T=%d, 16 heads), "
+                     "fp64 token-by-token recurrence, %.1f s wall" % (calls, B, T, el)}
+    # decode: the batched-decode recipe on a bounded subset of its sequences
+    spec = W.WORKLOADS["batched_decode"]
+    Nd = 160
+    # the first Nd sequences of the recipe's state draw (numpy fills the array
+    # in order, so a draw of Nd sequences is that prefix)
+    state = W.decode_state(spec["seed"], Nd, spec["H"], spec["dk"], spec["dv"],
+                           spec["state_sigma"]).astype(np.float64)
+    lam_d = W.decays_for(spec)
+    steps = 0
+    el = 0.0
+    while el < decode_budget_s and steps < spec["steps"]:
+        q, k, v = W.decode_tokens(spec["seed"], steps, spec["N"], spec["H"], spec["dk"],
+                                  spec["dv"])
+        q, k, v = q[:Nd].copy(), k[:Nd].copy(), v[:Nd].copy()
+        t1 = time.perf_counter()
+        O.gla_decode(q, k, v, lam_d, state, threads=threads)
+        el += time.perf_counter() - t1
+        steps += 1
+    out["decode"] = {"value": round(Nd * steps / el, 1), "unit": "seq-steps/s",
+                     "sample": "%d consecutive steps of the batched_decode recipe on %d of "
+                               "its 1280 sequences (16 heads each), fp64 state in place, "
+                               "%.1f s of oracle time" % (steps, Nd, el)}
+    del state
+    # one pass each over the long-context and the packed workloads
+    for name in ("long_context", "varlen"):
+        xs = W.spec_inputs(name)
+        t1 = time.perf_counter()
+        if name == "varlen":
+            O.gla_varlen(xs["cu_seqlens"], xs["q"], xs["k"], xs["v"], xs["decay"], 1.0,
+                         xs["s0"], threads=threads)
+            tokens = int(xs["cu_seqlens"][-1])
+        else:
+            O.gla_fwd(xs["q"], xs["k"], xs["v"], xs["decay"], 1.0, xs["s0"], threads=threads)
+            tokens = xs["q"].shape[0] * xs["q"].shape[1]
+        el = time.perf_counter() - t1
+        out[name] = {"value": round(tokens / el, 1), "unit": "tokens/s",
+                     "sample": "one pass over the whole %s workload (%d tokens, 16 heads), "
+                               "%.1f s wall" % (name, tokens, el)}
+        del xs
+    return out
 
 
 def copy_bandwidth(gib=1.0):
@@ -499,18 +728,31 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", choices=["prefill", "long", "decode", "decode_pool", "varlen",
                                        "backward", "long_backward", "short_conv",
-                                       "linear_attn"])
+                                       "linear_attn", "sweep", "cpu"])
+    ap.add_argument("--sweep-part", choices=["forward", "decode", "backward"],
+                    help="with --only sweep: one part of the shape sweep")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+    if args.only == "cpu":  # the oracle alone: no GPU needed
+        from chunked_gated_recurrent_amd import workloads as W
+        x = W.spec_inputs("laplace_prefill")
+        print(json.dumps(cpu_baseline(x, x["decay"])))
+        return
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     from chunked_gated_recurrent_amd import gla
     gla.lib()
 
+    if args.only == "sweep":
+        for name, fn in (("forward", sweep_forward), ("decode", sweep_decode),
+                         ("backward", sweep_backward)):
+            if args.sweep_part in (None, name):
+                fn()
+        return
     if args.only:
         fn = {"prefill": lambda: bench_prefill(args.steps, args.warmup),
               "long": lambda: bench_long(args.steps, args.warmup),
