@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gla.h"
 #include "gla_internal.h"
 
@@ -348,6 +350,8 @@ const char *gla_status_str(gla_status s) {
     case GLA_ERR_WORKSPACE: return "workspace missing or too small";
     case GLA_ERR_HIP: return "a HIP kernel launch failed";
     case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case GLA_ERR_TOO_LARGE:
+      return "the call needs more scratch than the allocation-free entry point holds";
   }
   return "unknown status";
 }
@@ -538,14 +542,51 @@ size_t gla_chunk_fwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T,
   return plan_varlen(dt, N, total_T, H, dk, dv, chunk).ws_bytes;
 }
 
-gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
-                                int dk, int dv, int chunk,
-                                const int32_t *cu_seqlens, const void *q,
-                                const void *k, const void *v,
-                                const float *decay_host, float scale,
-                                const float *s0, void *o, float *s_final,
-                                void *workspace, size_t workspace_bytes,
-                                void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free entry point: one array per GPU, for
+// the life of the process, so that a call needs no hipMalloc. The name
+// `scratch` is a host-side stand-in in host code; the device address of each
+// GPU's copy comes from hipGetSymbolAddress with that GPU current, once per
+// device, and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = GLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices];  // device address of `scratch` per device, or null
+
+// This device's scratch (the current device's: the caller's stream must
+// belong to it).
+hipError_t noalloc_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = p;
+  }
+  *ptr = scratch_dev[dev];
+  return hipSuccess;
+}
+
+// gla_chunk_fwd_varlen with the workspace given (noalloc false), or taken
+// from this device's fixed scratch array (noalloc true: workspace and
+// workspace_bytes are ignored).
+gla_status fwd_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk,
+                      const int32_t *cu_seqlens, const void *q, const void *k,
+                      const void *v, const float *decay_host, float scale,
+                      const float *s0, void *o, float *s_final, void *workspace,
+                      size_t workspace_bytes, void *stream, bool noalloc) {
   gla_status st = check_common(dt, H, dk, dv, chunk);
   if (st != GLA_OK) return st;
   if (N < 1 || total_T < 0 || N > (1 << 28)) return GLA_ERR_SHAPE;
@@ -572,6 +613,16 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
       return GLA_ERR_ALIAS;
   }
   const HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk);
+  if (noalloc) {
+    // every check above is done; the scratch lookup is the first HIP call
+    if (hp.ws_bytes > kNoAllocScratchBytes) return GLA_ERR_TOO_LARGE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (hp.ws_bytes > 0) {
+      if (noalloc_scratch(&workspace) != hipSuccess) return GLA_ERR_HIP;
+      workspace_bytes = kNoAllocScratchBytes;
+    }
+  }
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes) return GLA_ERR_WORKSPACE;
     if (misaligned(workspace)) return GLA_ERR_ALIGN;
@@ -598,6 +649,33 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
   a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
   a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
   return run_forward(dt, hq, a, make_decay(decay_host, H), workspace, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
+                                int dk, int dv, int chunk,
+                                const int32_t *cu_seqlens, const void *q,
+                                const void *k, const void *v,
+                                const float *decay_host, float scale,
+                                const float *s0, void *o, float *s_final,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, decay_host,
+                    scale, s0, o, s_final, workspace, workspace_bytes, stream, false);
+}
+
+gla_status gla_chunk_fwd_varlen_noalloc(gla_dtype dt, int N, int total_T, int H,
+                                        int dk, int dv, int chunk,
+                                        const int32_t *cu_seqlens, const void *q,
+                                        const void *k, const void *v,
+                                        const float *decay_host, float scale,
+                                        const float *s0, void *o, float *s_final,
+                                        void *stream) {
+  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, decay_host,
+                    scale, s0, o, s_final, nullptr, 0, stream, true);
 }
 
 size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,

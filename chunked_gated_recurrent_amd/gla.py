@@ -9,6 +9,7 @@ of any kind. If libgla.so has not been built the first call raises.
 Functions mirror the C entry points:
     gla_chunk_fwd(q, k, v, decay, ...)          -> (o, s_final)
     gla_chunk_fwd_varlen(q, k, v, cu, decay, ...) -> (o, s_final)
+    gla_chunk_fwd_varlen_noalloc(q, k, v, cu, decay, out, ...) -> (out, s_final)
     gla_decode_step(q, k, v, decay, state, ...)  -> o   (state updated in place)
     gla_decode_step_pool(q, k, v, decay, state_pool, slots, ...) -> o
     gla_chunk_bwd(q, k, v, decay, dout, ...)    -> (dq, dk, dv, ds0)
@@ -46,6 +47,8 @@ _SIGS = {
     "gla_chunk_fwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_chunk_fwd_varlen": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
                                          _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "gla_chunk_fwd_varlen_noalloc": ([_I] * 7 + [_P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                                 _P, _P, _P], _I),
     "gla_linear_attn_fwd_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_linear_attn_fwd": ([_I] * 7 + [_P] * 9 + [ctypes.c_size_t, _P], _I),
     "gla_linear_attn_decode_step": ([_I] * 5 + [_P] * 7, _I),
@@ -335,6 +338,39 @@ def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,
     if rc != 0:
         raise GlaError(rc, "gla_chunk_fwd_varlen")
     return o, sf
+
+
+def gla_chunk_fwd_varlen_noalloc(q, k, v, cu_seqlens, decay, out, scale: float = 1.0,
+                                 initial_state=None, final_state=None, chunk: int = 0):
+    """gla_chunk_fwd_varlen without a workspace: the library's fixed
+    per-GPU scratch array serves instead, and nothing is allocated here
+    either, so the outputs come in: out [total_T, H, dv] (dtype of q) and
+    final_state [N, H, dk, dv] fp32 or None. Calls that overlap in time on
+    one GPU share that array and must not be issued. Returns (out,
+    final_state)."""
+    import torch
+    dev = q.device
+    total, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu_seqlens.shape[0] - 1
+    _check(q, "q", dev)
+    _check(k, "k", dev, q.dtype, (total, H, dk))
+    _check(v, "v", dev, q.dtype, (total, H, dv))
+    _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    dt = _dt(q)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", dev, torch.float32, (N, H, dk, dv))
+    _check(out, "out", dev, q.dtype, (total, H, dv))
+    if final_state is not None:
+        _check(final_state, "final_state", dev, torch.float32, (N, H, dk, dv))
+    _d, dptr = _decay_array(decay, H)
+    rc = lib().gla_chunk_fwd_varlen_noalloc(dt, N, total, H, dk, dv, chunk,
+                                            _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                            dptr, float(scale), _ptr(initial_state),
+                                            _ptr(out), _ptr(final_state), _stream(dev))
+    if rc != 0:
+        raise GlaError(rc, "gla_chunk_fwd_varlen_noalloc")
+    return out, final_state
 
 
 def gla_decode_step(q, k, v, decay, state, scale: float = 1.0, out=None):

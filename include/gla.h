@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 1
+#define GLA_ABI_VERSION 2
 #define GLA_MAX_HEADS 64
 
 typedef enum gla_status {
@@ -77,7 +77,8 @@ typedef enum gla_status {
   GLA_ERR_UNSUPPORTED = 6, /* valid but unsupported (dk, dv, H or chunk)       */
   GLA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required       */
   GLA_ERR_HIP = 8,         /* a HIP launch failed                              */
-  GLA_ERR_ALIGN = 9        /* a tensor pointer is not 16-byte aligned          */
+  GLA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned          */
+  GLA_ERR_TOO_LARGE = 10   /* needs more than GLA_NOALLOC_SCRATCH_BYTES        */
 } gla_status;
 
 typedef enum gla_dtype { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
@@ -144,6 +145,36 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
                                 const float *s0, void *o, float *s_final,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * gla_chunk_fwd_varlen for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, checks and results (bitwise) as
+ * gla_chunk_fwd_varlen, without the workspace: the scratch comes from a
+ * fixed array of GLA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's array (hipGetSymbolAddress), so the
+ * current device must be the one `stream` belongs to.
+ *   - A call whose plan needs more scratch than the array holds returns
+ *     GLA_ERR_TOO_LARGE and launches nothing. At H = 16, dk = 96, dv = 192
+ *     every packed batch fits (the largest plan, 7 long sequences cut into
+ *     22 time segments, needs about 26 MB); gla_chunk_fwd_varlen_workspace_
+ *     bytes() gives the need of any other shape.
+ *   - Every call on a GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams, or from different threads)
+ *     race and must not be issued. Calls in sequence on one stream are
+ *     safe. No byte of the array needs to start at zero: each call writes
+ *     every scratch value it reads.
+ */
+#define GLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+gla_status gla_chunk_fwd_varlen_noalloc(gla_dtype dt, int N, int total_T, int H,
+                                        int dk, int dv, int chunk,
+                                        const int32_t *cu_seqlens, const void *q,
+                                        const void *k, const void *v,
+                                        const float *decay_host, float scale,
+                                        const float *s0, void *o, float *s_final,
+                                        void *stream);
 
 /*
  * Backward of gla_chunk_fwd (training): given dL/do and optionally

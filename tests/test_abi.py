@@ -15,7 +15,7 @@ from chunked_gated_recurrent_amd import gla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gla.h")
 
-OK, NULL, SHAPE, DTYPE, DECAY, ALIAS, UNSUP, WS, HIP, ALIGN = range(10)
+OK, NULL, SHAPE, DTYPE, DECAY, ALIAS, UNSUP, WS, HIP, ALIGN, TOO_LARGE = range(11)
 BF16, F32 = gla.GLA_BF16, gla.GLA_F32
 
 
@@ -45,9 +45,9 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gla_abi_version() == 1
+    assert L.gla_abi_version() == 2
     seen = set()
-    for code in range(10):
+    for code in range(11):
         s = gla.status_str(code)
         assert s and s not in seen
         seen.add(s)
@@ -153,6 +153,39 @@ def test_varlen_argument_errors(L):
     assert varlen(L, chunk=128) == UNSUP
     # one short sequence needs no scratch at all
     assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 1, 100, 16, 96, 192, 0) == 0
+
+
+def test_noalloc_argument_errors(L, monkeypatch):
+    """The allocation-free packed forward validates exactly like
+    gla_chunk_fwd_varlen, and refuses a plan larger than its fixed scratch,
+    all before any HIP call."""
+    def na(dt=BF16, N=3, total=300, H=4, dk=96, dv=192, chunk=0, cu=A[6], q=A[0],
+           k=A[1], v=A[2], decay=None, s0=None, o=A[3], sf=None):
+        dec = GOOD if decay is None else decay
+        return L.gla_chunk_fwd_varlen_noalloc(dt, N, total, H, dk, dv, chunk, cu, q, k, v,
+                                              dptr(dec), 1.0, s0, o, sf, None)
+    assert na(dt=5) == DTYPE
+    assert na(N=0) == SHAPE
+    assert na(total=-1) == SHAPE
+    assert na(cu=None) == NULL
+    assert na(q=None) == NULL
+    assert na(chunk=128) == UNSUP
+    assert na(dk=8) == UNSUP
+    assert na(cu=ctypes.c_void_p(A[6].value + 2)) == ALIGN
+    assert na(o=A[6]) == ALIAS
+    d = GOOD.copy()
+    d[0] = -1.0
+    assert na(decay=d) == DECAY
+    dec16 = np.full(16, 0.9, np.float32)
+    # the largest default plan at the Laplace head shape fits the scratch
+    # (7 long sequences, 22 time segments)
+    assert L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 7, 7 * 65536, 16, 96, 192, 0) <= 32 << 20
+    # a plan beyond the fixed scratch (time segments of 128 tokens forced)
+    monkeypatch.setenv("GLA_TARGET_WGS", "100000")
+    need = L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 0)
+    assert need > (32 << 20)
+    assert na(N=1, total=65536, H=16, decay=dec16) == TOO_LARGE
+    assert gla.status_str(TOO_LARGE).startswith("the call needs more scratch")
 
 
 def test_decode_argument_errors(L):
