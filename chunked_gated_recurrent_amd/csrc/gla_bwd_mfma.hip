@@ -555,8 +555,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // Local carries of time segments: for every item but a sequence's first,
 // U_g = scale sum_{t in item} lambda^(t - t0 + 1) q_t^T dO_t (the carried
-// gradient the item passes back when nothing flows into it), by the same
-// reverse chunk walk as the dv waves of bwd_dkdv_kernel, into slot g.
+// gradient the item passes back when nothing flows into it), into slot g.
+// A plain weighted sum, so the chunks are taken first to last (chunk c
+// weighted by lambda^(64 c) on top of its in-chunk powers): the walk ends on
+// the item's last rows, where the reverse walk that consumes the carry starts
+// next, so those rows are still in the last-level cache.
 // ---------------------------------------------------------------------------
 template <int DVT, int DKT>
 __device__ __forceinline__ void carry_role(
@@ -603,15 +606,17 @@ __device__ __forceinline__ void carry_role(
     for (int m = 0; m < VV; ++m)
       rd[m] = __builtin_amdgcn_raw_buffer_load_b128(bd, rowB[m] * rowVb + colB[m] * 16, 0, 0);
   };
-  // q enters the carry only as scale * lambda^(t+1) q_t: it is stored scaled
+  // q enters the carry only as scale * lambda^(t - t0 + 1) q_t: it is stored
+  // scaled, by its in-chunk power times the chunk's lambda^(64 c) (pc)
   float fqr[QV];
-  auto store = [&](int buf, const u32x4(&rq)[QV], const u32x4(&rd)[VV]) {
+  auto store = [&](int buf, float pc, const u32x4(&rq)[QV], const u32x4(&rd)[VV]) {
 #pragma unroll
     for (int m = 0; m < QV; ++m) {
       const bf16x8 qv = __builtin_bit_cast(bf16x8, rq[m]);
+      const float f = fqr[m] * pc;
       bf16x8 qs;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)qv[e] * fqr[m]);
+      for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)qv[e] * f);
       *reinterpret_cast<bf16x8 *>(sQ + buf * KBUF + rowA[m] * QS + 8 * colA[m]) = qs;
     }
 #pragma unroll
@@ -625,26 +630,25 @@ __device__ __forceinline__ void carry_role(
 #pragma unroll
     for (int b = 0; b < SCT; ++b) accC[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   u32x4 qa_[QV], da_[VV], qb_[QV], db_[VV];
-  load(nch - 1, qa_, da_);
-  load(nch - 2, qb_, db_);
+  load(0, qa_, da_);
+  load(1, qb_, db_);
   __syncthreads();  // sPow ready
 #pragma unroll
   for (int m = 0; m < QV; ++m) fqr[m] = scale * sPow[rowA[m] + 1];
-  store((nch - 1) & 1, qa_, da_);
+  // lambda^(64 c) for the chunk whose rows are stored next (underflows to
+  // zero harmlessly for strong decay)
+  const float lam64 = sPow[C];
+  float pc = 1.0f;
+  store(0, pc, qa_, da_);
 
   auto body = [&](int ch, u32x4(&nq)[QV], u32x4(&nd)[VV], const u32x4(&xq)[QV],
                   const u32x4(&xd)[VV]) {
-    const int L = rows_of(ch);
     const int cur = ch & 1;
-    __syncthreads();  // chunk ch is in LDS; the chunk after is done
-    load(ch - 2, nq, nd);
-    store(cur ^ 1, xq, xd);
+    __syncthreads();  // chunk ch is in LDS; the chunk before is done
+    load(ch + 2, nq, nd);
+    pc *= lam64;
+    store(cur ^ 1, pc, xq, xd);
     const bf16 *cQ = sQ + cur * KBUF, *cD = sD + cur * VBUF;
-    const float lamL = sPow[L];
-#pragma unroll
-    for (int a = 0; a < SDT; ++a)
-#pragma unroll
-      for (int b = 0; b < SCT; ++b) accC[a][b] *= lamL;
 #pragma unroll
     for (int s = 0; s < NJS; ++s) {
       bf16x8 qs[SDT], dfr[SCT];
@@ -665,9 +669,9 @@ __device__ __forceinline__ void carry_role(
         for (int b = 0; b < SCT; ++b) accC[a][b] = mfma(qs[a], dfr[b], accC[a][b]);
     }
   };
-  for (int p = 0; p < nch; p += 2) {
-    body(nch - 1 - p, qa_, da_, qb_, db_);
-    body(nch - 2 - p, qb_, db_, qa_, da_);
+  for (int ch = 0; ch < nch; ch += 2) {  // a chunk past the end is all zeros
+    body(ch, qa_, da_, qb_, db_);
+    body(ch + 1, qb_, db_, qa_, da_);
   }
   float *dst = cslots + ((long long)idx * H + h) * DK * dv;
 #pragma unroll
@@ -788,13 +792,16 @@ template <int DVT, int DKT>
 static void launch_bwd_dvt(const Plan &p, const BwdArgs &a, const Decay &dec,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
-  hipLaunchKernelGGL((bwd_dq_kernel<DVT, DKT>), dim3(grid), dim3(512), 0, s,
-                     (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
-                     a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv);
+  // reverse walk first (it starts where the boundary pass ended and ends
+  // where the dq walk starts: both begin on rows still in the last-level
+  // cache)
   hipLaunchKernelGGL((bwd_dkdv_kernel<DVT, DKT>), dim3(grid), dim3(512), 0, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      (const bf16 *)a.dout, a.ds_final, a.cslots, (bf16 *)a.dv_out,
                      a.ds0, a.part_dk, p, dec, a.scale, a.H, a.dv);
+  hipLaunchKernelGGL((bwd_dq_kernel<DVT, DKT>), dim3(grid), dim3(512), 0, s,
+                     (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout,
+                     a.s0, a.slots, a.part_dq, p, dec, a.scale, a.H, a.dv);
 }
 
 hipError_t launch_bwd_mfma(int dvt, const Plan &p, const BwdArgs &a,

@@ -724,17 +724,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
 bool bwd_wide_ok(int dk, int dv) { return wide_shape(dk, dv); }
 
 // One head shape; see launch_bwd_wide.
+// The reverse walk runs first: it starts at the segments' last rows, which
+// the boundary pass read last, and ends at their first rows, where the dq
+// walk starts, so both walks begin on rows still in the last-level cache.
 template <int DKT, int DV>
 static void launch_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
                            hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, 1);
-  hipLaunchKernelGGL((bwd_dq_wide_kernel<DKT, DV>), dim3(grid), dim3(512), 0, s, (const bf16 *)a.k,
-                     (const bf16 *)a.v, (const bf16 *)a.dout, a.s0, a.slots, (bf16 *)a.dq, p,
-                     dec, a.scale, a.H, pair);
   hipLaunchKernelGGL((bwd_dkdv_wide_kernel<DKT, DV>), dim3(grid), dim3(512), 0, s, (const bf16 *)a.q,
                      (const bf16 *)a.k, (const bf16 *)a.v, (const bf16 *)a.dout, a.ds_final,
                      a.cslots, (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H,
                      pair);
+  hipLaunchKernelGGL((bwd_dq_wide_kernel<DKT, DV>), dim3(grid), dim3(512), 0, s, (const bf16 *)a.k,
+                     (const bf16 *)a.v, (const bf16 *)a.dout, a.s0, a.slots, (bf16 *)a.dq, p,
+                     dec, a.scale, a.H, pair);
 }
 
 // pair: the segment slots hold unscanned local quantities and every sequence

@@ -269,7 +269,10 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
   if (it.flags & kLastSeg) return;  // no later segment reads it
   const int tid = threadIdx.x;
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
-  state_role<DVT, false, NORM, DKT, DKT == 128>(k, v, nullptr, nullptr, slots, it, idx, h, H, dv,
+  // backward walk: it ends on the segment's first rows, where the output
+  // pass starts next
+  state_role<DVT, false, NORM, DKT, DKT == 128, true>(k, v, nullptr, nullptr, slots, it, idx,
+                                                      h, H, dv,
                                dtile * DVT, 0, tid, __builtin_amdgcn_readfirstlane(tid >> 6),
                                nullptr, sKs, sV, nullptr, nullptr, sPow, np);
 }

@@ -121,8 +121,15 @@ __device__ __forceinline__ int chunk_rows(const Item &it, int ch) {
 //          the Ks^T tile with a B operand of ones (every column of the
 //          result holds z); z is published in row DVT of the state buffer.
 //          Every dv tile's workgroup computes z; the one at c0 = 0 stores it.
+//   REV:   (state-only pass) the chunks are taken last to first. The local
+//          end state is a plain weighted sum, sum_t lambda^(t1-1-t) k_t^T v_t,
+//          so each chunk's decay-scaled k carries the decay of the rows after
+//          the chunk as well (pc) and the sum is never rescaled; the walk
+//          ends on the item's first rows, where the output pass that follows
+//          starts, so those k and v rows are still in the last-level cache.
 // ---------------------------------------------------------------------------
-template <int DVT, bool FUSED, bool NORM = false, int DKT = 96, bool KSR = false>
+template <int DVT, bool FUSED, bool NORM = false, int DKT = 96, bool KSR = false,
+          bool REV = false>
 __device__ __forceinline__ void state_role(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ s0, float *__restrict__ s_final,
@@ -134,6 +141,7 @@ __device__ __forceinline__ void state_role(
   // raw k tile (sK when FUSED, else sKs) is scaled as its fragments are
   // read, with the same rounding as the copy
   using M = MfCfg<DVT, DKT>;
+  static_assert(!(REV && FUSED), "only the state-only pass walks backward");
   constexpr int C = M::C, DK = M::DK, QS = M::QS, VS = M::VS;
   constexpr int SDT = M::SDT, SCT = M::SCT, QV = M::QV, VV = M::VV;
   const int lane = rt & 63, l16 = lane & 15, g = lane >> 4;
@@ -141,6 +149,8 @@ __device__ __forceinline__ void state_role(
   const unsigned rowKb = (unsigned)(H * DK * 2), rowVb = (unsigned)(H * dv * 2);
   const int nch = (it.t1 - it.t0 + C - 1) / C;
   const int dt0 = SDT * (w >> 1), ct0 = SCT * (w & 1);
+  // rows of chunk ch (0 for chunks before the first or past the last)
+  auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
 
   f32x4 accS[SDT][SCT];
   {
@@ -200,8 +210,8 @@ __device__ __forceinline__ void state_role(
     colV[m] = vi - rowV[m] * M::NVV;
   }
   auto load_kv = [&](int ch, u32x4(&rk)[QV], u32x4(&rv)[VV]) {
-    const long long tb = (long long)it.t0 + (long long)ch * C;
-    const unsigned L = (unsigned)chunk_rows(it, ch);
+    const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
+    const unsigned L = (unsigned)rows_of(ch);
     const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, L * rowKb);
     const __amdgpu_buffer_rsrc_t bv =
         buf_rsrc(v + tb * H * dv + (long long)h * dv + c0, L * rowVb);
@@ -213,7 +223,9 @@ __device__ __forceinline__ void state_role(
       rv[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, rowV[m] * rowVb + colV[m] * 16, 0, 0);
   };
   constexpr int KBUF = C * QS, VBUF = C * VS;  // elements per chunk buffer
-  auto store_kv = [&](int L, int buf, const u32x4(&rk)[QV], const u32x4(&rv)[VV]) {
+  // pc: an extra decay factor on the whole chunk (REV; 1 otherwise)
+  auto store_kv = [&](int L, int buf, float pc, const u32x4(&rk)[QV],
+                      const u32x4(&rv)[VV]) {
     bf16 *dK = sK + buf * KBUF, *dV = sV + buf * VBUF;
     bf16 *dKs = KSR && FUSED ? nullptr : sKs + buf * KBUF;
 #pragma unroll
@@ -226,7 +238,7 @@ __device__ __forceinline__ void state_role(
         continue;
       }
       // decay-scaled copy lambda^(L-1-r) k_r; rows past the end are zero
-      const float wgt = r < L ? sPow[max(L - 1 - r, 0)] : 0.f;
+      const float wgt = r < L ? sPow[max(L - 1 - r, 0)] * pc : 0.f;
       const bf16x8 kv = __builtin_bit_cast(bf16x8, kr);
       bf16x8 ks;
 #pragma unroll
@@ -260,22 +272,28 @@ __device__ __forceinline__ void state_role(
   };
 
   // Chunk ch lives in LDS buffer ch & 1. Per chunk: one barrier, then the
-  // loads of chunk ch+2 are issued, the registers holding chunk ch+1 are
-  // written to the other buffer, and chunk ch is processed.
+  // loads of chunk ch+2 (REV: ch-2) are issued, the registers holding chunk
+  // ch+1 (REV: ch-1) are written to the other buffer, and chunk ch is
+  // processed. REV: pc_cur is lambda^(rows of the item after chunk ch).
+  constexpr int STEP = REV ? -1 : 1;
+  const int ch_first = REV ? nch - 1 : 0;
+  float pc_cur = 1.0f;
   u32x4 ka[QV], kb[QV], va[VV], vb[VV];
-  load_kv(0, ka, va);
-  load_kv(1, kb, vb);
+  load_kv(ch_first, ka, va);
+  load_kv(ch_first + STEP, kb, vb);
   __syncthreads();  // sPow ready
-  store_kv(chunk_rows(it, 0), 0, ka, va);
+  store_kv(rows_of(ch_first), ch_first & 1, 1.0f, ka, va);
   if (FUSED) publish(sSt1);  // S_{-1}: the incoming state
 
   auto body = [&](int ch, u32x4(&rkn)[QV], u32x4(&rvn)[VV], const u32x4(&rkx)[QV],
                   const u32x4(&rvx)[VV], bf16 *st_pub) {
-    const int L = chunk_rows(it, ch);
+    const int L = rows_of(ch);
     const int cur = ch & 1;
-    __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
-    load_kv(ch + 2, rkn, rvn);
-    store_kv(chunk_rows(it, ch + 1), cur ^ 1, rkx, rvx);
+    __syncthreads();  // chunk ch and S_{ch-1} are in LDS; the chunk before is done
+    load_kv(ch + 2 * STEP, rkn, rvn);
+    // REV: the chunk before ch is followed by ch's rows as well
+    const float pc_next = REV ? pc_cur * sPow[L] : 1.0f;
+    store_kv(rows_of(ch + STEP), cur ^ 1, pc_next, rkx, rvx);
     const bf16 *cKs = (KSR && FUSED ? sK : sKs) + cur * KBUF, *cV = sV + cur * VBUF;
     const float lamL = sPow[L];
     // KSR: lambda^(L-1-t) for the rows t of this lane's fragments (P k-set),
@@ -287,17 +305,19 @@ __device__ __forceinline__ void state_role(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t0 = 32 * s + 4 * g + e, t1 = t0 + 16;
-          wk[s][e] = t0 < L ? sPow[max(L - 1 - t0, 0)] : 0.f;
-          wk[s][4 + e] = t1 < L ? sPow[max(L - 1 - t1, 0)] : 0.f;
+          wk[s][e] = t0 < L ? sPow[max(L - 1 - t0, 0)] * pc_cur : 0.f;
+          wk[s][4 + e] = t1 < L ? sPow[max(L - 1 - t1, 0)] * pc_cur : 0.f;
         }
     }
+    if (!REV) {
 #pragma unroll
-    for (int a = 0; a < SDT; ++a)
+      for (int a = 0; a < SDT; ++a)
 #pragma unroll
-      for (int b = 0; b < SCT; ++b) accS[a][b] *= lamL;
-    if (zw) {
+        for (int b = 0; b < SCT; ++b) accS[a][b] *= lamL;
+      if (zw) {
 #pragma unroll
-      for (int a = 0; a < SDT; ++a) accZ[a] *= lamL;
+        for (int a = 0; a < SDT; ++a) accZ[a] *= lamL;
+      }
     }
 #pragma unroll
     for (int s = 0; s < M::NJS; ++s) {
@@ -328,10 +348,12 @@ __device__ __forceinline__ void state_role(
       }
     }
     if (FUSED) publish(st_pub);  // S_ch for the next chunk's readout
+    pc_cur = pc_next;
   };
-  for (int ch = 0; ch < nch; ch += 2) {  // a past-the-end chunk is all zeros
-    body(ch, ka, va, kb, vb, sSt0);
-    body(ch + 1, kb, vb, ka, va, sSt1);
+  // a chunk past the end (REV: before the start) is all zeros
+  for (int p = 0; p < nch; p += 2) {
+    body(ch_first + STEP * p, ka, va, kb, vb, sSt0);
+    body(ch_first + STEP * (p + 1), kb, vb, ka, va, sSt1);
   }
 
   float *dst = nullptr;
