@@ -13,6 +13,22 @@
 
 using namespace gla;
 
+// Debug builds (-DGLA_DEBUG; the host sanitizer tests build one) check the
+// plan and workspace arithmetic as it is made; release builds compile the
+// checks away.
+#ifdef GLA_DEBUG
+#include <stdio.h>
+#define GLA_HOST_CHECK(c)                                                       \
+  do {                                                                          \
+    if (!(c)) {                                                                 \
+      fprintf(stderr, "%s:%d: plan check failed: %s\n", __FILE__, __LINE__, #c); \
+      abort();                                                                  \
+    }                                                                           \
+  } while (0)
+#else
+#define GLA_HOST_CHECK(c) ((void)0)
+#endif
+
 namespace {
 
 constexpr long long kMaxTokens = 0x7fffffffLL;  // token indices are int32 on device
@@ -108,6 +124,11 @@ HostPlan plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk,
   hp.segmented = G > 1;
   hp.off_slots = 0;
   hp.ws_bytes = hp.segmented ? (size_t)B * G * H * dk * dv * sizeof(float) : 0;
+  // segments are whole chunks, cover the sequence, and none is empty
+  GLA_HOST_CHECK(C > 0 && seg > 0 && seg % C == 0 && G >= 1);
+  GLA_HOST_CHECK((long long)seg * G >= T);
+  GLA_HOST_CHECK(T == 0 || (long long)seg * (G - 1) < T);
+  GLA_HOST_CHECK((long long)p.max_items == (long long)B * G);
   return hp;
 }
 
@@ -131,6 +152,7 @@ HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chun
     hp.ordered = N > 1 && N <= kOrderMaxItems;
     hp.off_order = 0;
     hp.ws_bytes = hp.ordered ? align256(sizeof(int32_t) * (size_t)N) : 0;
+    GLA_HOST_CHECK(!hp.ordered || hp.ws_bytes >= sizeof(int32_t) * (size_t)N);
     return hp;
   }
   const long long want = (target + chains - 1) / chains;  // segments per sequence
@@ -149,6 +171,18 @@ HostPlan plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chun
   hp.off_slots = hp.off_order +
                  (hp.ordered ? align256(sizeof(int32_t) * (size_t)p.max_items) : 0);
   hp.ws_bytes = hp.off_slots + (size_t)p.max_items * H * dk * dv * sizeof(float);
+  // a sequence of L tokens becomes ceil(L / seg) items (one if empty), and
+  // sum_n ceil(L_n / seg) <= N + total_T / seg: the item slots suffice
+  GLA_HOST_CHECK(seg % C == 0 && seg >= 2 * C);
+  GLA_HOST_CHECK(p.max_items >= N);
+  // index, item table, order and state slots: 256-byte aligned, in this
+  // order, without overlap
+  GLA_HOST_CHECK(hp.off_index == 0 && hp.off_items % 256 == 0 && hp.off_order % 256 == 0 &&
+                 hp.off_slots % 256 == 0);
+  GLA_HOST_CHECK(hp.off_items >= sizeof(int32_t) * ((size_t)N + 2));
+  GLA_HOST_CHECK(hp.off_order >= hp.off_items + sizeof(int4) * (size_t)p.max_items);
+  GLA_HOST_CHECK(hp.off_slots >= hp.off_order +
+                                     (hp.ordered ? sizeof(int32_t) * (size_t)p.max_items : 0));
   return hp;
 }
 
@@ -210,8 +244,10 @@ size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
 // one z slot ([item][H][dk] fp32) per item after the state slots.
 HostPlan with_zslots(HostPlan hp, int H, int dk) {
   if (hp.segmented) {
+    const size_t state_end = hp.ws_bytes;
     hp.off_zslots = align256(hp.ws_bytes);
     hp.ws_bytes = hp.off_zslots + (size_t)hp.p.max_items * H * dk * sizeof(float);
+    GLA_HOST_CHECK(hp.off_zslots % 256 == 0 && hp.off_zslots >= state_end);
   }
   return hp;
 }
@@ -270,6 +306,13 @@ BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv)
   bp.off_part = base + slot_bytes;
   bp.part_bytes = bp.wide ? 0 : align256((size_t)bp.ndt * H * total_T * dk * sizeof(float));
   bp.ws_bytes = total_T > 0 ? bp.off_part + 2 * bp.part_bytes : 0;
+  // the forward's layout, then the carried-gradient slots, then the two
+  // partial-sum arrays, each 256-byte aligned and after the one before
+  GLA_HOST_CHECK(bp.ndt >= 1 && bp.dvt * bp.ndt == dv);
+  GLA_HOST_CHECK(bp.off_cslots % 256 == 0 && bp.off_cslots >= hp.ws_bytes);
+  GLA_HOST_CHECK(bp.off_part % 256 == 0 && bp.part_bytes % 256 == 0);
+  GLA_HOST_CHECK(!hp.segmented ||
+                 bp.off_part >= bp.off_cslots + (size_t)hp.p.max_items * H * dk * dv * 4);
   return bp;
 }
 
@@ -352,6 +395,8 @@ const char *gla_status_str(gla_status s) {
     case GLA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case GLA_ERR_TOO_LARGE:
       return "the call needs more scratch than the allocation-free entry point holds";
+    case GLA_STATUS_RANGE_:
+      break;
   }
   return "unknown status";
 }

@@ -29,7 +29,7 @@ __device__ __forceinline__ float pow_f64(float lam, long long n) {
   return (float)r;
 }
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) {
+__host__ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
@@ -37,8 +37,9 @@ struct Item {
   int n, t0, t1, flags;
 };
 
-// Item `idx` of the plan; false when idx is past the last item.
-__device__ __forceinline__ bool load_item(const Plan &p, int idx, Item &it) {
+// Item `idx` of the plan; false when idx is past the last item. (Host and
+// device: the host-side plan checks decode items with the same code.)
+__host__ __device__ __forceinline__ bool load_item(const Plan &p, int idx, Item &it) {
   if (p.mode == kPlanFixed) {
     if (idx >= p.max_items) return false;
     const int n = idx / p.G;
@@ -71,7 +72,7 @@ __device__ __forceinline__ bool load_item(const Plan &p, int idx, Item &it) {
 }
 
 // Sequence n's item range [first, last) in the plan.
-__device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
+__host__ __device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
                                           int &last) {
   if (p.mode == kPlanFixed) {
     first = n * p.G;
@@ -88,7 +89,7 @@ __device__ __forceinline__ void seq_items(const Plan &p, int n, int &first,
 
 // Dispatch slot -> (item index, item). Slots are taken longest item first
 // when the plan carries an order; false past the last item.
-__device__ __forceinline__ bool slot_item(const Plan &p, int slot, int &idx,
+__host__ __device__ __forceinline__ bool slot_item(const Plan &p, int slot, int &idx,
                                           Item &it) {
   int cnt = p.max_items;
   if (p.mode == kPlanVarlenDirect) cnt = p.n_seq;
@@ -123,7 +124,7 @@ __device__ __forceinline__ void make_uniform(int &idx, Item &it) {
 //    pass that skips last segments).
 // (xcd_unit_at takes the workgroup id P explicitly: a launch that runs two
 // kind of work gives each its own id range starting at a multiple of 8.)
-__device__ __forceinline__ void xcd_unit_at(const Plan &p, int P, int ndt, int units,
+__host__ __device__ __forceinline__ void xcd_unit_at(const Plan &p, int P, int ndt, int units,
                                             int &unit, int &dtile) {
   const int xcd = P & 7;
   const int r = P >> 3;

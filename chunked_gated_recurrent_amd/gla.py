@@ -68,6 +68,16 @@ class GlaError(RuntimeError):
         super().__init__("%s: %s (status %d)" % (where, status_str(code), code))
 
 
+def bind(L):
+    """Declare the C signatures of every exported entry point on a loaded
+    ctypes library handle; returns it."""
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
 def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
@@ -77,12 +87,7 @@ def lib():
                 "libgla.so is not built (%s); run "
                 "`python -m chunked_gated_recurrent_amd.build`" % LIB_PATH)
         import torch  # noqa: F401  -- bind to the HIP runtime torch loaded
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (args, res) in _SIGS.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = res
-        _lib = L
+        _lib = bind(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

@@ -78,10 +78,19 @@ typedef enum gla_status {
   GLA_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required       */
   GLA_ERR_HIP = 8,         /* a HIP launch failed                              */
   GLA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned          */
-  GLA_ERR_TOO_LARGE = 10   /* needs more than GLA_NOALLOC_SCRATCH_BYTES        */
+  GLA_ERR_TOO_LARGE = 10,  /* needs more than GLA_NOALLOC_SCRATCH_BYTES        */
+  /* not a status: widens the type's range to int, so that any int a caller
+     passes is a value of the type (and unknown ones are well-defined) */
+  GLA_STATUS_RANGE_ = 0x7fffffff
 } gla_status;
 
-typedef enum gla_dtype { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+typedef enum gla_dtype {
+  GLA_F32 = 0,
+  GLA_BF16 = 1,
+  /* not a dtype: widens the type's range to int, so that an unknown value
+     passed by a caller is rejected with GLA_ERR_DTYPE, not undefined */
+  GLA_DTYPE_RANGE_ = 0x7fffffff
+} gla_dtype;
 
 /* ABI version of the loaded library (GLA_ABI_VERSION at build time). */
 int gla_abi_version(void);

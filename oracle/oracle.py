@@ -38,9 +38,14 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        # a sanitizer build of the same source (the host sanitizer tests run
+        # the oracle's pins against one), else the regular build
+        path = os.environ.get("GLA_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB):
+                build(force=False)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         lib.oracle_gla_varlen.argtypes = [
             ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,

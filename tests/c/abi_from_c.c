@@ -34,7 +34,7 @@ int main(void) {
   int s;
 
   EXPECT(gla_abi_version() == GLA_ABI_VERSION);
-  for (s = GLA_OK; s <= GLA_ERR_ALIGN; ++s) {
+  for (s = GLA_OK; s <= GLA_ERR_TOO_LARGE; ++s) {
     const char *t = gla_status_str((gla_status)s);
     EXPECT(t != NULL && strlen(t) > 0);
   }
@@ -70,6 +70,16 @@ int main(void) {
          GLA_ERR_NULL);
   EXPECT(gla_decode_step_pool(GLA_BF16, 4, 16, 96, 192, A, B, C, lam, 1.0f, NULL, 8,
                               (float *)O, (char *)O + 4096 * 1024, NULL) == GLA_ERR_NULL);
+  /* the allocation-free packed forward validates the same way, and refuses a
+     chunk it does not run */
+  EXPECT(gla_chunk_fwd_varlen_noalloc(GLA_BF16, 2, 128, 16, 96, 192, 0, NULL, A, B, C, lam,
+                                      1.0f, NULL, O, NULL, NULL) == GLA_ERR_NULL);
+  EXPECT(gla_chunk_fwd_varlen_noalloc(GLA_BF16, 2, 128, 16, 96, 192, 128, (int32_t *)O, A, B,
+                                      C, lam, 1.0f, NULL, (char *)O + 4096, NULL,
+                                      NULL) == GLA_ERR_UNSUPPORTED);
+  EXPECT(gla_chunk_fwd_varlen_noalloc(GLA_BF16, 0, 128, 16, 96, 192, 0, (int32_t *)O, A, B, C,
+                                      lam, 1.0f, NULL, (char *)O + 4096, NULL,
+                                      NULL) == GLA_ERR_SHAPE);
   /* empty batches are valid and do nothing */
   EXPECT(gla_decode_step(GLA_BF16, 0, 16, 96, 192, A, B, C, lam, 1.0f, (float *)O, A, NULL) ==
          GLA_OK);

@@ -19,12 +19,28 @@ OK, NULL, SHAPE, DTYPE, DECAY, ALIAS, UNSUP, WS, HIP, ALIGN, TOO_LARGE = range(1
 BF16, F32 = gla.GLA_BF16, gla.GLA_F32
 
 
+# A host-sanitizer build of the library (tests/test_host_sanitizers.py runs
+# this file against one, in a process with the sanitizer runtime preloaded):
+# loaded directly, without torch.
+HOST_LIB = os.environ.get("GLA_TEST_HOST_LIB")
+
+
+def lib_path():
+    return HOST_LIB or gla.LIB_PATH
+
+
 @pytest.fixture(scope="module")
 def L():
+    if HOST_LIB:
+        return gla.bind(ctypes.CDLL(HOST_LIB))
     if not os.path.exists(gla.LIB_PATH):
         from chunked_gated_recurrent_amd import build
         build.build(verbose=False)
     return gla.lib()
+
+
+def status_text(L, code):
+    return L.gla_status_str(code).decode()
 
 
 def declared_functions():
@@ -36,7 +52,7 @@ def declared_functions():
 def test_exports_every_declared_function(L):
     names = declared_functions()
     assert set(names) == set(gla.EXPORTS), names
-    out = subprocess.run(["nm", "-D", "--defined-only", gla.LIB_PATH],
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path()],
                          stdout=subprocess.PIPE, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (gla_\w+)", out))
     for n in names:
@@ -48,10 +64,10 @@ def test_version_and_status_strings(L):
     assert L.gla_abi_version() == 2
     seen = set()
     for code in range(11):
-        s = gla.status_str(code)
+        s = status_text(L, code)
         assert s and s not in seen
         seen.add(s)
-    assert gla.status_str(99) == "unknown status"
+    assert status_text(L, 99) == "unknown status"
 
 
 # fake, 256-byte aligned, far-apart device addresses: never dereferenced
@@ -185,7 +201,7 @@ def test_noalloc_argument_errors(L, monkeypatch):
     need = L.gla_chunk_fwd_varlen_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 0)
     assert need > (32 << 20)
     assert na(N=1, total=65536, H=16, decay=dec16) == TOO_LARGE
-    assert gla.status_str(TOO_LARGE).startswith("the call needs more scratch")
+    assert status_text(L, TOO_LARGE).startswith("the call needs more scratch")
 
 
 def test_decode_argument_errors(L):
