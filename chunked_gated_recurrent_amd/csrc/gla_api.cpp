@@ -57,6 +57,18 @@ gla_status check_decay(const float *d, int H) {
 
 bool misaligned(const void *p) { return p && ((uintptr_t)p & 15u) != 0; }
 
+// The public gate codes map one to one onto the kernels' (checked below);
+// anything else, "no gate" included, becomes a code check_gate refuses.
+int gate_code(gla_gate g) {
+  return (g == GLA_GATE_SIGMOID || g == GLA_GATE_SILU) ? (int)g : -1;
+}
+
+gla_status check_gate(int gate) {
+  static_assert(GLA_GATE_SIGMOID == kGateSigmoid && GLA_GATE_SILU == kGateSilu, "gate codes");
+  if (gate != kGateNone && gate != kGateSigmoid && gate != kGateSilu) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
 // [a, a+na) and [b, b+nb) share a byte (empty ranges never overlap)
 bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
@@ -409,13 +421,19 @@ size_t gla_chunk_fwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
   return plan_fixed(dt, B, T, H, dk, dv, chunk).ws_bytes;
 }
 
-gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
-                         int chunk, const void *q, const void *k,
-                         const void *v, const float *decay_host, float scale,
-                         const float *s0, void *o, float *s_final,
-                         void *workspace, size_t workspace_bytes,
-                         void *stream) {
+}  // extern "C"
+
+namespace {
+
+// gla_chunk_fwd, with the output gate when gate != kGateNone (g: o's layout
+// and dtype)
+gla_status fwd_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk, const void *q,
+                     const void *k, const void *v, const void *g, int gate,
+                     const float *decay_host, float scale, const float *s0, void *o,
+                     float *s_final, void *workspace, size_t workspace_bytes, void *stream) {
   gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  st = check_gate(gate);
   if (st != GLA_OK) return st;
   if (B < 1 || T < 0 || (long long)B * T > kMaxTokens) return GLA_ERR_SHAPE;
   if (!isfinite(scale)) return GLA_ERR_SHAPE;
@@ -423,19 +441,22 @@ gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   if (st != GLA_OK) return st;
   const long long tok = (long long)B * T;
   if (tok > 0 && (!q || !k || !v || !o)) return GLA_ERR_NULL;
+  if (gate != kGateNone && tok > 0 && !g) return GLA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
-      misaligned(s0) || misaligned(s_final))
+      misaligned(s0) || misaligned(s_final) || misaligned(g))
     return GLA_ERR_ALIGN;
   const size_t es = elem_size(dt);
   const size_t nqk = (size_t)tok * H * dk * es, nv = (size_t)tok * H * dv * es;
   const size_t ns = (size_t)B * H * dk * dv * sizeof(float);
+  const size_t ng = gate != kGateNone ? nv : 0;
   if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
-      overlap(o, nv, s0, ns))
+      overlap(o, nv, s0, ns) || overlap(o, nv, g, ng))
     return GLA_ERR_ALIAS;
   if (s_final) {
     if (s_final != s0 && overlap(s_final, ns, s0, ns)) return GLA_ERR_ALIAS;
     if (overlap(s_final, ns, q, nqk) || overlap(s_final, ns, k, nqk) ||
-        overlap(s_final, ns, v, nv) || overlap(s_final, ns, o, nv))
+        overlap(s_final, ns, v, nv) || overlap(s_final, ns, o, nv) ||
+        overlap(s_final, ns, g, ng))
       return GLA_ERR_ALIAS;
   }
   const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
@@ -444,7 +465,8 @@ gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
     if (misaligned(workspace)) return GLA_ERR_ALIGN;
     if (overlap(workspace, hp.ws_bytes, q, nqk) || overlap(workspace, hp.ws_bytes, k, nqk) ||
         overlap(workspace, hp.ws_bytes, v, nv) || overlap(workspace, hp.ws_bytes, o, nv) ||
-        overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns))
+        overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns) ||
+        overlap(workspace, hp.ws_bytes, g, ng))
       return GLA_ERR_ALIAS;
   }
   hipStream_t s = (hipStream_t)stream;
@@ -459,8 +481,33 @@ gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
   a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
+  a.g = g; a.gate = gate;
   return run_forward(dt, hp, a, make_decay(decay_host, H), workspace, s);
 }
+
+}  // namespace
+
+extern "C" {
+
+gla_status gla_chunk_fwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                         int chunk, const void *q, const void *k,
+                         const void *v, const float *decay_host, float scale,
+                         const float *s0, void *o, float *s_final,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  return fwd_fixed(dt, B, T, H, dk, dv, chunk, q, k, v, nullptr, kGateNone, decay_host,
+                   scale, s0, o, s_final, workspace, workspace_bytes, stream);
+}
+
+gla_status gla_chunk_fwd_gated(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                               int chunk, const void *q, const void *k, const void *v,
+                               const void *g, gla_gate gate, const float *decay_host,
+                               float scale, const float *s0, void *o, float *s_final,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_fixed(dt, B, T, H, dk, dv, chunk, q, k, v, g, gate_code(gate), decay_host,
+                   scale, s0, o, s_final, workspace, workspace_bytes, stream);
+}
+
 
 size_t gla_linear_attn_fwd_workspace_bytes(gla_dtype dt, int B, int T, int H,
                                            int dk, int dv, int chunk) {
@@ -629,10 +676,12 @@ hipError_t noalloc_scratch(void **ptr) {
 // workspace_bytes are ignored).
 gla_status fwd_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk,
                       const int32_t *cu_seqlens, const void *q, const void *k,
-                      const void *v, const float *decay_host, float scale,
-                      const float *s0, void *o, float *s_final, void *workspace,
+                      const void *v, const void *g, int gate, const float *decay_host,
+                      float scale, const float *s0, void *o, float *s_final, void *workspace,
                       size_t workspace_bytes, void *stream, bool noalloc) {
   gla_status st = check_common(dt, H, dk, dv, chunk);
+  if (st != GLA_OK) return st;
+  st = check_gate(gate);
   if (st != GLA_OK) return st;
   if (N < 1 || total_T < 0 || N > (1 << 28)) return GLA_ERR_SHAPE;
   if (!isfinite(scale)) return GLA_ERR_SHAPE;
@@ -640,21 +689,23 @@ gla_status fwd_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chu
   if (st != GLA_OK) return st;
   if (!cu_seqlens) return GLA_ERR_NULL;
   if (total_T > 0 && (!q || !k || !v || !o)) return GLA_ERR_NULL;
+  if (gate != kGateNone && total_T > 0 && !g) return GLA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
-      misaligned(s0) || misaligned(s_final) || ((uintptr_t)cu_seqlens & 3u))
+      misaligned(s0) || misaligned(s_final) || misaligned(g) || ((uintptr_t)cu_seqlens & 3u))
     return GLA_ERR_ALIGN;
   const size_t es = elem_size(dt);
   const size_t nqk = (size_t)total_T * H * dk * es, nv = (size_t)total_T * H * dv * es;
   const size_t ns = (size_t)N * H * dk * dv * sizeof(float);
   const size_t ncu = sizeof(int32_t) * ((size_t)N + 1);
+  const size_t ng = gate != kGateNone ? nv : 0;
   if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
-      overlap(o, nv, s0, ns) || overlap(o, nv, cu_seqlens, ncu))
+      overlap(o, nv, s0, ns) || overlap(o, nv, cu_seqlens, ncu) || overlap(o, nv, g, ng))
     return GLA_ERR_ALIAS;
   if (s_final) {
     if (s_final != s0 && overlap(s_final, ns, s0, ns)) return GLA_ERR_ALIAS;
     if (overlap(s_final, ns, q, nqk) || overlap(s_final, ns, k, nqk) ||
         overlap(s_final, ns, v, nv) || overlap(s_final, ns, o, nv) ||
-        overlap(s_final, ns, cu_seqlens, ncu))
+        overlap(s_final, ns, cu_seqlens, ncu) || overlap(s_final, ns, g, ng))
       return GLA_ERR_ALIAS;
   }
   const HostPlan hp = plan_varlen(dt, N, total_T, H, dk, dv, chunk);
@@ -674,7 +725,7 @@ gla_status fwd_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chu
     if (overlap(workspace, hp.ws_bytes, q, nqk) || overlap(workspace, hp.ws_bytes, k, nqk) ||
         overlap(workspace, hp.ws_bytes, v, nv) || overlap(workspace, hp.ws_bytes, o, nv) ||
         overlap(workspace, hp.ws_bytes, s0, ns) || overlap(workspace, hp.ws_bytes, s_final, ns) ||
-        overlap(workspace, hp.ws_bytes, cu_seqlens, ncu))
+        overlap(workspace, hp.ws_bytes, cu_seqlens, ncu) || overlap(workspace, hp.ws_bytes, g, ng))
       return GLA_ERR_ALIAS;
   }
   hipStream_t s = (hipStream_t)stream;
@@ -693,6 +744,7 @@ gla_status fwd_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chu
   memset(&a, 0, sizeof(a));
   a.q = q; a.k = k; a.v = v; a.o = o; a.s0 = s0; a.s_final = s_final;
   a.scale = scale; a.H = H; a.dk = dk; a.dv = dv;
+  a.g = g; a.gate = gate;
   return run_forward(dt, hq, a, make_decay(decay_host, H), workspace, s);
 }
 
@@ -708,8 +760,18 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
                                 const float *s0, void *o, float *s_final,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream) {
-  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, decay_host,
-                    scale, s0, o, s_final, workspace, workspace_bytes, stream, false);
+  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, nullptr, kGateNone,
+                    decay_host, scale, s0, o, s_final, workspace, workspace_bytes, stream, false);
+}
+
+gla_status gla_chunk_fwd_varlen_gated(gla_dtype dt, int N, int total_T, int H, int dk, int dv,
+                                      int chunk, const int32_t *cu_seqlens, const void *q,
+                                      const void *k, const void *v, const void *g,
+                                      gla_gate gate, const float *decay_host, float scale,
+                                      const float *s0, void *o, float *s_final,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, g, gate_code(gate),
+                    decay_host, scale, s0, o, s_final, workspace, workspace_bytes, stream, false);
 }
 
 gla_status gla_chunk_fwd_varlen_noalloc(gla_dtype dt, int N, int total_T, int H,
@@ -719,8 +781,8 @@ gla_status gla_chunk_fwd_varlen_noalloc(gla_dtype dt, int N, int total_T, int H,
                                         const float *decay_host, float scale,
                                         const float *s0, void *o, float *s_final,
                                         void *stream) {
-  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, decay_host,
-                    scale, s0, o, s_final, nullptr, 0, stream, true);
+  return fwd_varlen(dt, N, total_T, H, dk, dv, chunk, cu_seqlens, q, k, v, nullptr, kGateNone,
+                    decay_host, scale, s0, o, s_final, nullptr, 0, stream, true);
 }
 
 size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
@@ -916,11 +978,18 @@ gla_status gla_short_conv_decode_step(gla_dtype dt, int N, int D, const void *x,
   return GLA_OK;
 }
 
-gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
-                           const void *q, const void *k, const void *v,
-                           const float *decay_host, float scale, float *state,
-                           void *o, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// gla_decode_step, with the output gate when gate != kGateNone (g [N, H, dv]
+// in o's dtype)
+gla_status decode_step(int dt, int N, int H, int dk, int dv, const void *q, const void *k,
+                       const void *v, const void *g, int gate, const float *decay_host,
+                       float scale, float *state, void *o, void *stream) {
   gla_status st = check_common(dt, H, dk, dv, 0);
+  if (st != GLA_OK) return st;
+  st = check_gate(gate);
   if (st != GLA_OK) return st;
   if (N < 0 || (long long)N * H > kMaxTokens) return GLA_ERR_SHAPE;
   if (!isfinite(scale)) return GLA_ERR_SHAPE;
@@ -928,20 +997,44 @@ gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
   if (st != GLA_OK) return st;
   if (N == 0) return GLA_OK;
   if (!q || !k || !v || !o || !state) return GLA_ERR_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(state))
+  if (gate != kGateNone && !g) return GLA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(state) ||
+      misaligned(g))
     return GLA_ERR_ALIGN;
   const size_t es = elem_size(dt);
   const size_t nqk = (size_t)N * H * dk * es, nv = (size_t)N * H * dv * es;
   const size_t ns = (size_t)N * H * dk * dv * sizeof(float);
+  const size_t ng = gate != kGateNone ? nv : 0;
   if (overlap(state, ns, q, nqk) || overlap(state, ns, k, nqk) ||
-      overlap(state, ns, v, nv) || overlap(state, ns, o, nv) ||
-      overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv))
+      overlap(state, ns, v, nv) || overlap(state, ns, o, nv) || overlap(state, ns, g, ng) ||
+      overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
+      overlap(o, nv, g, ng))
     return GLA_ERR_ALIAS;
   (void)hipGetLastError();
   if (launch_decode(dt, N, H, dk, dv, q, k, v, make_decay(decay_host, H), scale,
-                    state, o, (hipStream_t)stream) != hipSuccess)
+                    state, o, (hipStream_t)stream, nullptr, 0, nullptr, g, gate) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gla_status gla_decode_step(gla_dtype dt, int N, int H, int dk, int dv,
+                           const void *q, const void *k, const void *v,
+                           const float *decay_host, float scale, float *state,
+                           void *o, void *stream) {
+  return decode_step(dt, N, H, dk, dv, q, k, v, nullptr, kGateNone, decay_host, scale, state,
+                     o, stream);
+}
+
+gla_status gla_decode_step_gated(gla_dtype dt, int N, int H, int dk, int dv, const void *q,
+                                 const void *k, const void *v, const void *g, gla_gate gate,
+                                 const float *decay_host, float scale, float *state, void *o,
+                                 void *stream) {
+  return decode_step(dt, N, H, dk, dv, q, k, v, g, gate_code(gate), decay_host, scale, state,
+                     o, stream);
 }
 
 gla_status gla_linear_attn_decode_step(gla_dtype dt, int N, int H, int dk, int dv,

@@ -29,6 +29,15 @@ __device__ __forceinline__ float pow_f64(float lam, long long n) {
   return (float)r;
 }
 
+// The output gate's activation: sigmoid(z) = 1 / (1 + e^-z), or SiLU(z) =
+// z sigmoid(z), with the hardware exponential and reciprocal (about 1e-6
+// relative, far below the bf16 rounding of the outputs and the fp32 path's
+// tolerance); e^-z overflowing to infinity gives 0, not NaN.
+__device__ __forceinline__ float gate_act(float z, int gate) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+  return gate == kGateSilu ? z * s : s;
+}
+
 __host__ __device__ __forceinline__ int clampi(int x, int lo, int hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }

@@ -49,10 +49,14 @@ namespace gla {
 // ---------------------------------------------------------------------------
 // Output role: 4 waves (role wave w owns rows 16 w .. 16 w + 15 of a chunk).
 // ---------------------------------------------------------------------------
-template <int DVT, bool NORM, int DKT>
+// GATE: the output gate y = o * act(g) is applied to each output value in
+// fp32, before its single rounding to bf16; g is read from global memory in
+// the output tiles' own layout (this lane's 4 columns of each column tile of
+// its row), issued at the top of the chunk so it lands during the products.
+template <int DVT, bool NORM, int DKT, bool GATE>
 __device__ __forceinline__ void output_role(
-    const bf16 *__restrict__ q, bf16 *__restrict__ o, const Item &it, int h,
-    int H, int dv, int c0, float scale, int rt, int w, bf16 *sQ,
+    const bf16 *__restrict__ q, bf16 *__restrict__ o, const bf16 *__restrict__ gt, int gate,
+    const Item &it, int h, int H, int dv, int c0, float scale, int rt, int w, bf16 *sQ,
     const bf16 *sK, const bf16 *sV, const bf16 *sSt0, const bf16 *sSt1,
     const float *sPow) {
   using M = MfCfg<DVT, DKT>;
@@ -110,6 +114,15 @@ __device__ __forceinline__ void output_role(
     __syncthreads();  // chunk ch and S_{ch-1} are in LDS; chunk ch-1 is done
     load_q(ch + 2, rnew);
     store_q(cur ^ 1, rnext);
+    u32x2 graw[NCT];  // GATE: g of this lane's outputs (rows past the end read 0)
+    if (GATE) {
+      const __amdgpu_buffer_rsrc_t bg =
+          buf_rsrc(gt + tb * H * dv + (long long)h * dv + c0, (unsigned)L * rowVb);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        graw[ct] = __builtin_amdgcn_raw_buffer_load_b64(
+            bg, (unsigned)i_row * rowVb + (unsigned)(16 * ct + 4 * g) * 2, 0, 0);
+    }
     const bf16 *cQ = sQ + cur * KBUF, *cK = sK + cur * KBUF, *cV = sV + cur * VBUF;
     bf16x8 qf[NKS];
 #pragma unroll
@@ -182,8 +195,15 @@ __device__ __forceinline__ void output_role(
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       bf16x4 t;
+      if (GATE) {
+        const bf16x4 gv = __builtin_bit_cast(bf16x4, graw[ct]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] = (bf16)(coef * oacc[ct][r]);
+        for (int r = 0; r < 4; ++r)
+          t[r] = (bf16)(coef * oacc[ct][r] * gate_act((float)gv[r], gate));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = (bf16)(coef * oacc[ct][r]);
+      }
       *reinterpret_cast<bf16x4 *>(so + l16 * QS + 16 * ct + 4 * g) = t;
     }
     const __amdgpu_buffer_rsrc_t bo =
@@ -205,13 +225,13 @@ __device__ __forceinline__ void output_role(
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
-template <int DVT, bool NORM, int DKT>
+template <int DVT, bool NORM, int DKT, bool GATE>
 __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bf16 *__restrict__ v, bf16 *__restrict__ o,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H, int dv,
-    int final_in_slot, NormPtrs np) {
+    int final_in_slot, NormPtrs np, const bf16 *__restrict__ gt, int gate) {
   using M = MfCfg<DVT, DKT>;
   // dk 128: the state waves scale k in registers (no third 64 x 144 tile),
   // which leaves LDS room for 64-column d_v tiles
@@ -239,8 +259,8 @@ __global__ __launch_bounds__(512, 1) void fwd_out_kernel(
   const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = dtile * DVT;
   if (role_wave < 4)
-    output_role<DVT, NORM, DKT>(q, o, it, h, H, dv, c0, scale, tid & 255, role_wave, sQ,
-                                sK, sV, sSt0, sSt1, sPow);
+    output_role<DVT, NORM, DKT, GATE>(q, o, gt, gate, it, h, H, dv, c0, scale, tid & 255,
+                                      role_wave, sQ, sK, sV, sSt0, sSt1, sPow);
   else
     state_role<DVT, true, NORM, DKT, KSR>(k, v, s0, s_final, slots, it, idx, h, H, dv, c0,
                                      final_in_slot, tid & 255, role_wave - 4, sK, sKs, sV,
@@ -282,14 +302,24 @@ static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
                        const Decay &dec, hipStream_t s) {
   const unsigned grid = xcd_grid(p.deal, (long long)p.max_items * a.H, a.dv / DVT);
   const NormPtrs np = {a.z0, a.z_final, a.zslots};
-  if (state_only)
+  if (state_only) {
     hipLaunchKernelGGL((fwd_state_kernel<DVT, NORM, DKT>), dim3(grid), dim3(256), 0, s,
                        (const bf16 *)a.k, (const bf16 *)a.v, a.slots, p, dec, a.H, a.dv, np);
-  else
-    hipLaunchKernelGGL((fwd_out_kernel<DVT, NORM, DKT>), dim3(grid), dim3(512), 0, s,
-                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-                       (bf16 *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
-                       a.H, a.dv, a.final_in_slot, np);
+    return;
+  }
+  if constexpr (!NORM) {  // the gated readout (the normalised attention has no gate)
+    if (a.gate != kGateNone) {
+      hipLaunchKernelGGL((fwd_out_kernel<DVT, false, DKT, true>), dim3(grid), dim3(512), 0, s,
+                         (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                         (bf16 *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
+                         a.H, a.dv, a.final_in_slot, np, (const bf16 *)a.g, a.gate);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((fwd_out_kernel<DVT, NORM, DKT, false>), dim3(grid), dim3(512), 0, s,
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                     (bf16 *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
+                     a.H, a.dv, a.final_in_slot, np, (const bf16 *)nullptr, kGateNone);
 }
 
 // dk 96 runs d_v tiles of 96 or 64 columns, dk 64 tiles of 64 (a wave

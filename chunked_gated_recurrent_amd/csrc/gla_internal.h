@@ -59,9 +59,16 @@ struct FwdArgs {
   const float *z0;  // [n_seq][H][dk] or nullptr
   float *z_final;   // [n_seq][H][dk] or nullptr
   float *zslots;    // [max_items][H][dk] with time segments
+  // output gate (gate != kGateNone): g has o's layout and dtype
+  const void *g;
+  int gate;
 };
 
 constexpr float kLinearAttnEps = 1e-6f;
+
+// Output gate applied to the mixer's output, y = o * act(g): none, sigmoid
+// or SiLU (the values of the public gla_gate enum).
+constexpr int kGateNone = 0, kGateSigmoid = 1, kGateSilu = 2;
 
 // Normalised linear attention: where the normaliser sum z enters and leaves
 // (all [.][H][dk] fp32, nullptr when absent); kernel argument.
@@ -136,6 +143,7 @@ hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
                          const void *k, const void *v, const Decay &dec,
                          float scale, float *state, void *o, hipStream_t s,
                          const int32_t *slots = nullptr, int n_slots = 0,
-                         float *zsum = nullptr);
+                         float *zsum = nullptr, const void *g = nullptr,
+                         int gate = kGateNone);
 
 }  // namespace gla

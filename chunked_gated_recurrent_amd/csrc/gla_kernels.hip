@@ -50,13 +50,16 @@ __device__ __forceinline__ void st_out(Tin *p, float x) {
   *p = (Tin)x;
 }
 
+// gt (gate != kGateNone): the output gate, o = readout * act(g), g in o's
+// layout and dtype.
 template <typename Tin, bool STATE_ONLY, bool NORM>
 __global__ __launch_bounds__(256) void fwd_valu_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k,
     const Tin *__restrict__ v, Tin *__restrict__ o,
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, Plan plan, Decay dec, float scale, int H,
-    int dk, int dv, int C, int final_in_slot, NormPtrs np) {
+    int dk, int dv, int C, int final_in_slot, NormPtrs np, const Tin *__restrict__ gt,
+    int gate) {
   extern __shared__ float vsm[];
   float *sQ = vsm;                      // [C][dk]
   float *sK = sQ + C * dk;              // [C][dk]
@@ -159,8 +162,10 @@ __global__ __launch_bounds__(256) void fwd_valu_kernel(
           float intra = 0.f;
           for (int j = 0; j <= i; ++j) intra = fmaf(sP[i * C + j], sV[j * kValuDvt + c], intra);
           const float num = fmaf(sPow[i + 1], inter, intra);
-          st_out(o + (long long)(tb + i) * rowV + (long long)h * dv + c0 + c,
-                 NORM ? num / sDen[i] : scale * num);
+          const long long oi = (long long)(tb + i) * rowV + (long long)h * dv + c0 + c;
+          float y = NORM ? num / sDen[i] : scale * num;
+          if (gate != kGateNone) y *= gate_act(ld_in(gt + oi), gate);
+          st_out(o + oi, y);
         }
       }
       __syncthreads();
@@ -482,12 +487,15 @@ typedef float f32x4n __attribute__((ext_vector_type(4)));
 // NORM (normalised linear attention, lambda = 1 from the host): q and k
 // pass through ReLU, the normaliser z [rows][dk] is updated in place beside
 // the state, and the output is the readout over phi(q) . z + eps.
+// gt (gate != kGateNone): the output gate, o = readout * act(g) with g
+// [N, H, dv] in o's dtype.
 template <typename Tin, int RPT, bool NORM>
 __global__ __launch_bounds__(512) void decode_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k,
     const Tin *__restrict__ v, Decay dec, float scale, float *__restrict__ state,
     Tin *__restrict__ o, int H, int dk, int dv, int rpt_rt,
-    const int32_t *__restrict__ slots, int n_slots, float *__restrict__ zsum) {
+    const int32_t *__restrict__ slots, int n_slots, float *__restrict__ zsum,
+    const Tin *__restrict__ gt, int gate) {
   extern __shared__ float dsm[];
   const int quads = dv / 4;
   const int rpt = RPT > 0 ? RPT : rpt_rt;
@@ -572,7 +580,9 @@ __global__ __launch_bounds__(512) void decode_kernel(
   for (int c = tid; c < dv; c += blockDim.x) {
     float sum = 0.f;
     for (int r = 0; r < rg_n; ++r) sum += part[r * dv + c];
-    o[unit * dv + c] = (Tin)(coef * sum);
+    float y = coef * sum;
+    if (gate != kGateNone) y *= gate_act((float)gt[unit * dv + c], gate);
+    o[unit * dv + c] = (Tin)y;
   }
 }
 
@@ -618,7 +628,8 @@ static void launch_valu_n(const Plan &p, const FwdArgs &a, const Decay &dec,
   hipLaunchKernelGGL((fwd_valu_kernel<Tin, SO, NORM>), dim3(grid), dim3(256), lds, s,
                      (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v,
                      (Tin *)a.o, a.s0, a.s_final, a.slots, p, dec, a.scale,
-                     a.H, a.dk, a.dv, C, a.final_in_slot, np);
+                     a.H, a.dk, a.dv, C, a.final_in_slot, np, (const Tin *)a.g,
+                     SO || NORM ? kGateNone : a.gate);
 }
 
 template <typename Tin, bool SO>
@@ -697,7 +708,8 @@ hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
 hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
                          const void *k, const void *v, const Decay &dec,
                          float scale, float *state, void *o, hipStream_t s,
-                         const int32_t *slots, int n_slots, float *zsum) {
+                         const int32_t *slots, int n_slots, float *zsum, const void *g,
+                         int gate) {
   const int quads = dv / 4;
   // row groups: the largest divisor of dk with quads * groups <= 320 threads
   // (for dk 96, dv 192: 6 groups of 16 rows, 288 threads)
@@ -711,7 +723,7 @@ hipError_t launch_decode(int dt, int N, int H, int dk, int dv, const void *q,
 #define GLA_DECODE(T, R, NORM)                                                       \
   hipLaunchKernelGGL((decode_kernel<T, R, NORM>), dim3(grid), dim3(threads), lds, s, \
                      (const T *)q, (const T *)k, (const T *)v, dec, scale,           \
-                     state, (T *)o, H, dk, dv, rpt, slots, n_slots, zsum)
+                     state, (T *)o, H, dk, dv, rpt, slots, n_slots, zsum, (const T *)g, gate)
   if (zsum) {
     if (dt == 1) {
       if (rpt == 16) GLA_DECODE(bf16, 16, true);

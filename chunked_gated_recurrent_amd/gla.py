@@ -11,6 +11,8 @@ Functions mirror the C entry points:
     gla_chunk_fwd_varlen(q, k, v, cu, decay, ...) -> (o, s_final)
     gla_chunk_fwd_varlen_noalloc(q, k, v, cu, decay, out, ...) -> (out, s_final)
     gla_decode_step(q, k, v, decay, state, ...)  -> o   (state updated in place)
+    gla_chunk_fwd_gated(q, k, v, g, decay, gate, ...) -> (o * act(g), s_final)
+      (and g=, gate= on gla_chunk_fwd_varlen and gla_decode_step: the gated calls)
     gla_decode_step_pool(q, k, v, decay, state_pool, slots, ...) -> o
     gla_chunk_bwd(q, k, v, decay, dout, ...)    -> (dq, dk, dv, ds0)
     gla_chunk_bwd_varlen(q, k, v, cu, decay, dout, ...) -> (dq, dk, dv, ds0)
@@ -28,6 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgla.so")
 
 GLA_F32, GLA_BF16 = 0, 1
+# the output gate's activation (gla_gate)
+GATES = {"sigmoid": 1, "silu": 2}
 _lib = None
 
 _P = ctypes.c_void_p
@@ -55,6 +59,12 @@ _SIGS = {
     "gla_linear_attn_fwd_varlen_workspace_bytes": ([_I] * 7, ctypes.c_size_t),
     "gla_linear_attn_fwd_varlen": ([_I] * 7 + [_P] * 10 + [ctypes.c_size_t, _P], _I),
     "gla_decode_step": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _P, _P], _I),
+    "gla_chunk_fwd_gated": ([_I] * 7 + [_P, _P, _P, _P, _I, _P, ctypes.c_float, _P, _P, _P,
+                                        _P, ctypes.c_size_t, _P], _I),
+    "gla_chunk_fwd_varlen_gated": ([_I] * 7 + [_P, _P, _P, _P, _P, _I, _P, ctypes.c_float,
+                                               _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "gla_decode_step_gated": ([_I] * 5 + [_P, _P, _P, _P, _I, _P, ctypes.c_float, _P, _P,
+                                          _P], _I),
     "gla_short_conv_fwd": ([_I] * 4 + [_P] * 7, _I),
     "gla_short_conv_decode_step": ([_I] * 3 + [_P] * 6, _I),
     "gla_decode_step_pool": ([_I] * 5 + [_P, _P, _P, _P, ctypes.c_float, _P, _I, _P, _P, _P], _I),
@@ -140,16 +150,14 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def gla_chunk_fwd(q, k, v, decay, scale: float = 1.0, initial_state=None,
-                  output_final_state: bool = True, chunk: int = 0, out=None,
-                  final_state=None, workspace=None):
-    """Chunked forward of a fixed-length batch.
+def _gate_code(gate):
+    if gate not in GATES:
+        raise ValueError("gate must be one of %s, got %r" % (tuple(GATES), gate))
+    return GATES[gate]
 
-    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype);
-    decay: H floats on the host; initial_state: [B, H, dk, dv] fp32 or None.
-    Returns (o [B, T, H, dv], s_final [B, H, dk, dv] fp32 or None).
-    `final_state` may be `initial_state` itself (updated in place).
-    """
+
+def _chunk_fwd(q, k, v, decay, scale, initial_state, output_final_state, chunk, out,
+               final_state, workspace, g=None, gate=None):
     import torch
     dev = q.device
     B, T, H, dk = q.shape
@@ -157,6 +165,8 @@ def gla_chunk_fwd(q, k, v, decay, scale: float = 1.0, initial_state=None,
     _check(q, "q", dev)
     _check(k, "k", dev, q.dtype, (B, T, H, dk))
     _check(v, "v", dev, q.dtype, (B, T, H, dv))
+    if g is not None:
+        _check(g, "g", dev, q.dtype, (B, T, H, dv))
     dt = _dt(q)
     if initial_state is not None:
         _check(initial_state, "initial_state", dev, torch.float32, (B, H, dk, dv))
@@ -174,12 +184,44 @@ def gla_chunk_fwd(q, k, v, decay, scale: float = 1.0, initial_state=None,
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _d, dptr = _decay_array(decay, H)
-    rc = L.gla_chunk_fwd(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v),
-                         dptr, float(scale), _ptr(initial_state), _ptr(o),
-                         _ptr(sf), _ptr(ws), wsb, _stream(dev))
+    if g is None:
+        rc = L.gla_chunk_fwd(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v),
+                             dptr, float(scale), _ptr(initial_state), _ptr(o),
+                             _ptr(sf), _ptr(ws), wsb, _stream(dev))
+        where = "gla_chunk_fwd"
+    else:
+        rc = L.gla_chunk_fwd_gated(dt, B, T, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(g), _gate_code(gate), dptr, float(scale),
+                                   _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(ws), wsb,
+                                   _stream(dev))
+        where = "gla_chunk_fwd_gated"
     if rc != 0:
-        raise GlaError(rc, "gla_chunk_fwd")
+        raise GlaError(rc, where)
     return o, sf
+
+
+def gla_chunk_fwd(q, k, v, decay, scale: float = 1.0, initial_state=None,
+                  output_final_state: bool = True, chunk: int = 0, out=None,
+                  final_state=None, workspace=None):
+    """Chunked forward of a fixed-length batch.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv] (bf16 or fp32, same dtype);
+    decay: H floats on the host; initial_state: [B, H, dk, dv] fp32 or None.
+    Returns (o [B, T, H, dv], s_final [B, H, dk, dv] fp32 or None).
+    `final_state` may be `initial_state` itself (updated in place).
+    """
+    return _chunk_fwd(q, k, v, decay, scale, initial_state, output_final_state, chunk, out,
+                      final_state, workspace)
+
+
+def gla_chunk_fwd_gated(q, k, v, g, decay, gate: str, scale: float = 1.0,
+                        initial_state=None, output_final_state: bool = True, chunk: int = 0,
+                        out=None, final_state=None, workspace=None):
+    """gla_chunk_fwd with the output gate: o * act(g) elementwise, act
+    "sigmoid" or "silu"; g: [B, T, H, dv] in q's dtype. The final state is the
+    ungated call's."""
+    return _chunk_fwd(q, k, v, decay, scale, initial_state, output_final_state, chunk, out,
+                      final_state, workspace, g, gate)
 
 
 def linear_attn_fwd(q, k, v, initial_state=None, initial_z=None,
@@ -304,11 +346,13 @@ def linear_attn_decode_step(q, k, v, state, z, out=None):
 def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,
                          initial_state=None, output_final_state: bool = True,
                          chunk: int = 0, out=None, final_state=None,
-                         workspace=None):
+                         workspace=None, g=None, gate=None):
     """Chunked forward of N packed sequences.
 
     q, k: [total_T, H, dk]; v: [total_T, H, dv]; cu_seqlens: [N+1] int32 on
     the device. Returns (o [total_T, H, dv], s_final [N, H, dk, dv] or None).
+    With g ([total_T, H, dv], q's dtype) and gate ("sigmoid" or "silu"):
+    the gated call gla_chunk_fwd_varlen_gated, o * act(g).
     """
     import torch
     dev = q.device
@@ -319,6 +363,8 @@ def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,
     _check(k, "k", dev, q.dtype, (total, H, dk))
     _check(v, "v", dev, q.dtype, (total, H, dv))
     _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+    if g is not None:
+        _check(g, "g", dev, q.dtype, (total, H, dv))
     dt = _dt(q)
     if initial_state is not None:
         _check(initial_state, "initial_state", dev, torch.float32, (N, H, dk, dv))
@@ -336,12 +382,21 @@ def gla_chunk_fwd_varlen(q, k, v, cu_seqlens, decay, scale: float = 1.0,
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _d, dptr = _decay_array(decay, H)
-    rc = L.gla_chunk_fwd_varlen(dt, N, total, H, dk, dv, chunk, _ptr(cu_seqlens),
-                                _ptr(q), _ptr(k), _ptr(v), dptr, float(scale),
-                                _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(ws),
-                                wsb, _stream(dev))
+    if g is None:
+        rc = L.gla_chunk_fwd_varlen(dt, N, total, H, dk, dv, chunk, _ptr(cu_seqlens),
+                                    _ptr(q), _ptr(k), _ptr(v), dptr, float(scale),
+                                    _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(ws),
+                                    wsb, _stream(dev))
+        where = "gla_chunk_fwd_varlen"
+    else:
+        rc = L.gla_chunk_fwd_varlen_gated(dt, N, total, H, dk, dv, chunk, _ptr(cu_seqlens),
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                          _gate_code(gate), dptr, float(scale),
+                                          _ptr(initial_state), _ptr(o), _ptr(sf), _ptr(ws),
+                                          wsb, _stream(dev))
+        where = "gla_chunk_fwd_varlen_gated"
     if rc != 0:
-        raise GlaError(rc, "gla_chunk_fwd_varlen")
+        raise GlaError(rc, where)
     return o, sf
 
 
@@ -378,9 +433,10 @@ def gla_chunk_fwd_varlen_noalloc(q, k, v, cu_seqlens, decay, out, scale: float =
     return out, final_state
 
 
-def gla_decode_step(q, k, v, decay, state, scale: float = 1.0, out=None):
+def gla_decode_step(q, k, v, decay, state, scale: float = 1.0, out=None, g=None, gate=None):
     """One decode step: state [N, H, dk, dv] fp32 is updated in place;
-    returns o [N, H, dv]."""
+    returns o [N, H, dv]. With g ([N, H, dv], q's dtype) and gate ("sigmoid"
+    or "silu"): the gated step gla_decode_step_gated, o * act(g)."""
     import torch
     dev = q.device
     N, H, dk = q.shape
@@ -389,14 +445,23 @@ def gla_decode_step(q, k, v, decay, state, scale: float = 1.0, out=None):
     _check(k, "k", dev, q.dtype, (N, H, dk))
     _check(v, "v", dev, q.dtype, (N, H, dv))
     _check(state, "state", dev, torch.float32, (N, H, dk, dv))
+    if g is not None:
+        _check(g, "g", dev, q.dtype, (N, H, dv))
     dt = _dt(q)
     o = torch.empty((N, H, dv), dtype=q.dtype, device=dev) if out is None else out
     _check(o, "out", dev, q.dtype, (N, H, dv))
     _d, dptr = _decay_array(decay, H)
-    rc = lib().gla_decode_step(dt, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), dptr,
-                               float(scale), _ptr(state), _ptr(o), _stream(dev))
+    if g is None:
+        rc = lib().gla_decode_step(dt, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), dptr,
+                                   float(scale), _ptr(state), _ptr(o), _stream(dev))
+        where = "gla_decode_step"
+    else:
+        rc = lib().gla_decode_step_gated(dt, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _gate_code(gate), dptr, float(scale), _ptr(state),
+                                         _ptr(o), _stream(dev))
+        where = "gla_decode_step_gated"
     if rc != 0:
-        raise GlaError(rc, "gla_decode_step")
+        raise GlaError(rc, where)
     return o
 
 

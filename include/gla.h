@@ -92,6 +92,16 @@ typedef enum gla_dtype {
   GLA_DTYPE_RANGE_ = 0x7fffffff
 } gla_dtype;
 
+/* Activation of the output gate (gla_chunk_fwd_gated and its packed and
+   decode forms): act(z) = 1 / (1 + e^-z) for sigmoid, z / (1 + e^-z) for
+   SiLU. */
+typedef enum gla_gate {
+  GLA_GATE_SIGMOID = 1,
+  GLA_GATE_SILU = 2,
+  /* not a gate: widens the type's range to int (see gla_dtype) */
+  GLA_GATE_RANGE_ = 0x7fffffff
+} gla_gate;
+
 /* ABI version of the loaded library (GLA_ABI_VERSION at build time). */
 int gla_abi_version(void);
 
@@ -154,6 +164,37 @@ gla_status gla_chunk_fwd_varlen(gla_dtype dt, int N, int total_T, int H,
                                 const float *s0, void *o, float *s_final,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * The mixer's output gate (Laplace 3B / Trainium2 page, section "QKVG
+ * projection": the fused input projection yields a gate vector g_t beside
+ * q_t, k_t and v_t, and g_t acts on the mixer's output). The page names no
+ * activation; the caller chooses sigmoid or SiLU:
+ *     y_t = o_t * act(g_t)     (elementwise; o_t the ungated output above)
+ * applied in fp32 to each output value before its single rounding to dt.
+ *   g   : [B, T, H, dv] dt (gla_chunk_fwd_gated), [total_T, H, dv] dt
+ *         (gla_chunk_fwd_varlen_gated), [N, H, dv] dt (gla_decode_step_gated):
+ *         o's layout; read only, and o must not overlap it
+ *   gate: GLA_GATE_SIGMOID or GLA_GATE_SILU (else GLA_ERR_UNSUPPORTED)
+ * Every other argument, check, workspace size (the ungated call's
+ * *_workspace_bytes query) and state result is that of the ungated call:
+ * the gate changes the outputs only, never the recurrence's state.
+ */
+gla_status gla_chunk_fwd_gated(gla_dtype dt, int B, int T, int H, int dk, int dv,
+                               int chunk, const void *q, const void *k, const void *v,
+                               const void *g, gla_gate gate, const float *decay_host,
+                               float scale, const float *s0, void *o, float *s_final,
+                               void *workspace, size_t workspace_bytes, void *stream);
+gla_status gla_chunk_fwd_varlen_gated(gla_dtype dt, int N, int total_T, int H, int dk, int dv,
+                                      int chunk, const int32_t *cu_seqlens, const void *q,
+                                      const void *k, const void *v, const void *g,
+                                      gla_gate gate, const float *decay_host, float scale,
+                                      const float *s0, void *o, float *s_final,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+gla_status gla_decode_step_gated(gla_dtype dt, int N, int H, int dk, int dv, const void *q,
+                                 const void *k, const void *v, const void *g, gla_gate gate,
+                                 const float *decay_host, float scale, float *state, void *o,
+                                 void *stream);
 
 /*
  * gla_chunk_fwd_varlen for callers that cannot allocate device memory: code

@@ -316,3 +316,48 @@ def linear_attention(q, k, v, s0=None, z0=None, eps=LINEAR_ATTN_EPS):
         den = np.einsum("bhd,bhd->bh", fq[:, t], z) + eps
         o[:, t] = num / den[:, :, None]
     return o, S, z
+
+
+GATES = ("sigmoid", "silu")
+
+
+def gate_activation(g, act):
+    """The output gate's activation in fp64, from its definition:
+    sigmoid(z) = 1 / (1 + e^-z) and SiLU(z) = z / (1 + e^-z). g: fp32 values
+    or bf16 bits (uint16)."""
+    z = widen(g).astype(np.float64)
+    with np.errstate(over="ignore"):
+        e = np.exp(-z)  # e^-z overflows to inf for very negative z: act -> 0
+    if act == "sigmoid":
+        return 1.0 / (1.0 + e)
+    if act == "silu":
+        return z / (1.0 + e)
+    raise ValueError("act must be one of %s" % (GATES,))
+
+
+def output_gate(o, g, act):
+    """The mixer output gated elementwise by its gate vector (Laplace 3B /
+    Trainium2 page, section "QKVG projection": the fused projection yields
+    g beside q, k and v, and g is applied after the mixer; the page gives no
+    activation, so the caller names one): y = o * act(g), in fp64.
+    o: fp64 (or fp32) array; g: the same shape (fp32 or bf16 bits)."""
+    return np.asarray(o, np.float64) * gate_activation(g, act)
+
+
+def gla_fwd_gated(q, k, v, g, decay, act, scale=1.0, s0=None, threads=None):
+    """The chunked forward's result with the output gate applied:
+    (o * act(g) [B, T, H, dv], s_final) in fp64; the state is the ungated
+    recurrence's."""
+    o, sf = gla_fwd(q, k, v, decay, scale, s0, threads=threads)
+    return output_gate(o, g, act), sf
+
+
+def gla_varlen_gated(cu_seqlens, q, k, v, g, decay, act, scale=1.0, s0=None, threads=None):
+    o, sf = gla_varlen(cu_seqlens, q, k, v, decay, scale, s0, threads=threads)
+    return output_gate(o, g, act), sf
+
+
+def gla_decode_gated(q, k, v, g, decay, act, state, scale=1.0, threads=None):
+    """One gated decode step: state updated in place as by gla_decode;
+    returns o * act(g) [N, H, dv] fp64."""
+    return output_gate(gla_decode(q, k, v, decay, state, scale, threads), g, act)

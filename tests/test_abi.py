@@ -204,6 +204,39 @@ def test_noalloc_argument_errors(L, monkeypatch):
     assert status_text(L, TOO_LARGE).startswith("the call needs more scratch")
 
 
+def test_gated_argument_errors(L):
+    """The gated forward, packed forward and decode step validate like their
+    ungated calls, plus the gate itself and its g array."""
+    def fg(gate=1, g=A[7], o=A[3], T=128, **kw):
+        return L.gla_chunk_fwd_gated(BF16, 2, T, 4, 96, 192, 0, A[0], A[1], A[2], g, gate,
+                                     dptr(GOOD), 1.0, None, o, None, None, 0, None)
+    assert fg(gate=0) == UNSUP
+    assert fg(gate=3) == UNSUP
+    assert fg(g=None) == NULL
+    assert fg(g=None, T=0) == OK           # no tokens: nothing read or launched
+    assert fg(g=ctypes.c_void_p(A[7].value + 8)) == ALIGN
+    assert fg(o=ctypes.c_void_p(A[7].value + 512)) == ALIAS   # o inside g
+    assert fg(g=A[3]) == ALIAS                                  # g is o
+
+    def vg(gate=2, g=A[7], o=A[3]):
+        return L.gla_chunk_fwd_varlen_gated(BF16, 3, 300, 4, 96, 192, 0, A[6], A[0], A[1], A[2],
+                                            g, gate, dptr(GOOD), 1.0, None, o, None, None, 0,
+                                            None)
+    assert vg(gate=7) == UNSUP
+    assert vg(g=None) == NULL
+    assert vg(g=A[3]) == ALIAS
+    assert vg() == WS          # valid otherwise: the dispatch order needs scratch
+
+    def dg(gate=1, g=A[7], o=A[4], N=4):
+        return L.gla_decode_step_gated(BF16, N, 4, 96, 192, A[0], A[1], A[2], g, gate,
+                                       dptr(GOOD), 1.0, A[3], o, None)
+    assert dg(gate=-1) == UNSUP
+    assert dg(g=None) == NULL
+    assert dg(g=None, N=0) == OK
+    assert dg(g=ctypes.c_void_p(A[3].value + 4096)) == ALIAS    # g inside the state
+    assert dg(g=ctypes.c_void_p(A[7].value + 4)) == ALIGN
+
+
 def test_decode_argument_errors(L):
     def dec(dt=BF16, N=4, H=4, dk=96, dv=192, q=A[0], k=A[1], v=A[2], st=A[3],
             o=A[4], decay=GOOD):
