@@ -304,6 +304,27 @@ int bwd_plan_ndt(int dt, int dk, int dv, int chunk) {
   return fast_path_ok(dt, dk, dv, chunk) ? dv / fwd_dv_tile(dk, dv) : 0;
 }
 
+// The backward's plan. On the workgroup-per-head path both walks can run in
+// one launch when no sequence needs time segments (two workgroups per unit,
+// so half the units fill the GPU): plan for that first, and fall back to
+// time segments (walks launched one after the other, one workgroup per
+// unit) only if it still needs them.
+HostPlan bwd_plan_fixed(int dt, int B, int T, int H, int dk, int dv, int chunk) {
+  if (bwd_wide_path(dt, dk, dv, chunk)) {
+    const HostPlan one = plan_fixed(dt, B, T, H, dk, dv, chunk, 2);
+    if (!one.segmented) return one;
+  }
+  return plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+}
+
+HostPlan bwd_plan_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chunk) {
+  if (bwd_wide_path(dt, dk, dv, chunk)) {
+    const HostPlan one = plan_varlen(dt, N, total_T, H, dk, dv, chunk, 2);
+    if (!one.segmented) return one;
+  }
+  return plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+}
+
 BwdPlan bwd_layout(const HostPlan &hp, long long total_T, int H, int dk, int dv) {
   BwdPlan bp;
   memset(&bp, 0, sizeof(bp));
@@ -380,7 +401,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
   }
   hipError_t e;
   if (bp.wide)
-    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, s);
+    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, !hp.segmented, s);
   else
     e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
   if (e != hipSuccess) return GLA_ERR_HIP;
@@ -408,6 +429,7 @@ const char *gla_status_str(gla_status s) {
     case GLA_ERR_TOO_LARGE:
       return "the call needs more scratch than the allocation-free entry point holds";
     case GLA_STATUS_RANGE_:
+    case GLA_STATUS_RANGE_MIN_:
       break;
   }
   return "unknown status";
@@ -791,7 +813,7 @@ size_t gla_chunk_bwd_workspace_bytes(gla_dtype dt, int B, int T, int H, int dk,
       B < 1 || T < 0 || (long long)B * T > kMaxTokens)
     return 0;
   const HostPlan hp =
-      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+      bwd_plan_fixed(dt, B, T, H, dk, dv, chunk);
   return bwd_layout(hp, (long long)B * T, H, dk, dv).ws_bytes;
 }
 
@@ -828,7 +850,7 @@ gla_status gla_chunk_bwd(gla_dtype dt, int B, int T, int H, int dk, int dv,
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
   const BwdPlan bp = bwd_layout(
-      plan_fixed(dt, B, T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk)), tok, H,
+      bwd_plan_fixed(dt, B, T, H, dk, dv, chunk), tok, H,
       dk, dv);
   if (bp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < bp.ws_bytes) return GLA_ERR_WORKSPACE;
@@ -859,7 +881,7 @@ size_t gla_chunk_bwd_varlen_workspace_bytes(gla_dtype dt, int N, int total_T, in
       N < 1 || N > (1 << 28) || total_T < 0)
     return 0;
   const HostPlan hp =
-      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+      bwd_plan_varlen(dt, N, total_T, H, dk, dv, chunk);
   return bwd_layout(hp, total_T, H, dk, dv).ws_bytes;
 }
 
@@ -897,7 +919,7 @@ gla_status gla_chunk_bwd_varlen(gla_dtype dt, int N, int total_T, int H, int dk,
       if (overlap(out[a], out_n[a], out[b], out_n[b])) return GLA_ERR_ALIAS;
   }
   HostPlan hp =
-      plan_varlen(dt, N, total_T, H, dk, dv, chunk, bwd_plan_ndt(dt, dk, dv, chunk));
+      bwd_plan_varlen(dt, N, total_T, H, dk, dv, chunk);
   hp.p.cu = cu_seqlens;
   const BwdPlan bp = bwd_layout(hp, total_T, H, dk, dv);
   if (bp.ws_bytes > 0) {

@@ -327,21 +327,36 @@ __device__ __forceinline__ void wide_state_role(
   }
 }
 
+// LDS of the two walks (bytes, 16-byte multiples): the dq walk holds k, its
+// decay-scaled copy, v, dO and the published S^T; the reverse walk q, its
+// decay-scaled copy, k, v, dO and the published Ch^T; both the decay powers.
 template <int DKT, int DV>
-__global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
+struct WideLds {
+  static constexpr int QT = 64 * (DKT + 16) * 2, VT = 64 * (DV + 16) * 2;
+  static constexpr int ST = DV * (DKT + 16) * 2, POW = 68 * 4;
+  static constexpr int DQ = 2 * QT + 2 * VT + ST + POW;
+  static constexpr int REV = 3 * QT + 2 * VT + ST + POW;
+  static constexpr int MAX = DQ > REV ? DQ : REV;
+};
+
+// The dq walk of the workgroup with id P in its walk's grid (see
+// bwd_dq_wide_kernel), on the LDS block `lds`.
+template <int DKT, int DV>
+__device__ __forceinline__ void dq_wide_walk(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
     const float *__restrict__ s0, const float *__restrict__ slots, bf16 *__restrict__ dq,
-    Plan plan, Decay dec, float scale, int H, int pair) {
+    const Plan &plan, const Decay &dec, float scale, int H, int pair, int P, char *lds) {
   WIDE_CONSTS(DKT, DV);
-  __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
-  __shared__ __attribute__((aligned(16))) bf16 sKs[kWC * kWQS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[kWC * kWVS];
-  __shared__ __attribute__((aligned(16))) bf16 sD[kWC * kWVS];
-  __shared__ __attribute__((aligned(16))) bf16 sSt[kWideDv * kWQS];
-  __shared__ float sPow[kWC + 4];
+  using LD = WideLds<DKT, DV>;
+  bf16 *sK = (bf16 *)lds;
+  bf16 *sKs = (bf16 *)(lds + LD::QT);
+  bf16 *sV = (bf16 *)(lds + 2 * LD::QT);
+  bf16 *sD = (bf16 *)(lds + 2 * LD::QT + LD::VT);
+  bf16 *sSt = (bf16 *)(lds + 2 * LD::QT + 2 * LD::VT);
+  float *sPow = (float *)(lds + 2 * LD::QT + 2 * LD::VT + LD::ST);
 
   int unit, dtile;
-  xcd_unit(plan, 1, plan.max_items * H, unit, dtile);
+  xcd_unit_at(plan, P, 1, plan.max_items * H, unit, dtile);
   if (unit >= plan.max_items * H) return;
   const int slot = unit / H;
   const int h = unit - slot * H;
@@ -366,6 +381,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
     wide_state_role<DKT, DV>(k, v, s0, slots, it, idx, h, H, tid & 255, role_wave - 4, sK, sKs, sV,
                     sSt, sPow, pair_add, pair_scale);
   }
+}
+
+template <int DKT, int DV>
+__global__ __launch_bounds__(512, 1) void bwd_dq_wide_kernel(
+    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
+    const float *__restrict__ s0, const float *__restrict__ slots, bf16 *__restrict__ dq,
+    Plan plan, Decay dec, float scale, int H, int pair) {
+  __shared__ __attribute__((aligned(16))) char lds[WideLds<DKT, DV>::DQ];
+  dq_wide_walk<DKT, DV>(k, v, dout, s0, slots, dq, plan, dec, scale, H, pair, (int)blockIdx.x,
+                        lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -678,23 +703,27 @@ __device__ __forceinline__ void wide_rev_role(
   }
 }
 
+// The reverse walk of the workgroup with id P in its walk's grid (see
+// bwd_dkdv_wide_kernel), on the LDS block `lds`.
 template <int DKT, int DV>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
+__device__ __forceinline__ void dkdv_wide_walk(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
-    float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H, int pair) {
+    float *__restrict__ ds0, const Plan &plan, const Decay &dec, float scale, int H, int pair,
+    int P, char *lds) {
   WIDE_CONSTS(DKT, DV);
-  __shared__ __attribute__((aligned(16))) bf16 sQ[kWC * kWQS];
-  __shared__ __attribute__((aligned(16))) bf16 sQs[kWC * kWQS];
-  __shared__ __attribute__((aligned(16))) bf16 sK[kWC * kWQS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[kWC * kWVS];
-  __shared__ __attribute__((aligned(16))) bf16 sD[kWC * kWVS];
-  __shared__ __attribute__((aligned(16))) bf16 sCt[kWideDv * kWQS];
-  __shared__ float sPow[kWC + 4];
+  using LD = WideLds<DKT, DV>;
+  bf16 *sQ = (bf16 *)lds;
+  bf16 *sQs = (bf16 *)(lds + LD::QT);
+  bf16 *sK = (bf16 *)(lds + 2 * LD::QT);
+  bf16 *sV = (bf16 *)(lds + 3 * LD::QT);
+  bf16 *sD = (bf16 *)(lds + 3 * LD::QT + LD::VT);
+  bf16 *sCt = (bf16 *)(lds + 3 * LD::QT + 2 * LD::VT);
+  float *sPow = (float *)(lds + 3 * LD::QT + 2 * LD::VT + LD::ST);
 
   int unit, dtile;
-  xcd_unit(plan, 1, plan.max_items * H, unit, dtile);
+  xcd_unit_at(plan, P, 1, plan.max_items * H, unit, dtile);
   if (unit >= plan.max_items * H) return;
   const int slot = unit / H;
   const int h = unit - slot * H;
@@ -721,6 +750,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
                          tid & 255, wave - 4, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
 }
 
+template <int DKT, int DV>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
+    const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
+    float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H, int pair) {
+  __shared__ __attribute__((aligned(16))) char lds[WideLds<DKT, DV>::REV];
+  dkdv_wide_walk<DKT, DV>(q, k, v, dout, ds_final, cslots, dv_out, dk_out, ds0, plan, dec, scale,
+                          H, pair, (int)blockIdx.x, lds);
+}
+
+// Both walks in one launch, for items that are whole sequences (no time
+// segments, so no slots): workgroups [0, n_rev) run the reverse walk, the
+// rest the dq walk. The walks share nothing, so neither waits on the other,
+// and with one workgroup of either kind per CU the batch needs half the
+// (sequence, head) units a walk alone needs to fill the GPU.
+// (slots, cslots and pair are the separate kernels' arguments; a plan
+// without segments never reads them.)
+template <int DKT, int DV>
+__global__ __launch_bounds__(512, 1) void bwd_fused_wide_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ s0,
+    const float *__restrict__ ds_final, const float *__restrict__ slots,
+    const float *__restrict__ cslots, bf16 *__restrict__ dq, bf16 *__restrict__ dv_out,
+    bf16 *__restrict__ dk_out, float *__restrict__ ds0, Plan plan, Decay dec, float scale,
+    int H, int pair, int n_rev) {
+  __shared__ __attribute__((aligned(16))) char lds[WideLds<DKT, DV>::MAX];
+  // n_rev is a multiple of 8, so both walks keep the id -> XCD dealing
+  if ((int)blockIdx.x < n_rev)
+    dkdv_wide_walk<DKT, DV>(q, k, v, dout, ds_final, cslots, dv_out, dk_out, ds0, plan, dec,
+                            scale, H, pair, (int)blockIdx.x, lds);
+  else
+    dq_wide_walk<DKT, DV>(k, v, dout, s0, slots, dq, plan, dec, scale, H, pair,
+                          (int)blockIdx.x - n_rev, lds);
+}
+
 bool bwd_wide_ok(int dk, int dv) { return wide_shape(dk, dv); }
 
 // One head shape; see launch_bwd_wide.
@@ -740,22 +805,38 @@ static void launch_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int p
                      dec, a.scale, a.H, pair);
 }
 
+template <int DKT, int DV>
+static void launch_fused(const Plan &p, const BwdArgs &a, const Decay &dec, hipStream_t s) {
+  const unsigned g = xcd_grid(p.deal, (long long)p.max_items * a.H, 1);
+  hipLaunchKernelGGL((bwd_fused_wide_kernel<DKT, DV>), dim3(2 * g), dim3(512), 0, s,
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                     (const bf16 *)a.dout, a.s0, a.ds_final, a.slots, a.cslots, (bf16 *)a.dq,
+                     (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H, 0, (int)g);
+}
+
 // pair: the segment slots hold unscanned local quantities and every sequence
-// has exactly two segments (the kernels join them on load).
+// has exactly two segments (the kernels join them on load). fused: no time
+// segments; both walks in one launch.
 hipError_t launch_bwd_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
-                           hipStream_t s) {
+                           bool fused, hipStream_t s) {
   // the shapes wide_shape() admits
+#define GLA_WIDE(DK_, DV_)                                \
+  case DK_ * 1000 + DV_:                                  \
+    if (fused) launch_fused<DK_, DV_>(p, a, dec, s);      \
+    else launch_wide<DK_, DV_>(p, a, dec, pair, s);       \
+    break;
   switch (a.dk_dim * 1000 + a.dv) {
-    case 96192: launch_wide<96, 192>(p, a, dec, pair, s); break;
-    case 96128: launch_wide<96, 128>(p, a, dec, pair, s); break;
-    case 96064: launch_wide<96, 64>(p, a, dec, pair, s); break;
-    case 64192: launch_wide<64, 192>(p, a, dec, pair, s); break;
-    case 64128: launch_wide<64, 128>(p, a, dec, pair, s); break;
-    case 64064: launch_wide<64, 64>(p, a, dec, pair, s); break;
-    case 128128: launch_wide<128, 128>(p, a, dec, pair, s); break;
-    case 128064: launch_wide<128, 64>(p, a, dec, pair, s); break;
+    GLA_WIDE(96, 192)
+    GLA_WIDE(96, 128)
+    GLA_WIDE(96, 64)
+    GLA_WIDE(64, 192)
+    GLA_WIDE(64, 128)
+    GLA_WIDE(64, 64)
+    GLA_WIDE(128, 128)
+    GLA_WIDE(128, 64)
     default: return hipErrorInvalidValue;
   }
+#undef GLA_WIDE
   return hipGetLastError();
 }
 

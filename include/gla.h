@@ -79,17 +79,20 @@ typedef enum gla_status {
   GLA_ERR_HIP = 8,         /* a HIP launch failed                              */
   GLA_ERR_ALIGN = 9,       /* a tensor pointer is not 16-byte aligned          */
   GLA_ERR_TOO_LARGE = 10,  /* needs more than GLA_NOALLOC_SCRATCH_BYTES        */
-  /* not a status: widens the type's range to int, so that any int a caller
-     passes is a value of the type (and unknown ones are well-defined) */
-  GLA_STATUS_RANGE_ = 0x7fffffff
+  /* not statuses: they widen the type's range to all of int, so that any
+     int a caller passes is a value of the type (unknown ones well-defined) */
+  GLA_STATUS_RANGE_ = 0x7fffffff,
+  GLA_STATUS_RANGE_MIN_ = -0x7fffffff - 1
 } gla_status;
 
 typedef enum gla_dtype {
   GLA_F32 = 0,
   GLA_BF16 = 1,
-  /* not a dtype: widens the type's range to int, so that an unknown value
-     passed by a caller is rejected with GLA_ERR_DTYPE, not undefined */
-  GLA_DTYPE_RANGE_ = 0x7fffffff
+  /* not dtypes: they widen the type's range to all of int, so that an
+     unknown value passed by a caller is rejected with GLA_ERR_DTYPE, not
+     undefined */
+  GLA_DTYPE_RANGE_ = 0x7fffffff,
+  GLA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1
 } gla_dtype;
 
 /* Activation of the output gate (gla_chunk_fwd_gated and its packed and
@@ -98,8 +101,9 @@ typedef enum gla_dtype {
 typedef enum gla_gate {
   GLA_GATE_SIGMOID = 1,
   GLA_GATE_SILU = 2,
-  /* not a gate: widens the type's range to int (see gla_dtype) */
-  GLA_GATE_RANGE_ = 0x7fffffff
+  /* not gates: they widen the type's range to all of int (see gla_dtype) */
+  GLA_GATE_RANGE_ = 0x7fffffff,
+  GLA_GATE_RANGE_MIN_ = -0x7fffffff - 1
 } gla_gate;
 
 /* ABI version of the loaded library (GLA_ABI_VERSION at build time). */

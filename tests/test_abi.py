@@ -68,6 +68,7 @@ def test_version_and_status_strings(L):
         assert s and s not in seen
         seen.add(s)
     assert status_text(L, 99) == "unknown status"
+    assert status_text(L, -1) == "unknown status"
 
 
 # fake, 256-byte aligned, far-apart device addresses: never dereferenced
@@ -90,6 +91,7 @@ def fwd(L, dt=BF16, B=2, T=128, H=4, dk=96, dv=192, chunk=0, q=A[0], k=A[1],
 
 def test_fwd_argument_errors(L):
     assert fwd(L, dt=7) == DTYPE
+    assert fwd(L, dt=-3) == DTYPE
     assert fwd(L, H=0) == SHAPE
     assert fwd(L, B=0) == SHAPE
     assert fwd(L, T=-1) == SHAPE
@@ -287,18 +289,20 @@ def test_backward_argument_errors(L):
     need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 256, 0)
     # dq and dk partials: 4 dv tiles x 16 heads x 16,384 tokens x 96 fp32, twice
     assert need == 2 * 4 * 16 * 8 * 2048 * 96 * 4
-    # dv = 128 and 64 take the workgroup-per-head kernels as dv = 192 does:
-    # no partials; 8 x 16 units in 2 time segments (states and carries)
-    for dv in (128, 64):
-        need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, dv, 0)
-        assert need == 2 * (8 * 2 * 16 * 96 * dv * 4), dv
+    # dv = 192, 128 and 64: one workgroup per (sequence, head) over all of
+    # dv, no partials. The 8 x 16 units of the Laplace batch fill the GPU with
+    # both walks in one launch: no time segments, no scratch
+    for dv in (192, 128, 64):
+        assert L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, dv, 0) == 0, dv
     assert L.gla_chunk_bwd_workspace_bytes(BF16, 2, 100, 4, 96, 128, 0) == 0
-    # dv = 192: one workgroup per (sequence, head) over all of dv, no partials;
-    # 8 x 16 units are split into 2 time segments, whose incoming states and
-    # carried gradients (fp32 96 x 192 per segment and head) are the workspace
-    need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 16, 96, 192, 0)
-    assert need == 2 * (8 * 2 * 16 * 96 * 192 * 4)
     assert L.gla_chunk_bwd_workspace_bytes(BF16, 256, 128, 16, 96, 192, 0) == 0
+    # 8 x 8 units do not: the walks run one after the other, one workgroup
+    # per unit, over 4 time segments per sequence (64 units x 4 fill the 256
+    # CUs), whose incoming states and carried gradients (fp32 96 x dv per
+    # segment and head) are the workspace
+    for dv in (192, 128, 64):
+        need = L.gla_chunk_bwd_workspace_bytes(BF16, 8, 2048, 8, 96, dv, 0)
+        assert need == 2 * (8 * 4 * 8 * 96 * dv * 4), dv
     # vector-ALU path: dv tiles of 64 columns, dk = 32
     assert L.gla_chunk_bwd_workspace_bytes(F32, 8, 2048, 16, 32, 192, 0) == \
         2 * 3 * 16 * 8 * 2048 * 32 * 4

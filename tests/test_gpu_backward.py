@@ -74,13 +74,22 @@ def test_backward_widest_value_head():
 
 @pytest.mark.parametrize("dv", [192, 128, 64])
 def test_backward_two_segments_joined_on_load(dv):
-    """8 x 16 units of 256 tokens: two time segments per sequence, whose
+    """8 x 8 units of 256 tokens: two time segments per sequence, whose
     local states and carries the wide kernels (one workgroup over all of
     d_v) join with S0 and dL/dS_final as they load them (no scan launch)."""
-    x, do, dsf = _inputs(707 + dv, 8, 256, 16, dv)
-    need = gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 16, 96, dv, 0)
-    assert need == 2 * (8 * 2 * 16 * 96 * dv * 4)  # two segments' states and carries
+    x, do, dsf = _inputs(707 + dv, 8, 256, 8, dv)
+    need = gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 8, 96, dv, 0)
+    assert need == 2 * (8 * 2 * 8 * 96 * dv * 4)  # two segments' states and carries
     _check("bwd two segments dv%d" % dv, _run(x, do, dsf), _oracle(x, do, dsf))
+
+
+@pytest.mark.parametrize("dv", [192, 128, 64])
+def test_backward_both_walks_in_one_launch(dv):
+    """8 x 16 units of 256 tokens fill the GPU with both walks in one launch:
+    no time segments, no scratch."""
+    x, do, dsf = _inputs(709 + dv, 8, 256, 16, dv)
+    assert gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 16, 96, dv, 0) == 0
+    _check("bwd one launch dv%d" % dv, _run(x, do, dsf), _oracle(x, do, dsf))
 
 
 def test_backward_max_heads_with_lambda_one():
