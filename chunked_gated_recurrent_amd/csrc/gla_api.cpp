@@ -87,6 +87,20 @@ int target_workgroups() {
   return 256;
 }
 
+// Share of every sequence's chunks (in 1/65536) whose dk and dv rows the
+// fused backward gives to the dq walk's workgroup: a chunk of the reverse
+// walk costs about 1.7 times one of the dq walk, so a quarter of the reverse
+// work moves over to even out the two. GLA_BWD_TAIL (a fraction in [0, 0.5])
+// overrides it.
+int bwd_tail_q16() {
+  const char *e = getenv("GLA_BWD_TAIL");
+  if (e && *e) {
+    const double f = strtod(e, nullptr);
+    if (f >= 0.0 && f <= 0.5) return (int)(f * 65536.0 + 0.5);
+  }
+  return 16384;
+}
+
 struct HostPlan {
   Plan p;
   bool fast;
@@ -401,7 +415,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
   }
   hipError_t e;
   if (bp.wide)
-    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, !hp.segmented, s);
+    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, !hp.segmented, bwd_tail_q16(), s);
   else
     e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
   if (e != hipSuccess) return GLA_ERR_HIP;

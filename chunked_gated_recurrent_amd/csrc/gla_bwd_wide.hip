@@ -175,17 +175,23 @@ __device__ __forceinline__ void wide_dq_role(
         const bf16 *base = sK + (32 * s + 4 * g + tr_row) * QS + 16 * dt + tr_col;
         acc[dt] = mfma(cat8(tr4(base), tr4(base + 16 * QS)), pb[s], acc[dt]);
       }
-    // dq row i: this lane holds dk values 16 dt + 4 g .. + 3
-    if (i_row < chunk_rows(it, ch)) {
-      bf16 *dst = dq + ((it.t0 + (long long)ch * C + i_row) * H + h) * DKT + 4 * g;
+    {  // dq row i: this lane holds dk values 16 dt + 4 g .. + 3 (rows past
+       // the item's end fall outside the descriptor)
+      const unsigned rowKb = (unsigned)(H * DKT * 2);
+      const __amdgpu_buffer_rsrc_t bo =
+          buf_rsrc(dq + ((it.t0 + (long long)ch * C) * H + h) * DKT,
+                   (unsigned)chunk_rows(it, ch) * rowKb);
+      const unsigned o0 = (unsigned)i_row * rowKb + 8 * g;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         bf16x4 t;
 #pragma unroll
         for (int r = 0; r < 4; ++r) t[r] = (bf16)(scale * acc[dt][r]);
-        *reinterpret_cast<bf16x4 *>(dst + 16 * dt) = t;
+        buf_store8(t, bo, o0 + 32 * dt);
       }
     }
+    // keep the result tiles' registers from living on into what follows
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // B: every read of chunk ch and S_{ch-1} is done
     store(rnext);
   };
@@ -404,7 +410,7 @@ __device__ __forceinline__ void wide_rev_role(
     const Item &it, int idx, int h, int H, float scale, int rt, int w, bf16 *sQ, bf16 *sQs,
     bf16 *sK,
     bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow, const float *pair_add,
-    float pair_scale) {
+    float pair_scale, int n_out) {
   WIDE_CONSTS(DKT, DV);
   constexpr int C = kWC, DK = DKT, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;
   constexpr int NDT = MW::NDT, NCT = MW::NCT, NJS = MW::NJS, NKS = MW::NKS;
@@ -429,13 +435,19 @@ __device__ __forceinline__ void wide_rev_role(
   const int drow0 = DV_ROLE ? 0 : 32;
   auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
 
+  // chunks from n_out on only carry the gradient: their k and v tiles are
+  // not needed, and an empty descriptor turns those loads into zeros that
+  // cost no memory traffic (a branch around them instead would make every
+  // later wait on the loads assume they were skipped, and wait for the
+  // next chunk's loads too)
   auto load = [&](int ch, u32x4(&r)[NL]) {
     const unsigned L = (unsigned)rows_of(ch);
+    const unsigned Lkv = ch < n_out ? L : 0u;
     const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
     const __amdgpu_buffer_rsrc_t bd = buf_rsrc(dout + (tb * H + h) * kWideDv, L * rowVb);
     if (DV_ROLE) {
       const __amdgpu_buffer_rsrc_t bq = buf_rsrc(q + (tb * H + h) * DK, L * rowKb);
-      const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, L * rowKb);
+      const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, Lkv * rowKb);
 #pragma unroll
       for (int m = 0; m < QV; ++m)
         r[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
@@ -443,7 +455,7 @@ __device__ __forceinline__ void wide_rev_role(
       for (int m = 0; m < QV; ++m)
         r[QV + m] = __builtin_amdgcn_raw_buffer_load_b128(bk, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
     } else {
-      const __amdgpu_buffer_rsrc_t bv = buf_rsrc(v + (tb * H + h) * kWideDv, L * rowVb);
+      const __amdgpu_buffer_rsrc_t bv = buf_rsrc(v + (tb * H + h) * kWideDv, Lkv * rowVb);
 #pragma unroll
       for (int m = 0; m < VV; ++m)
         r[m] = __builtin_amdgcn_raw_buffer_load_b128(bv, ia.row[m] * rowVb + ia.col[m] * 16, 0, 0);
@@ -535,6 +547,35 @@ __device__ __forceinline__ void wide_rev_role(
   for (int m = 0; m < NA; ++m) fqr[m] = DV_ROLE ? scale * sPow[ia.row[m] + 1] : 0.f;
   store(ra);
   publish();
+
+  // Ch <- lambda^L Ch + scale sum_t lambda^(t+1) q_t^T dO_t (this wave's
+  // tiles) over the L rows of the chunk in LDS
+  auto advance = [&](int L) {
+    const float lamL = sPow[L];
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+#pragma unroll
+      for (int b = 0; b < CB; ++b) accC[a][b] *= lamL;
+#pragma unroll
+    for (int s = 0; s < NJS; ++s) {
+      bf16x8 qa[RB], dfr[CB];  // scale lambda^(t+1) q_t (P k-set over t) and dO
+      const int row = 32 * s + 4 * g + tr_row;
+#pragma unroll
+      for (int a = 0; a < RB; ++a) {
+        const bf16 *base = sQs + row * QS + 16 * (dt0 + a) + tr_col;
+        qa[a] = cat8(tr4(base), tr4(base + 16 * QS));
+      }
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        const bf16 *base = sD + row * VS + 16 * (ct0 + b) + tr_col;
+        dfr[b] = cat8(tr4(base), tr4(base + 16 * VS));
+      }
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+#pragma unroll
+        for (int b = 0; b < CB; ++b) accC[a][b] = mfma(qa[a], dfr[b], accC[a][b]);
+    }
+  };
 
   auto body = [&](int ch, u32x4(&rn)[NL], const u32x4(&rx)[NL]) {
     const int L = rows_of(ch);
@@ -655,36 +696,28 @@ __device__ __forceinline__ void wide_rev_role(
         }
       }
     }
-    // Ch <- lambda^L Ch + scale sum_t lambda^(t+1) q_t^T dO_t (this wave's tiles)
-    const float lamL = sPow[L];
-#pragma unroll
-    for (int a = 0; a < RB; ++a)
-#pragma unroll
-      for (int b = 0; b < CB; ++b) accC[a][b] *= lamL;
-#pragma unroll
-    for (int s = 0; s < NJS; ++s) {
-      bf16x8 qa[RB], dfr[CB];  // scale lambda^(t+1) q_t (P k-set over t) and dO
-      const int row = 32 * s + 4 * g + tr_row;
-#pragma unroll
-      for (int a = 0; a < RB; ++a) {
-        const bf16 *base = sQs + row * QS + 16 * (dt0 + a) + tr_col;
-        qa[a] = cat8(tr4(base), tr4(base + 16 * QS));
-      }
-#pragma unroll
-      for (int b = 0; b < CB; ++b) {
-        const bf16 *base = sD + row * VS + 16 * (ct0 + b) + tr_col;
-        dfr[b] = cat8(tr4(base), tr4(base + 16 * VS));
-      }
-#pragma unroll
-      for (int a = 0; a < RB; ++a)
-#pragma unroll
-        for (int b = 0; b < CB; ++b) accC[a][b] = mfma(qa[a], dfr[b], accC[a][b]);
-    }
+    advance(L);
     __syncthreads();  // B: every read of chunk ch and Ch_in is done
     store(rx);
     publish();
   };
-  for (int p = 0; p < nch; p += 2) {  // a chunk before the first is all zeros
+  // chunks past n_out only carry the gradient back (their dk and dv rows
+  // are formed elsewhere): the same update of Ch, nothing else
+  auto carry_body = [&](int ch, u32x4(&rn)[NL], const u32x4(&rx)[NL]) {
+    __syncthreads();  // A: chunk ch is in LDS
+    load(ch - 2, rn);
+    advance(rows_of(ch));
+    __syncthreads();  // B: every read of chunk ch is done
+    store(rx);
+    publish();
+  };
+  // nch - n_out is even, so both loops keep the two register stages in turn
+  int p = 0;
+  for (; p < nch - n_out; p += 2) {
+    carry_body(nch - 1 - p, ra, rb);
+    carry_body(nch - 2 - p, rb, ra);
+  }
+  for (; p < nch; p += 2) {  // a chunk before the first is all zeros
     body(nch - 1 - p, ra, rb);
     body(nch - 2 - p, rb, ra);
   }
@@ -703,15 +736,39 @@ __device__ __forceinline__ void wide_rev_role(
   }
 }
 
-// The reverse walk of the workgroup with id P in its walk's grid (see
-// bwd_dkdv_wide_kernel), on the LDS block `lds`.
+// The (item, head) unit of the workgroup with id P in its walk's grid;
+// false past the last unit.
+__device__ __forceinline__ bool wide_unit(const Plan &plan, int P, int H, int &h, int &idx,
+                                          Item &it) {
+  int unit, dtile;
+  xcd_unit_at(plan, P, 1, plan.max_items * H, unit, dtile);
+  if (unit >= plan.max_items * H) return false;
+  const int slot = unit / H;
+  h = unit - slot * H;
+  if (!slot_item(plan, slot, idx, it)) return false;
+  make_uniform(idx, it);
+  return true;
+}
+
+// Chunks at the end of item `it` whose dk and dv rows the dq walk's
+// workgroup forms once its own walk is done (see bwd_fused_wide_kernel):
+// the share tail_q16 / 65536 of the item's chunks, rounded down to an even
+// count and leaving at least one chunk to the reverse walk.
+__device__ __forceinline__ int wide_tail_chunks(const Item &it, int tail_q16) {
+  const int nch = (it.t1 - it.t0 + 63) / 64;
+  const int half = (int)(((long long)nch * tail_q16) >> 17);
+  return min(2 * half, (nch - 1) & ~1);
+}
+
+// The reverse walk of item `it`, head h, on the LDS block `lds`: dk and dv
+// rows of its first n_out chunks (the rest only carry the gradient back).
 template <int DKT, int DV>
-__device__ __forceinline__ void dkdv_wide_walk(
+__device__ __forceinline__ void rev_walk(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
-    float *__restrict__ ds0, const Plan &plan, const Decay &dec, float scale, int H, int pair,
-    int P, char *lds) {
+    float *__restrict__ ds0, const Item &it, int idx, int h, int H, const Decay &dec,
+    float scale, const float *pair_add, float pair_scale, int n_out, char *lds) {
   WIDE_CONSTS(DKT, DV);
   using LD = WideLds<DKT, DV>;
   bf16 *sQ = (bf16 *)lds;
@@ -721,19 +778,32 @@ __device__ __forceinline__ void dkdv_wide_walk(
   bf16 *sD = (bf16 *)(lds + 3 * LD::QT + LD::VT);
   bf16 *sCt = (bf16 *)(lds + 3 * LD::QT + 2 * LD::VT);
   float *sPow = (float *)(lds + 3 * LD::QT + 2 * LD::VT + LD::ST);
-
-  int unit, dtile;
-  xcd_unit_at(plan, P, 1, plan.max_items * H, unit, dtile);
-  if (unit >= plan.max_items * H) return;
-  const int slot = unit / H;
-  const int h = unit - slot * H;
-  int idx;
-  Item it;
-  if (!slot_item(plan, slot, idx, it)) return;
-  make_uniform(idx, it);
   const int tid = threadIdx.x;
   if (tid <= kWC) sPow[tid] = pow_f64(dec.lam[h], tid);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < 4)
+    wide_rev_role<DKT, DV, true>(q, k, v, dout, ds_final, cslots, dv_out, ds0, it, idx, h, H,
+                                 scale, tid & 255, wave, sQ, sQs, sK, sV, sD, sCt, sPow,
+                                 pair_add, pair_scale, n_out);
+  else
+    wide_rev_role<DKT, DV, false>(q, k, v, dout, ds_final, cslots, dk_out, ds0, it, idx, h, H,
+                                  scale, tid & 255, wave - 4, sQ, sQs, sK, sV, sD, sCt, sPow,
+                                  pair_add, pair_scale, n_out);
+}
+
+// The reverse walk of the workgroup with id P in its walk's grid (see
+// bwd_dkdv_wide_kernel), on the LDS block `lds`; the last
+// wide_tail_chunks(tail_q16) chunks of its item only carry the gradient.
+template <int DKT, int DV>
+__device__ __forceinline__ void dkdv_wide_walk(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
+    const float *__restrict__ cslots, bf16 *__restrict__ dv_out, bf16 *__restrict__ dk_out,
+    float *__restrict__ ds0, const Plan &plan, const Decay &dec, float scale, int H, int pair,
+    int tail_q16, int P, char *lds) {
+  int h, idx;
+  Item it;
+  if (!wide_unit(plan, P, H, h, idx, it)) return;
   const float *pair_add = nullptr;
   float pair_scale = 0.f;
   if (pair && !(it.flags & kLastSeg) && ds_final) {  // first of two segments
@@ -742,12 +812,9 @@ __device__ __forceinline__ void dkdv_wide_walk(
     pair_add = ds_final + ((long long)it.n * H + h) * DKT * DV;
     pair_scale = pow_f64(dec.lam[h], next.t1 - next.t0);
   }
-  if (wave < 4)
-    wide_rev_role<DKT, DV, true>(q, k, v, dout, ds_final, cslots, dv_out, ds0, it, idx, h, H, scale,
-                        tid & 255, wave, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
-  else
-    wide_rev_role<DKT, DV, false>(q, k, v, dout, ds_final, cslots, dk_out, ds0, it, idx, h, H, scale,
-                         tid & 255, wave - 4, sQ, sQs, sK, sV, sD, sCt, sPow, pair_add, pair_scale);
+  const int nch = (it.t1 - it.t0 + 63) / 64;
+  rev_walk<DKT, DV>(q, k, v, dout, ds_final, cslots, dv_out, dk_out, ds0, it, idx, h, H, dec,
+                    scale, pair_add, pair_scale, nch - wide_tail_chunks(it, tail_q16), lds);
 }
 
 template <int DKT, int DV>
@@ -758,7 +825,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
     float *__restrict__ ds0, Plan plan, Decay dec, float scale, int H, int pair) {
   __shared__ __attribute__((aligned(16))) char lds[WideLds<DKT, DV>::REV];
   dkdv_wide_walk<DKT, DV>(q, k, v, dout, ds_final, cslots, dv_out, dk_out, ds0, plan, dec, scale,
-                          H, pair, (int)blockIdx.x, lds);
+                          H, pair, 0, (int)blockIdx.x, lds);
 }
 
 // Both walks in one launch, for items that are whole sequences (no time
@@ -766,6 +833,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
 // rest the dq walk. The walks share nothing, so neither waits on the other,
 // and with one workgroup of either kind per CU the batch needs half the
 // (sequence, head) units a walk alone needs to fill the GPU.
+// A chunk costs the reverse walk more than the dq walk, so the work is
+// evened out: the reverse workgroup only carries the gradient back through
+// the last wide_tail_chunks(tail_q16) chunks of its sequence (no dk, dv),
+// and the dq workgroup first runs a reverse walk over just those chunks,
+// starting from dL/dS_final as the sequence's own walk does, then its dq
+// walk. Both form every carry with the same operations in the same order,
+// so the rows are those of a single walk, bit for bit, and neither
+// workgroup waits on the other; both start on the same last chunks of the
+// sequence, on the same XCD, so the q and dO rows the carry needs are
+// mostly fetched into that XCD's L2 once for the two.
 // (slots, cslots and pair are the separate kernels' arguments; a plan
 // without segments never reads them.)
 template <int DKT, int DV>
@@ -775,15 +852,30 @@ __global__ __launch_bounds__(512, 1) void bwd_fused_wide_kernel(
     const float *__restrict__ ds_final, const float *__restrict__ slots,
     const float *__restrict__ cslots, bf16 *__restrict__ dq, bf16 *__restrict__ dv_out,
     bf16 *__restrict__ dk_out, float *__restrict__ ds0, Plan plan, Decay dec, float scale,
-    int H, int pair, int n_rev) {
+    int H, int pair, int n_rev, int tail_q16) {
   __shared__ __attribute__((aligned(16))) char lds[WideLds<DKT, DV>::MAX];
   // n_rev is a multiple of 8, so both walks keep the id -> XCD dealing
-  if ((int)blockIdx.x < n_rev)
+  if ((int)blockIdx.x < n_rev) {
     dkdv_wide_walk<DKT, DV>(q, k, v, dout, ds_final, cslots, dv_out, dk_out, ds0, plan, dec,
-                            scale, H, pair, (int)blockIdx.x, lds);
-  else
-    dq_wide_walk<DKT, DV>(k, v, dout, s0, slots, dq, plan, dec, scale, H, pair,
-                          (int)blockIdx.x - n_rev, lds);
+                            scale, H, pair, tail_q16, (int)blockIdx.x, lds);
+    return;
+  }
+  const int P = (int)blockIdx.x - n_rev;
+  int h, idx;
+  Item it;
+  if (!wide_unit(plan, P, H, h, idx, it)) return;
+  const int tail = (it.flags & kLastSeg) ? wide_tail_chunks(it, tail_q16) : 0;
+  if (tail > 0) {
+    // the last `tail` chunks as an item of their own: its walk starts from
+    // dL/dS_final and leaves dL/dS0 to the sequence's reverse workgroup
+    Item t = it;
+    t.t0 = it.t0 + (((it.t1 - it.t0 + 63) / 64) - tail) * 64;
+    t.flags = kLastSeg;
+    rev_walk<DKT, DV>(q, k, v, dout, ds_final, cslots, dv_out, dk_out, nullptr, t, idx, h, H,
+                      dec, scale, nullptr, 0.f, tail, lds);
+    __syncthreads();  // every wave is done with the reverse walk's LDS
+  }
+  dq_wide_walk<DKT, DV>(k, v, dout, s0, slots, dq, plan, dec, scale, H, pair, P, lds);
 }
 
 bool bwd_wide_ok(int dk, int dv) { return wide_shape(dk, dv); }
@@ -806,24 +898,27 @@ static void launch_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int p
 }
 
 template <int DKT, int DV>
-static void launch_fused(const Plan &p, const BwdArgs &a, const Decay &dec, hipStream_t s) {
+static void launch_fused(const Plan &p, const BwdArgs &a, const Decay &dec, int tail_q16,
+                         hipStream_t s) {
   const unsigned g = xcd_grid(p.deal, (long long)p.max_items * a.H, 1);
   hipLaunchKernelGGL((bwd_fused_wide_kernel<DKT, DV>), dim3(2 * g), dim3(512), 0, s,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      (const bf16 *)a.dout, a.s0, a.ds_final, a.slots, a.cslots, (bf16 *)a.dq,
-                     (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H, 0, (int)g);
+                     (bf16 *)a.dv_out, (bf16 *)a.dk, a.ds0, p, dec, a.scale, a.H, 0, (int)g,
+                     tail_q16);
 }
 
 // pair: the segment slots hold unscanned local quantities and every sequence
 // has exactly two segments (the kernels join them on load). fused: no time
-// segments; both walks in one launch.
+// segments; both walks in one launch, the dq walk's workgroups taking the
+// dk and dv rows of the share tail_q16 / 65536 of each sequence's chunks.
 hipError_t launch_bwd_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
-                           bool fused, hipStream_t s) {
+                           bool fused, int tail_q16, hipStream_t s) {
   // the shapes wide_shape() admits
-#define GLA_WIDE(DK_, DV_)                                \
-  case DK_ * 1000 + DV_:                                  \
-    if (fused) launch_fused<DK_, DV_>(p, a, dec, s);      \
-    else launch_wide<DK_, DV_>(p, a, dec, pair, s);       \
+#define GLA_WIDE(DK_, DV_)                                     \
+  case DK_ * 1000 + DV_:                                       \
+    if (fused) launch_fused<DK_, DV_>(p, a, dec, tail_q16, s); \
+    else launch_wide<DK_, DV_>(p, a, dec, pair, s);            \
     break;
   switch (a.dk_dim * 1000 + a.dv) {
     GLA_WIDE(96, 192)

@@ -124,10 +124,12 @@ hipError_t launch_bicombine(const Plan &p, const float *s0, float *slots,
                             int dk, int dv, hipStream_t s);
 // matrix-core backward with one workgroup per (item, head) over all of dv
 // (gla_bwd_wide.hip), no partial sums. pair: two time segments per sequence
-// joined on load; fused: no time segments, both walks in one launch
+// joined on load; fused: no time segments, both walks in one launch, with
+// the dk and dv rows of the last tail_q16 / 65536 of every sequence's
+// chunks formed by its dq walk's workgroup
 bool bwd_wide_ok(int dk, int dv);
 hipError_t launch_bwd_wide(const Plan &p, const BwdArgs &a, const Decay &dec, int pair,
-                           bool fused, hipStream_t s);
+                           bool fused, int tail_q16, hipStream_t s);
 // vector-ALU backward (gla_bwd_valu.hip): dv tiles of valu_bwd_tile(dv)
 // columns, fp32 partial rows [dv tile][H][token][dk]
 int valu_bwd_tile(int dv);

@@ -36,6 +36,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base,
                                            0x00020000);
 }
 
+// Four bf16 (8 bytes) stored at byte offset `off` through a buffer
+// descriptor: the hardware drops a store whose offset lies past the
+// descriptor's range. Rows past an item's end are skipped this way rather
+// than by a branch around the stores, because the wait the compiler places
+// before a later use of loaded data counts the vector memory operations
+// issued in between, and a branch that may skip the stores makes it assume
+// none were, so it waits for loads issued after the ones it needs.
+__device__ __forceinline__ void buf_store8(bf16x4 t, __amdgpu_buffer_rsrc_t r, unsigned off) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, t), r, off, 0, 0);
+}
+
 // Four bf16 of one column from four consecutive rows: in each 16-lane group,
 // lane i receives element i % 4 of the 8-byte loads of lanes 4e + i / 4, so
 // when lane s of the group loads row kb + s / 4, columns nb + 4 (s % 4) .. +3,

@@ -8,7 +8,7 @@ import torch
 from chunked_gated_recurrent_amd import gla
 from chunked_gated_recurrent_amd import workloads as W
 from oracle import oracle as O
-from gla_testutil import TOL, dev, host, rel_err
+from gla_testutil import TOL, dev, env, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,27 @@ def test_backward_both_walks_in_one_launch(dv):
     x, do, dsf = _inputs(709 + dv, 8, 256, 16, dv)
     assert gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, 256, 16, 96, dv, 0) == 0
     _check("bwd one launch dv%d" % dv, _run(x, do, dsf), _oracle(x, do, dsf))
+
+
+@pytest.mark.parametrize("T,dv", [(1000, 192), (2048, 128), (300, 192), (64, 192)])
+def test_backward_tail_share_changes_no_bit(T, dv):
+    """In the one-launch backward the dq walk's workgroups form the dk and dv
+    rows of the last chunks of each sequence (GLA_BWD_TAIL: the share of
+    chunks moved, 0 to 0.5) while the reverse walk only carries the gradient
+    through them. Every carry is formed by the same operations in the same
+    order either way, so every output equals the one-walk result bit for bit;
+    and it matches the oracle."""
+    x, do, dsf = _inputs(716 + T + dv, 8, T, 16, dv)
+    assert gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, T, 16, 96, dv, 0) == 0
+    with env(GLA_BWD_TAIL="0"):
+        base = _run(x, do, dsf)
+    for share in ("0.25", "0.5"):
+        with env(GLA_BWD_TAIL=share):
+            got = _run(x, do, dsf)
+        for n, u, w in zip(("dq", "dk", "dv", "dS0"), base, got):
+            np.testing.assert_array_equal(u, w, err_msg="%s share %s" % (n, share))
+    if T <= 1000:
+        _check("bwd tail share T%d dv%d" % (T, dv), got, _oracle(x, do, dsf))
 
 
 def test_backward_max_heads_with_lambda_one():
@@ -231,6 +252,21 @@ def test_backward_varlen_matches_oracle(lengths, dv):
     for n, L in enumerate(lengths):
         if L == 0:
             np.testing.assert_array_equal(got[3][n], dsf[n].astype(np.float64))
+
+
+def test_backward_varlen_tail_share_changes_no_bit():
+    """The same over packed sequences of mixed lengths (empty, one token,
+    ragged, long) in the one-launch backward."""
+    x, do, dsf = _varlen_case(741, [300, 1, 0, 1000, 64, 129, 700, 5], H=16)
+    with env(GLA_BWD_TAIL="0"):
+        base = _run_varlen(x, do, dsf)
+    with env(GLA_BWD_TAIL="0.5"):
+        got = _run_varlen(x, do, dsf)
+    for n, u, w in zip(("dq", "dk", "dv", "dS0"), base, got):
+        np.testing.assert_array_equal(u, w, err_msg=n)
+    ref = O.gla_bwd_varlen(x["cu_seqlens"], x["q"], x["k"], x["v"], x["decay"], do, 1.0,
+                           x["s0"], dsf)
+    _check("bwd varlen tail share", got, ref)
 
 
 def test_backward_varlen_equals_fixed_batch():
