@@ -151,6 +151,17 @@ __host__ __device__ __forceinline__ void xcd_unit_at(const Plan &p, int P, int n
   }
 }
 
+// The chained scan's workgroups run item-major: id = item * U + u with U =
+// H * ndt (a multiple of 8). Within an item, XCD x (= u mod 8) takes the
+// x-th eighth of the (head, d_v tile) units in head-major order, so a
+// head's d_v tiles (H a multiple of 8 makes U / 8 a multiple of ndt) and
+// neighbouring heads share one L2.
+__host__ __device__ __forceinline__ void chain_unit(int u, int U, int ndt, int &h, int &dtile) {
+  const int su = (u & 7) * (U >> 3) + (u >> 3);
+  h = su / ndt;
+  dtile = su - h * ndt;
+}
+
 __device__ __forceinline__ void xcd_unit(const Plan &p, int ndt, int units,
                                          int &unit, int &dtile) {
   xcd_unit_at(p, (int)blockIdx.x, ndt, units, unit, dtile);

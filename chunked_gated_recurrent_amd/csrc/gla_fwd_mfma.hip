@@ -297,6 +297,279 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
                                nullptr, sKs, sV, nullptr, nullptr, sPow, np);
 }
 
+// ---------------------------------------------------------------------------
+// Long sequences in one launch: the chained scan
+// ---------------------------------------------------------------------------
+// The segmented forward as one pass over the segments (Laplace 3B /
+// Trainium2 page, "Challenge 1": only the state chain between chunks is
+// sequential; states compose as affine maps, [RecFree] section 3.2). The
+// workgroup of (item i, head, d_v tile):
+//   1. unless i is its sequence's last item: forms the item's local end
+//      state U_i (waves 0-3 over the first half of its chunks, waves 4-7 over
+//      the rest; U_i = lambda^(len of the rest) U_first + U_rest), writes it
+//      to its slot and raises its flag to 1;
+//   2. forms its incoming state S_in(i): s0 for a sequence's first item,
+//      else by looking back over the items before it, nearest first: an
+//      item whose flag is 2 has published S after it (its inclusive state)
+//      and ends the look-back; an item at flag 1 contributes its U and the
+//      look-back goes on (past the first item, s0 ends it):
+//      S_in(i) = sum over the terms of lambda^(t0_i - end of term) x term.
+//      Unless i is last, it then publishes its own inclusive state
+//      lambda^(len i) S_in(i) + U_i and raises its flag to 2;
+//   3. runs the output walk from S_in(i), as fwd_out_kernel.
+// Workgroup ids run item-major, and a workgroup only waits on items before
+// its own in the same sequence, i.e. on smaller ids; the dispatcher hands
+// out each XCD's workgroups in id order and step 1 never waits, so every
+// awaited flag is raised whether or not the grid fits the GPU at once. Each
+// wait is still bounded (about a second of wall clock); a workgroup that
+// gives up fills its S_in with NaN, so the failure shows in every output of
+// its item instead of passing silently.
+// Within an item's id block the units are dealt to the XCDs by chain_unit.
+// It is the library's second scheme for long sequences, selected with
+// GLA_FWD_CHAIN=1; the three launches stay the default because they measured
+// faster (one 65,536-token sequence, 16 heads: 369 against 493 us per call).
+// Timestamps taken inside a copy of this kernel put the difference in three
+// places: the local states end at 127-168 us against 123 us for the state
+// pass (two half-walks per workgroup, and the last items' workgroups idle);
+// the look-back costs 20-70 us, one memory round trip per term while every
+// other workgroup streams; and the output walks then start up to 80 us
+// apart, so the d_v tiles of a head no longer read their q and k rows
+// together (270-300 us against 242 us for the output pass).
+// Workspace (each [max_items][H][dk][dv] fp32 but the flags): slots (U_i),
+// incl (inclusive states), sin (S_in(i) at sin[i-1], the layout the output
+// walk reads; sin[i] is the second half-walk's scratch until item i+1
+// writes it) and flags [max_items][H][d_v tiles], zeroed before the launch.
+constexpr int kChainMaxItems = 256;  // items of one sequence (look-back table)
+
+template <int DVT, int DKT, bool GATE>
+__global__ __launch_bounds__(512, 1) void fwd_chain_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    bf16 *__restrict__ o, const float *__restrict__ s0, float *__restrict__ s_final,
+    float *__restrict__ slots, float *__restrict__ incl, float *__restrict__ sin,
+    int *__restrict__ flags, Plan plan, Decay dec, float scale, int H, int dv,
+    int final_in_slot, const bf16 *__restrict__ gt, int gate) {
+  using M = MfCfg<DVT, DKT>;
+  // d_k 128 keeps the three-launch path: its output walk scales k in
+  // registers to fit the LDS, which leaves no room for the second half-walk
+  static_assert(DKT != 128, "the chained scan takes d_k 64 and 96");
+  static_assert(M::VS <= M::QS, "the second half-walk keeps its v tiles in sK");
+  constexpr bool KSR = false;
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sK[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sKs[2 * M::C * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2 * M::C * M::VS];
+  __shared__ __attribute__((aligned(16))) bf16 sSt0[M::SROWS * M::QS];
+  __shared__ __attribute__((aligned(16))) bf16 sSt1[M::SROWS * M::QS];
+  __shared__ float sPow[M::C + 4];
+  // look-back terms: j >= 0 is U_j, -1 - j the inclusive state of item j,
+  // kS0Term the sequence's s0; sA their decays
+  constexpr int kS0Term = -0x40000000;
+  __shared__ int sTerm[kChainMaxItems + 1];
+  __shared__ float sA[kChainMaxItems + 1];
+  __shared__ int sN, sFail;
+
+  const int ndt = dv / DVT;
+  const int U = H * ndt;  // workgroups per item (H is a multiple of 8)
+  const int idx = (int)blockIdx.x / U;
+  int h, dtile;
+  chain_unit((int)blockIdx.x - idx * U, U, ndt, h, dtile);
+  const int su = h * ndt + dtile;  // this unit's flag within the item
+  Item it;
+  if (!load_item(plan, idx, it)) return;
+  int idx_u = idx;
+  make_uniform(idx_u, it);
+  const int tid = threadIdx.x;
+  if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
+  const int role_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = dtile * DVT;
+  const long long item_stride = (long long)H * DKT * dv;
+  const long long tile_off = (long long)h * DKT * dv + c0;  // this tile within a slot
+  constexpr int NE = DKT * DVT;  // state elements of the tile
+  int *flag = flags + (long long)idx * U + su;
+  const bool last = (it.flags & kLastSeg) != 0, first = (it.flags & kFirstSeg) != 0;
+
+  // 1. local end state
+  if (!last) {
+    const int nch = (it.t1 - it.t0 + M::C - 1) / M::C;
+    const int nA = (nch + 1) >> 1;
+    const int niter = (nA + 1) & ~1;  // both halves pass the same barriers
+    const int tm = min(it.t0 + nA * M::C, it.t1);
+    Item part = it;
+    if (role_wave < 4) {
+      part.t1 = tm;
+      state_role<DVT, false, false, DKT, KSR, true>(k, v, nullptr, nullptr, slots, part, idx,
+                                                    h, H, dv, c0, 0, tid, role_wave, nullptr,
+                                                    sKs, sV, nullptr, nullptr, sPow,
+                                                    NormPtrs{}, niter);
+    } else {
+      part.t0 = tm;
+      state_role<DVT, false, false, DKT, KSR, true>(k, v, nullptr, nullptr, sin, part, idx,
+                                                    h, H, dv, c0, 0, tid & 255,
+                                                    role_wave - 4, nullptr, sQ, sK, nullptr,
+                                                    nullptr, sPow, NormPtrs{}, niter);
+    }
+    __syncthreads();  // both half states are written
+    const float aB = pow_f64(dec.lam[h], it.t1 - tm);
+    float *ua = slots + (long long)idx * item_stride + tile_off;
+    const float *ub = sin + (long long)idx * item_stride + tile_off;
+    for (int e = tid; e < NE; e += 512) {
+      const long long off = (long long)(e / DVT) * dv + (e % DVT);
+      ua[off] = fmaf(aB, ua[off], ub[off]);
+    }
+    // every thread's stores reach the device-coherent level before the flag
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 2. incoming state; inclusive state published
+  if (tid == 0) {
+    int n = 0, fail = 0;
+    if (first) {
+      sTerm[n] = kS0Term;
+      sA[n++] = 1.0f;
+    } else {
+      int seq_first, seq_last;
+      seq_items(plan, it.n, seq_first, seq_last);
+      const unsigned long long t_start = wall_clock64();
+      const unsigned long long limit = 100000000ull;  // 1 s of the 100 MHz wall clock
+      for (int j = idx - 1;; --j) {
+        if (j < seq_first || n == kChainMaxItems) {  // (the host keeps n below the cap)
+          Item f0 = {0, it.t0, it.t0, 0};
+          load_item(plan, seq_first, f0);
+          sTerm[n] = kS0Term;
+          sA[n++] = pow_f64(dec.lam[h], it.t0 - f0.t0);
+          break;
+        }
+        const int *fj = flags + (long long)j * U + su;
+        int fv;
+        while ((fv = __hip_atomic_load(fj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+          if ((unsigned long long)wall_clock64() - t_start > limit) {
+            fail = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (fail) break;
+        Item pj = {0, it.t0, it.t0, 0};
+        load_item(plan, j, pj);
+        sA[n] = pow_f64(dec.lam[h], it.t0 - pj.t1);
+        if (fv == 2) {
+          sTerm[n++] = -1 - j;
+          break;
+        }
+        sTerm[n++] = j;
+      }
+    }
+    sN = n;
+    sFail = fail;
+  }
+  __syncthreads();  // look-back done (or given up)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  {
+    // the tile as float4s, a fixed set per thread, so every load of a term
+    // is in flight at once (d_v tiles are multiples of 4 columns)
+    constexpr int NV = NE / 4, PER = (NV + 511) / 512;
+    static_assert(DVT % 4 == 0, "float4 rows");
+    long long off4[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e4 = min(tid + 512 * m, NV - 1);  // a thread past the end repeats the last
+      off4[m] = tile_off + (long long)(e4 / (DVT / 4)) * dv + 4 * (e4 % (DVT / 4));
+    }
+    const bool mine_last = tid + 512 * (PER - 1) < NV;  // its last float4 is its own
+    const int nt = sN;
+    const bool fail = sFail != 0;
+    float4 S[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) S[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t = 0; t < nt; ++t) {
+      const int tm = sTerm[t];
+      const float a = sA[t];
+      const float *src = tm == kS0Term ? (s0 ? s0 + (long long)it.n * item_stride : nullptr)
+                         : tm < 0     ? incl + (long long)(-1 - tm) * item_stride
+                                      : slots + (long long)tm * item_stride;
+      if (!src) continue;  // no s0: zeros
+      float4 x[PER];
+#pragma unroll
+      for (int m = 0; m < PER; ++m) x[m] = *reinterpret_cast<const float4 *>(src + off4[m]);
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        S[m].x = fmaf(a, x[m].x, S[m].x);
+        S[m].y = fmaf(a, x[m].y, S[m].y);
+        S[m].z = fmaf(a, x[m].z, S[m].z);
+        S[m].w = fmaf(a, x[m].w, S[m].w);
+      }
+    }
+    if (fail) {
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int m = 0; m < PER; ++m) S[m] = make_float4(nan, nan, nan, nan);
+    }
+    const float aI = pow_f64(dec.lam[h], it.t1 - it.t0);
+    float4 Ui[PER];
+    if (!last) {
+      const float *ui = slots + (long long)idx * item_stride;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) Ui[m] = *reinterpret_cast<const float4 *>(ui + off4[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      if (m == PER - 1 && !mine_last) break;
+      if (!first)
+        *reinterpret_cast<float4 *>(sin + (long long)(idx - 1) * item_stride + off4[m]) = S[m];
+      if (!last) {
+        float4 y;
+        y.x = fmaf(aI, S[m].x, Ui[m].x);
+        y.y = fmaf(aI, S[m].y, Ui[m].y);
+        y.z = fmaf(aI, S[m].z, Ui[m].z);
+        y.w = fmaf(aI, S[m].w, Ui[m].w);
+        *reinterpret_cast<float4 *>(incl + (long long)idx * item_stride + off4[m]) = y;
+      }
+    }
+    if (!last) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();  // S_in(i) is written for the output walk's state waves
+    if (!last && tid == 0)
+      __hip_atomic_store(flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 3. output walk (a sequence's first item reads s0 itself)
+  if (role_wave < 4)
+    output_role<DVT, false, DKT, GATE>(q, o, gt, gate, it, h, H, dv, c0, scale, tid & 255,
+                                       role_wave, sQ, sK, sV, sSt0, sSt1, sPow);
+  else
+    state_role<DVT, true, false, DKT, KSR>(k, v, s0, s_final, sin, it, idx, h, H, dv, c0,
+                                           final_in_slot, tid & 255, role_wave - 4, sK, sKs,
+                                           sV, sSt0, sSt1, sPow);
+}
+
+template <int DVT, int DKT>
+static void launch_chain_dvt(const Plan &p, const FwdArgs &a, const Decay &dec, float *incl,
+                             float *sin, int *flags, hipStream_t s) {
+  const unsigned grid = (unsigned)((long long)p.max_items * a.H * (a.dv / DVT));
+  if (a.gate != kGateNone)
+    hipLaunchKernelGGL((fwd_chain_kernel<DVT, DKT, true>), dim3(grid), dim3(512), 0, s,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o,
+                       a.s0, a.s_final, a.slots, incl, sin, flags, p, dec, a.scale, a.H, a.dv,
+                       a.final_in_slot, (const bf16 *)a.g, a.gate);
+  else
+    hipLaunchKernelGGL((fwd_chain_kernel<DVT, DKT, false>), dim3(grid), dim3(512), 0, s,
+                       (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, (bf16 *)a.o,
+                       a.s0, a.s_final, a.slots, incl, sin, flags, p, dec, a.scale, a.H, a.dv,
+                       a.final_in_slot, (const bf16 *)nullptr, kGateNone);
+}
+
+bool fwd_chain_ok(int dk, int H, int items_per_seq) {
+  return (dk == 64 || dk == 96) && H % 8 == 0 && items_per_seq <= kChainMaxItems;
+}
+
+void launch_fwd_chain(int dvt, const Plan &p, const FwdArgs &a, const Decay &dec, float *incl,
+                      float *sin, int *flags, hipStream_t s) {
+  if (a.dk == 64) launch_chain_dvt<64, 64>(p, a, dec, incl, sin, flags, s);
+  else if (dvt == 96) launch_chain_dvt<96, 96>(p, a, dec, incl, sin, flags, s);
+  else launch_chain_dvt<64, 96>(p, a, dec, incl, sin, flags, s);
+}
+
 template <int DVT, bool NORM, int DKT>
 static void launch_dvt(bool state_only, const Plan &p, const FwdArgs &a,
                        const Decay &dec, hipStream_t s) {

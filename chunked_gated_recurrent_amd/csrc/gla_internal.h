@@ -139,6 +139,14 @@ void launch_fwd_mfma(bool state_only, int dvt, const Plan &p, const FwdArgs &a,
                      const Decay &dec, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const FwdArgs &a, const Decay &dec,
                           hipStream_t s);
+// Segmented bf16 forward (matrix cores, no normaliser) in one launch, the
+// chained scan (gla_fwd_mfma.hip): a.slots, incl and sin each
+// [max_items][H][dk][dv] fp32 (local, inclusive and incoming states), flags
+// [max_items][H][dv / dvt] ints, zeroed before the launch.
+bool fwd_chain_ok(int dk, int H, int items_per_seq);
+void launch_fwd_chain(int dvt, const Plan &p, const FwdArgs &a, const Decay &dec, float *incl,
+                      float *sin, int *flags, hipStream_t s);
+hipError_t launch_zero_i32(int32_t *p, long long n, hipStream_t s);
 hipError_t launch_final_gather(const Plan &p, const FwdArgs &a, hipStream_t s);
 hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
                              const float *s0, float *s_final, hipStream_t s);

@@ -697,6 +697,19 @@ hipError_t launch_final_gather(const Plan &p, const FwdArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Zeroes n ints (the chained scan's flags): a kernel, not a memset, so that
+// a captured graph replays it like any other node.
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *__restrict__ p, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t *p, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_fill(int n_states, int H, int dk, int dv,
                              const float *s0, float *s_final, hipStream_t s) {
   const long long n4 = (long long)n_states * H * dk * dv / 4;

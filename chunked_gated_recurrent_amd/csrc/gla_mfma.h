@@ -133,6 +133,8 @@ __device__ __forceinline__ int chunk_rows(const Item &it, int ch) {
 //          the Ks^T tile with a B operand of ones (every column of the
 //          result holds z); z is published in row DVT of the state buffer.
 //          Every dv tile's workgroup computes z; the one at c0 = 0 stores it.
+//   niter: (state-only pass) run at least this many chunk steps (the
+//          barriers of a walk are 1 + its steps rounded up to even).
 //   REV:   (state-only pass) the chunks are taken last to first. The local
 //          end state is a plain weighted sum, sum_t lambda^(t1-1-t) k_t^T v_t,
 //          so each chunk's decay-scaled k carries the decay of the rows after
@@ -147,7 +149,7 @@ __device__ __forceinline__ void state_role(
     const float *__restrict__ s0, float *__restrict__ s_final,
     float *__restrict__ slots, const Item &it, int idx, int h, int H, int dv,
     int c0, int final_in_slot, int rt, int w, bf16 *sK, bf16 *sKs, bf16 *sV,
-    bf16 *sSt0, bf16 *sSt1, const float *sPow, NormPtrs np = NormPtrs{}) {
+    bf16 *sSt0, bf16 *sSt1, const float *sPow, NormPtrs np = NormPtrs{}, int niter = 0) {
   // sK (FUSED only), sKs and sV hold two chunk buffers each. KSR: no
   // decay-scaled copy of k in LDS (it frees a third q/k-sized tile); the
   // raw k tile (sK when FUSED, else sKs) is scaled as its fragments are
@@ -362,8 +364,11 @@ __device__ __forceinline__ void state_role(
     if (FUSED) publish(st_pub);  // S_ch for the next chunk's readout
     pc_cur = pc_next;
   };
-  // a chunk past the end (REV: before the start) is all zeros
-  for (int p = 0; p < nch; p += 2) {
+  // a chunk past the end (REV: before the start) is all zeros and leaves
+  // the state as it is, so a walk may run longer than the item (niter:
+  // two groups of waves that must pass the same barriers)
+  const int nit = niter > nch ? niter : nch;
+  for (int p = 0; p < nit; p += 2) {
     body(ch_first + STEP * p, ka, va, kb, vb, sSt0);
     body(ch_first + STEP * (p + 1), kb, vb, ka, va, sSt1);
   }

@@ -18,6 +18,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <array>
 #include <string>
 #include <vector>
 
@@ -188,6 +189,35 @@ void check_forward(const HostPlan &hp, const std::vector<int32_t> &cu, int H, in
   if (!hp.segmented && !hp.ordered) EXPECT(hp.ws_bytes == 0);
 }
 
+// The chained scan's workspace (local, inclusive and incoming states, then
+// the flags, each 256-byte aligned, no overlap, nothing past the query's
+// size) and its workgroup -> (head, d_v tile) dealing: a bijection within
+// each item whose XCD (id mod 8) is the same for every d_v tile of a head.
+void check_chain(const HostPlan &hp, int H, int dk, int dv) {
+  const Plan &p = hp.p;
+  EXPECT(hp.segmented && hp.fast && p.mode == kPlanFixed);
+  EXPECT(fwd_chain_ok(dk, H, p.G));
+  const size_t slot_bytes = (size_t)p.max_items * H * dk * dv * sizeof(float);
+  EXPECT(hp.off_slots == 0 && hp.off_incl % 256 == 0 && hp.off_sin % 256 == 0 &&
+         hp.off_flags % 256 == 0);
+  EXPECT(hp.off_incl >= slot_bytes && hp.off_sin >= hp.off_incl + slot_bytes &&
+         hp.off_flags >= hp.off_sin + slot_bytes);
+  EXPECT(hp.off_flags + (size_t)p.max_items * H * hp.ndt * sizeof(int32_t) == hp.ws_bytes);
+  const int U = H * hp.ndt;
+  EXPECT(U % 8 == 0);
+  std::vector<int> seen((size_t)U, 0), xcd_of_head((size_t)H, -1);
+  for (int u = 0; u < U; ++u) {
+    int h = -1, dt = -1;
+    chain_unit(u, U, hp.ndt, h, dt);
+    EXPECT(h >= 0 && h < H && dt >= 0 && dt < hp.ndt);
+    if (h < 0 || h >= H || dt < 0 || dt >= hp.ndt) continue;
+    ++seen[(size_t)h * hp.ndt + dt];
+    if (xcd_of_head[h] < 0) xcd_of_head[h] = u & 7;
+    EXPECT(xcd_of_head[h] == (u & 7));
+  }
+  for (int c : seen) EXPECT(c == 1);
+}
+
 void check_backward(const BwdPlan &bp, const std::vector<int32_t> &cu, int H, int dk, int dv,
                     long long total_T) {
   const HostPlan &hp = bp.hp;
@@ -216,8 +246,13 @@ void fixed_case(int dt, int B, int T, int H, int dk, int dv, int chunk, long lon
   where = b;
   std::vector<int> lens((size_t)B, T);
   const std::vector<int32_t> cu = cu_of(lens);
-  const HostPlan hp = plan_fixed(dt, B, T, H, dk, dv, chunk);
+  const HostPlan hp = plan_fwd_fixed(dt, B, T, H, dk, dv, chunk);
   if (T > 0) check_forward(hp, cu, H, dk, dv, false);
+  if (hp.chain) check_chain(hp, H, dk, dv);
+  // the chained scan (when selected) takes every segmented bf16 matrix-core
+  // plan it can
+  EXPECT(hp.chain == (fwd_chain_enabled() && hp.fast && hp.segmented &&
+                      fwd_chain_ok(dk, H, hp.p.G)));
   EXPECT(hp.ws_bytes == gla_chunk_fwd_workspace_bytes((gla_dtype)dt, B, T, H, dk, dv, chunk));
   const HostPlan hz = plan_linear_attn(dt, B, T, H, dk, dv, chunk);
   if (T > 0) check_forward(hz, cu, H, dk, dv, true);
@@ -276,6 +311,17 @@ int main(int argc, char **argv) {
     fixed_case(BF, 8, 2048, 16, 96, 192, 64, tg);   // Laplace-shaped prefill
     fixed_case(BF, 1, 65536, 16, 96, 192, 64, tg);  // long context
     fixed_case(F32, 1, 256, 2, 16, 32, 32, tg);     // tiny check
+    // the chained scan's plans (heads a multiple of 8), up to and past its
+    // 256 segments per sequence, with and without it selected
+    for (const char *chain : {"1", "0"}) {
+      setenv("GLA_FWD_CHAIN", chain, 1);
+      for (int H : {8, 16, 24})
+        for (int T : {1000, 4097, 25600, 38400, 65536})
+          for (const auto &sh : {std::array<int, 2>{96, 192}, std::array<int, 2>{96, 64},
+                                 std::array<int, 2>{64, 128}})
+            fixed_case(BF, 1 + (T < 5000), T, H, sh[0], sh[1], 0, tg);
+    }
+    unsetenv("GLA_FWD_CHAIN");
     for (const auto &sh : shapes)
       for (int T : {1, 63, 64, 65, 129, 1000, 4097})
         for (int chunk : {0, 32}) fixed_case(sh[0], 2, T, 3, sh[1], sh[2], chunk, tg);

@@ -120,10 +120,36 @@ def test_fwd_argument_errors(L):
     assert fwd(L, sf=A[3]) == ALIAS
 
 
+class env:
+    """Temporarily set environment variables (the library reads its tuning
+    knobs at every call)."""
+
+    def __init__(self, **kv):
+        self.kv, self.old = kv, {}
+
+    def __enter__(self):
+        for k, v in self.kv.items():
+            self.old[k] = os.environ.get(k)
+            os.environ[k] = v
+
+    def __exit__(self, *a):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 def test_fwd_workspace_contract(L):
-    # one long sequence must be split into segments and needs scratch
+    # one long sequence must be split into segments (8 at 16 heads) and needs
+    # scratch: the segments' local states for the three launches; with the
+    # chained scan (GLA_FWD_CHAIN=1) also the inclusive and incoming states
+    # and a flag per (segment, head, d_v tile)
     need = L.gla_chunk_fwd_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 0)
-    assert need > 0 and need % (16 * 96 * 192 * 4) == 0
+    assert need == 8 * 16 * 96 * 192 * 4
+    with env(GLA_FWD_CHAIN="1"):
+        assert L.gla_chunk_fwd_workspace_bytes(BF16, 1, 65536, 16, 96, 192, 0) == \
+            3 * 8 * 16 * 96 * 192 * 4 + 8 * 16 * 2 * 4
     dec = np.full(16, 0.9, np.float32)
     assert fwd(L, B=1, T=65536, H=16, decay=dec) == WS
     assert fwd(L, B=1, T=65536, H=16, decay=dec, ws=A[5], wsb=need - 1) == WS

@@ -1,0 +1,136 @@
+"""GPU parity of the chained scan (GLA_FWD_CHAIN=1): a fixed batch with time
+segments (bf16, d_k 64 or 96, heads a multiple of 8) runs local states, the
+look-back combine and the output walks in one launch (fwd_chain_kernel)
+instead of three (the default, which measured faster). Compared with the
+fp64 oracle (bar 1e-2 of max|oracle|, outputs and final states) and with the
+three-launch path, which composes the same states in another order."""
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_recurrent_amd import gla
+from chunked_gated_recurrent_amd import workloads as W
+from gla_testutil import TOL, dev, env, host, oracle_fixed, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gla.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(x, in_place=False, g=None, act=None, scale=1.0, chain=True):
+    with env(GLA_FWD_CHAIN="1" if chain else "0"):
+        return _run_env(x, in_place, g, act, scale)
+
+
+def _run_env(x, in_place, g, act, scale):
+    q, k, v, s0 = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["s0"])
+    kw = dict(initial_state=s0, scale=scale)
+    if in_place:
+        kw["final_state"] = s0
+    if g is None:
+        o, sf = gla.gla_chunk_fwd(q, k, v, x["decay"], **kw)
+    else:
+        o, sf = gla.gla_chunk_fwd_gated(q, k, v, dev(g), x["decay"], act, **kw)
+    torch.cuda.synchronize()
+    return host(o), host(sf)
+
+
+def _check(name, got, ref, tol=TOL["bf16"]):
+    eo, es = rel_err(got[0], ref[0]), rel_err(got[1], ref[1])
+    print("%s: o err %.3e  S err %.3e" % (name, eo, es))
+    assert np.isfinite(got[0]).all() and np.isfinite(got[1]).all(), name
+    assert eo <= tol and es <= tol, (name, eo, es)
+
+
+def _chain_ws(B, T, H, dk, dv):
+    """Workspace bytes of the chained scan: three state arrays and the flags."""
+    with env(GLA_FWD_CHAIN="1"):
+        return gla.lib().gla_chunk_fwd_workspace_bytes(1, B, T, H, dk, dv, 0)
+
+
+# (B, T, H, dk, dv): ragged lengths, both d_v tile widths at d_k 96, d_k 64
+CASES = [(2, 1000, 8, 96, 192), (1, 700, 8, 96, 64), (1, 900, 8, 64, 128),
+         (3, 1300, 16, 96, 128)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
+def test_chain_matches_oracle_and_three_launches(case):
+    B, T, H, dk, dv = case
+    x = W.prefill_inputs(900 + T + dk, B, T, H, dk, dv, "bf16", 0.1, W.geometric_decays(H))
+    ref = oracle_fixed(x)
+    with env(GLA_TARGET_WGS=100000):  # as many segments as the length allows
+        three = _run(x, chain=False)
+        plain_ws = gla.lib().gla_chunk_fwd_workspace_bytes(1, B, T, H, dk, dv, 0)
+        got = _run(x)
+        assert _chain_ws(B, T, H, dk, dv) > 2 * plain_ws > 0  # the chain ran
+    _check("chain %s" % (case,), got, ref)
+    _check("three launches %s" % (case,), three, ref)
+    # the same states composed in another order (and k scaled by other
+    # decay factors before its bf16 rounding in the state half-walks): the
+    # two differ by about one bf16 step of the largest outputs, inside the bar
+    assert rel_err(got[0], three[0]) <= TOL["bf16"] and rel_err(got[1], three[1]) <= TOL["bf16"]
+
+
+def test_chain_in_place_final_state():
+    x = W.prefill_inputs(911, 2, 1000, 8, 96, 192, "bf16", 0.1, W.geometric_decays(8))
+    ref = oracle_fixed(x)
+    with env(GLA_TARGET_WGS=100000):
+        _check("chain in place", _run(x, in_place=True), ref)
+
+
+def test_chain_without_initial_state_and_scaled():
+    from oracle import oracle as O
+    x = W.prefill_inputs(912, 1, 1500, 8, 96, 192, "bf16", None, W.geometric_decays(8))
+    ref = O.gla_fwd(x["q"], x["k"], x["v"], x["decay"], 0.37, None)
+    with env(GLA_TARGET_WGS=100000):
+        _check("chain no s0, scale 0.37", _run(x, scale=0.37), ref)
+
+
+@pytest.mark.parametrize("act", ["sigmoid", "silu"])
+def test_chain_gated(act):
+    from oracle import oracle as O
+    x = W.prefill_inputs(913, 2, 800, 8, 96, 192, "bf16", 0.1, W.geometric_decays(8))
+    g = W.bf16_bits(np.random.default_rng(914).standard_normal((2, 800, 8, 192),
+                                                             dtype=np.float32) * np.float32(2))
+    ro, rs = O.gla_fwd_gated(x["q"], x["k"], x["v"], g, x["decay"], act, 1.0, x["s0"])
+    with env(GLA_TARGET_WGS=100000):
+        _check("chain gated %s" % act, _run(x, g=g, act=act), (ro, rs))
+
+
+def test_chain_many_segments_and_the_cap():
+    """A sequence cut into 200 segments (every workgroup looks back over a
+    long chain) runs the chained scan; past 256 segments a sequence takes the
+    three launches."""
+    for T, chained in ((64 * 2 * 200, True), (64 * 2 * 300, False)):
+        x = W.prefill_inputs(915, 1, T, 8, 96, 192, "bf16", 0.1, W.geometric_decays(8))
+        ref = oracle_fixed(x, heads=[0, 7])
+        with env(GLA_TARGET_WGS=100000):
+            need = _chain_ws(1, T, 8, 96, 192)
+            plain = gla.lib().gla_chunk_fwd_workspace_bytes(1, 1, T, 8, 96, 192, 0)
+            assert (need > 2 * plain) == chained, (T, need, plain)
+            o, s = _run(x)
+        _check("T %d" % T, (o[:, :, [0, 7]], s[:, [0, 7]]), ref)
+
+
+def test_chain_long_context_workload_full():
+    """B1 T65536 H16 (8 segments of 8,192 tokens): every head, against the
+    oracle, through the chained scan."""
+    x = W.spec_inputs("long_context")
+    assert _chain_ws(1, 65536, 16, 96, 192) == 3 * 8 * 16 * 96 * 192 * 4 + 8 * 16 * 2 * 4
+    got = _run(x)
+    _check("long context chain", got, oracle_fixed(x))
+
+
+def test_chain_is_bitwise_deterministic():
+    x = W.prefill_inputs(916, 2, 1000, 8, 96, 192, "bf16", 0.1, W.geometric_decays(8))
+    with env(GLA_TARGET_WGS=100000):
+        a = _run(x)
+        b = _run(x)
+    for u, w in zip(a, b):
+        np.testing.assert_array_equal(u, w)
