@@ -271,12 +271,18 @@ def bench_backward(steps, warmup, workload="laplace_prefill"):
     tokens = B * T
     bytes_call = tokens * BACKWARD_BYTES_PER_TOKEN + 2 * B * STATE_BYTES
     name = "laplace_backward" if workload == "laplace_prefill" else workload + "_backward"
+    # no scratch: whole sequences, both walks in one launch; else time segments
+    if need == 0:
+        key = label = "bwd_fused_wide_kernel"
+        label += " (dq walk and reverse walk in one launch)"
+    else:
+        key = "whole call"
+        label = "whole call (segment boundaries + scans + dq pass + dk/dv pass)"
     return {"workload": name, "config": {"B": B, "T": T, "chunk": 64},
             "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
             "ms_per_call": round(wall / steps * 1e3, 4),
-            "roofline": dict(roofline(bytes_call, ev_ms),
-                             kernel="whole call (segment boundaries + scans + dq pass + dk/dv pass)",
-                             traffic=measured_traffic("whole call@" + name)),
+            "roofline": dict(roofline(bytes_call, ev_ms), kernel=label,
+                             traffic=measured_traffic(key + "@" + name)),
             "workspace_bytes": need}
 
 

@@ -88,10 +88,10 @@ int target_workgroups() {
 }
 
 // Share of every sequence's chunks (in 1/65536) whose dk and dv rows the
-// fused backward gives to the dq walk's workgroup: a chunk of the reverse
-// walk costs about 1.7 times one of the dq walk, so a quarter of the reverse
-// work moves over to even out the two. GLA_BWD_TAIL (a fraction in [0, 0.5])
-// overrides it.
+// fused backward gives to the dq walk's workgroup when both walks fit one
+// round of the CUs: a chunk of the reverse walk costs about 1.45 times one
+// of the dq walk, so a quarter of the reverse work moves over to even out
+// the two. GLA_BWD_TAIL (a fraction in [0, 0.5]) overrides it.
 int bwd_tail_q16() {
   const char *e = getenv("GLA_BWD_TAIL");
   if (e && *e) {
@@ -466,10 +466,16 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     }
   }
   hipError_t e;
-  if (bp.wide)
-    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, !hp.segmented, bwd_tail_q16(), s);
-  else
+  if (bp.wide) {
+    // the tail share evens out the two walks when all their workgroups run
+    // side by side; past one round of the CUs it only adds the carry-only
+    // chunks (B32 T2048 H16: 742 us with it, 699 us without)
+    const bool one_round = 2LL * p.max_items * a.H <= target_workgroups();
+    e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, !hp.segmented,
+                        one_round ? bwd_tail_q16() : 0, s);
+  } else {
     e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
+  }
   if (e != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
