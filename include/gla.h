@@ -43,10 +43,20 @@
  *     enqueued on it as kernel launches; no call synchronises, allocates or
  *     records a memset, so a sequence of calls may be captured into a HIP
  *     graph and replayed (the decay values and sizes are fixed at capture).
- *   - Environment: GLA_TARGET_WGS (default 256, one per compute unit) is the
- *     number of workgroups below which a call splits its sequences into time
+ *   - Environment, read at every call (a workspace query and the call it
+ *     sizes must see the same values):
+ *     GLA_TARGET_WGS (default 256, one per compute unit) is the number of
+ *     workgroups below which a call splits its sequences into time
  *     segments; it changes the workspace size, never the results beyond
- *     rounding. It is read at every call.
+ *     rounding.
+ *     GLA_FWD_CHAIN=1 runs a bf16 forward of a fixed batch with time
+ *     segments (d_k 64 or 96, H a multiple of 8) as one chained-scan
+ *     launch instead of state pass, combine and output pass; it needs a
+ *     larger workspace and agrees with the default within rounding.
+ *     GLA_BWD_TAIL (a fraction in [0, 0.5], default 0.25) is the share of
+ *     each sequence's chunks whose dk and dv rows the one-launch backward
+ *     gives to the dq walk's workgroups; results are identical bit for bit
+ *     at every share.
  *   - Arguments are validated on the host before any HIP call. On an error
  *     nothing is launched and no output is touched. A launch failure returns
  *     GLA_ERR_HIP; faults inside kernels surface at the caller's next
