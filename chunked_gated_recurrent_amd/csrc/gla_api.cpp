@@ -76,8 +76,9 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Workgroups the forward should have in flight before it pays for splitting
-// sequences into time segments (two per compute unit on a 256-CU part).
+// Workgroups a call should have in flight before it pays for splitting
+// sequences into time segments (one per compute unit on a 256-CU part: the
+// matrix-core kernels hold one workgroup per CU).
 int target_workgroups() {
   const char *e = getenv("GLA_TARGET_WGS");
   if (e && *e) {
@@ -252,7 +253,8 @@ Decay make_decay(const float *d, int H) {
 }
 
 // Launch the planned forward: [planner] -> [local end states -> combine] ->
-// outputs -> [final gather].
+// outputs -> [final gather], or, for the chained scan, [flag reset] ->
+// one launch -> [final gather].
 gla_status run_forward(int dt, const HostPlan &hp, FwdArgs a, const Decay &dec,
                        void *workspace, hipStream_t s) {
   Plan p = hp.p;
@@ -322,7 +324,7 @@ size_t elem_size(int dt) { return dt == GLA_BF16 ? 2 : 4; }
 // one z slot ([item][H][dk] fp32) per item after the state slots.
 HostPlan with_zslots(HostPlan hp, int H, int dk) {
   if (hp.segmented) {
-    const size_t state_end = hp.ws_bytes;
+    [[maybe_unused]] const size_t state_end = hp.ws_bytes;  // read by the debug checks
     hp.off_zslots = align256(hp.ws_bytes);
     hp.ws_bytes = hp.off_zslots + (size_t)hp.p.max_items * H * dk * sizeof(float);
     GLA_HOST_CHECK(hp.off_zslots % 256 == 0 && hp.off_zslots >= state_end);

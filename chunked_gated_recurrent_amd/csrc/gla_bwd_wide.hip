@@ -11,9 +11,11 @@
 // (at dv 192, 125 KB in the dq pass and 140 KB in the reverse walk; 94 and
 // 109 KB at dv 128) fit only once, so
 // every chunk takes two barriers (tiles and published state ready / all
-// reads done) instead of double buffers, and the batch's parallelism comes
-// from time segments (the planner splits sequences when batch x heads
-// cannot fill the GPU).
+// reads done) instead of double buffers, and one workgroup per CU does.
+// When the batch's (sequence, head) units with two workgroups each fill
+// the GPU, both walks run in one launch (bwd_fused_wide_kernel); otherwise
+// the planner cuts sequences into time segments and the walks run one
+// after the other.
 //
 //   bwd_dq_wide_kernel   forward walk. Waves 0-3 ("dq waves", rows 16 w ..
 //                        16 w + 15 of each chunk) form dq; waves 4-7 rebuild
@@ -24,6 +26,9 @@
 //                        of the carried gradient Ch (the first half of the
 //                        column tiles on the dv waves, the second on the dk
 //                        waves), published as bf16 Ch^T every chunk.
+//   bwd_fused_wide_kernel both walks in one launch, the dq walk's
+//                        workgroups also forming the dk and dv rows of each
+//                        sequence's last chunks.
 // Outputs are written from registers: each lane stores the 4 consecutive
 // values of one row that an MFMA result tile gives it (8-byte stores).
 #include "gla_mfma.h"
@@ -49,9 +54,9 @@ constexpr bool wide_shape(int dk, int dv) {
 // dv 192: C 64, QS 112, VS 208, NCT 12, NDT 6.
 #define WIDE_CONSTS(DK_, DV_)                                                 \
   using MW = MfCfg<DV_, DK_>;                                                 \
-  constexpr int kWideDv = DV_;                                                \
-  constexpr int kWC = MW::C, kWQS = MW::QS, kWVS = MW::VS;                    \
-  constexpr int kWNCS = DV_ / 32; /* 32-deep steps over dv */                 \
+  [[maybe_unused]] constexpr int kWideDv = DV_;                               \
+  [[maybe_unused]] constexpr int kWC = MW::C, kWQS = MW::QS, kWVS = MW::VS;   \
+  [[maybe_unused]] constexpr int kWNCS = DV_ / 32; /* 32-deep steps over dv */ \
   static_assert(wide_shape(DK_, DV_), "head shape of the wide backward")
 
 // The state S^T published by the dq pass's state waves keeps its 8-column
@@ -840,9 +845,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
 // starting from dL/dS_final as the sequence's own walk does, then its dq
 // walk. Both form every carry with the same operations in the same order,
 // so the rows are those of a single walk, bit for bit, and neither
-// workgroup waits on the other; both start on the same last chunks of the
-// sequence, on the same XCD, so the q and dO rows the carry needs are
-// mostly fetched into that XCD's L2 once for the two.
+// workgroup waits on the other. Both start on the same last chunks of the
+// sequence, on the same XCD, so some of the q and dO rows the carry needs
+// come from that XCD's L2 for the second reader (the carry-only pass runs
+// about twice as fast, so the two drift apart within a few chunks).
 // (slots, cslots and pair are the separate kernels' arguments; a plan
 // without segments never reads them.)
 template <int DKT, int DV>
