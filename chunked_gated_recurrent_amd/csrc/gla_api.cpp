@@ -748,17 +748,27 @@ constexpr int kMaxDevices = 64;
 std::mutex scratch_mu;
 void *scratch_dev[kMaxDevices];  // device address of `scratch` per device, or null
 
-// This device's scratch (the current device's: the caller's stream must
-// belong to it).
-hipError_t noalloc_scratch(void **ptr) {
+// The scratch of the device that stream `s` belongs to (the current device
+// for the null stream). The first call on a device looks the array's
+// address up with that device current, switching to it for the lookup if
+// the caller's current device is another one.
+hipError_t noalloc_scratch(hipStream_t s, void **ptr) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(scratch_mu);
   if (!scratch_dev[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void *p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
     scratch_dev[dev] = p;
@@ -811,7 +821,7 @@ gla_status fwd_varlen(int dt, int N, int total_T, int H, int dk, int dv, int chu
     workspace = nullptr;
     workspace_bytes = 0;
     if (hp.ws_bytes > 0) {
-      if (noalloc_scratch(&workspace) != hipSuccess) return GLA_ERR_HIP;
+      if (noalloc_scratch((hipStream_t)stream, &workspace) != hipSuccess) return GLA_ERR_HIP;
       workspace_bytes = kNoAllocScratchBytes;
     }
   }

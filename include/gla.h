@@ -218,8 +218,9 @@ gla_status gla_decode_step_gated(gla_dtype dt, int N, int H, int dk, int dv, con
  * fixed array of GLA_NOALLOC_SCRATCH_BYTES that the library holds on each
  * GPU it runs on until the process ends. The call allocates nothing (no
  * hipMalloc, hipFree or allocating library routine); its first call on a
- * device looks up that device's array (hipGetSymbolAddress), so the
- * current device must be the one `stream` belongs to.
+ * device looks up that device's array (hipGetSymbolAddress, with that
+ * device made current for the lookup). The device is the one `stream`
+ * belongs to (the current device for the null stream).
  *   - A call whose plan needs more scratch than the array holds returns
  *     GLA_ERR_TOO_LARGE and launches nothing. At H = 16, dk = 96, dv = 192
  *     every packed batch fits (the largest plan, 7 long sequences cut into
