@@ -1,5 +1,6 @@
 // gla_bwd_wide.hip -- backward of the chunked Simple GLA forward for bf16
-// inputs with dk = 96 and dv = 192 (the Laplace 3B head), 128 or 64, one
+// inputs with dk 64, 96 or 128 and dv 64, 128 or 192 (the Laplace 3B head:
+// dk 96, dv 192; not dk 128 with dv 192, whose tiles exceed the LDS), one
 // workgroup per (work item, head) owning all value columns.
 //
 // Same gradients and chunk formulas as gla_bwd_mfma.hip (Laplace 3B /
@@ -413,8 +414,7 @@ __device__ __forceinline__ void wide_rev_role(
     const bf16 *__restrict__ dout, const float *__restrict__ ds_final,
     const float *__restrict__ cslots, bf16 *__restrict__ out, float *__restrict__ ds0,
     const Item &it, int idx, int h, int H, float scale, int rt, int w, bf16 *sQ, bf16 *sQs,
-    bf16 *sK,
-    bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow, const float *pair_add,
+    bf16 *sK, bf16 *sV, bf16 *sD, bf16 *sCt, const float *sPow, const float *pair_add,
     float pair_scale, int n_out) {
   WIDE_CONSTS(DKT, DV);
   constexpr int C = kWC, DK = DKT, QS = kWQS, VS = kWVS, QV = MW::QV, VV = MW::VV;

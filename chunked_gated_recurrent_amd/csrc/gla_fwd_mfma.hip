@@ -291,10 +291,9 @@ __global__ __launch_bounds__(256, 2) void fwd_state_kernel(
   if (tid <= M::C) sPow[tid] = pow_f64(dec.lam[h], tid);
   // backward walk: it ends on the segment's first rows, where the output
   // pass starts next
-  state_role<DVT, false, NORM, DKT, DKT == 128, true>(k, v, nullptr, nullptr, slots, it, idx,
-                                                      h, H, dv,
-                               dtile * DVT, 0, tid, __builtin_amdgcn_readfirstlane(tid >> 6),
-                               nullptr, sKs, sV, nullptr, nullptr, sPow, np);
+  state_role<DVT, false, NORM, DKT, DKT == 128, true>(
+      k, v, nullptr, nullptr, slots, it, idx, h, H, dv, dtile * DVT, 0, tid,
+      __builtin_amdgcn_readfirstlane(tid >> 6), nullptr, sKs, sV, nullptr, nullptr, sPow, np);
 }
 
 // ---------------------------------------------------------------------------

@@ -15,13 +15,23 @@
 // (a scan over segments; U_g is the segment's end state from a zero start).
 //
 // Kernels:
-//   (the bf16 dk = 96 matrix-core forward lives in gla_fwd_mfma.hip)
-//   fwd_valu   any supported shape, fp32 or bf16 inputs, fp32 arithmetic
-//              on the vector ALUs (the fp32 path and the fallback).
-//   planner    varlen: cuts packed sequences into items on the device.
-//   combine    scan of segment end states.
-//   decode     one token per sequence: streams the fp32 state from HBM once
-//              (read-modify-write), float4 per lane, readout reduced in LDS.
+//   (the bf16 matrix-core forward, d_k 64, 96 or 128, lives in
+//   gla_fwd_mfma.hip; the backward in gla_bwd_*.hip)
+//   fwd_valu    any supported shape, fp32 or bf16 inputs, fp32 arithmetic
+//               on the vector ALUs (the fp32 path and the fallback).
+//   planner     varlen: cuts packed sequences into items on the device.
+//   order       varlen: workgroup slots take items longest first (a
+//               counting sort over chunk counts).
+//   combine     scan of segment end states; rcombine and bicombine the
+//               backward's reverse scan of carried gradients and both scans
+//               in one launch.
+//   final_gather, state_fill   a sequence's final state out of its last
+//               segment's slot; S_final = S0 for empty sequences.
+//   decode      one token per sequence: streams the fp32 state from HBM once
+//               (read-modify-write), float4 per lane, readout reduced in LDS;
+//               with a slot table for the state pool.
+//   zero_i32    clears the chained scan's flags (a fill kernel, so a graph
+//               capture of the call holds no memset node).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
