@@ -109,13 +109,13 @@ def test_chain_many_segments_and_the_cap():
     three launches."""
     for T, chained in ((64 * 2 * 200, True), (64 * 2 * 300, False)):
         x = W.prefill_inputs(915, 1, T, 8, 96, 192, "bf16", 0.1, W.geometric_decays(8))
-        ref = oracle_fixed(x, heads=[0, 7])
+        ref = oracle_fixed(x)
         with env(GLA_TARGET_WGS=100000):
             need = _chain_ws(1, T, 8, 96, 192)
             plain = gla.lib().gla_chunk_fwd_workspace_bytes(1, 1, T, 8, 96, 192, 0)
             assert (need > 2 * plain) == chained, (T, need, plain)
-            o, s = _run(x)
-        _check("T %d" % T, (o[:, :, [0, 7]], s[:, [0, 7]]), ref)
+            got = _run(x)
+        _check("T %d" % T, got, ref)
 
 
 def test_chain_long_context_workload_full():

@@ -45,9 +45,8 @@ def test_short_conv_without_bias_or_window_and_laplace_size():
     x, w, _, _ = _case(810, 8, 2048, 3072, "bf16", False, False)
     y, wo = gla.short_conv_fwd(dev(x), _t(w))
     torch.cuda.synchronize()
-    sl = np.s_[:, ::97]                    # every 97th token of every channel
-    ry, rwo = O.short_conv(x, w)
-    assert rel_err(host(y)[sl], ry[sl]) <= TOL["bf16"]
+    ry, rwo = O.short_conv(x, w)          # every token of every channel
+    assert rel_err(host(y), ry) <= TOL["bf16"]
     np.testing.assert_array_equal(host(wo), rwo)
 
 
