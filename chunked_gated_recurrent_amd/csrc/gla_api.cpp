@@ -90,16 +90,20 @@ int target_workgroups() {
 
 // Share of every sequence's chunks (in 1/65536) whose dk and dv rows the
 // fused backward gives to the dq walk's workgroup when both walks fit one
-// round of the CUs: a chunk of the reverse walk costs about 1.45 times one
-// of the dq walk, so a quarter of the reverse work moves over to even out
-// the two. GLA_BWD_TAIL (a fraction in [0, 0.5]) overrides it.
-int bwd_tail_q16() {
+// round of the CUs. A chunk of the reverse walk costs about 1.45 times one
+// of the dq walk, and the reverse workgroup still carries the gradient
+// through the chunks it gives away, so the split that evens out the two
+// was measured per d_k (B8 T2048 H16, us per call at shares 1/4 and 3/16):
+// d_k 64 at 1/4 (d_v 192: 154 against 162), d_k 96 and 128 at 3/16 (d_k
+// 96, d_v 192: 179 against 184; d_k 128, d_v 128: 167 against 176).
+// GLA_BWD_TAIL (a fraction in [0, 0.5]) overrides it.
+int bwd_tail_q16(int dk) {
   const char *e = getenv("GLA_BWD_TAIL");
   if (e && *e) {
     const double f = strtod(e, nullptr);
     if (f >= 0.0 && f <= 0.5) return (int)(f * 65536.0 + 0.5);
   }
-  return 16384;
+  return dk <= 64 ? 16384 : 12288;
 }
 
 struct HostPlan {
@@ -474,7 +478,7 @@ gla_status run_backward(int dt, const BwdPlan &bp, BwdArgs a, const Decay &dec,
     // chunks (B32 T2048 H16: 742 us with it, 699 us without)
     const bool one_round = 2LL * p.max_items * a.H <= target_workgroups();
     e = launch_bwd_wide(p, a, dec, pair ? 1 : 0, !hp.segmented,
-                        one_round ? bwd_tail_q16() : 0, s);
+                        one_round ? bwd_tail_q16(a.dk_dim) : 0, s);
   } else {
     e = hp.fast ? launch_bwd_mfma(bp.dvt, p, a, dec, s) : launch_bwd_valu(dt, p, a, dec, s);
   }

@@ -67,6 +67,12 @@ constexpr bool wide_shape(int dk, int dv) {
 // conflicts of the publish (16 rows written at one column offset).
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ (r & 8); }
 
+// A compile-time switch passed to generic lambdas (`if constexpr` on it).
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 // One tile load pattern: `n` 16-byte vectors per role thread over a chunk
 // tile of `per_row` vectors per row.
 template <int N>
@@ -440,26 +446,31 @@ __device__ __forceinline__ void wide_rev_role(
   const int drow0 = DV_ROLE ? 0 : 32;
   auto rows_of = [&](int ch) { return ch < 0 ? 0 : chunk_rows(it, ch); };
 
-  // chunks from n_out on only carry the gradient: their k and v tiles are
-  // not needed, and an empty descriptor turns those loads into zeros that
-  // cost no memory traffic (a branch around them instead would make every
-  // later wait on the loads assume they were skipped, and wait for the
-  // next chunk's loads too)
-  auto load = [&](int ch, u32x4(&r)[NL]) {
+  // A chunk from n_out on only carries the gradient, which needs its q and
+  // dO alone: `kv` false leaves out the k and v tiles (their loads and LDS
+  // stores; the slots of r they would fill stay unused). Which chunks get
+  // which form is fixed by the straight-line code around each call, so the
+  // compiler's waits on the loads stay exact (a branch around loads makes
+  // every later wait assume they were skipped and wait for newer loads too).
+  // A k or v load of a chunk at or past n_out gets an empty descriptor and
+  // reads zeros without memory traffic.
+  auto load_kv = [&](auto kv, int ch, u32x4(&r)[NL]) {
     const unsigned L = (unsigned)rows_of(ch);
     const unsigned Lkv = ch < n_out ? L : 0u;
     const long long tb = (long long)it.t0 + (long long)(ch < 0 ? 0 : ch) * C;
     const __amdgpu_buffer_rsrc_t bd = buf_rsrc(dout + (tb * H + h) * kWideDv, L * rowVb);
     if (DV_ROLE) {
       const __amdgpu_buffer_rsrc_t bq = buf_rsrc(q + (tb * H + h) * DK, L * rowKb);
-      const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, Lkv * rowKb);
 #pragma unroll
       for (int m = 0; m < QV; ++m)
         r[m] = __builtin_amdgcn_raw_buffer_load_b128(bq, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
+      if constexpr (decltype(kv)::value) {
+        const __amdgpu_buffer_rsrc_t bk = buf_rsrc(k + (tb * H + h) * DK, Lkv * rowKb);
 #pragma unroll
-      for (int m = 0; m < QV; ++m)
-        r[QV + m] = __builtin_amdgcn_raw_buffer_load_b128(bk, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
-    } else {
+        for (int m = 0; m < QV; ++m)
+          r[QV + m] = __builtin_amdgcn_raw_buffer_load_b128(bk, ia.row[m] * rowKb + ia.col[m] * 16, 0, 0);
+      }
+    } else if constexpr (decltype(kv)::value) {
       const __amdgpu_buffer_rsrc_t bv = buf_rsrc(v + (tb * H + h) * kWideDv, Lkv * rowVb);
 #pragma unroll
       for (int m = 0; m < VV; ++m)
@@ -470,13 +481,16 @@ __device__ __forceinline__ void wide_rev_role(
       r[NL - ND + m] = __builtin_amdgcn_raw_buffer_load_b128(
           bd, (drow0 + idh.row[m]) * rowVb + idh.col[m] * 16, 0, 0);
   };
+  auto load = [&](int ch, u32x4(&r)[NL]) { load_kv(Flag<true>{}, ch, r); };
   float fqr[NA];  // dv role: scale * lambda^(t+1) of the q rows this thread stores
-  auto store = [&](const u32x4(&r)[NL]) {
+  auto store_kv = [&](auto kv, const u32x4(&r)[NL]) {
     if (DV_ROLE) {
 #pragma unroll
       for (int m = 0; m < QV; ++m) {
-        *reinterpret_cast<u32x4 *>(sQ + ia.row[m] * QS + 8 * ia.col[m]) = r[m];
-        *reinterpret_cast<u32x4 *>(sK + ia.row[m] * QS + 8 * ia.col[m]) = r[QV + m];
+        if constexpr (decltype(kv)::value) {
+          *reinterpret_cast<u32x4 *>(sQ + ia.row[m] * QS + 8 * ia.col[m]) = r[m];
+          *reinterpret_cast<u32x4 *>(sK + ia.row[m] * QS + 8 * ia.col[m]) = r[QV + m];
+        }
         // the carry's decay-scaled copy of q, made once per chunk
         const bf16x8 qv = __builtin_bit_cast(bf16x8, r[m]);
         bf16x8 qs;
@@ -484,7 +498,7 @@ __device__ __forceinline__ void wide_rev_role(
         for (int e = 0; e < 8; ++e) qs[e] = (bf16)((float)qv[e] * fqr[m]);
         *reinterpret_cast<bf16x8 *>(sQs + ia.row[m] * QS + 8 * ia.col[m]) = qs;
       }
-    } else {
+    } else if constexpr (decltype(kv)::value) {
 #pragma unroll
       for (int m = 0; m < VV; ++m)
         *reinterpret_cast<u32x4 *>(sV + ia.row[m] * VS + 8 * ia.col[m]) = r[m];
@@ -493,6 +507,7 @@ __device__ __forceinline__ void wide_rev_role(
     for (int m = 0; m < ND; ++m)
       *reinterpret_cast<u32x4 *>(sD + (drow0 + idh.row[m]) * VS + 8 * idh.col[m]) = r[NL - ND + m];
   };
+  auto store = [&](const u32x4(&r)[NL]) { store_kv(Flag<true>{}, r); };
 
   // this wave's RB x CB tiles of the carried gradient Ch: d tiles dt0..,
   // column tiles ct0.. (the first half on the dv role, the second half on
@@ -550,8 +565,15 @@ __device__ __forceinline__ void wide_rev_role(
     }
 #pragma unroll
   for (int m = 0; m < NA; ++m) fqr[m] = DV_ROLE ? scale * sPow[ia.row[m] + 1] : 0.f;
-  store(ra);
-  publish();
+  // carry-only chunks: the last nc of the item (an even count); Ch^T is
+  // read only by full chunks, so it is published before the first of them
+  const int nc = nch - n_out;
+  if (nc > 0) {
+    store_kv(Flag<false>{}, ra);
+  } else {
+    store(ra);
+    publish();
+  }
 
   // Ch <- lambda^L Ch + scale sum_t lambda^(t+1) q_t^T dO_t (this wave's
   // tiles) over the L rows of the chunk in LDS
@@ -706,21 +728,33 @@ __device__ __forceinline__ void wide_rev_role(
     store(rx);
     publish();
   };
-  // chunks past n_out only carry the gradient back (their dk and dv rows
-  // are formed elsewhere): the same update of Ch, nothing else
-  auto carry_body = [&](int ch, u32x4(&rn)[NL], const u32x4(&rx)[NL]) {
+  // chunks from n_out on only carry the gradient back (their dk and dv rows
+  // are formed elsewhere): the same update of Ch, nothing else. `kv`: the
+  // chunk two ahead (whose loads this one issues) is a full one; `first`:
+  // the next chunk is the first full one (full tiles and Ch^T stored)
+  auto carry_body = [&](auto kv, auto first, int ch, u32x4(&rn)[NL], const u32x4(&rx)[NL]) {
     __syncthreads();  // A: chunk ch is in LDS
-    load(ch - 2, rn);
+    load_kv(kv, ch - 2, rn);
     advance(rows_of(ch));
     __syncthreads();  // B: every read of chunk ch is done
-    store(rx);
-    publish();
+    if constexpr (decltype(first)::value) {
+      store(rx);
+      publish();
+    } else {
+      store_kv(Flag<false>{}, rx);
+    }
   };
-  // nch - n_out is even, so both loops keep the two register stages in turn
+  // nc is even, so both loops keep the two register stages in turn; the
+  // last carry pair issues the loads of the first two full chunks
   int p = 0;
-  for (; p < nch - n_out; p += 2) {
-    carry_body(nch - 1 - p, ra, rb);
-    carry_body(nch - 2 - p, rb, ra);
+  for (; p + 2 < nc; p += 2) {
+    carry_body(Flag<false>{}, Flag<false>{}, nch - 1 - p, ra, rb);
+    carry_body(Flag<false>{}, Flag<false>{}, nch - 2 - p, rb, ra);
+  }
+  if (p < nc) {
+    carry_body(Flag<true>{}, Flag<false>{}, nch - 1 - p, ra, rb);
+    carry_body(Flag<true>{}, Flag<true>{}, nch - 2 - p, rb, ra);
+    p += 2;
   }
   for (; p < nch; p += 2) {  // a chunk before the first is all zeros
     body(nch - 1 - p, ra, rb);
@@ -847,8 +881,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_wide_kernel(
 // so the rows are those of a single walk, bit for bit, and neither
 // workgroup waits on the other. Both start on the same last chunks of the
 // sequence, on the same XCD, so some of the q and dO rows the carry needs
-// come from that XCD's L2 for the second reader (the carry-only pass runs
-// about twice as fast, so the two drift apart within a few chunks).
+// come from that XCD's L2 for the second reader (the carry-only pass,
+// which loads and stores only q and dO, runs several times as fast, so the
+// two drift apart within a few chunks).
 // (slots, cslots and pair are the separate kernels' arguments; a plan
 // without segments never reads them.)
 template <int DKT, int DV>

@@ -53,10 +53,10 @@
  *     segments (d_k 64 or 96, H a multiple of 8) as one chained-scan
  *     launch instead of state pass, combine and output pass; it needs a
  *     larger workspace and agrees with the default within rounding.
- *     GLA_BWD_TAIL (a fraction in [0, 0.5], default 0.25) is the share of
- *     each sequence's chunks whose dk and dv rows the one-launch backward
- *     gives to the dq walk's workgroups; results are identical bit for bit
- *     at every share.
+ *     GLA_BWD_TAIL (a fraction in [0, 0.5]; default 0.25 at dk 64, 0.1875
+ *     otherwise) is the share of each sequence's chunks whose dk and dv
+ *     rows the one-launch backward gives to the dq walk's workgroups;
+ *     results are identical bit for bit at every share.
  *   - Arguments are validated on the host before any HIP call. On an error
  *     nothing is launched and no output is touched. A launch failure returns
  *     GLA_ERR_HIP; faults inside kernels surface at the caller's next

@@ -104,7 +104,7 @@ def test_backward_tail_share_changes_no_bit(T, dv):
     assert gla.lib().gla_chunk_bwd_workspace_bytes(1, 8, T, 16, 96, dv, 0) == 0
     with env(GLA_BWD_TAIL="0"):
         base = _run(x, do, dsf)
-    for share in ("0.25", "0.5"):
+    for share in ("0.1875", "0.25", "0.5"):
         with env(GLA_BWD_TAIL=share):
             got = _run(x, do, dsf)
         for n, u, w in zip(("dq", "dk", "dv", "dS0"), base, got):
